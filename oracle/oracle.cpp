@@ -1,0 +1,429 @@
+// Oracle for the stateful causal short convolution.
+//
+// TEST INFRASTRUCTURE ONLY. This file is a plain, slow CPU implementation of
+// what the GPU path computes, written from the defining pages. Only the test
+// suite, the smoke check and the benchmark's CPU-baseline leg load it; the
+// product library never links, loads or calls it, and it shares no code,
+// header, table or helper with the GPU sources.
+//
+// Sources (cited by page title and section):
+//  * "vllm.model_executor.models.zaya", class ZayaCCA: the layer's two Conv1d
+//    modules (depthwise, then grouped), `project` (residual mix, value layout)
+//    and `_mix_with_state` (request resolution, history gather with the
+//    has-state mask, delayed value shift, history write-back).
+//  * "vllm.model_executor.layers.mamba.ops.cpu.gdn_attention": decode and
+//    varlen prefill conv calls (`_spec_aware_nonspec`), bias + SiLU, the
+//    (num_slots, dim, state_len) state view (`_conv_buffer_view`), the
+//    per-sequence conv over [prior, x] in `_spec_forward`.
+//  * "vllm.models.qwen4_exp.nvidia.ple_layer", Qwen4ExpPLELayer: dilated
+//    conv (state length (kernel-1)*dilation, Conv1d with padding and
+//    dilation), prefill checkpoints ("the conv window ending at a checkpoint
+//    is a copy of its last inputs"; offsets are multiples of the grid).
+//
+// Arithmetic: every convolution output is accumulated in double, bias first,
+// then taps in order, and rounded once to the output type (round to nearest,
+// ties to even). The one exception is the CCA depthwise intermediate, which the
+// pages materialise in the model dtype before the grouped conv; its pre-rounding
+// value is taken in fp32 (fmaf chain, bias first, taps in order), the kernel's
+// precision, so that both sides round the same number.
+//
+// Parity pins: every function here is pinned by the CPU tests (zero-state vs.
+// a library convolution, a dense Toeplitz formulation, chunked == one-shot
+// state carry, checkpoint == one-shot prefix state, tiny brute force, CCA vs.
+// library depthwise+grouped convolutions and its special cases).
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <thread>
+#include <vector>
+
+namespace {
+
+enum Dtype { F32 = 0, BF16 = 1, F64 = 2 };
+
+double bf16_to_double(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  std::memcpy(&f, &u, 4);
+  return (double)f;
+}
+
+// One round-to-nearest-even from double to bfloat16 (8 significant bits,
+// exponent range of fp32). The value is scaled by a power of two so that the
+// bf16 spacing becomes 1, rounded with nearbyint (ties to even under the
+// default rounding mode), and scaled back; all steps but the rounding are exact.
+uint16_t double_to_bf16(double v) {
+  if (std::isnan(v)) return 0x7FC0;
+  double a = std::fabs(v);
+  uint16_t sign = std::signbit(v) ? 0x8000 : 0;
+  if (a == 0.0) return sign;
+  if (std::isinf(a)) return sign | 0x7F80;
+  int e;
+  std::frexp(a, &e);            // a in [2^(e-1), 2^e)
+  int pe = e - 8;               // spacing of 8-bit significands there
+  if (pe < -133) pe = -133;     // subnormal spacing
+  double q = std::ldexp(1.0, pe);
+  double r = std::nearbyint(a / q) * q;
+  if (r >= std::ldexp(1.0, 128)) return sign | 0x7F80;   // overflow -> inf
+  float f = (float)r;           // exact: r has <= 8 significant bits
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  return sign | (uint16_t)(u >> 16);
+}
+
+double ld(const void* p, int dt, int64_t i) {
+  switch (dt) {
+    case F32: return (double)((const float*)p)[i];
+    case BF16: return bf16_to_double(((const uint16_t*)p)[i]);
+    default: return ((const double*)p)[i];
+  }
+}
+
+// Stores one value; for a value that is already representable in `dt` (a state
+// copy) this is an exact copy.
+void st(void* p, int dt, int64_t i, double v) {
+  switch (dt) {
+    case F32: ((float*)p)[i] = (float)v; break;   // C conversion: nearest-even
+    case BF16: ((uint16_t*)p)[i] = double_to_bf16(v); break;
+    default: ((double*)p)[i] = v; break;
+  }
+}
+
+bool dtype_ok(int dt) { return dt == F32 || dt == BF16 || dt == F64; }
+
+// A resolved request: token rows [start, start+len), its state slot, and
+// whether it continues from saved history.
+struct Req {
+  int64_t start, len;
+  int32_t slot;
+  int has_state;
+};
+
+// Request resolution ("_mix_with_state" builds slots/starts/lens/has-state
+// with decodes first, then prefills from query_start_loc; the GDN and PLE
+// pages split the batch the same way: decode rows first, prefill rows after).
+// Decode requests own q rows each (q = 1 for plain decode; the GDN page's
+// multi-token update views x as (B, q, dim)).
+std::vector<Req> resolve(int32_t num_decodes, int32_t q, const int32_t* dslots,
+                         int64_t dstride, const uint8_t* dh, int32_t num_prefills,
+                         const int32_t* qsl_p, const int32_t* pslots,
+                         int64_t pstride, const uint8_t* ph) {
+  std::vector<Req> rs;
+  for (int32_t i = 0; i < num_decodes; ++i)
+    rs.push_back({(int64_t)i * q, (int64_t)q, dslots[i * dstride],
+                  dh ? (int)(dh[i] != 0) : 1});
+  int64_t base = (int64_t)num_decodes * q;
+  for (int32_t r = 0; r < num_prefills; ++r)
+    rs.push_back({base + qsl_p[r], (int64_t)qsl_p[r + 1] - qsl_p[r],
+                  pslots[r * pstride], ph ? (int)(ph[r] != 0) : 1});
+  return rs;
+}
+
+template <class F>
+void parallel_for(int n, int nthreads, F f) {
+  if (nthreads <= 1 || n <= 1) {
+    f(0, n);
+    return;
+  }
+  if (nthreads > n) nthreads = n;
+  std::vector<std::thread> th;
+  for (int i = 0; i < nthreads; ++i) {
+    int a = (int)((int64_t)n * i / nthreads), b = (int)((int64_t)n * (i + 1) / nthreads);
+    th.emplace_back([=] { f(a, b); });
+  }
+  for (auto& t : th) t.join();
+}
+
+struct ConvArgs {
+  int32_t C, K, d, act, io, odt;
+  const void* x;
+  int64_t x_rs;
+  void* out;
+  int64_t out_rs;
+  double* absum;
+  const void* w;
+  const void* bias;
+  void* pool;
+  int32_t num_slots;
+  int32_t ckpt_grid;
+  const int32_t* cu_ckpt;
+  const int32_t* ckpt_slots;
+  int32_t first_prefill;     // index in the request list of prefill 0
+  const uint8_t* row_mask;
+};
+
+// Depthwise causal conv of one channel range over every request.
+//
+// For request r and channel c, ext is the request's tokens extended on the left
+// by its saved history (H = (K-1)*d raw inputs, oldest first), or by zeros when
+// it has no initial state. Output t is the cross-correlation
+//   z = b_c + sum_k w[c,k] * ext[H + t - (K-1-k)*d],
+// (w[c,K-1] multiplies the current token), then SiLU or identity. The new
+// history is the last H entries of ext; a checkpoint at offset p (a multiple of
+// the grid, p <= len) receives ext[p .. p+H), the inputs just before p.
+void conv_channels(const ConvArgs& a, const std::vector<Req>& reqs, int c0, int c1) {
+  const int H = (a.K - 1) * a.d;
+  std::vector<double> ext;
+  for (size_t ri = 0; ri < reqs.size(); ++ri) {
+    const Req& r = reqs[ri];
+    if (r.len <= 0) continue;   // a zero-length request has no rows; slot untouched
+    const bool valid = r.slot >= 0 && r.slot < a.num_slots;
+    for (int c = c0; c < c1; ++c) {
+      ext.assign((size_t)(H + r.len), 0.0);
+      for (int u = 0; u < H; ++u)
+        ext[u] = (r.has_state && valid)
+                     ? ld(a.pool, a.io, ((int64_t)r.slot * a.C + c) * H + u)
+                     : 0.0;
+      for (int64_t t = 0; t < r.len; ++t)
+        ext[H + t] = ld(a.x, a.io, (r.start + t) * a.x_rs + c);
+      const double b = a.bias ? ld(a.bias, a.io, c) : 0.0;
+      for (int64_t t = 0; t < r.len; ++t) {
+        const int64_t row = r.start + t;
+        if (a.row_mask && !a.row_mask[row]) continue;
+        double z = b, A = std::fabs(b);
+        for (int k = 0; k < a.K; ++k) {
+          double term = ld(a.w, a.io, (int64_t)c * a.K + k) *
+                        ext[H + t - (int64_t)(a.K - 1 - k) * a.d];
+          z += term;
+          A += std::fabs(term);
+        }
+        double y = a.act ? z / (1.0 + std::exp(-z)) : z;
+        st(a.out, a.odt, row * a.out_rs + c, y);
+        if (a.absum) a.absum[row * a.C + c] = A;
+      }
+      if (valid)
+        for (int j = 0; j < H; ++j)
+          st(a.pool, a.io, ((int64_t)r.slot * a.C + c) * H + j, ext[r.len + j]);
+      if (a.ckpt_grid > 0 && (int)ri >= a.first_prefill && a.cu_ckpt) {
+        const int pr = (int)ri - a.first_prefill;
+        const int32_t cnt = a.cu_ckpt[pr + 1] - a.cu_ckpt[pr];
+        for (int32_t m = 1; m <= cnt; ++m) {
+          const int64_t p = (int64_t)m * a.ckpt_grid;
+          if (p > r.len) break;
+          const int32_t dst = a.ckpt_slots[a.cu_ckpt[pr] + m - 1];
+          if (dst < 0 || dst >= a.num_slots) continue;
+          for (int j = 0; j < H; ++j)
+            st(a.pool, a.io, ((int64_t)dst * a.C + c) * H + j, ext[p + j]);
+        }
+      }
+    }
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+int oracle_abi_version(void) { return 1; }
+
+// Exposed for the rounding pins.
+uint16_t oracle_double_to_bf16(double v) { return double_to_bf16(v); }
+
+// Depthwise stateful causal conv over one batch (decode rows, then prefills).
+// x, w, bias and pool share io_dtype; out is written in out_dtype (F64 allowed
+// so that pins compare unrounded sums). pool is (num_slots, C, H), H=(K-1)*d.
+// absum (nullable, (T, C) doubles) receives |b| + sum_k |w*x| per output.
+// row_mask (nullable, T bytes): rows with mask 0 are not written.
+int oracle_conv(int32_t C, int32_t K, int32_t d, int32_t act, int32_t io_dtype,
+                int32_t out_dtype, const void* x, int64_t x_rs, void* out,
+                int64_t out_rs, double* absum, const void* w, const void* bias,
+                void* pool, int32_t num_slots, int32_t num_decodes, int32_t q,
+                const int32_t* decode_slots, int64_t decode_slot_stride,
+                const uint8_t* decode_h, int32_t num_prefills,
+                const int32_t* qsl_p, const int32_t* prefill_slots,
+                int64_t prefill_slot_stride, const uint8_t* prefill_h,
+                int32_t ckpt_grid, const int32_t* cu_ckpt,
+                const int32_t* ckpt_slots, const uint8_t* row_mask,
+                int32_t nthreads) {
+  if (C <= 0 || K <= 0 || d <= 0 || q < 0 || num_decodes < 0 || num_prefills < 0)
+    return -2;
+  if (!dtype_ok(io_dtype) || !dtype_ok(out_dtype)) return -3;
+  std::vector<Req> reqs =
+      resolve(num_decodes, q, decode_slots, decode_slot_stride, decode_h,
+              num_prefills, qsl_p, prefill_slots, prefill_slot_stride, prefill_h);
+  ConvArgs a{C, K, d, act, io_dtype, out_dtype, x, x_rs, out, out_rs, absum, w,
+             bias, pool, num_slots, ckpt_grid, cu_ckpt, ckpt_slots, num_decodes,
+             row_mask};
+  parallel_for(C, nthreads, [&](int c0, int c1) { conv_channels(a, reqs, c0, c1); });
+  return 0;
+}
+
+// CCA q/k conv with delayed value (ZayaCCA.project + _mix_with_state).
+//
+// Channels: raw qk = [q (nq*hd), k (nkv*hd)], C = (nq+nkv)*hd; history
+// n = t0 + t1 - 2 raw inputs per channel. Per request and channel, ext is the
+// raw input extended by the history (zeros without initial state).
+//   dw(c,u)  = b1_c + sum_{a<t0} w1[c,a] * ext[c][u-(t0-1)+a]
+//              (dw_mode 1: fp32 fmaf chain then rounded to io dtype;
+//               dw_mode 0: exact double, not rounded)
+//   yg(o,t)  = b2_o + sum_{j<hd} sum_{b<t1} W2[o,j,b] * dw(g*hd+j, n+t-(t1-1)+b),
+//              g = o / hd  (grouped conv weight (C, hd, t1))
+//   qres[h]  = 0.5 * (q[h] + k[h / G]),  G = nq / nkv      (per head, per dim)
+//   kres[g]  = mean_{i<G} qres[g*G + i]
+//   out row  = [yg_q + qres | yg_k + kres | v_cur | dprev]
+//   dprev(t) = v_del[row-1] for t >= 1 in the request, else the saved delayed
+//              value (has state) or delayed_init (NULL = zeros).
+// State: conv_state[slot][c][j] = ext[c][len + j] (j < n);
+//        delayed_state[slot] = v_del[last row of the request].
+int oracle_cca(int32_t nq, int32_t nkv, int32_t hd, int32_t t0, int32_t t1,
+               int32_t io_dtype, int32_t out_dtype, int32_t dw_mode,
+               const void* qp, int64_t q_rs, const void* kp, int64_t k_rs,
+               const void* vcur, int64_t vc_rs, const void* vdel, int64_t vd_rs,
+               void* out, int64_t out_rs, double* absum, const void* w_dw,
+               const void* b_dw, const void* w_gr, const void* b_gr,
+               const void* delayed_init, void* conv_state, void* delayed_state,
+               int32_t num_slots, int32_t num_decodes, const int32_t* decode_slots,
+               int64_t dstride, int32_t num_prefills, const int32_t* qsl_p,
+               const int32_t* prefill_slots, int64_t pstride,
+               const uint8_t* prefill_h, const uint8_t* row_mask,
+               int32_t nthreads) {
+  if (nq <= 0 || nkv <= 0 || hd <= 0 || t0 <= 0 || t1 <= 0 || nq % nkv) return -2;
+  if (!dtype_ok(io_dtype) || !dtype_ok(out_dtype)) return -3;
+  const int C = (nq + nkv) * hd, n = t0 + t1 - 2, G = nq / nkv;
+  const int qdim = nq * hd, vd = nkv * hd / 2, W = (nq + 2 * nkv) * hd;
+  const int ngroups = nq + nkv;
+  std::vector<Req> reqs = resolve(num_decodes, 1, decode_slots, dstride, nullptr,
+                                  num_prefills, qsl_p, prefill_slots, pstride,
+                                  prefill_h);
+
+  auto raw = [&](int64_t row, int c) -> double {
+    return c < qdim ? ld(qp, io_dtype, row * q_rs + c)
+                    : ld(kp, io_dtype, row * k_rs + (c - qdim));
+  };
+
+  // Conv part, one group (hd dw channels in, hd conv channels out) at a time.
+  auto groups = [&](int g0, int g1) {
+    std::vector<double> ext, dw;
+    for (const Req& r : reqs) {
+      if (r.len <= 0) continue;
+      const bool valid = r.slot >= 0 && r.slot < num_slots;
+      const int64_t E = n + r.len;
+      for (int g = g0; g < g1; ++g) {
+        // ext and dw for the group's input channels, indexed [j][u]
+        ext.assign((size_t)hd * E, 0.0);
+        dw.assign((size_t)hd * E, 0.0);
+        for (int j = 0; j < hd; ++j) {
+          const int c = g * hd + j;
+          double* e = &ext[(size_t)j * E];
+          for (int u = 0; u < n; ++u)
+            e[u] = (r.has_state && valid)
+                       ? ld(conv_state, io_dtype, ((int64_t)r.slot * C + c) * n + u)
+                       : 0.0;
+          for (int64_t t = 0; t < r.len; ++t) e[n + t] = raw(r.start + t, c);
+          for (int64_t u = t0 - 1; u < E; ++u) {
+            double v;
+            if (dw_mode == 1) {
+              float acc = (float)ld(b_dw, io_dtype, c);
+              for (int a = 0; a < t0; ++a)
+                acc = std::fmaf((float)ld(w_dw, io_dtype, (int64_t)c * t0 + a),
+                                (float)e[u - (t0 - 1) + a], acc);
+              // materialised in the io dtype (round from the fp32 value)
+              if (io_dtype == BF16) v = bf16_to_double(double_to_bf16(acc));
+              else v = (double)acc;
+            } else {
+              v = ld(b_dw, io_dtype, c);
+              for (int a = 0; a < t0; ++a)
+                v += ld(w_dw, io_dtype, (int64_t)c * t0 + a) * e[u - (t0 - 1) + a];
+            }
+            dw[(size_t)j * E + u] = v;
+          }
+        }
+        for (int64_t t = 0; t < r.len; ++t) {
+          const int64_t row = r.start + t, u = n + t;
+          if (row_mask && !row_mask[row]) continue;
+          for (int oo = 0; oo < hd; ++oo) {
+            const int o = g * hd + oo;
+            double y = ld(b_gr, io_dtype, o), A = std::fabs(y);
+            for (int j = 0; j < hd; ++j)
+              for (int b = 0; b < t1; ++b) {
+                double term = ld(w_gr, io_dtype, ((int64_t)o * hd + j) * t1 + b) *
+                              dw[(size_t)j * E + u - (t1 - 1) + b];
+                y += term;
+                A += std::fabs(term);
+              }
+            double res;
+            if (o < qdim) {   // query head h = g, paired key head h / G
+              const int e = oo, h = g;
+              const double qv = raw(row, h * hd + e), kv = raw(row, qdim + (h / G) * hd + e);
+              res = 0.5 * (qv + kv);
+              A += 0.5 * (std::fabs(qv) + std::fabs(kv));
+            } else {          // key head kg: mean of its G query residuals
+              const int kg = g - nq, e = oo;
+              const double kv = raw(row, qdim + kg * hd + e);
+              double s = 0.0;
+              for (int i = 0; i < G; ++i) {
+                const double qv = raw(row, (kg * G + i) * hd + e);
+                s += 0.5 * (qv + kv);
+                A += 0.5 * (std::fabs(qv) + std::fabs(kv)) / G;
+              }
+              res = s / G;
+            }
+            st(out, out_dtype, row * out_rs + o, y + res);
+            if (absum) absum[row * W + o] = A;
+          }
+        }
+        if (valid)
+          for (int j = 0; j < hd; ++j)
+            for (int jj = 0; jj < n; ++jj)
+              st(conv_state, io_dtype, ((int64_t)r.slot * C + g * hd + j) * n + jj,
+                 ext[(size_t)j * E + r.len + jj]);
+      }
+    }
+  };
+  parallel_for(ngroups, nthreads, groups);
+
+  // Value part: current value copied, delayed value shifted by one token.
+  for (const Req& r : reqs) {
+    if (r.len <= 0) continue;
+    const bool valid = r.slot >= 0 && r.slot < num_slots;
+    for (int64_t t = 0; t < r.len; ++t) {
+      const int64_t row = r.start + t;
+      if (row_mask && !row_mask[row]) continue;
+      for (int e = 0; e < vd; ++e) {
+        st(out, out_dtype, row * out_rs + C + e, ld(vcur, io_dtype, row * vc_rs + e));
+        double dp;
+        if (t >= 1) dp = ld(vdel, io_dtype, (row - 1) * vd_rs + e);
+        else if (r.has_state && valid) dp = ld(delayed_state, io_dtype, (int64_t)r.slot * vd + e);
+        else dp = delayed_init ? ld(delayed_init, io_dtype, e) : 0.0;
+        st(out, out_dtype, row * out_rs + C + vd + e, dp);
+        if (absum) {
+          absum[row * W + C + e] = 0.0;
+          absum[row * W + C + vd + e] = 0.0;
+        }
+      }
+    }
+    if (valid)
+      for (int e = 0; e < vd; ++e)
+        st(delayed_state, io_dtype, (int64_t)r.slot * vd + e,
+           ld(vdel, io_dtype, (r.start + r.len - 1) * vd_rs + e));
+  }
+  return 0;
+}
+
+// Plain copies between a dense (n, row_elems) buffer and pool rows idx[i].
+// Negative or out-of-range indices are skipped.
+int oracle_state_gather(int32_t elsize, int64_t row_elems, const void* pool,
+                        int32_t num_slots, const int32_t* idx, int64_t idx_stride,
+                        int32_t n, void* dense) {
+  const int64_t rb = row_elems * elsize;
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t s = idx[i * idx_stride];
+    if (s < 0 || s >= num_slots) continue;
+    std::memcpy((char*)dense + i * rb, (const char*)pool + s * rb, (size_t)rb);
+  }
+  return 0;
+}
+
+int oracle_state_scatter(int32_t elsize, int64_t row_elems, const void* dense,
+                         const int32_t* idx, int64_t idx_stride, int32_t n,
+                         void* pool, int32_t num_slots) {
+  const int64_t rb = row_elems * elsize;
+  for (int32_t i = 0; i < n; ++i) {
+    const int32_t s = idx[i * idx_stride];
+    if (s < 0 || s >= num_slots) continue;
+    std::memcpy((char*)pool + s * rb, (const char*)dense + i * rb, (size_t)rb);
+  }
+  return 0;
+}
+
+}  // extern "C"
