@@ -401,15 +401,18 @@ int oracle_cca(int32_t nq, int32_t nkv, int32_t hd, int32_t t0, int32_t t1,
 }
 
 // Plain copies between a dense (n, row_elems) buffer and pool rows idx[i].
-// Negative or out-of-range indices are skipped.
+// Gather of an index outside [0, num_slots) yields a zero row (a padding row
+// has no history: _mix_with_state masks history by has-state); scatter skips it.
 int oracle_state_gather(int32_t elsize, int64_t row_elems, const void* pool,
                         int32_t num_slots, const int32_t* idx, int64_t idx_stride,
                         int32_t n, void* dense) {
   const int64_t rb = row_elems * elsize;
   for (int32_t i = 0; i < n; ++i) {
     const int32_t s = idx[i * idx_stride];
-    if (s < 0 || s >= num_slots) continue;
-    std::memcpy((char*)dense + i * rb, (const char*)pool + s * rb, (size_t)rb);
+    if (s < 0 || s >= num_slots)
+      std::memset((char*)dense + i * rb, 0, (size_t)rb);
+    else
+      std::memcpy((char*)dense + i * rb, (const char*)pool + s * rb, (size_t)rb);
   }
   return 0;
 }

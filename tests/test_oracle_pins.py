@@ -456,7 +456,7 @@ def test_gather_scatter_are_row_copies():
     rng = np.random.default_rng(3)
     pool = rng.integers(0, 65535, size=(10, 6, 3), dtype=np.uint16)
     idx = np.array([7, -1, 2, 9], np.int32)
-    dense = np.zeros((4, 6, 3), np.uint16)
+    dense = np.full((4, 6, 3), 0xBEEF, np.uint16)
     oracle.state_gather(pool, idx, dense)
     np.testing.assert_array_equal(dense[[0, 2, 3]], pool[[7, 2, 9]])
     np.testing.assert_array_equal(dense[1], 0)
