@@ -1,0 +1,198 @@
+/*
+ * statefulconv.h — C ABI of the MI355X (gfx950) stateful causal short
+ * convolution library (libstatefulconv.so).
+ *
+ * The operation: a per-channel (depthwise) causal conv1d over variable-length
+ * token batches, optionally dilated, with bias and SiLU, whose per-request
+ * history of the last (width-1)*dilation raw inputs lives in a slot-indexed
+ * state pool; plus the CCA variant (depthwise then per-head grouped conv, a
+ * residual mix and a one-token-delayed value).
+ *
+ * Defining passages (page title, section):
+ *  - "vllm.model_executor.layers.mamba.ops.cpu.gdn_attention":
+ *    _spec_aware_nonspec (decode conv update, then varlen prefill conv with
+ *    query_start_loc / cache_indices / has_initial_state, bias, SiLU),
+ *    _conv_buffer_view (state as (num_slots, dim, state_len)),
+ *    cpu_gdn_attention_core (zero tokens is a no-op; state_len vs width-1).
+ *  - "vllm.models.qwen4_exp.nvidia.ple_layer", Qwen4ExpPLELayer:
+ *    conv_state_len = (kernel-1)*dilation, dilated depthwise Conv1d,
+ *    _short_conv (state capacity check, weights cast to the input dtype),
+ *    _short_conv_dilated_dispatch (decode call, then prefill call, then the
+ *    prefill checkpoint export), get_kv_cache_spec (checkpoint grid >= state
+ *    length, so a checkpoint window holds inputs only).
+ *  - "vllm.model_executor.models.zaya", ZayaCCA: the two Conv1d modules,
+ *    project (residual mix, output layout) and _mix_with_state (decodes first,
+ *    then prefills; history masked by has-state; new history = last n inputs;
+ *    delayed value shifted by one token).
+ *
+ * Conventions for every entry point:
+ *  - Pointers marked (device) are device pointers; (host) are host pointers,
+ *    read during the call only. The library never allocates or frees device
+ *    memory: the caller owns every buffer.
+ *  - Calls are asynchronous on `stream` (a hipStream_t passed as void*; NULL
+ *    is the default stream). No call synchronises with the host or reads
+ *    device memory from the host, so calls may be captured in a HIP graph.
+ *  - Arguments are validated on the host before any launch; an error status
+ *    means nothing was launched. A launch failure returns SC_ERR_HIP.
+ *  - Device-side metadata is trusted but never dereferenced out of bounds:
+ *    a slot outside [0, num_slots) is a padding row (zero history, no state
+ *    read or write); token rows are clamped to [0, num_tokens).
+ *  - Documented, unchecked preconditions (checking needs a host sync):
+ *    query_start_loc is non-decreasing with first entry 0 and last entry
+ *    num_tokens; slots (and checkpoint slots) are distinct within one call;
+ *    `out` does not overlap `x` (exact aliasing is rejected).
+ *  - Zero tokens or zero requests: SC_OK, nothing launched; descriptor and
+ *    size arguments are still validated, but no pointer is required then
+ *    (empty tensors may carry NULL data pointers).
+ */
+#ifndef STATEFULCONV_H
+#define STATEFULCONV_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SC_ABI_VERSION 1
+
+typedef enum {
+  SC_OK = 0,
+  SC_ERR_NULL_ARG = -1,        /* a required pointer is NULL */
+  SC_ERR_INVALID_ARG = -2,     /* a size, stride, enum or grid is out of range */
+  SC_ERR_DTYPE = -3,           /* dtype not supported by this entry point */
+  SC_ERR_STATE_CAPACITY = -4,  /* state_len < (width-1)*dilation */
+  SC_ERR_UNSUPPORTED = -5,     /* valid but not built here (e.g. state_len > H) */
+  SC_ERR_HIP = -6              /* the HIP runtime reported a launch error */
+} sc_status;
+
+typedef enum { SC_DTYPE_F32 = 0, SC_DTYPE_BF16 = 1 } sc_dtype;
+typedef enum { SC_ACT_NONE = 0, SC_ACT_SILU = 1 } sc_activation;
+
+/* Depthwise conv descriptor (host struct, read during the call only).
+ * x, out, weight, bias and the state pool share `dtype` (the PLE layer casts
+ * its weights to the input dtype); accumulation is fp32. */
+typedef struct {
+  int32_t channels;       /* C >= 1 */
+  int32_t width;          /* K in [1, 8] */
+  int32_t dilation;       /* d >= 1 */
+  int32_t state_len;      /* S; S < (K-1)*d -> SC_ERR_STATE_CAPACITY,
+                             S > (K-1)*d (speculative rolling window) -> SC_ERR_UNSUPPORTED */
+  int32_t dtype;          /* sc_dtype */
+  int32_t activation;     /* sc_activation */
+  int64_t x_row_stride;   /* elements between token rows of x, >= C */
+  int64_t out_row_stride; /* elements between token rows of out, >= C */
+  int64_t state_indices_stride; /* >= 1; row stride of a 2-D index tensor whose
+                                   column 0 holds the slot */
+} sc_conv_desc;
+
+/* Prefill checkpoint export (optional). For prefill request r, the m-th
+ * checkpoint (m = 1 .. cu_ckpt[r+1]-cu_ckpt[r], and m*grid <= L_r) writes the
+ * state window ending at token offset p = m*grid of this chunk — the raw inputs
+ * x_r[p-H .. p) — into pool slot ckpt_slots[cu_ckpt[r] + m - 1]. */
+typedef struct {
+  int32_t grid;              /* g; 0 = no export; else g >= H required */
+  const int32_t* cu_ckpt;    /* (device) B+1 exclusive prefix of checkpoint counts */
+  const int32_t* ckpt_slots; /* (device) destination slots, flat */
+} sc_ckpt_desc;
+
+/* Varlen prefill: for request r (token rows [qsl[r], qsl[r+1]) of x), slot
+ * s = state_indices[r*stride], flag h = has_initial_state[r]:
+ *   ext = [h ? pool[s] : zeros (C x H, oldest first), x_r]
+ *   out[t, c] = act(bias[c] + sum_k weight[c, k] * ext[c, H + t - (K-1-k)*d])
+ *   pool[s] = last H entries of ext (bit-exact copy of inputs/history)
+ * A zero-length request produces nothing and leaves its slot untouched.
+ *   x                 (device) (num_tokens, C) rows of x_row_stride elements
+ *   out               (device) (num_tokens, C) rows of out_row_stride
+ *   weight            (device) (C, K) row-major
+ *   bias              (device) (C) or NULL
+ *   state_pool        (device) (num_slots, C, S) contiguous
+ *   query_start_loc   (device) int32 (batch+1)
+ *   state_indices     (device) int32, entry r at r*state_indices_stride
+ *   has_initial_state (device) uint8 (batch), required (the PLE page raises
+ *                     without it)
+ *   ckpt              (host) NULL or a checkpoint descriptor */
+sc_status sc_conv_prefill_varlen(const sc_conv_desc* desc, const void* x, void* out,
+                                 const void* weight, const void* bias,
+                                 void* state_pool, int32_t num_slots,
+                                 const int32_t* query_start_loc,
+                                 const int32_t* state_indices,
+                                 const uint8_t* has_initial_state, int32_t batch,
+                                 int64_t num_tokens, const sc_ckpt_desc* ckpt,
+                                 void* stream);
+
+/* Decode / multi-token update: `batch` requests of exactly q tokens each,
+ * request r owning rows [r*q, (r+1)*q) of x (x viewed as (batch, q, C)), all q
+ * tokens consumed. Same arithmetic and state rule as the prefill call.
+ *   has_initial_state (device) uint8 (batch) or NULL = every request continues
+ *                     its saved state (decodes always do). */
+sc_status sc_conv_update(const sc_conv_desc* desc, const void* x, void* out,
+                         const void* weight, const void* bias, void* state_pool,
+                         int32_t num_slots, const int32_t* state_indices,
+                         const uint8_t* has_initial_state, int32_t batch,
+                         int32_t q, void* stream);
+
+/* Row copies between a slot pool and a dense buffer; each row is row_bytes.
+ * gather: dense[i] = pool[idx[i*idx_stride]], or zeros when that index is
+ *         outside [0, num_slots) (a padding row has no history).
+ * scatter: pool[idx[i*idx_stride]] = dense[i]; out-of-range indices skipped.
+ *   pool, dense, idx (device); n rows; row_bytes >= 1. */
+sc_status sc_state_gather(const void* pool, int32_t num_slots, int64_t row_bytes,
+                          const int32_t* idx, int64_t idx_stride, int32_t n,
+                          void* dense, void* stream);
+sc_status sc_state_scatter(const void* dense, int64_t row_bytes,
+                           const int32_t* idx, int64_t idx_stride, int32_t n,
+                           void* pool, int32_t num_slots, void* stream);
+
+/* CCA q/k conv descriptor (host struct). bf16 only (SC_ERR_DTYPE otherwise). */
+typedef struct {
+  int32_t num_q_heads;    /* nq */
+  int32_t num_kv_heads;   /* nkv; nq % nkv == 0 */
+  int32_t head_dim;       /* hd */
+  int32_t t0;             /* depthwise kernel size */
+  int32_t t1;             /* grouped kernel size */
+  int32_t dtype;          /* SC_DTYPE_BF16 */
+  int64_t q_row_stride, k_row_stride, v_cur_row_stride, v_del_row_stride;
+  int64_t out_row_stride;
+  int64_t decode_slot_stride, prefill_slot_stride;
+} sc_cca_desc;
+
+/* CCA q/k conv with per-request state (ZayaCCA.project + _mix_with_state).
+ * Tokens: num_decodes one-token decode rows first (always continuing their
+ * state), then prefill rows with offsets prefill_qsl (rebased to 0).
+ * With C = (nq+nkv)*hd raw channels [q | k] and n = t0+t1-2:
+ *   dw   = depthwise conv (t0 taps, bias) of [history, raw], materialised in
+ *          bf16 (fp32 fused multiply-add chain, bias first, taps in order)
+ *   yg   = grouped conv (nq+nkv groups of hd, t1 taps, bias) of dw, fp32 acc.
+ *   out row = [yg_q + 0.5(q + k of the head's kv group) |
+ *              yg_k + mean over the group's q heads of that residual |
+ *              v_cur | previous token's v_del (first token: saved delayed
+ *              value if it has state, else delayed_init, NULL = zeros)]
+ *   conv_state[s] = last n raw inputs; delayed_state[s] = last v_del row.
+ *   q (T, nq*hd), k (T, nkv*hd), v_cur, v_del (T, nkv*hd/2), out
+ *   (T, (nq+2*nkv)*hd); w_dw (C, t0), b_dw (C), w_gr (C, hd, t1), b_gr (C),
+ *   delayed_init (nkv*hd/2) or NULL; conv_state (num_slots, C, n),
+ *   delayed_state (num_slots, nkv*hd/2); slot arrays int32, has-state uint8.
+ *   All (device). num_tokens must equal num_decodes + prefill_qsl[last]. */
+sc_status sc_cca_qk_conv(const sc_cca_desc* desc, const void* q, const void* k,
+                         const void* v_cur, const void* v_del, void* out,
+                         const void* w_dw, const void* b_dw, const void* w_gr,
+                         const void* b_gr, const void* delayed_init,
+                         void* conv_state, void* delayed_state, int32_t num_slots,
+                         int32_t num_decodes, const int32_t* decode_slots,
+                         int32_t num_prefills, const int32_t* prefill_qsl,
+                         const int32_t* prefill_slots,
+                         const uint8_t* prefill_has_initial_state,
+                         int64_t num_tokens, void* stream);
+
+/* Static string for a status code. */
+const char* sc_status_string(sc_status status);
+
+/* SC_ABI_VERSION of the built library. */
+int32_t sc_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* STATEFULCONV_H */

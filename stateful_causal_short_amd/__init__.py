@@ -1,0 +1,266 @@
+"""MI355X (gfx950) stateful causal short convolution.
+
+Thin Python binding of ``libstatefulconv.so`` (C ABI in
+``include/statefulconv.h``). Every function here only marshals arguments —
+device pointers, sizes, strides, the current HIP stream — and calls the
+library; every step of the computation runs in the library's HIP kernels.
+PyTorch provides device memory and streams. There is no CPU fallback: if the
+library is missing, import-time loading fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libstatefulconv.so")
+
+SC_OK = 0
+STATUS = {0: "SC_OK", -1: "SC_ERR_NULL_ARG", -2: "SC_ERR_INVALID_ARG",
+          -3: "SC_ERR_DTYPE", -4: "SC_ERR_STATE_CAPACITY",
+          -5: "SC_ERR_UNSUPPORTED", -6: "SC_ERR_HIP"}
+SC_DTYPE_F32, SC_DTYPE_BF16 = 0, 1
+SC_ACT_NONE, SC_ACT_SILU = 0, 1
+
+EXPORTS = ("sc_conv_prefill_varlen", "sc_conv_update", "sc_state_gather",
+           "sc_state_scatter", "sc_cca_qk_conv", "sc_status_string",
+           "sc_abi_version")
+
+
+class ScError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        msg = lib().sc_status_string(status).decode()
+        super().__init__(f"{fn}: {STATUS.get(status, status)} ({msg})")
+
+
+class sc_conv_desc(ctypes.Structure):
+    _fields_ = [("channels", ctypes.c_int32), ("width", ctypes.c_int32),
+                ("dilation", ctypes.c_int32), ("state_len", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("activation", ctypes.c_int32),
+                ("x_row_stride", ctypes.c_int64), ("out_row_stride", ctypes.c_int64),
+                ("state_indices_stride", ctypes.c_int64)]
+
+
+class sc_ckpt_desc(ctypes.Structure):
+    _fields_ = [("grid", ctypes.c_int32), ("cu_ckpt", ctypes.c_void_p),
+                ("ckpt_slots", ctypes.c_void_p)]
+
+
+class sc_cca_desc(ctypes.Structure):
+    _fields_ = [("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("t0", ctypes.c_int32),
+                ("t1", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("q_row_stride", ctypes.c_int64), ("k_row_stride", ctypes.c_int64),
+                ("v_cur_row_stride", ctypes.c_int64), ("v_del_row_stride", ctypes.c_int64),
+                ("out_row_stride", ctypes.c_int64), ("decode_slot_stride", ctypes.c_int64),
+                ("prefill_slot_stride", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libstatefulconv.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -c 'import __graft_entry__ as g; g.build()'` "
+                "(there is no fallback implementation)")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+        D = ctypes.POINTER(sc_conv_desc)
+        L.sc_conv_prefill_varlen.restype = I32
+        L.sc_conv_prefill_varlen.argtypes = [D, P, P, P, P, P, I32, P, P, P, I32, I64,
+                                             ctypes.POINTER(sc_ckpt_desc), P]
+        L.sc_conv_update.restype = I32
+        L.sc_conv_update.argtypes = [D, P, P, P, P, P, I32, P, P, I32, I32, P]
+        L.sc_state_gather.restype = I32
+        L.sc_state_gather.argtypes = [P, I32, I64, P, I64, I32, P, P]
+        L.sc_state_scatter.restype = I32
+        L.sc_state_scatter.argtypes = [P, I64, P, I64, I32, P, I32, P]
+        L.sc_cca_qk_conv.restype = I32
+        L.sc_cca_qk_conv.argtypes = [ctypes.POINTER(sc_cca_desc), P, P, P, P, P, P, P,
+                                     P, P, P, P, P, I32, I32, P, I32, P, P, P, I64, P]
+        L.sc_status_string.restype = ctypes.c_char_p
+        L.sc_status_string.argtypes = [I32]
+        L.sc_abi_version.restype = I32
+        L.sc_abi_version.argtypes = []
+        _lib = L
+    return _lib
+
+
+# ---------------------------------------------------------------------------
+# marshalling helpers
+# ---------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return SC_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return SC_DTYPE_F32
+    return -1
+
+
+def _rows(t, name):
+    if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
+        raise ValueError(f"{name}: expected a 2-D tensor with unit channel stride")
+    # with at most one row the row stride is never used
+    return t.stride(0) if t.shape[0] > 1 else t.shape[1]
+
+
+def _index(t, name) -> Tuple[int, int]:
+    """int32 slot indices: 1-D, or 2-D whose column 0 holds the slot."""
+    torch = _torch()
+    if t.dtype != torch.int32:
+        raise ValueError(f"{name}: expected int32")
+    if t.dim() not in (1, 2):
+        raise ValueError(f"{name}: expected a 1-D or 2-D tensor")
+    # with at most one row the stride is never used (empty tensors may report 0)
+    return t.data_ptr(), (t.stride(0) if t.shape[0] > 1 else 1)
+
+
+def _flags(t, name):
+    torch = _torch()
+    if t is None:
+        return None
+    if t.dtype not in (torch.bool, torch.uint8) or not t.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous bool/uint8 tensor")
+    return t.data_ptr()
+
+
+def _check(fn: str, status: int):
+    if status != SC_OK:
+        raise ScError(fn, status)
+
+
+def _conv_desc(x, out, weight, state_pool, dilation, activation, state_indices):
+    C = x.shape[1]
+    K = weight.shape[-1]
+    act = {"silu": SC_ACT_SILU, "none": SC_ACT_NONE, None: SC_ACT_NONE}[activation]
+    if weight.numel() != C * K or not weight.is_contiguous():
+        raise ValueError("weight: expected a contiguous (C, K) or (C, 1, K) tensor")
+    if not state_pool.is_contiguous() or state_pool.dim() != 3:
+        raise ValueError("state_pool: expected a contiguous (num_slots, C, S) tensor")
+    _, sst = _index(state_indices, "state_indices")
+    return sc_conv_desc(channels=C, width=K, dilation=dilation,
+                        state_len=state_pool.shape[2], dtype=_dtype_code(x),
+                        activation=act, x_row_stride=_rows(x, "x"),
+                        out_row_stride=_rows(out, "out"), state_indices_stride=sst)
+
+
+# ---------------------------------------------------------------------------
+# entry points (same names as the C ABI)
+# ---------------------------------------------------------------------------
+def sc_conv_prefill_varlen(x, out, weight, bias, state_pool, query_start_loc,
+                           state_indices, has_initial_state, *, dilation: int = 1,
+                           activation: Optional[str] = "silu", ckpt=None, stream=None):
+    """Varlen prefill conv; updates ``state_pool`` in place.
+
+    x, out: (num_tokens, C); weight (C, K); bias (C) or None; state_pool
+    (num_slots, C, (K-1)*dilation); query_start_loc int32 (B+1);
+    state_indices int32 (B) or (B, n) using column 0; has_initial_state
+    bool/uint8 (B); ckpt = None or (grid, cu_ckpt int32 (B+1), ckpt_slots int32).
+    """
+    desc = _conv_desc(x, out, weight, state_pool, dilation, activation, state_indices)
+    cd = None
+    if ckpt is not None:
+        grid, cu, slots = ckpt
+        cd = ctypes.byref(sc_ckpt_desc(grid=grid, cu_ckpt=_ptr(cu), ckpt_slots=_ptr(slots)))
+    st = lib().sc_conv_prefill_varlen(
+        ctypes.byref(desc), _ptr(x), _ptr(out), _ptr(weight), _ptr(bias),
+        _ptr(state_pool), state_pool.shape[0], _ptr(query_start_loc),
+        _index(state_indices, "state_indices")[0],
+        _flags(has_initial_state, "has_initial_state"),
+        query_start_loc.shape[0] - 1, x.shape[0], cd, _stream(stream))
+    _check("sc_conv_prefill_varlen", st)
+
+
+def sc_conv_update(x, out, weight, bias, state_pool, state_indices,
+                   has_initial_state=None, *, q: int = 1, dilation: int = 1,
+                   activation: Optional[str] = "silu", stream=None):
+    """Decode / multi-token update: x (B*q, C) rows, request r owns rows
+    [r*q, (r+1)*q); updates ``state_pool`` in place."""
+    if x.shape[0] % max(q, 1):
+        raise ValueError("x rows must be a multiple of q")
+    desc = _conv_desc(x, out, weight, state_pool, dilation, activation, state_indices)
+    B = x.shape[0] // q if q else 0
+    st = lib().sc_conv_update(
+        ctypes.byref(desc), _ptr(x), _ptr(out), _ptr(weight), _ptr(bias),
+        _ptr(state_pool), state_pool.shape[0], _index(state_indices, "state_indices")[0],
+        _flags(has_initial_state, "has_initial_state"), B, q, _stream(stream))
+    _check("sc_conv_update", st)
+
+
+def sc_state_gather(state_pool, idx, dense, *, stream=None):
+    """dense[i] = state_pool[idx[i]] (zeros for an index outside the pool)."""
+    row = state_pool[0].numel() * state_pool.element_size() if state_pool.shape[0] else \
+        dense[0].numel() * dense.element_size()
+    p, s = _index(idx, "idx")
+    st = lib().sc_state_gather(_ptr(state_pool), state_pool.shape[0], row, p, s,
+                               idx.shape[0], _ptr(dense), _stream(stream))
+    _check("sc_state_gather", st)
+
+
+def sc_state_scatter(dense, idx, state_pool, *, stream=None):
+    """state_pool[idx[i]] = dense[i] (indices outside the pool skipped)."""
+    row = dense[0].numel() * dense.element_size() if dense.shape[0] else 1
+    p, s = _index(idx, "idx")
+    st = lib().sc_state_scatter(_ptr(dense), row, p, s, idx.shape[0], _ptr(state_pool),
+                                state_pool.shape[0], _stream(stream))
+    _check("sc_state_scatter", st)
+
+
+def sc_cca_qk_conv(q, k, v_cur, v_del, out, w_dw, b_dw, w_gr, b_gr, delayed_init,
+                   conv_state, delayed_state, decode_slots, prefill_qsl, prefill_slots,
+                   prefill_has_initial_state, *, num_q_heads: int, num_kv_heads: int,
+                   head_dim: int, t0: int, t1: int, stream=None):
+    """CCA q/k conv with per-request state; updates both state pools in place.
+
+    Rows: len(decode_slots) one-token decodes, then prefills (prefill_qsl
+    rebased to 0). Pass decode_slots / prefill tensors as None when absent."""
+    nd = 0 if decode_slots is None else decode_slots.shape[0]
+    npf = 0 if prefill_qsl is None else prefill_qsl.shape[0] - 1
+    dp, ds = _index(decode_slots, "decode_slots") if nd else (None, 1)
+    pp, ps = _index(prefill_slots, "prefill_slots") if npf else (None, 1)
+    desc = sc_cca_desc(num_q_heads=num_q_heads, num_kv_heads=num_kv_heads,
+                       head_dim=head_dim, t0=t0, t1=t1, dtype=_dtype_code(q),
+                       q_row_stride=_rows(q, "q"), k_row_stride=_rows(k, "k"),
+                       v_cur_row_stride=_rows(v_cur, "v_cur"),
+                       v_del_row_stride=_rows(v_del, "v_del"),
+                       out_row_stride=_rows(out, "out"), decode_slot_stride=ds,
+                       prefill_slot_stride=ps)
+    for name, t in (("w_dw", w_dw), ("b_dw", b_dw), ("w_gr", w_gr), ("b_gr", b_gr),
+                    ("conv_state", conv_state), ("delayed_state", delayed_state)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name}: expected a contiguous tensor")
+    st = lib().sc_cca_qk_conv(
+        ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v_cur), _ptr(v_del), _ptr(out),
+        _ptr(w_dw), _ptr(b_dw), _ptr(w_gr), _ptr(b_gr), _ptr(delayed_init),
+        _ptr(conv_state), _ptr(delayed_state), conv_state.shape[0], nd, dp, npf,
+        _ptr(prefill_qsl), pp, _flags(prefill_has_initial_state, "prefill_has_initial_state"),
+        q.shape[0], _stream(stream))
+    _check("sc_cca_qk_conv", st)
+
+
+__all__ = ["lib", "ScError", "LIB_PATH", "EXPORTS", "sc_conv_desc", "sc_ckpt_desc",
+           "sc_cca_desc", "sc_conv_prefill_varlen", "sc_conv_update", "sc_state_gather",
+           "sc_state_scatter", "sc_cca_qk_conv"]

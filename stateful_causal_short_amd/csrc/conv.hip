@@ -1,0 +1,441 @@
+// Depthwise stateful causal conv1d kernels for gfx950 (varlen prefill and
+// decode / multi-token update), with the state gather, the state write-back
+// and the prefill checkpoint export fused into the same pass.
+//
+// Operation (GDN page "vllm.model_executor.layers.mamba.ops.cpu.gdn_attention",
+// _spec_aware_nonspec; PLE page "vllm.models.qwen4_exp.nvidia.ple_layer",
+// Qwen4ExpPLELayer): for each request, ext = [history (H = (K-1)*d raw inputs,
+// oldest first, zeros without initial state), tokens]; out[t] = act(b +
+// sum_k w[k] * ext[H + t - (K-1-k)*d]); the slot then holds the last H entries
+// of ext; a checkpoint at offset p (multiple of the grid) receives ext[p..p+H).
+//
+// Layout: x / out token-major (rows of C channels, channel-contiguous), state
+// pool (num_slots, C, H). A lane owns one 16-byte vector of channels (8 bf16 or
+// 4 fp32), so a wave reads 1 KiB contiguous per token row. A workgroup (4 waves)
+// covers 256 vectors of channels for one chunk of one request's tokens and keeps
+// the causal window in registers while it walks the chunk: every input row is
+// read once by the chunk plus an H-row halo from the previous chunk.
+//
+// State hazard: only the chunk holding a request's first tokens reads the
+// request's slot (chunks are at least H long, so later chunks take their halo
+// from x), and the same lanes write the new state after reading the old one.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace sc {
+
+// ---------------------------------------------------------------------------
+// request / chunk resolution
+// ---------------------------------------------------------------------------
+
+// Logical workgroup index from the hardware one. Workgroups are dealt to the
+// 8 XCDs round-robin; this gives each XCD a contiguous run of logical blocks,
+// so consecutive chunks of the same channels (whose halos overlap) share an L2.
+__device__ __forceinline__ int logical_block(int n_logical, int per_xcd) {
+  const int b = (int)blockIdx.x;
+  const int lb = (b % kXcds) * per_xcd + b / kXcds;
+  return lb < n_logical ? lb : -1;
+}
+
+// Chunk ids of request r are [base(r), base(r+1)) with
+// base(r) = floor(qsl[r] / chunk) + r, an upper bound on the chunks the request
+// needs that is monotone in r and computable per request. So the request owning
+// chunk id `id` is #{i in [1, B] : base(i) <= id}, counted wave-parallel.
+// Must be called by full waves (uses ballot).
+__device__ __forceinline__ int find_request(const int32_t* qsl, int B, int id, int chunk) {
+  const int lane = (int)(threadIdx.x & 63);
+  int cnt = 0;
+  for (int i0 = 1; i0 <= B; i0 += 64) {
+    const int i = i0 + lane;
+    bool p = false;
+    if (i <= B) p = (qsl[i] / chunk + i) <= id;
+    cnt += __popcll(__ballot(p));
+  }
+  return cnt;
+}
+
+struct Work {
+  int r, j, L, t0, t1;
+  int64_t start;
+  int32_t slot;
+  bool valid, h;
+};
+
+__device__ __forceinline__ bool resolve_work(const ConvArgs& a, int cid, Work& w) {
+  if (a.qsl == nullptr) {   // uniform update: batch x q rows
+    const int cpr = (a.q + a.chunk - 1) / a.chunk;
+    w.r = cid / cpr;
+    w.j = cid - w.r * cpr;
+    if (w.r >= a.batch) return false;
+    w.start = (int64_t)w.r * a.q;
+    w.L = a.q;
+  } else {
+    w.r = find_request(a.qsl, a.batch, cid, a.chunk);
+    if (w.r >= a.batch) return false;
+    const int s0 = a.qsl[w.r], s1 = a.qsl[w.r + 1];
+    if (s0 < 0) return false;
+    w.j = cid - (s0 / a.chunk + w.r);
+    w.start = s0;
+    w.L = s1 - s0;
+  }
+  if (w.j < 0 || w.L <= 0 || w.start >= a.num_tokens) return false;
+  if (w.start + w.L > a.num_tokens) w.L = (int)(a.num_tokens - w.start);
+  w.t0 = w.j * a.chunk;
+  if (w.t0 >= w.L) return false;
+  w.t1 = min(w.L, w.t0 + a.chunk);
+  w.slot = a.slots[(int64_t)w.r * a.slot_stride];
+  w.valid = w.slot >= 0 && w.slot < a.num_slots;
+  w.h = w.valid && (a.has_init ? a.has_init[w.r] != 0 : true);
+  return true;
+}
+
+// ---------------------------------------------------------------------------
+// register-window helpers (all indices compile-time after unrolling)
+// ---------------------------------------------------------------------------
+template <class E>
+__device__ __forceinline__ float widen(uint32_t b) {
+  if constexpr (E::VEC == 8) return __uint_as_float(b << 16);
+  else return __uint_as_float(b);
+}
+
+// element e of a flat array of 16-byte vectors
+template <class E>
+__device__ __forceinline__ uint32_t get_flat(const u32x4* v, int e) {
+  return E::get(v[e / E::VEC], e % E::VEC);
+}
+template <class E>
+__device__ __forceinline__ void set_flat(u32x4* v, int e, uint32_t val) {
+  E::set(v[e / E::VEC], e % E::VEC, val);
+}
+
+template <class E, int K>
+__device__ __forceinline__ void load_weights(const void* w, int c0, float (*wt)[E::VEC]) {
+  constexpr int VEC = E::VEC;
+  using S = typename E::S;
+  const S* wp = (const S*)w + (int64_t)c0 * K;
+  float flat[VEC * K];
+#pragma unroll
+  for (int v = 0; v < K; ++v) E::unpack(ld16(wp + v * VEC), flat + v * VEC);
+#pragma unroll
+  for (int ch = 0; ch < VEC; ++ch)
+#pragma unroll
+    for (int k = 0; k < K; ++k) wt[k][ch] = flat[ch * K + k];
+}
+
+// History vectors ((ch, u) order, as in the pool) to window rows 0..H-1.
+template <class E, int H>
+__device__ __forceinline__ void hist_to_win(const u32x4* old, float (*win)[E::VEC]) {
+#pragma unroll
+  for (int u = 0; u < H; ++u)
+#pragma unroll
+    for (int ch = 0; ch < E::VEC; ++ch) win[u][ch] = widen<E>(get_flat<E>(old, ch * H + u));
+}
+
+template <class E, int K, int D, bool SILU>
+__device__ __forceinline__ void conv_point(const float (*win)[E::VEC], int pos,
+                                           const float (*wt)[E::VEC], const float* bs,
+                                           float* z) {
+#pragma unroll
+  for (int ch = 0; ch < E::VEC; ++ch) {
+    float acc = bs[ch];
+#pragma unroll
+    for (int k = 0; k < K; ++k) acc = __builtin_fmaf(wt[k][ch], win[pos - (K - 1 - k) * D][ch], acc);
+    z[ch] = SILU ? silu(acc) : acc;
+  }
+}
+
+// Store the window x rows [p-H, p) (all >= 0) as a (ch, jj) state row.
+template <class E, int H>
+__device__ __forceinline__ void store_window_from_x(typename E::S* dst,
+                                                    const typename E::S* xb,
+                                                    int64_t xrs, int p) {
+  u32x4 xr[H], nv[H];
+#pragma unroll
+  for (int jj = 0; jj < H; ++jj) xr[jj] = ld16(xb + (int64_t)(p - H + jj) * xrs);
+#pragma unroll
+  for (int jj = 0; jj < H; ++jj)
+#pragma unroll
+    for (int ch = 0; ch < E::VEC; ++ch) set_flat<E>(nv, ch * H + jj, E::get(xr[jj], ch));
+#pragma unroll
+  for (int v = 0; v < H; ++v) st16(dst + v * E::VEC, nv[v]);
+}
+
+// New state = ext[L .. L+H) for a request of runtime length L.
+template <class E, int H>
+__device__ __forceinline__ void write_state(typename E::S* sp, const u32x4* old, int L,
+                                            const typename E::S* xb, int64_t xrs) {
+  if (L >= H) {
+    store_window_from_x<E, H>(sp, xb, xrs, L);
+    return;
+  }
+  // 1 <= L < H: entries jj < H-L keep old[L + jj], the rest are the L tokens.
+  u32x4 xr[H], nv[H];
+#pragma unroll
+  for (int jj = 0; jj < H; ++jj) {
+    const int p = L - H + jj;
+    xr[jj] = p >= 0 ? ld16(xb + (int64_t)p * xrs) : u32x4{0, 0, 0, 0};
+  }
+#pragma unroll
+  for (int jj = 0; jj < H; ++jj)
+#pragma unroll
+    for (int ch = 0; ch < E::VEC; ++ch) {
+      uint32_t val = E::get(xr[jj], ch);
+#pragma unroll
+      for (int m = 1; m < H; ++m)
+        if (m + jj < H && m == L) val = get_flat<E>(old, ch * H + m + jj);
+      set_flat<E>(nv, ch * H + jj, val);
+    }
+#pragma unroll
+  for (int v = 0; v < H; ++v) st16(sp + v * E::VEC, nv[v]);
+}
+
+// ---------------------------------------------------------------------------
+// fast kernel: compile-time K, D; QC > 0 is a compile-time update length
+// ---------------------------------------------------------------------------
+template <class E, int K, int D, int U, bool SILU, int QC>
+__global__ __launch_bounds__(kBlock) void conv_fast(ConvArgs a) {
+  constexpr int H = (K - 1) * D;
+  constexpr int VEC = E::VEC;
+  using S = typename E::S;
+  static_assert(K >= 2, "K = 1 has no history; use the generic kernel");
+
+  const int lb = logical_block(a.n_logical, a.per_xcd);
+  if (lb < 0) return;
+  const int cid = lb / a.n_cblk, cb = lb - cid * a.n_cblk;
+  Work w;
+  if (!resolve_work(a, cid, w)) return;
+  const int c0 = (cb * kBlock + (int)threadIdx.x) * VEC;
+  if (c0 >= a.C) return;
+
+  float wt[K][VEC], bs[VEC];
+  load_weights<E, K>(a.w, c0, wt);
+  if (a.bias) {
+    E::unpack(ld16((const S*)a.bias + c0), bs);
+  } else {
+#pragma unroll
+    for (int ch = 0; ch < VEC; ++ch) bs[ch] = 0.f;
+  }
+
+  const int64_t xrs = a.x_rs, ors = a.out_rs;
+  const S* xb = (const S*)a.x + w.start * xrs + c0;
+  S* ob = (S*)a.out + w.start * ors + c0;
+  S* sp = (S*)a.pool + ((int64_t)(w.valid ? w.slot : 0) * a.C + c0) * H;
+
+  u32x4 old[H];
+#pragma unroll
+  for (int v = 0; v < H; ++v) old[v] = u32x4{0, 0, 0, 0};
+  if (w.j == 0 && w.h) {
+#pragma unroll
+    for (int v = 0; v < H; ++v) old[v] = ld16(sp + v * VEC);
+  }
+
+  if constexpr (QC > 0) {
+    // Update of exactly QC tokens (the host launches this only when q == QC).
+    u32x4 xr[QC];
+#pragma unroll
+    for (int u = 0; u < QC; ++u) xr[u] = ld16(xb + (int64_t)u * xrs);
+    float win[H + QC][VEC];
+    hist_to_win<E, H>(old, win);
+#pragma unroll
+    for (int u = 0; u < QC; ++u) E::unpack(xr[u], win[H + u]);
+#pragma unroll
+    for (int u = 0; u < QC; ++u) {
+      float z[VEC];
+      conv_point<E, K, D, SILU>(win, H + u, wt, bs, z);
+      st16_stream(ob + (int64_t)u * ors, E::pack(z));
+    }
+    if (w.valid) {
+      u32x4 nv[H];
+#pragma unroll
+      for (int jj = 0; jj < H; ++jj)
+#pragma unroll
+        for (int ch = 0; ch < VEC; ++ch) {
+          const int e = QC + jj;   // ext index of new-state entry jj
+          const uint32_t val = e < H ? get_flat<E>(old, ch * H + e) : E::get(xr[e - H], ch);
+          set_flat<E>(nv, ch * H + jj, val);
+        }
+#pragma unroll
+      for (int v = 0; v < H; ++v) st16(sp + v * VEC, nv[v]);
+    }
+  } else {
+    float win[H + U][VEC];
+    if (w.j == 0) {
+      hist_to_win<E, H>(old, win);
+    } else {
+#pragma unroll
+      for (int u = 0; u < H; ++u) E::unpack(ld16(xb + (int64_t)(w.t0 - H + u) * xrs), win[u]);
+    }
+    for (int tb = w.t0; tb < w.t1; tb += U) {
+      u32x4 xr[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int t = min(tb + u, w.t1 - 1);
+        xr[u] = ld16(xb + (int64_t)t * xrs);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) E::unpack(xr[u], win[H + u]);
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (tb + u < w.t1) {
+          float z[VEC];
+          conv_point<E, K, D, SILU>(win, H + u, wt, bs, z);
+          st16_stream(ob + (int64_t)(tb + u) * ors, E::pack(z));
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < H; ++i)
+#pragma unroll
+        for (int ch = 0; ch < VEC; ++ch) win[i][ch] = win[i + U][ch];
+    }
+    if (w.j == 0 && w.valid) write_state<E, H>(sp, old, w.L, xb, xrs);
+    if (a.ckpt_grid > 0 && a.qsl != nullptr) {
+      // checkpoints at p = m*g with t0 < p <= t1: the chunk holding token p-1
+      const int g = a.ckpt_grid;
+      const int cu0 = a.cu_ckpt[w.r], cnt = a.cu_ckpt[w.r + 1] - cu0;
+      for (int m = w.t0 / g + 1; m <= cnt && (int64_t)m * g <= w.t1; ++m) {
+        const int32_t dst = a.ckpt_slots[cu0 + m - 1];
+        if (dst < 0 || dst >= a.num_slots) continue;
+        store_window_from_x<E, H>((S*)a.pool + ((int64_t)dst * a.C + c0) * H, xb, xrs, m * g);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// generic kernel: any K <= 8, any dilation, any alignment; one channel a lane,
+// each tap read through the cache
+// ---------------------------------------------------------------------------
+template <class E>
+__device__ __forceinline__ uint32_t ld_el(const typename E::S* p) { return (uint32_t)*p; }
+
+template <class E>
+__device__ __forceinline__ typename E::S narrow(float v) {
+  if constexpr (E::VEC == 8) return __builtin_bit_cast(uint16_t, (__bf16)v);
+  else return __float_as_uint(v);
+}
+
+template <class E, bool SILU>
+__global__ __launch_bounds__(kBlock) void conv_generic(ConvArgs a, int K, int D) {
+  using S = typename E::S;
+  const int lb = logical_block(a.n_logical, a.per_xcd);
+  if (lb < 0) return;
+  const int cid = lb / a.n_cblk, cb = lb - cid * a.n_cblk;
+  Work w;
+  if (!resolve_work(a, cid, w)) return;
+  const int c = cb * kBlock + (int)threadIdx.x;
+  if (c >= a.C) return;
+  const int H = (K - 1) * D;
+  float wt[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+    wt[k] = k < K ? widen<E>(ld_el<E>((const S*)a.w + (int64_t)c * K + k)) : 0.f;
+  const float b = a.bias ? widen<E>(ld_el<E>((const S*)a.bias + c)) : 0.f;
+  const int64_t xrs = a.x_rs, ors = a.out_rs;
+  const S* xb = (const S*)a.x + w.start * xrs + c;
+  S* ob = (S*)a.out + w.start * ors + c;
+  S* sp = (S*)a.pool + ((int64_t)(w.valid ? w.slot : 0) * a.C + c) * H;
+  for (int t = w.t0; t < w.t1; ++t) {
+    float acc = b;
+    for (int k = 0; k < K; ++k) {
+      const int p = t - (K - 1 - k) * D;
+      float v = 0.f;
+      if (p >= 0) v = widen<E>(ld_el<E>(xb + (int64_t)p * xrs));
+      else if (w.h) v = widen<E>(ld_el<E>(sp + H + p));
+      acc = __builtin_fmaf(wt[k], v, acc);
+    }
+    if (SILU) acc = silu(acc);
+    ob[(int64_t)t * ors] = narrow<E>(acc);
+  }
+  if (w.j == 0 && w.valid) {
+    // ascending jj reads old entry L + jj > jj before it is overwritten
+    for (int jj = 0; jj < H; ++jj) {
+      const int p = w.L - H + jj;
+      S v = 0;
+      if (p >= 0) v = xb[(int64_t)p * xrs];
+      else if (w.h) v = sp[w.L + jj];
+      sp[jj] = v;
+    }
+  }
+  if (a.ckpt_grid > 0 && a.qsl != nullptr) {
+    const int g = a.ckpt_grid;
+    const int cu0 = a.cu_ckpt[w.r], cnt = a.cu_ckpt[w.r + 1] - cu0;
+    for (int m = w.t0 / g + 1; m <= cnt && (int64_t)m * g <= w.t1; ++m) {
+      const int32_t dst = a.ckpt_slots[cu0 + m - 1];
+      if (dst < 0 || dst >= a.num_slots) continue;
+      S* dp = (S*)a.pool + ((int64_t)dst * a.C + c) * H;
+      for (int jj = 0; jj < H; ++jj) dp[jj] = xb[(int64_t)(m * g - H + jj) * xrs];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// host-side launch selection
+// ---------------------------------------------------------------------------
+namespace {
+
+template <class E, int K, int D, bool SILU>
+hipError_t launch_kd(const ConvArgs& a, int qc, dim3 grid, hipStream_t s) {
+  constexpr int U = ((K - 1) * D <= 4) ? 8 : 4;
+  switch (qc) {
+    case 1: hipLaunchKernelGGL((conv_fast<E, K, D, U, SILU, 1>), grid, dim3(kBlock), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((conv_fast<E, K, D, U, SILU, 2>), grid, dim3(kBlock), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((conv_fast<E, K, D, U, SILU, 4>), grid, dim3(kBlock), 0, s, a); break;
+    default: hipLaunchKernelGGL((conv_fast<E, K, D, U, SILU, 0>), grid, dim3(kBlock), 0, s, a); break;
+  }
+  return hipGetLastError();
+}
+
+template <class E, bool SILU>
+hipError_t launch_typed(const ConvArgs& a, int K, int D, bool fast, int qc, dim3 grid,
+                        hipStream_t s) {
+  if (fast) {
+    if (K == 4 && D == 1) return launch_kd<E, 4, 1, SILU>(a, qc, grid, s);
+    if (K == 4 && D == 3) return launch_kd<E, 4, 3, SILU>(a, qc, grid, s);
+    if (K == 4 && D == 2) return launch_kd<E, 4, 2, SILU>(a, qc, grid, s);
+    if (K == 3 && D == 1) return launch_kd<E, 3, 1, SILU>(a, qc, grid, s);
+    if (K == 2 && D == 1) return launch_kd<E, 2, 1, SILU>(a, qc, grid, s);
+  }
+  hipLaunchKernelGGL((conv_generic<E, SILU>), grid, dim3(kBlock), 0, s, a, K, D);
+  return hipGetLastError();
+}
+
+bool fast_shape(int K, int D) {
+  return (K == 4 && (D == 1 || D == 2 || D == 3)) || (D == 1 && (K == 2 || K == 3));
+}
+
+}  // namespace
+
+// Fills the grid fields of `a` and launches. `uniform` = update mode (batch x q).
+hipError_t launch_conv(ConvArgs a, int dtype, int K, int D, bool silu_act, bool aligned16,
+                       hipStream_t stream, ConvLaunchInfo* info) {
+  const int vec = dtype == 1 ? 8 : 4;
+  const int H = (K - 1) * D;
+  const bool fast = aligned16 && (a.C % vec == 0) && fast_shape(K, D);
+  const bool uniform = a.qsl == nullptr;
+  a.chunk = fast ? kChunk : (H > kChunk ? H : kChunk);
+  int qc = 0;
+  if (fast && uniform && (a.q == 1 || a.q == 2 || a.q == 4)) qc = a.q;
+  const int64_t per_block_ch = (int64_t)kBlock * (fast ? vec : 1);
+  a.n_cblk = (int)((a.C + per_block_ch - 1) / per_block_ch);
+  int64_t n_chunks;
+  if (uniform) n_chunks = (int64_t)a.batch * ((a.q + a.chunk - 1) / a.chunk);
+  else n_chunks = a.num_tokens / a.chunk + a.batch;
+  const int64_t n_logical = n_chunks * a.n_cblk;
+  if (n_logical > 0x7FFFFFF0LL) return hipErrorInvalidValue;
+  a.n_logical = (int)n_logical;
+  a.per_xcd = (int)((n_logical + kXcds - 1) / kXcds);
+  dim3 grid((unsigned)(a.per_xcd * kXcds));
+  if (info) {
+    info->fast = fast;
+    info->qc = qc;
+    info->grid = (int64_t)grid.x;
+    info->chunk = a.chunk;
+  }
+  if (dtype == 1)
+    return silu_act ? launch_typed<BF16, true>(a, K, D, fast, qc, grid, stream)
+                    : launch_typed<BF16, false>(a, K, D, fast, qc, grid, stream);
+  return silu_act ? launch_typed<F32, true>(a, K, D, fast, qc, grid, stream)
+                  : launch_typed<F32, false>(a, K, D, fast, qc, grid, stream);
+}
+
+}  // namespace sc

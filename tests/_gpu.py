@@ -1,0 +1,108 @@
+"""Test-side helpers: move synthetic cases to the GPU and run them through the
+C ABI (via the thin binding), and the output tolerance of the parity tests."""
+from __future__ import annotations
+
+import numpy as np
+
+from synthetic import bf16_to_f32
+
+
+def dev(a: np.ndarray, dtype: str = None):
+    """NumPy array -> cuda tensor. uint16 arrays are bf16 bit patterns unless
+    dtype says otherwise."""
+    import torch
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16 and dtype != "u16":
+        t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(a)
+    return t.cuda()
+
+
+def host(t) -> np.ndarray:
+    import torch
+    t = t.detach().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def as_f64(a: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "bf16":
+        return bf16_to_f32(a).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def run_conv_case(case, *, pool=None, x_pad: int = 0, slot_2d: int = 0, stream=None):
+    """Runs a ConvCase on the GPU: decode rows through sc_conv_update, then
+    prefill rows through sc_conv_prefill_varlen (as the PLE layer's dispatch
+    does). Returns (out, pool_after) as NumPy arrays.
+
+    x_pad > 0 stores x and out with row stride C + x_pad (strided rows);
+    slot_2d > 0 passes slots as column 0 of a (B, slot_2d) int32 tensor."""
+    import torch
+    import stateful_causal_short_amd as scs
+    T, C = case.T, case.C
+    if x_pad:
+        xs = np.zeros((T, C + x_pad), case.x.dtype)
+        xs[:, :C] = case.x
+        xd = dev(xs)[:, :C]
+        od = dev(np.zeros((T, C + x_pad), case.x.dtype))[:, :C]
+    else:
+        xd = dev(case.x)
+        od = dev(np.zeros((T, C), case.x.dtype))
+    pd = dev(case.pool if pool is None else pool)
+    wd = dev(case.w)
+    bd = None if case.bias is None else dev(case.bias)
+
+    def slots(a):
+        a = np.asarray(a, np.int32)
+        if slot_2d:
+            m = np.full((a.shape[0], slot_2d), -7, np.int32)
+            m[:, 0] = a
+            return dev(m)
+        return dev(a)
+
+    nd = case.num_decode_tokens
+    if case.num_decodes:
+        dh = None if case.decode_h is None else dev(np.asarray(case.decode_h, np.uint8))
+        scs.sc_conv_update(xd[:nd], od[:nd], wd, bd, pd, slots(case.decode_slots), dh,
+                           q=case.q, dilation=case.d, activation=case.act, stream=stream)
+    if case.num_prefills:
+        ck = None
+        if case.ckpt_grid:
+            ck = (case.ckpt_grid, dev(case.cu_ckpt), dev(case.ckpt_slots))
+        scs.sc_conv_prefill_varlen(xd[nd:], od[nd:], wd, bd, pd, dev(case.qsl_p),
+                                   slots(case.prefill_slots),
+                                   dev(np.asarray(case.prefill_h, np.uint8)),
+                                   dilation=case.d, activation=case.act, ckpt=ck,
+                                   stream=stream)
+    torch.cuda.synchronize()
+    return host(od.contiguous()), host(pd)
+
+
+def ulp_bf16(ref: np.ndarray) -> np.ndarray:
+    a = np.maximum(np.abs(ref), 2.0 ** -126)
+    return np.exp2(np.floor(np.log2(a)) - 7)
+
+
+def check_close(gpu: np.ndarray, ref64: np.ndarray, absum: np.ndarray, dtype: str,
+                floor_rel: float, *, what: str = "out", mask=None):
+    """Output tolerance: |gpu - ref| <= 2 bf16 ulp(ref) (bf16) or 1e-5 |ref|
+    (fp32), or <= floor_rel * (sum of |terms|) — the fp32 accumulation bound,
+    which only matters where the sum cancels. Returns the share of elements
+    that passed through the floor alone."""
+    if mask is not None:
+        gpu, ref64, absum = gpu[mask], ref64[mask], absum[mask]
+    g = as_f64(gpu, dtype)
+    diff = np.abs(g - ref64)
+    tol = 2.0 * ulp_bf16(ref64) if dtype == "bf16" else 1e-5 * np.abs(ref64)
+    floor = floor_rel * absum
+    ok = (diff <= tol) | (diff <= floor)
+    if not ok.all():
+        bad = np.argwhere(~ok)
+        i = tuple(bad[0])
+        raise AssertionError(
+            f"{what}: {len(bad)} of {ok.size} outside tolerance; first at {i}: "
+            f"gpu={g[i]!r} ref={ref64[i]!r} tol={tol[i]!r} floor={floor[i]!r}")
+    return float(((diff > tol) & (diff <= floor)).sum()) / max(1, ok.size)

@@ -1,0 +1,167 @@
+"""C-ABI boundary checks that need no GPU: the library loads, exports every
+function include/statefulconv.h declares, and rejects bad arguments on the host
+with the documented status before any launch (fake device pointers are never
+dereferenced on these paths)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import stateful_causal_short_amd as scs
+from stateful_causal_short_amd import sc_cca_desc, sc_ckpt_desc, sc_conv_desc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "statefulconv.h")
+
+OK, NULL, INVALID, DTYPE, CAPACITY, UNSUPPORTED = 0, -1, -2, -3, -4, -5
+P = ctypes.c_void_p(0x10000)   # a fake device pointer: never dereferenced here
+P2 = ctypes.c_void_p(0x20000)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:sc_status|const char\*|int32_t)\s+(sc_\w+)\s*\(",
+                                 text, re.M)))
+
+
+def test_library_exports_every_declared_function():
+    lib = scs.lib()
+    names = declared_functions()
+    assert set(names) == set(scs.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.sc_abi_version() == 1
+    for s in (0, -1, -2, -3, -4, -5, -6):
+        assert lib.sc_status_string(s)
+
+
+def desc(**kw):
+    d = dict(channels=64, width=4, dilation=1, state_len=3, dtype=1, activation=1,
+             x_row_stride=64, out_row_stride=64, state_indices_stride=1)
+    d.update(kw)
+    return sc_conv_desc(**d)
+
+
+def prefill(d, *, x=P, out=P2, w=P, bias=None, pool=P, num_slots=4, qsl=P, slots=P,
+            h=P, batch=2, T=10, ckpt=None):
+    return scs.lib().sc_conv_prefill_varlen(
+        None if d is None else ctypes.byref(d), x, out, w, bias, pool, num_slots, qsl,
+        slots, h, batch, T, None if ckpt is None else ctypes.byref(ckpt), None)
+
+
+def update(d, *, x=P, out=P2, w=P, pool=P, num_slots=4, slots=P, h=None, batch=2, q=1):
+    return scs.lib().sc_conv_update(None if d is None else ctypes.byref(d), x, out, w,
+                                    None, pool, num_slots, slots, h, batch, q, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=7), DTYPE),
+    (dict(channels=0), INVALID),
+    (dict(width=0), INVALID),
+    (dict(width=9, state_len=8), UNSUPPORTED),
+    (dict(dilation=0), INVALID),
+    (dict(activation=3), INVALID),
+    (dict(x_row_stride=63), INVALID),
+    (dict(out_row_stride=10), INVALID),
+    (dict(state_indices_stride=0), INVALID),
+    (dict(state_len=2), CAPACITY),                 # (4-1)*1 = 3 needed
+    (dict(dilation=3, state_len=8), CAPACITY),     # 9 needed
+    (dict(state_len=7), UNSUPPORTED),              # speculative rolling window
+])
+def test_descriptor_validation(kw, status):
+    assert prefill(desc(**kw)) == status
+    assert update(desc(**kw)) == status
+
+
+def test_null_arguments():
+    d = desc()
+    assert prefill(None) == NULL
+    assert prefill(d, x=None) == NULL
+    assert prefill(d, out=None) == NULL
+    assert prefill(d, w=None) == NULL
+    assert prefill(d, qsl=None) == NULL
+    assert prefill(d, slots=None) == NULL
+    assert prefill(d, h=None) == NULL            # required for prefill
+    assert prefill(d, pool=None) == NULL
+    assert update(None) == NULL
+    assert update(d, x=None, out=None, w=None, slots=None, pool=None, batch=0) == OK
+    assert update(d, slots=None) == NULL
+    assert update(d, pool=None) == NULL
+
+
+def test_size_and_alias_rules():
+    d = desc()
+    assert prefill(d, batch=-1) == INVALID
+    assert prefill(d, T=-5) == INVALID
+    assert prefill(d, num_slots=-1) == INVALID
+    assert prefill(d, out=P) == INVALID           # out aliases x
+    assert update(d, q=-1) == INVALID
+    assert update(d, out=P) == INVALID
+    # zero work: success without a launch
+    assert prefill(d, batch=0) == OK
+    assert prefill(d, T=0) == OK
+    assert update(d, batch=0) == OK
+    assert update(d, q=0) == OK
+
+
+def test_checkpoint_rules():
+    d = desc(dilation=3, state_len=9)
+    assert prefill(d, ckpt=sc_ckpt_desc(grid=8, cu_ckpt=P, ckpt_slots=P), batch=0) == INVALID
+    assert prefill(d, ckpt=sc_ckpt_desc(grid=-1, cu_ckpt=P, ckpt_slots=P), batch=0) == INVALID
+    assert prefill(d, ckpt=sc_ckpt_desc(grid=16, cu_ckpt=None, ckpt_slots=P)) == NULL
+    assert prefill(d, ckpt=sc_ckpt_desc(grid=16, cu_ckpt=P, ckpt_slots=None)) == NULL
+    # zero work needs no pointers at all (empty tensors carry NULL pointers)
+    assert prefill(d, x=None, out=None, w=None, qsl=None, slots=None, h=None, pool=None,
+                   ckpt=sc_ckpt_desc(grid=16, cu_ckpt=None, ckpt_slots=None), T=0) == OK
+    assert prefill(d, ckpt=sc_ckpt_desc(grid=16, cu_ckpt=P, ckpt_slots=P), batch=0) == OK
+    assert prefill(d, ckpt=sc_ckpt_desc(grid=0, cu_ckpt=None, ckpt_slots=None), batch=0) == OK
+
+
+def test_state_copy_validation():
+    L = scs.lib()
+    assert L.sc_state_gather(P, 4, 96, P, 1, 3, None, None) == NULL
+    assert L.sc_state_gather(P, 4, 0, P, 1, 3, P2, None) == INVALID
+    assert L.sc_state_gather(P, 4, 96, P, 0, 3, P2, None) == INVALID
+    assert L.sc_state_gather(P, 4, 96, P, 1, 0, P2, None) == OK
+    assert L.sc_state_scatter(P, 96, None, 1, 3, P2, 4, None) == NULL
+    assert L.sc_state_scatter(P, 96, P, 1, -1, P2, 4, None) == INVALID
+    assert L.sc_state_scatter(P, 96, P, 1, 0, P2, 4, None) == OK
+
+
+def cca_desc(**kw):
+    d = dict(num_q_heads=16, num_kv_heads=4, head_dim=128, t0=2, t1=2, dtype=1,
+             q_row_stride=2048, k_row_stride=512, v_cur_row_stride=256,
+             v_del_row_stride=256, out_row_stride=3072, decode_slot_stride=1,
+             prefill_slot_stride=1)
+    d.update(kw)
+    return sc_cca_desc(**d)
+
+
+def cca(d, *, nd=2, npf=1, T=5, di=P, cs=P, ds=P, dslots=P, qsl=P, h=P):
+    return scs.lib().sc_cca_qk_conv(ctypes.byref(d), P, P, P, P, P2, P, P, P, P, di, cs,
+                                    ds, 8, nd, dslots, npf, qsl, P, h, T, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=0), DTYPE),
+    (dict(num_kv_heads=3), INVALID),
+    (dict(head_dim=127), INVALID),
+    (dict(t0=0), INVALID),
+    (dict(q_row_stride=100), INVALID),
+    (dict(out_row_stride=3071), INVALID),
+    (dict(decode_slot_stride=0), INVALID),
+])
+def test_cca_validation(kw, status):
+    assert cca(cca_desc(**kw)) == status
+
+
+def test_cca_null_and_empty():
+    d = cca_desc()
+    assert cca(d, dslots=None) == NULL
+    assert cca(d, qsl=None) == NULL
+    assert cca(d, h=None) == NULL
+    assert cca(d, cs=None) == NULL
+    assert cca(d, T=1) == INVALID                 # fewer rows than decodes
+    assert cca(d, nd=0, npf=0, T=0) == OK
+    assert cca(d, nd=0, npf=1, T=0, dslots=None) == OK

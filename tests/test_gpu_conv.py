@@ -1,0 +1,264 @@
+"""GPU parity of the depthwise stateful conv (sc_conv_prefill_varlen,
+sc_conv_update) and of the state row copies, against the CPU oracle.
+
+Bar: state bit-exact always; outputs within 2 bf16 ulp (bf16) or 1e-5 relative
+(fp32) of the oracle's float64 result, or within 2^-20 of the sum of |terms|
+(the fp32 accumulation bound for <= 9 terms, only reached where the sum
+cancels)."""
+from dataclasses import replace
+
+import numpy as np
+import pytest
+
+import oracle
+import synthetic
+from synthetic import conv_case
+from tests._gpu import check_close, dev, host, run_conv_case
+
+pytestmark = pytest.mark.gpu
+
+FLOOR = 2.0 ** -20
+
+
+def sample_rows(case, n_random=256, seed=0):
+    """Rows whose outputs are checked at full size: each request's first and
+    last rows, rows around every 64-token chunk edge, and random rows."""
+    m = np.zeros(case.T, np.uint8)
+    starts = [i * case.q for i in range(case.num_decodes)]
+    lens = [case.q] * case.num_decodes
+    base = case.num_decode_tokens
+    starts += [base + int(case.qsl_p[r]) for r in range(case.num_prefills)]
+    lens += [int(case.qsl_p[r + 1] - case.qsl_p[r]) for r in range(case.num_prefills)]
+    for s, L in zip(starts, lens):
+        m[s:s + min(L, 12)] = 1
+        m[max(s, s + L - 12):s + L] = 1
+        for e in range(64, L, 64):
+            m[s + e - 2:s + min(L, e + 2)] = 1
+    rng = np.random.default_rng(seed)
+    m[rng.integers(0, case.T, n_random)] = 1
+    return m
+
+
+def parity(case, *, full_rows=True, **kw):
+    print(f"[gpu] {case.name} T={case.T} C={case.C} K={case.K} d={case.d} "
+          f"{case.dtype} act={case.act} kw={kw}", flush=True)
+    out, pool = run_conv_case(case, **kw)
+    mask = None if full_rows else sample_rows(case)
+    ref, ref_pool, absum = oracle.conv(case, out_dtype="f64", absum=True, row_mask=mask)
+    np.testing.assert_array_equal(pool, ref_pool, err_msg="state pool not bit-exact")
+    m = None if mask is None else mask.astype(bool)
+    frac = check_close(out, ref, absum, case.dtype, FLOOR, mask=m)
+    print(f"[gpu] {case.name}: ok (floor-only share {frac:.2e})", flush=True)
+    return out, pool
+
+
+# ----------------------------------------------------------------------------
+# the five workload shapes (CCA is in test_gpu_cca.py)
+# ----------------------------------------------------------------------------
+def test_config1_single_sequence_f32():
+    parity(synthetic.config1())
+
+
+def test_config2_small_ragged():
+    parity(synthetic.config2(C=512, B=8, max_len=300))
+
+
+def test_config2_full():
+    parity(synthetic.config2(), full_rows=False)
+
+
+def test_config3a_decode_full():
+    parity(synthetic.config3a())
+
+
+def test_config3b_multi_token_full():
+    parity(synthetic.config3b())
+
+
+def test_config4_small_dilated_mixed_with_checkpoints():
+    parity(synthetic.config4(C=512, num_decodes=16, Bp=6, min_len=5, max_len=700,
+                             grid=64, num_slots=128))
+
+
+def test_config4_full():
+    parity(synthetic.config4(), full_rows=False)
+
+
+# ----------------------------------------------------------------------------
+# edge cases
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("d", [1, 3])
+def test_chunk_edges_and_short_requests(d):
+    lens = [1, 2, 3, 8, 9, 10, 63, 64, 65, 127, 128, 129, 200]
+    case = conv_case("edges", 500 + d, C=256, K=4, d=d, dtype="bf16", act="silu",
+                     w_std=0.25, bias_std=0.1, num_slots=96, prefill_lens=lens,
+                     prefill_h_p=0.5, ckpt_grid=max(16, 3 * d))
+    parity(case)
+
+
+def test_padding_and_out_of_range_slots():
+    case = conv_case("pad", 601, C=256, K=4, d=1, dtype="bf16", act="silu", w_std=0.25,
+                     bias_std=0.1, num_slots=16, num_decodes=4,
+                     prefill_lens=[5, 70, 2], prefill_h_all=1)
+    case.decode_slots[1] = -1
+    case.decode_slots[2] = 16          # out of range: a padding row too
+    case.prefill_slots[1] = -3
+    parity(case)
+
+
+def test_zero_length_requests_and_empty_batch():
+    case = conv_case("zero", 602, C=512, K=4, d=1, dtype="bf16", act="none", w_std=0.25,
+                     bias_std=None, num_slots=16, prefill_lens=[0, 7, 0, 0, 66, 0],
+                     prefill_h_p=0.5)
+    parity(case)
+    import torch
+    import stateful_causal_short_amd as scs
+    x = dev(case.x)
+    out = torch.zeros_like(x)
+    pool = dev(case.pool)
+    scs.sc_conv_prefill_varlen(x[:0], out[:0], dev(case.w), None, pool,
+                               dev(np.zeros(1, np.int32)), dev(np.zeros(0, np.int32)),
+                               dev(np.zeros(0, np.uint8)), activation="none")
+    torch.cuda.synchronize()
+    assert np.array_equal(host(pool), case.pool)
+
+
+def test_strided_rows_and_2d_slot_indices():
+    case = conv_case("strided", 603, C=512, K=4, d=3, dtype="bf16", act="none",
+                     w_std=0.05, bias_std=None, num_slots=64, num_decodes=8,
+                     prefill_lens=[100, 3, 250], prefill_h_p=0.5, ckpt_grid=32)
+    parity(case, x_pad=24, slot_2d=3)
+
+
+@pytest.mark.parametrize("C,K,d,dtype,act", [
+    (100, 4, 1, "bf16", "silu"),     # C not a multiple of the vector width
+    (256, 5, 2, "bf16", "silu"),     # width 5: generic kernel
+    (256, 1, 1, "f32", "none"),      # width 1: no history
+    (96, 3, 4, "f32", "silu"),       # generic dilation, fp32
+    (64, 8, 9, "bf16", "none"),      # H = 63 < chunk
+    (64, 8, 12, "f32", "none"),      # H = 84 > default chunk
+])
+def test_generic_kernel_shapes(C, K, d, dtype, act):
+    case = conv_case("generic", 700 + C + K + d, C=C, K=K, d=d, dtype=dtype, act=act,
+                     w_std=0.3, bias_std=0.1, num_slots=32, num_decodes=3, q=2,
+                     prefill_lens=[1, 40, 150, 300], prefill_h_p=0.5,
+                     ckpt_grid=max(64, (K - 1) * d))
+    parity(case)
+
+
+@pytest.mark.parametrize("dtype,d", [("f32", 1), ("f32", 3), ("bf16", 2)])
+def test_fast_kernel_other_dtypes_and_dilations(dtype, d):
+    case = conv_case("fast", 800 + d, C=1024, K=4, d=d, dtype=dtype, act="silu",
+                     w_std=0.25, bias_std=0.1, num_slots=64, num_decodes=5, q=1,
+                     prefill_lens=[1, 33, 64, 65, 300, 1000], prefill_h_p=0.5,
+                     ckpt_grid=64)
+    parity(case)
+
+
+@pytest.mark.parametrize("q", [1, 2, 3, 4, 5, 70])
+@pytest.mark.parametrize("d", [1, 3])
+def test_update_lengths_and_flags(q, d):
+    case = conv_case("update", 900 + q + d, C=512, K=4, d=d, dtype="bf16", act="silu",
+                     w_std=0.25, bias_std=0.1, num_slots=64, num_decodes=20, q=q)
+    case.decode_h = (np.arange(20) % 3 != 0).astype(np.uint8)
+    parity(case)
+
+
+def test_unaligned_rows_take_the_generic_path():
+    # x and out start one element into their buffers: not 16-byte aligned
+    import torch
+    import stateful_causal_short_amd as scs
+    case = conv_case("unaligned", 950, C=256, K=4, d=1, dtype="bf16", act="silu",
+                     w_std=0.25, bias_std=0.1, num_slots=8,
+                     prefill_lens=[9, 80], prefill_h_p=0.5)
+    xs = np.zeros(case.T * case.C + 1, np.uint16)
+    xs[1:] = case.x.reshape(-1)
+    xd = dev(xs)[1:].view(case.T, case.C)
+    od = torch.zeros(case.T * case.C + 1, dtype=torch.bfloat16, device="cuda")[1:].view(case.T, case.C)
+    pool = dev(case.pool)
+    scs.sc_conv_prefill_varlen(xd, od, dev(case.w), dev(case.bias), pool, dev(case.qsl_p),
+                               dev(case.prefill_slots), dev(case.prefill_h),
+                               activation="silu")
+    torch.cuda.synchronize()
+    ref, ref_pool, absum = oracle.conv(case, out_dtype="f64", absum=True)
+    np.testing.assert_array_equal(host(pool), ref_pool)
+    check_close(host(od.contiguous()), ref, absum, "bf16", FLOOR)
+
+
+def test_rounding_ties_to_even():
+    # weights, bias and inputs chosen so every fp32 sum is exact: any output
+    # difference would be a rounding-mode difference (bf16 ties to even).
+    rng = np.random.default_rng(77)
+    C, T = 512, 300
+    x = synthetic.bf16_bits((rng.integers(128, 256, (T, C)) / 128.0) *
+                            rng.choice([-1, 1], (T, C)) * np.exp2(rng.integers(-2, 3, (T, C))))
+    w = synthetic.bf16_bits(rng.choice([-2, -1, -0.5, 0.5, 1, 2], (C, 4)))
+    b = synthetic.bf16_bits(rng.choice([-1, 1], C) * np.exp2(rng.integers(-2, 3, C)))
+    pool = synthetic.bf16_bits(rng.choice([-1.5, 1.25], (4, C, 3)))
+    case = synthetic.ConvCase(name="ties", C=C, K=4, d=1, S=3, dtype="bf16", act="none",
+                              x=x, w=w, bias=b, pool=pool,
+                              qsl_p=np.array([0, 100, 300], np.int32),
+                              prefill_slots=np.array([0, 2], np.int32),
+                              prefill_h=np.array([1, 0], np.uint8))
+    out, gpool = run_conv_case(case)
+    ref, rpool, _ = oracle.conv(case)
+    np.testing.assert_array_equal(gpool, rpool)
+    np.testing.assert_array_equal(out, ref)
+
+
+def test_gpu_chunked_equals_gpu_one_shot():
+    # state carry on the GPU: prefill in pieces, then decodes == one shot
+    L = 600
+    src = conv_case("carry", 960, C=1024, K=4, d=3, dtype="bf16", act="silu", w_std=0.25,
+                    bias_std=0.1, num_slots=2, prefill_lens=[L], prefill_h_all=1)
+
+    def one(lo, hi, pool, as_decode):
+        if as_decode:
+            c = replace(src, x=src.x[lo:hi].copy(), num_decodes=hi - lo, q=1,
+                        decode_slots=np.ones(hi - lo, np.int32),
+                        qsl_p=np.zeros(1, np.int32), prefill_slots=np.zeros(0, np.int32),
+                        prefill_h=np.zeros(0, np.uint8))
+        else:
+            c = replace(src, x=src.x[lo:hi].copy(), qsl_p=np.array([0, hi - lo], np.int32),
+                        prefill_slots=np.array([1], np.int32),
+                        prefill_h=np.array([1], np.uint8))
+        return run_conv_case(c, pool=pool)
+
+    whole = replace(src, prefill_slots=np.array([1], np.int32))
+    o_all, p_all = run_conv_case(whole)
+    pool = src.pool.copy()
+    outs = []
+    for lo, hi, dec in [(0, 1, False), (1, 70, False), (70, 71, True), (71, 500, False),
+                        (500, 501, True), (501, 600, False)]:
+        o, pool = one(lo, hi, pool, dec)
+        outs.append(o)
+    np.testing.assert_array_equal(np.concatenate(outs), o_all)
+    np.testing.assert_array_equal(pool, p_all)
+
+
+@pytest.mark.parametrize("row_bytes,dtype", [(3 * 8192 * 2, np.uint16), (6, np.uint16),
+                                             (12, np.float32)])
+def test_state_gather_scatter(row_bytes, dtype):
+    import torch
+    import stateful_causal_short_amd as scs
+    rng = np.random.default_rng(row_bytes)
+    per = row_bytes // np.dtype(dtype).itemsize
+    if dtype == np.uint16:
+        pool = rng.integers(0, 0x7F00, (50, per)).astype(np.uint16)   # finite bf16 bits
+    else:
+        pool = rng.standard_normal((50, per)).astype(np.float32)
+    idx = rng.permutation(50)[:20].astype(np.int32)
+    idx[3] = -1
+    idx[7] = 50
+    dense0 = np.full((20, per), 7, dtype)
+    exp_dense = oracle.state_gather(pool, idx, dense0.copy())
+    pd = dev(pool)
+    dd = dev(dense0)
+    scs.sc_state_gather(pd, dev(idx), dd)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(dd), exp_dense)
+    newd = (pool[:20] + 1).astype(dtype)
+    exp_pool = oracle.state_scatter(newd, idx, pool.copy())
+    scs.sc_state_scatter(dev(newd), dev(idx), pd)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(pd), exp_pool)
