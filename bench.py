@@ -1,0 +1,333 @@
+#!/usr/bin/env python3
+"""Benchmark of the stateful causal short conv on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step = one pass of the hot path over one batch already resident in HBM.
+The default workload is the varlen prefill batch (8 sequences, lengths
+U{1..2048}, 8192 channels, width 4, bf16, bias + SiLU, 64-slot state pool):
+state gather, conv, bias, SiLU and state write-back in one kernel. Other
+workloads (decode, multi-token update, dilated mixed batch with checkpoints,
+CCA) are selectable for measurement tables.
+
+Timing: W untimed eager steps, then K steps timed twice, bracketed by device
+synchronisation and HIP events on the launch stream: as eager back-to-back
+launches and as one replay of the K steps captured in a HIP graph (no host
+launch cost inside the timed region); the faster is reported, both are kept.
+For a batch with two kernels, each kernel's average comes from K launches of
+that kernel alone, timed the same way. Several
+identical buffer sets (x, out, state pool) are rotated so that each step's
+inputs were last touched >= 1 GiB of traffic earlier and come from HBM, not the
+256 MB Infinity Cache. Prints one JSON line on stdout; progress on stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "tokens/s and achieved HBM GB/s (% of peak), varlen prefill + decode conv"
+PEAK_GBPS = 8000.0          # MI355X HBM3E, vendor figure
+ROTATE_BYTES = 1 << 30      # rotate buffer sets until >= 1 GiB is cycled
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# workloads
+# ---------------------------------------------------------------------------
+def conv_workload(name):
+    import synthetic
+    return {
+        "varlen_prefill": synthetic.config2,
+        "single": synthetic.config1,
+        "decode": synthetic.config3a,
+        "update_q4": synthetic.config3b,
+        "ple_mixed": synthetic.config4,
+    }[name]()
+
+
+def conv_alg_bytes(case):
+    """Algorithmic HBM bytes of one pass: every input element read once,
+    every output and state element written once (state read only for
+    requests with initial state), weights and bias read once; checkpoint
+    windows written once."""
+    es = case.elsize
+    C, H = case.C, case.H
+    b = case.T * C * es * 2                     # x read + out write
+    hs = [1] * case.num_decodes if case.decode_h is None else list(case.decode_h)
+    hs += list(case.prefill_h)
+    slots = list(case.decode_slots) + list(case.prefill_slots)
+    for h, s in zip(hs, slots):
+        if 0 <= s < case.num_slots:
+            b += (int(h) + 1) * C * H * es      # state read (if any) + write
+    b += C * case.K * es + (C * es if case.bias is not None else 0)
+    if case.ckpt_grid:
+        b += int(case.cu_ckpt[-1]) * C * H * es
+    return b
+
+
+def conv_kernel_bytes(case):
+    """Per-kernel split for mixed batches: (decode_update_bytes, prefill_bytes)."""
+    from dataclasses import replace
+    import numpy as np
+    es, C, H = case.elsize, case.C, case.H
+    w = C * case.K * es + (C * es if case.bias is not None else 0)
+    dec = 0
+    if case.num_decodes:
+        hs = [1] * case.num_decodes if case.decode_h is None else list(case.decode_h)
+        dec = case.num_decode_tokens * C * es * 2 + w
+        dec += sum((int(h) + 1) * C * H * es for h in hs)
+    pre = conv_alg_bytes(case) - dec + (w if case.num_decodes else 0)
+    return dec, pre
+
+
+class ConvRunner:
+    def __init__(self, case, nsets):
+        import numpy as np
+        import torch
+        from tests._gpu import dev
+        self.case = case
+        nd = case.num_decode_tokens
+        self.nd = nd
+        base = dict(w=dev(case.w), b=None if case.bias is None else dev(case.bias),
+                    dslots=dev(case.decode_slots), qsl=dev(case.qsl_p),
+                    pslots=dev(case.prefill_slots),
+                    ph=dev(np.asarray(case.prefill_h, np.uint8)),
+                    dh=None if case.decode_h is None else dev(np.asarray(case.decode_h, np.uint8)),
+                    ck=None)
+        if case.ckpt_grid:
+            base["ck"] = (case.ckpt_grid, dev(case.cu_ckpt), dev(case.ckpt_slots))
+        self.base = base
+        x0, p0 = dev(case.x), dev(case.pool)
+        self.sets = []
+        for i in range(nsets):
+            x = x0 if i == 0 else x0.clone()
+            out = torch.empty_like(x)
+            pool = p0 if i == 0 else p0.clone()
+            self.sets.append((x, out, pool))
+        self.kernels = (["decode_update"] if case.num_decodes else []) + \
+                       (["prefill"] if case.num_prefills else [])
+
+    def step(self, i, only=None):
+        """One pass over the batch (decode rows, then prefill rows, as the PLE
+        layer dispatches them); `only` restricts it to one kernel for timing."""
+        import stateful_causal_short_amd as scs
+        c, b = self.case, self.base
+        x, out, pool = self.sets[i % len(self.sets)]
+        if c.num_decodes and only in (None, "decode_update"):
+            scs.sc_conv_update(x[:self.nd], out[:self.nd], b["w"], b["b"], pool,
+                               b["dslots"], b["dh"], q=c.q, dilation=c.d, activation=c.act)
+        if c.num_prefills and only in (None, "prefill"):
+            scs.sc_conv_prefill_varlen(x[self.nd:], out[self.nd:], b["w"], b["b"], pool,
+                                       b["qsl"], b["pslots"], b["ph"], dilation=c.d,
+                                       activation=c.act, ckpt=b["ck"])
+
+
+def cpu_baseline_conv(case, budget_s=10.0):
+    """The oracle, as it stands, on the same batch; repeated until ~budget_s."""
+    import oracle
+    threads = min(16, oracle.default_threads())
+    runs, t0 = 0, time.perf_counter()
+    while True:
+        oracle.conv(case, nthreads=threads)
+        runs += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or runs >= 50:
+            break
+    return {"value": case.T * runs / el, "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"the full batch ({case.T} tokens) run {runs}x through the fp64 "
+                      f"oracle, {el:.1f} s wall on {threads} threads"}
+
+
+def source_sha(files=("conv.hip", "common.hpp", "kernels.hpp")):
+    """Digest of the sources the depthwise kernels are built from."""
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "stateful_causal_short_amd", "csrc")
+    for f in files:
+        with open(os.path.join(d, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel_key):
+    """HBM bytes per launch from the committed PMC summary, if it was taken on
+    the current kernel sources (else null)."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(p) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = t.get(kernel_key)
+    if not e or e.get("source_sha") != source_sha():
+        return None
+    return e.get("bytes_per_launch")
+
+
+def copy_calibration(args):
+    """Plain copy of known size through the library's row-copy kernel
+    (sc_state_gather with identity indices): 1 GiB read + 1 GiB written per
+    launch. Gives the practical HBM ceiling and the scale of the FETCH_SIZE /
+    WRITE_SIZE counters."""
+    import torch
+    import stateful_causal_short_amd as scs
+    row = 48 * 1024
+    rows = (1 << 30) // row
+    nsets = 2
+    src = [torch.empty(rows, row, dtype=torch.uint8, device="cuda") for _ in range(nsets)]
+    dst = [torch.empty_like(src[0]) for _ in range(nsets)]
+    for t in src:
+        t.fill_(1)
+    idx = torch.arange(rows, dtype=torch.int32, device="cuda")
+    for i in range(args.warmup):
+        scs.sc_state_gather(src[i % nsets], idx, dst[i % nsets])
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for i in range(args.steps):
+        scs.sc_state_gather(src[i % nsets], idx, dst[i % nsets])
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / args.steps
+    nbytes = rows * row
+    print(json.dumps({"workload": "copy_calibration", "kernel": "row_copy",
+                      "bytes_read_per_launch": nbytes, "bytes_written_per_launch": nbytes,
+                      "us_per_launch": ms * 1e3,
+                      "GBps": 2 * nbytes / (ms * 1e-3) / 1e9}), flush=True)
+
+
+# ---------------------------------------------------------------------------
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="varlen_prefill",
+                    choices=["varlen_prefill", "single", "decode", "update_q4",
+                             "ple_mixed", "cca", "copy"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (this path has no multi-GPU leg); "
+              f"--gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import stateful_causal_short_amd as scs
+    scs.lib()
+    torch.cuda.set_device(0)
+    log(f"device {torch.cuda.get_device_name(0)}; workload {args.workload}")
+
+    if args.workload == "cca":
+        raise SystemExit("cca workload: the CCA kernel is not built yet")
+    if args.workload == "copy":
+        return copy_calibration(args)
+
+    case = conv_workload(args.workload)
+    alg = conv_alg_bytes(case)
+    dec_b, pre_b = conv_kernel_bytes(case)
+    set_bytes = case.T * case.C * case.elsize * 2 + case.pool.nbytes
+    nsets = int(min(8, max(2, -(-ROTATE_BYTES // set_bytes))))
+    log(f"T={case.T} C={case.C} K={case.K} d={case.d} {case.dtype} act={case.act}; "
+        f"alg bytes/step={alg}; {nsets} rotating buffer sets")
+    run = ConvRunner(case, nsets)
+    for i in range(args.warmup):
+        run.step(i)
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} done")
+
+    timing = {}
+
+    def timed(name, fn_steps):
+        """Average GPU time per launch of K back-to-back launches, measured two
+        ways with HIP events on the launch stream: eager launches, and one
+        replay of the K launches captured in a HIP graph (no host launch cost).
+        Small kernels can outrun the host's launch rate eagerly; graph replay
+        adds a few us between nodes on large ones. The faster is reported and
+        both are kept."""
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        s.record()
+        fn_steps()
+        e.record()
+        torch.cuda.synchronize()
+        eager = s.elapsed_time(e) / args.steps
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn_steps()
+        g.replay()                        # untimed first replay
+        torch.cuda.synchronize()
+        s.record()
+        g.replay()
+        e.record()
+        torch.cuda.synchronize()
+        graph = s.elapsed_time(e) / args.steps
+        timing[name] = {"eager_us": eager * 1e3, "graph_us": graph * 1e3}
+        return min(eager, graph)
+
+    # timed region: K back-to-back steps
+    ms_step = timed("step", lambda: [run.step(args.warmup + i) for i in range(args.steps)])
+    # per-kernel averages: with one kernel per step, the timed region itself;
+    # otherwise K launches of each kernel alone, timed the same way
+    if len(run.kernels) == 1:
+        kms = {run.kernels[0]: ms_step}
+    else:
+        kms = {k: timed(k, lambda k=k: [run.step(i, only=k) for i in range(args.steps)])
+               for k in run.kernels}
+    log(f"timed {args.steps} steps: {ms_step * 1e3:.2f} us/step; per-kernel us: "
+        + ", ".join(f"{k}={v * 1e3:.2f}" for k, v in kms.items()))
+
+    # dominant kernel: the prefill kernel when present
+    dom = "prefill" if "prefill" in kms else run.kernels[0]
+    dom_bytes = pre_b if dom == "prefill" else dec_b
+    achieved = dom_bytes / (kms[dom] * 1e-3) / 1e9
+    key = f"{args.workload}:{dom}"
+    result = {
+        "metric": METRIC,
+        "value": case.T / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": case.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": case.name, "decodes": case.num_decodes, "decode_q": case.q,
+            "prefills": case.num_prefills, "tokens": case.T, "channels": case.C,
+            "width": case.K, "dilation": case.d, "activation": case.act,
+            "state_slots": case.num_slots, "checkpoint_grid": case.ckpt_grid,
+        },
+        "hbm_gbps": alg / (ms_step * 1e-3) / 1e9,
+        "pct_peak": 100.0 * alg / (ms_step * 1e-3) / 1e9 / PEAK_GBPS,
+        "kernel_us": {k: v * 1e3 for k, v in kms.items()},
+        "timing": timing,
+        "roofline": {
+            "kernel": dom, "bound": "hbm", "achieved": achieved, "peak": PEAK_GBPS,
+            "unit": "GB/s", "frac": achieved / PEAK_GBPS,
+            "traffic": traffic_for(key), "alg_bytes_per_launch": dom_bytes,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        result["cpu_baseline"] = cpu_baseline_conv(case)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -5,6 +5,7 @@
 
 #include "statefulconv.h"
 #include "kernels.hpp"
+#include "cca.hpp"
 
 namespace {
 

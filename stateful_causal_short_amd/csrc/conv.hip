@@ -54,6 +54,29 @@ __device__ __forceinline__ int find_request(const int32_t* qsl, int B, int id, i
   return cnt;
 }
 
+// Request lookup that also returns qsl[r] and qsl[r+1]. With B < 64 every
+// needed entry is loaded once by one lane (lane l holds qsl[l]) and read back
+// with readlane; larger batches fall back to find_request plus two loads.
+// Must be called by full waves.
+__device__ __forceinline__ int find_request_bounds(const int32_t* qsl, int B, int id, int chunk,
+                                                   int& s0, int& s1) {
+  if (B < 64) {
+    const int lane = (int)(threadIdx.x & 63);
+    const int v = lane <= B ? qsl[lane] : 0x7FFFFFFF;
+    const bool p = lane >= 1 && lane <= B && (v / chunk + lane) <= id;
+    const int r = __popcll(__ballot(p));
+    s0 = __builtin_amdgcn_readlane(v, r);
+    s1 = __builtin_amdgcn_readlane(v, min(r + 1, 63));
+    return r;
+  }
+  const int r = find_request(qsl, B, id, chunk);
+  if (r < B) {
+    s0 = qsl[r];
+    s1 = qsl[r + 1];
+  }
+  return r;
+}
+
 struct Work {
   int r, j, L, t0, t1;
   int64_t start;
@@ -194,6 +217,10 @@ __device__ __forceinline__ void write_state(typename E::S* sp, const u32x4* old,
 // ---------------------------------------------------------------------------
 template <class E, int K, int D, int U, bool SILU, int QC>
 __global__ __launch_bounds__(kBlock) void conv_fast(ConvArgs a) {
+#if SC_LDS_PAD > 0
+  __shared__ uint8_t occupancy_pad[SC_LDS_PAD];
+  if (a.C < 0) occupancy_pad[threadIdx.x] = 0;
+#endif
   constexpr int H = (K - 1) * D;
   constexpr int VEC = E::VEC;
   using S = typename E::S;
@@ -270,7 +297,7 @@ __global__ __launch_bounds__(kBlock) void conv_fast(ConvArgs a) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int t = min(tb + u, w.t1 - 1);
-        xr[u] = ld16(xb + (int64_t)t * xrs);
+        xr[u] = SC_NT_LOADS ? ld16_stream(xb + (int64_t)t * xrs) : ld16(xb + (int64_t)t * xrs);
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) E::unpack(xr[u], win[H + u]);
@@ -296,6 +323,312 @@ __global__ __launch_bounds__(kBlock) void conv_fast(ConvArgs a) {
         const int32_t dst = a.ckpt_slots[cu0 + m - 1];
         if (dst < 0 || dst >= a.num_slots) continue;
         store_window_from_x<E, H>((S*)a.pool + ((int64_t)dst * a.C + c0) * H, xb, xrs, m * g);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bf16 one-pass kernel for an even number of taps: a workgroup handles one
+// chunk of at most U tokens in one pass (all rows issued up front), and taps
+// are consumed in pairs by v_dot2c_f32_bf16 straight from bf16 data: the pair
+// (x[s-D][c], x[s][c]) is built from two token rows with one v_perm_b32 and
+// reused by every output that needs it. UPDATE: requests of exactly U tokens.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float dot2_bf16(uint32_t w_pair, uint32_t x_pair, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w_pair),
+                                         __builtin_bit_cast(bf16x2, x_pair), acc, false);
+}
+
+// Pair of channel ch's values from rows a (older, low half) and b (newer).
+__device__ __forceinline__ uint32_t row_pair(const u32x4& ra, const u32x4& rb, int ch) {
+  return __builtin_amdgcn_perm(rb[ch >> 1], ra[ch >> 1], (ch & 1) ? 0x07060302u : 0x05040100u);
+}
+
+template <int K, int D, int U, bool SILU, bool UPDATE>
+__global__ __launch_bounds__(kBlock) void conv_pairs(ConvArgs a) {
+#if SC_LDS_PAD > 0
+  __shared__ uint8_t occupancy_pad[SC_LDS_PAD];
+  if (a.C < 0) occupancy_pad[threadIdx.x] = 0;
+#endif
+  using E = BF16;
+  using S = E::S;
+  constexpr int H = (K - 1) * D;
+  constexpr int NP = K / 2;
+  constexpr int VEC = 8;
+  static_assert(K % 2 == 0 && K >= 2, "pairs of taps");
+  static_assert(U >= H, "the chunk must cover the history (halo from x only)");
+
+  const int lb = logical_block(a.n_logical, a.per_xcd);
+  if (lb < 0) return;
+  const int cid = lb / a.n_cblk, cb = lb - cid * a.n_cblk;
+  const int c0 = (cb * kBlock + (int)threadIdx.x) * VEC;
+  const bool lane_ok = c0 < a.C;
+
+  // Loads in the order they are consumed (vmcnt retires in issue order).
+  // The weights do not depend on the request: issue them before the lookup.
+  uint32_t wp[NP][VEC];
+  u32x4 bsv = u32x4{0, 0, 0, 0};
+  {
+    u32x4 wv[NP * 2];
+#pragma unroll
+    for (int v = 0; v < NP * 2; ++v)
+      wv[v] = lane_ok ? ld16((const S*)a.w + (int64_t)c0 * K + v * VEC) : u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int ch = 0; ch < VEC; ++ch)
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        const int word = ch * NP + p;
+        wp[p][ch] = wv[word >> 2][word & 3];
+      }
+    if (a.bias && lane_ok) bsv = ld16((const S*)a.bias + c0);
+  }
+
+  // chunk -> request (one round of loads), bounds and chunk range
+  int r, s0 = 0, s1 = 0;
+  if (UPDATE || a.qsl == nullptr) {
+    const int cpr = (a.q + a.chunk - 1) / a.chunk;
+    r = cid / cpr;
+    s0 = r * a.q;
+    s1 = s0 + a.q;
+  } else {
+    r = find_request_bounds(a.qsl, a.batch, cid, a.chunk, s0, s1);
+  }
+  if (r >= a.batch || s0 < 0) return;
+  const int j = (UPDATE || a.qsl == nullptr) ? cid - r * ((a.q + a.chunk - 1) / a.chunk)
+                                             : cid - (s0 / a.chunk + r);
+  int L = s1 - s0;
+  if (j < 0 || L <= 0 || s0 >= a.num_tokens) return;
+  if ((int64_t)s0 + L > a.num_tokens) L = (int)(a.num_tokens - s0);
+  const int t0 = j * a.chunk;
+  if (t0 >= L || !lane_ok) return;
+  const int t1 = min(L, t0 + a.chunk);
+
+  const int64_t xrs = a.x_rs, ors = a.out_rs;
+  const S* xb = (const S*)a.x + (int64_t)s0 * xrs + c0;
+  S* ob = (S*)a.out + (int64_t)s0 * ors + c0;
+
+  u32x4 raw[H + U];
+  if (j > 0) {
+#pragma unroll
+    for (int u = 0; u < H; ++u) raw[u] = ld16(xb + (int64_t)(t0 - H + u) * xrs);
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int t = UPDATE ? u : min(t0 + u, t1 - 1);
+    raw[H + u] = ld16(xb + (int64_t)t * xrs);
+  }
+  // the slot is needed by the request's first chunk only (history and write-back)
+  int32_t slot = -1;
+  bool valid = false, hflag = false;
+  u32x4 old[H];
+#pragma unroll
+  for (int v = 0; v < H; ++v) old[v] = u32x4{0, 0, 0, 0};
+  if (j == 0) {
+    slot = a.slots[(int64_t)r * a.slot_stride];
+    valid = slot >= 0 && slot < a.num_slots;
+    hflag = valid && (a.has_init ? a.has_init[r] != 0 : true);
+  }
+  S* sp = (S*)a.pool + ((int64_t)(valid ? slot : 0) * a.C + c0) * H;
+  if (hflag) {
+#pragma unroll
+    for (int v = 0; v < H; ++v) old[v] = ld16(sp + v * VEC);
+  }
+  Work w;
+  w.r = r;
+  w.j = j;
+  w.L = L;
+  w.t0 = t0;
+  w.t1 = t1;
+  w.start = s0;
+  w.slot = slot;
+  w.valid = valid;
+  w.h = hflag;
+  float bs[VEC];
+  E::unpack(bsv, bs);
+  if (w.j == 0) {
+    // history (ch, u) layout -> rows
+#pragma unroll
+    for (int u = 0; u < H; ++u) {
+      raw[u] = u32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int ch = 0; ch < VEC; ++ch) E::set(raw[u], ch, get_flat<E>(old, ch * H + u));
+    }
+  }
+
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    if (UPDATE || w.t0 + u < w.t1) {
+      float z[VEC];
+#pragma unroll
+      for (int ch = 0; ch < VEC; ++ch) {
+        float acc = bs[ch];
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+          // taps 2p and 2p+1 sit at rows H+u-(K-1-2p)*D and D later
+          const int r0 = H + u - (K - 1 - 2 * p) * D;
+          acc = dot2_bf16(wp[p][ch], row_pair(raw[r0], raw[r0 + D], ch), acc);
+        }
+        z[ch] = SILU ? silu(acc) : acc;
+      }
+      st16_stream(ob + (int64_t)(w.t0 + u) * ors, E::pack(z));
+    }
+  }
+
+  if (w.j == 0 && w.valid) {
+    if constexpr (UPDATE) {
+      // new state = ext[U .. U+H), all in registers
+      u32x4 nv[H];
+#pragma unroll
+      for (int jj = 0; jj < H; ++jj)
+#pragma unroll
+        for (int ch = 0; ch < VEC; ++ch) set_flat<E>(nv, ch * H + jj, E::get(raw[U + jj], ch));
+#pragma unroll
+      for (int v = 0; v < H; ++v) st16(sp + v * VEC, nv[v]);
+    } else {
+      write_state<E, H>(sp, old, w.L, xb, xrs);
+    }
+  }
+  if (!UPDATE && a.ckpt_grid > 0 && a.qsl != nullptr) {
+    const int g = a.ckpt_grid;
+    const int cu0 = a.cu_ckpt[w.r], cnt = a.cu_ckpt[w.r + 1] - cu0;
+    for (int m = w.t0 / g + 1; m <= cnt && (int64_t)m * g <= w.t1; ++m) {
+      const int32_t dst = a.ckpt_slots[cu0 + m - 1];
+      if (dst < 0 || dst >= a.num_slots) continue;
+      store_window_from_x<E, H>((S*)a.pool + ((int64_t)dst * a.C + c0) * H, xb, xrs, m * g);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bf16 decode / multi-token update (requests of exactly Q tokens), R requests
+// per workgroup. The state rows of a workgroup's channels are contiguous in the
+// (slot, C, H) pool; they are loaded and stored with unit-stride lanes and
+// transposed to and from the per-lane (channel, tap) order through LDS. The
+// weights are loaded once for the R requests. Same tap pairing and dot2 order
+// as conv_pairs, so a decode step equals the matching prefill token bit for bit.
+// ---------------------------------------------------------------------------
+template <int K, int D, int Q, int R, bool SILU>
+__global__ __launch_bounds__(kBlock) void conv_update_pairs(ConvArgs a) {
+  using E = BF16;
+  using S = E::S;
+  constexpr int H = (K - 1) * D;
+  constexpr int NP = K / 2;
+  constexpr int VEC = 8;
+  __shared__ u32x4 xch[H * kBlock];
+
+  const int lb = logical_block(a.n_logical, a.per_xcd);
+  if (lb < 0) return;                       // uniform over the workgroup
+  const int grp = lb / a.n_cblk, cb = lb - grp * a.n_cblk;
+  const int tid = (int)threadIdx.x;
+  const int cbase = cb * kBlock * VEC;      // first channel of the workgroup
+  const int c0 = cbase + tid * VEC;
+  const bool lane_ok = c0 < a.C;
+  // vectors of the workgroup's state region that exist (partial last block)
+  const int nvec = (min(a.C - cbase, kBlock * VEC) / VEC) * H;
+
+  uint32_t wp[NP][VEC];
+  u32x4 bsv = u32x4{0, 0, 0, 0};
+  if (lane_ok) {
+    u32x4 wv[NP * 2];
+#pragma unroll
+    for (int v = 0; v < NP * 2; ++v) wv[v] = ld16((const S*)a.w + (int64_t)c0 * K + v * VEC);
+#pragma unroll
+    for (int ch = 0; ch < VEC; ++ch)
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        const int word = ch * NP + p;
+        wp[p][ch] = wv[word >> 2][word & 3];
+      }
+    if (a.bias) bsv = ld16((const S*)a.bias + c0);
+  }
+
+  // issue every request's loads: the token rows first (independent of the
+  // slot), then the slot indices, then the state (unit stride over the region)
+  int32_t slot[R];
+  bool valid[R], hflag[R];
+  u32x4 st[R][H], xr[R][Q];
+#pragma unroll
+  for (int rr = 0; rr < R; ++rr) {
+    const int r = grp * R + rr;
+#pragma unroll
+    for (int u = 0; u < Q; ++u)
+      xr[rr][u] = (r < a.batch && lane_ok)
+                      ? ld16((const S*)a.x + ((int64_t)r * Q + u) * a.x_rs + c0)
+                      : u32x4{0, 0, 0, 0};
+  }
+#pragma unroll
+  for (int rr = 0; rr < R; ++rr) {
+    const int r = grp * R + rr;
+    slot[rr] = r < a.batch ? a.slots[(int64_t)r * a.slot_stride] : -1;
+    valid[rr] = slot[rr] >= 0 && slot[rr] < a.num_slots;
+    hflag[rr] = valid[rr] && (a.has_init ? a.has_init[r] != 0 : true);
+  }
+#pragma unroll
+  for (int rr = 0; rr < R; ++rr) {
+    const S* sp = (const S*)a.pool + ((int64_t)(valid[rr] ? slot[rr] : 0) * a.C + cbase) * H;
+#pragma unroll
+    for (int k = 0; k < H; ++k) {
+      const int vi = tid + k * kBlock;
+      st[rr][k] = (hflag[rr] && vi < nvec) ? ld16(sp + vi * VEC) : u32x4{0, 0, 0, 0};
+    }
+  }
+  float bs[VEC];
+  E::unpack(bsv, bs);
+
+#pragma unroll
+  for (int rr = 0; rr < R; ++rr) {
+    const int r = grp * R + rr;
+    // state region -> per-lane (channel, tap) order
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < H; ++k) xch[tid + k * kBlock] = st[rr][k];
+    __syncthreads();
+    u32x4 old[H];
+#pragma unroll
+    for (int k = 0; k < H; ++k) old[k] = xch[tid * H + k];
+    u32x4 raw[H + Q];
+#pragma unroll
+    for (int u = 0; u < H; ++u) {
+      raw[u] = u32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int ch = 0; ch < VEC; ++ch) E::set(raw[u], ch, get_flat<E>(old, ch * H + u));
+    }
+#pragma unroll
+    for (int u = 0; u < Q; ++u) raw[H + u] = xr[rr][u];
+    if (r < a.batch && lane_ok) {
+#pragma unroll
+      for (int u = 0; u < Q; ++u) {
+        float z[VEC];
+#pragma unroll
+        for (int ch = 0; ch < VEC; ++ch) {
+          float acc = bs[ch];
+#pragma unroll
+          for (int p = 0; p < NP; ++p) {
+            const int r0 = H + u - (K - 1 - 2 * p) * D;
+            acc = dot2_bf16(wp[p][ch], row_pair(raw[r0], raw[r0 + D], ch), acc);
+          }
+          z[ch] = SILU ? silu(acc) : acc;
+        }
+        st16_stream((S*)a.out + ((int64_t)r * Q + u) * a.out_rs + c0, E::pack(z));
+      }
+    }
+    // new state = ext[Q .. Q+H) in (channel, tap) order -> region order
+    u32x4 nv[H];
+#pragma unroll
+    for (int jj = 0; jj < H; ++jj)
+#pragma unroll
+      for (int ch = 0; ch < VEC; ++ch) set_flat<E>(nv, ch * H + jj, E::get(raw[Q + jj], ch));
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < H; ++k) xch[tid * H + k] = nv[k];
+    __syncthreads();
+    if (valid[rr]) {
+      S* dp = (S*)a.pool + ((int64_t)slot[rr] * a.C + cbase) * H;
+#pragma unroll
+      for (int k = 0; k < H; ++k) {
+        const int vi = tid + k * kBlock;
+        if (vi < nvec) st16(dp + vi * VEC, xch[vi]);
       }
     }
   }
@@ -373,9 +706,16 @@ __global__ __launch_bounds__(kBlock) void conv_generic(ConvArgs a, int K, int D)
 // ---------------------------------------------------------------------------
 namespace {
 
+bool fast_shape(int K, int D) {
+  return (K == 4 && (D == 1 || D == 2 || D == 3)) || (D == 1 && (K == 2 || K == 3));
+}
+bool pairs_shape(int K, int D) {
+  return (K == 4 && (D == 1 || D == 2 || D == 3)) || (K == 2 && D == 1);
+}
+
 template <class E, int K, int D, bool SILU>
 hipError_t launch_kd(const ConvArgs& a, int qc, dim3 grid, hipStream_t s) {
-  constexpr int U = ((K - 1) * D <= 4) ? 8 : 4;
+  constexpr int U = ((K - 1) * D <= 4) ? SC_UNROLL_SMALL_H : SC_UNROLL_LARGE_H;
   switch (qc) {
     case 1: hipLaunchKernelGGL((conv_fast<E, K, D, U, SILU, 1>), grid, dim3(kBlock), 0, s, a); break;
     case 2: hipLaunchKernelGGL((conv_fast<E, K, D, U, SILU, 2>), grid, dim3(kBlock), 0, s, a); break;
@@ -385,9 +725,37 @@ hipError_t launch_kd(const ConvArgs& a, int qc, dim3 grid, hipStream_t s) {
   return hipGetLastError();
 }
 
+// tokens per one-pass prefill chunk for history length H (must be >= H)
+constexpr int pairs_chunk(int H) { return H <= 4 ? SC_PAIRS_CHUNK_SMALL : (H <= 8 ? 8 : 16); }
+// requests per update workgroup
+constexpr int update_reqs(int H, int Q) { return (H <= 4 && Q == 1) ? SC_UPDATE_REQS : (H <= 4 ? 2 : (Q == 1 ? 2 : 1)); }
+
+template <int K, int D, bool SILU>
+hipError_t launch_pairs_kd(const ConvArgs& a, int qc, dim3 grid, hipStream_t s) {
+  constexpr int H = (K - 1) * D;
+  switch (qc) {
+    case 1: hipLaunchKernelGGL((conv_update_pairs<K, D, 1, update_reqs(H, 1), SILU>), grid, dim3(kBlock), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((conv_update_pairs<K, D, 2, update_reqs(H, 2), SILU>), grid, dim3(kBlock), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((conv_update_pairs<K, D, 4, update_reqs(H, 4), SILU>), grid, dim3(kBlock), 0, s, a); break;
+    default: hipLaunchKernelGGL((conv_pairs<K, D, pairs_chunk(H), SILU, false>), grid, dim3(kBlock), 0, s, a); break;
+  }
+  return hipGetLastError();
+}
+
+template <bool SILU>
+hipError_t launch_pairs(const ConvArgs& a, int K, int D, int qc, dim3 grid, hipStream_t s) {
+  if (K == 4 && D == 1) return launch_pairs_kd<4, 1, SILU>(a, qc, grid, s);
+  if (K == 4 && D == 2) return launch_pairs_kd<4, 2, SILU>(a, qc, grid, s);
+  if (K == 4 && D == 3) return launch_pairs_kd<4, 3, SILU>(a, qc, grid, s);
+  return launch_pairs_kd<2, 1, SILU>(a, qc, grid, s);
+}
+
 template <class E, bool SILU>
 hipError_t launch_typed(const ConvArgs& a, int K, int D, bool fast, int qc, dim3 grid,
                         hipStream_t s) {
+  if (a.chunk == pairs_chunk((K - 1) * D) && fast && E::VEC == 8 && pairs_shape(K, D) &&
+      !SC_NO_PAIRS)
+    return launch_pairs<SILU>(a, K, D, qc, grid, s);
   if (fast) {
     if (K == 4 && D == 1) return launch_kd<E, 4, 1, SILU>(a, qc, grid, s);
     if (K == 4 && D == 3) return launch_kd<E, 4, 3, SILU>(a, qc, grid, s);
@@ -399,9 +767,7 @@ hipError_t launch_typed(const ConvArgs& a, int K, int D, bool fast, int qc, dim3
   return hipGetLastError();
 }
 
-bool fast_shape(int K, int D) {
-  return (K == 4 && (D == 1 || D == 2 || D == 3)) || (D == 1 && (K == 2 || K == 3));
-}
+
 
 }  // namespace
 
@@ -411,15 +777,23 @@ hipError_t launch_conv(ConvArgs a, int dtype, int K, int D, bool silu_act, bool 
   const int vec = dtype == 1 ? 8 : 4;
   const int H = (K - 1) * D;
   const bool fast = aligned16 && (a.C % vec == 0) && fast_shape(K, D);
+  // the one-pass kernel takes its halo from x: its chunk covers H by construction
+  const bool pairs = fast && dtype == 1 && pairs_shape(K, D) && !SC_NO_PAIRS;
   const bool uniform = a.qsl == nullptr;
-  a.chunk = fast ? kChunk : (H > kChunk ? H : kChunk);
+  a.chunk = pairs ? pairs_chunk(H) : fast ? kChunk : (H > kChunk ? H : kChunk);
   int qc = 0;
-  if (fast && uniform && (a.q == 1 || a.q == 2 || a.q == 4)) qc = a.q;
+  if (fast && uniform && (a.q == 1 || a.q == 2 || a.q == 4) && a.q <= a.chunk) qc = a.q;
   const int64_t per_block_ch = (int64_t)kBlock * (fast ? vec : 1);
   a.n_cblk = (int)((a.C + per_block_ch - 1) / per_block_ch);
   int64_t n_chunks;
-  if (uniform) n_chunks = (int64_t)a.batch * ((a.q + a.chunk - 1) / a.chunk);
-  else n_chunks = a.num_tokens / a.chunk + a.batch;
+  if (pairs && qc) {
+    const int R = update_reqs(H, qc);
+    n_chunks = (a.batch + R - 1) / R;     // workgroup groups of R requests
+  } else if (uniform) {
+    n_chunks = (int64_t)a.batch * ((a.q + a.chunk - 1) / a.chunk);
+  } else {
+    n_chunks = a.num_tokens / a.chunk + a.batch;
+  }
   const int64_t n_logical = n_chunks * a.n_cblk;
   if (n_logical > 0x7FFFFFF0LL) return hipErrorInvalidValue;
   a.n_logical = (int)n_logical;

@@ -7,7 +7,31 @@
 
 namespace sc {
 
-constexpr int kChunk = 64;   // tokens per prefill chunk (>= H for the fast kernels)
+#ifndef SC_PREFILL_CHUNK
+#define SC_PREFILL_CHUNK 16
+#endif
+#ifndef SC_UNROLL_SMALL_H
+#define SC_UNROLL_SMALL_H 16
+#endif
+#ifndef SC_UNROLL_LARGE_H
+#define SC_UNROLL_LARGE_H 16
+#endif
+#ifndef SC_NT_LOADS
+#define SC_NT_LOADS 0
+#endif
+#ifndef SC_LDS_PAD
+#define SC_LDS_PAD 0
+#endif
+#ifndef SC_NO_PAIRS
+#define SC_NO_PAIRS 0
+#endif
+#ifndef SC_PAIRS_CHUNK_SMALL
+#define SC_PAIRS_CHUNK_SMALL 8
+#endif
+#ifndef SC_UPDATE_REQS
+#define SC_UPDATE_REQS 4
+#endif
+constexpr int kChunk = SC_PREFILL_CHUNK;   // tokens per prefill chunk (>= H for the fast kernels)
 
 // Depthwise conv launch arguments (by value into the kernel).
 struct ConvArgs {
@@ -42,29 +66,6 @@ hipError_t launch_state_copy(bool gather, const void* src, void* dst, int64_t ro
                              int32_t num_slots, const int32_t* idx, int64_t idx_stride,
                              int32_t n, hipStream_t stream);
 
-// CCA launch arguments.
-struct CcaArgs {
-  const void* q;
-  const void* k;
-  const void* v_cur;
-  const void* v_del;
-  void* out;
-  const void* w_dw;
-  const void* b_dw;
-  const void* w_gr;
-  const void* b_gr;
-  const void* delayed_init;   // nullable
-  void* conv_state;
-  void* delayed_state;
-  const int32_t* decode_slots;
-  const int32_t* prefill_qsl;
-  const int32_t* prefill_slots;
-  const uint8_t* prefill_h;
-  int64_t q_rs, k_rs, vc_rs, vd_rs, out_rs, dslot_stride, pslot_stride;
-  int64_t num_tokens;
-  int32_t nq, nkv, hd, t0, t1, num_slots, num_decodes, num_prefills;
-};
 
-hipError_t launch_cca(const CcaArgs& a, hipStream_t stream);
 
 }  // namespace sc

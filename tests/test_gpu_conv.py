@@ -89,9 +89,9 @@ def test_config4_full():
 # ----------------------------------------------------------------------------
 @pytest.mark.parametrize("d", [1, 3])
 def test_chunk_edges_and_short_requests(d):
-    lens = [1, 2, 3, 8, 9, 10, 63, 64, 65, 127, 128, 129, 200]
+    lens = [1, 2, 3, 8, 9, 10, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 200]
     case = conv_case("edges", 500 + d, C=256, K=4, d=d, dtype="bf16", act="silu",
-                     w_std=0.25, bias_std=0.1, num_slots=96, prefill_lens=lens,
+                     w_std=0.25, bias_std=0.1, num_slots=128, prefill_lens=lens,
                      prefill_h_p=0.5, ckpt_grid=max(16, 3 * d))
     parity(case)
 
