@@ -132,6 +132,51 @@ class ConvRunner:
                                        activation=c.act, ckpt=b["ck"])
 
 
+def cca_alg_bytes(case):
+    """Algorithmic HBM bytes of one CCA pass (main kernel + state update):
+    q, k, v_cur, v_del read once, the output row written once, each request's
+    conv history and delayed value read (when continued) and written once,
+    weights and biases read once. Returns (main_bytes, state_update_bytes)."""
+    es, T, C, n = 2, case.T, case.C, case.n
+    vd = case.nkv * case.hd // 2
+    main = T * (C + 2 * vd) * es + T * case.out_width * es
+    main += (C * case.t0 + C + C * case.hd * case.t1 + C + vd) * es
+    hs = [1] * case.num_decodes + [int(h) for h in case.prefill_h]
+    slots = list(case.decode_slots) + list(case.prefill_slots)
+    live = [h for h, s in zip(hs, slots) if 0 <= s < case.num_slots]
+    main += sum(live) * (C * n + vd) * es            # history read for continued requests
+    upd = len(live) * (C * n + vd) * es              # new history and delayed value
+    return main, upd
+
+
+class CcaRunner:
+    def __init__(self, case, nsets):
+        import numpy as np
+        import torch
+        from tests._gpu import dev
+        self.case = case
+        c = case
+        self.w = [dev(c.w_dw), dev(c.b_dw), dev(c.w_gr), dev(c.b_gr), dev(c.delayed_init)]
+        self.meta = [dev(c.decode_slots), dev(c.qsl_p), dev(c.prefill_slots),
+                     dev(np.asarray(c.prefill_h, np.uint8))]
+        base = [dev(c.q), dev(c.k), dev(c.v_cur), dev(c.v_del), dev(c.conv_state),
+                dev(c.delayed_state)]
+        self.sets = []
+        for i in range(nsets):
+            q, k, vc, vdl, cs, ds = base if i == 0 else [t.clone() for t in base]
+            out = torch.empty((c.T, c.out_width), dtype=torch.bfloat16, device="cuda")
+            self.sets.append((q, k, vc, vdl, out, cs, ds))
+        self.kernels = ["cca_main+state"]
+
+    def step(self, i, only=None):
+        import stateful_causal_short_amd as scs
+        c = self.case
+        q, k, vc, vdl, out, cs, ds = self.sets[i % len(self.sets)]
+        scs.sc_cca_qk_conv(q, k, vc, vdl, out, *self.w, cs, ds, *self.meta,
+                           num_q_heads=c.nq, num_kv_heads=c.nkv, head_dim=c.hd,
+                           t0=c.t0, t1=c.t1)
+
+
 def cpu_baseline_conv(case, budget_s=10.0):
     """The oracle, as it stands, on the same batch; repeated until ~budget_s."""
     import oracle
@@ -172,6 +217,52 @@ def traffic_for(kernel_key):
     if not e or e.get("source_sha") != source_sha():
         return None
     return e.get("bytes_per_launch")
+
+
+def cca_bench(args):
+    """CCA q/k conv on the 32k-token mixed batch (512 decodes + 64 prefills,
+    16 q heads, 4 kv heads, head_dim 128, kernels 2 and 2). One step = one
+    sc_cca_qk_conv call: the fused main kernel, then the state update."""
+    import numpy as np
+    import torch
+    import synthetic
+    case = synthetic.config5()
+    main_b, upd_b = cca_alg_bytes(case)
+    set_bytes = main_b
+    nsets = int(min(6, max(2, -(-ROTATE_BYTES // set_bytes))))
+    log(f"CCA T={case.T} C={case.C}; alg bytes/step main={main_b} state={upd_b}; "
+        f"{nsets} rotating buffer sets")
+    run = CcaRunner(case, nsets)
+    for i in range(args.warmup):
+        run.step(i)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for i in range(args.steps):
+        run.step(args.warmup + i)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / args.steps
+    flops = 2.0 * case.T * case.C * case.hd * case.t1
+    result = {
+        "metric": "tokens/s and achieved HBM GB/s (% of peak), CCA q/k conv",
+        "value": case.T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": case.name, "decodes": case.num_decodes,
+                   "prefills": case.num_prefills, "tokens": case.T, "q_heads": case.nq,
+                   "kv_heads": case.nkv, "head_dim": case.hd, "t0": case.t0, "t1": case.t1},
+        "hbm_gbps": (main_b + upd_b) / (ms * 1e-3) / 1e9,
+        "pct_peak": 100.0 * (main_b + upd_b) / (ms * 1e-3) / 1e9 / PEAK_GBPS,
+        "grouped_conv_tflops": flops / (ms * 1e-3) / 1e12,
+        "roofline": {"kernel": "cca_main+state", "bound": "hbm",
+                     "achieved": (main_b + upd_b) / (ms * 1e-3) / 1e9, "peak": PEAK_GBPS,
+                     "unit": "GB/s", "frac": (main_b + upd_b) / (ms * 1e-3) / 1e9 / PEAK_GBPS,
+                     "traffic": None, "alg_bytes_per_launch": main_b + upd_b},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(result), flush=True)
 
 
 def copy_calibration(args):
@@ -230,7 +321,7 @@ def main():
     log(f"device {torch.cuda.get_device_name(0)}; workload {args.workload}")
 
     if args.workload == "cca":
-        raise SystemExit("cca workload: the CCA kernel is not built yet")
+        return cca_bench(args)
     if args.workload == "copy":
         return copy_calibration(args)
 

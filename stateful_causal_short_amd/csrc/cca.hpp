@@ -6,6 +6,13 @@
 
 namespace sc {
 
+#ifndef SC_CCA_TILE
+#define SC_CCA_TILE 64       // token rows per CCA workgroup (multiple of 32)
+#endif
+#ifndef SC_CCA_GENERIC
+#define SC_CCA_GENERIC 0     // 1 = always use the scalar CCA kernel
+#endif
+
 // CCA launch arguments.
 struct CcaArgs {
   const void* q;

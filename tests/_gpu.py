@@ -106,3 +106,50 @@ def check_close(gpu: np.ndarray, ref64: np.ndarray, absum: np.ndarray, dtype: st
             f"{what}: {len(bad)} of {ok.size} outside tolerance; first at {i}: "
             f"gpu={g[i]!r} ref={ref64[i]!r} tol={tol[i]!r} floor={floor[i]!r}")
     return float(((diff > tol) & (diff <= floor)).sum()) / max(1, ok.size)
+
+
+def run_cca_case(case, *, conv_state=None, delayed_state=None, fused=False,
+                 no_delayed_init=False):
+    """Runs a CcaCase through sc_cca_qk_conv. Returns (out, conv_state_after,
+    delayed_state_after) as NumPy arrays. fused=True passes q, k, v_cur and
+    v_del as column slices of one (T, X) projection output (strided rows)."""
+    import torch
+    import stateful_causal_short_amd as scs
+    T = case.T
+    if fused:
+        parts = [case.q, case.k, case.v_cur, case.v_del]
+        widths = [p.shape[1] for p in parts]
+        big = np.zeros((T, sum(widths) + 8), np.uint16)
+        off, views = 0, []
+        for p_, wdt in zip(parts, widths):
+            big[:, off:off + wdt] = p_
+            off += wdt
+        bd = dev(big)
+        off, views = 0, []
+        for wdt in widths:
+            views.append(bd[:, off:off + wdt])
+            off += wdt
+        qd, kd, vcd, vdd = views
+    else:
+        qd, kd, vcd, vdd = dev(case.q), dev(case.k), dev(case.v_cur), dev(case.v_del)
+    out = torch.zeros((T, case.out_width), dtype=torch.bfloat16, device="cuda")
+    cs = dev(case.conv_state if conv_state is None else conv_state)
+    ds = dev(case.delayed_state if delayed_state is None else delayed_state)
+    dsl = dev(case.decode_slots) if case.num_decodes else None
+    qsl = dev(case.qsl_p) if case.num_prefills else None
+    psl = dev(case.prefill_slots) if case.num_prefills else None
+    ph = dev(np.asarray(case.prefill_h, np.uint8)) if case.num_prefills else None
+    scs.sc_cca_qk_conv(qd, kd, vcd, vdd, out, dev(case.w_dw), dev(case.b_dw),
+                       dev(case.w_gr), dev(case.b_gr),
+                       None if no_delayed_init else dev(case.delayed_init), cs, ds,
+                       dsl, qsl, psl, ph, num_q_heads=case.nq, num_kv_heads=case.nkv,
+                       head_dim=case.hd, t0=case.t0, t1=case.t1)
+    torch.cuda.synchronize()
+    return host(out), host(cs), host(ds)
+
+
+def cca_floor_rel(case) -> float:
+    """fp32 accumulation bound for one CCA output: bias + hd*t1 products +
+    residual terms (2 per query head, 2G per key head), gamma_n = n * 2^-24."""
+    G = case.nq // case.nkv
+    return (case.hd * case.t1 + 2 * G + 4) * 2.0 ** -24

@@ -1,0 +1,119 @@
+"""GPU parity of the CCA q/k conv (sc_cca_qk_conv) against the CPU oracle.
+
+Bar: conv and delayed states bit-exact; value half of the output (v_cur copy
+and delayed shift) bit-exact; q/k outputs within 2 bf16 ulp of the oracle's
+float64 result, or within the fp32 accumulation bound n * 2^-24 of the sum of
+|terms| (n = bias + hd*t1 products + residual terms). Both sides take the
+depthwise intermediate's bf16 rounding from the same fp32 fused multiply-add
+chain (bias first, taps in order), so that decision is identical."""
+from dataclasses import replace
+
+import numpy as np
+import pytest
+
+import oracle
+import synthetic
+from tests._gpu import cca_floor_rel, check_close, run_cca_case
+
+pytestmark = pytest.mark.gpu
+
+
+def parity(case, *, row_mask=None, **kw):
+    print(f"[gpu] cca {case.name} T={case.T} nq={case.nq} nkv={case.nkv} hd={case.hd} "
+          f"t0={case.t0} t1={case.t1} kw={kw}", flush=True)
+    out, cs, ds = run_cca_case(case, **kw)
+    ocase = case
+    if kw.get("no_delayed_init"):
+        ocase = replace(case, delayed_init=np.zeros_like(case.delayed_init))
+    ref, _, _, absum = oracle.cca(ocase, out_dtype="f64", dw_mode=1, absum=True,
+                                  row_mask=row_mask)
+    _, rcs, rds, _ = oracle.cca(ocase, dw_mode=1, row_mask=np.zeros(case.T, np.uint8))
+    np.testing.assert_array_equal(cs, rcs, err_msg="conv state not bit-exact")
+    np.testing.assert_array_equal(ds, rds, err_msg="delayed state not bit-exact")
+    C = case.C
+    m = None if row_mask is None else row_mask.astype(bool)
+    # value half: exact copies
+    ref_v = ref[:, C:] if m is None else ref[m][:, C:]
+    got_v = out[:, C:] if m is None else out[m][:, C:]
+    np.testing.assert_array_equal(synthetic.bf16_to_f32(got_v).astype(np.float64), ref_v,
+                                  err_msg="value half not bit-exact")
+    frac = check_close(out[:, :C], ref[:, :C], absum[:, :C], "bf16", cca_floor_rel(case),
+                       what="q/k", mask=m)
+    print(f"[gpu] cca {case.name}: ok (floor-only share {frac:.2e})", flush=True)
+
+
+def sample_rows(case, n_random=384, seed=1):
+    m = np.zeros(case.T, np.uint8)
+    m[:min(case.T, 80)] = 1                              # decodes and first tile
+    starts = case.num_decodes + case.qsl_p[:-1]
+    for s, L in zip(starts, np.diff(case.qsl_p)):
+        m[s:s + min(int(L), 3)] = 1                      # history rows
+        m[max(s, s + L - 2):s + L] = 1
+    for e in range(64, case.T, 64):
+        m[e - 1:e + 1] = 1                               # tile edges
+    rng = np.random.default_rng(seed)
+    m[rng.integers(0, case.T, n_random)] = 1
+    return m
+
+
+def test_config5_full():
+    case = synthetic.config5()
+    parity(case, row_mask=sample_rows(case))
+
+
+def test_config5_small_tile_edges():
+    case = synthetic.cca_case("cca_edges", 501, num_decodes=70,
+                              prefill_lens=[1, 2, 3, 62, 63, 64, 65, 130, 7], num_slots=128)
+    case.prefill_h[:] = [0, 1, 1, 0, 1, 0, 1, 1, 0]
+    parity(case)
+
+
+@pytest.mark.parametrize("nq,nkv,t0", [(4, 4, 2), (8, 1, 2), (4, 2, 1), (4, 2, 3), (2, 1, 4)])
+def test_mfma_shapes(nq, nkv, t0):
+    case = synthetic.cca_case("cca_shape", 600 + nq * 10 + nkv + t0, nq=nq, nkv=nkv, hd=128,
+                              t0=t0, t1=2, num_decodes=9,
+                              prefill_lens=[1, 5, 70, 33], num_slots=64)
+    parity(case)
+
+
+@pytest.mark.parametrize("hd,t0,t1", [(64, 2, 2), (32, 2, 3), (16, 3, 1)])
+def test_generic_shapes(hd, t0, t1):
+    case = synthetic.cca_case("cca_generic", 700 + hd + t0 + t1, nq=4, nkv=2, hd=hd,
+                              t0=t0, t1=t1, num_decodes=5, prefill_lens=[1, 2, 9, 20],
+                              num_slots=32)
+    parity(case)
+
+
+def test_padding_slots_fused_rows_and_no_delayed_init():
+    case = synthetic.cca_case("cca_pad", 801, num_decodes=6, prefill_lens=[4, 80, 1],
+                              num_slots=16)
+    case.decode_slots[2] = -1
+    case.decode_slots[4] = 16               # out of range: padding row
+    case.prefill_slots[1] = -5
+    case.prefill_h[:] = 1
+    parity(case, fused=True, no_delayed_init=True)
+
+
+def test_gpu_cca_chunked_equals_one_shot():
+    L = 150
+    src = synthetic.cca_case("cca_carry", 901, num_decodes=0, prefill_lens=[L], num_slots=2)
+    src.prefill_h[:] = 1
+    src.prefill_slots[:] = 1
+    one, cs1, ds1 = run_cca_case(src)
+    cs, ds = src.conv_state.copy(), src.delayed_state.copy()
+    outs = []
+    for lo, hi, dec in [(0, 1, False), (1, 70, False), (70, 71, True), (71, 149, False),
+                        (149, 150, True)]:
+        sl = slice(lo, hi)
+        kw = dict(q=src.q[sl], k=src.k[sl], v_cur=src.v_cur[sl], v_del=src.v_del[sl])
+        if dec:
+            c = replace(src, num_decodes=hi - lo, decode_slots=np.ones(hi - lo, np.int32),
+                        qsl_p=np.zeros(1, np.int32), prefill_slots=np.zeros(0, np.int32),
+                        prefill_h=np.zeros(0, np.uint8), **kw)
+        else:
+            c = replace(src, qsl_p=np.array([0, hi - lo], np.int32), **kw)
+        o, cs, ds = run_cca_case(c, conv_state=cs, delayed_state=ds)
+        outs.append(o)
+    np.testing.assert_array_equal(np.concatenate(outs), one)
+    np.testing.assert_array_equal(cs, cs1)
+    np.testing.assert_array_equal(ds, ds1)
