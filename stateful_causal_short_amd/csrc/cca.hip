@@ -38,6 +38,11 @@ namespace {
 constexpr int kQslCache = 1024;   // prefill boundaries cached in LDS (else searched in HBM)
 
 __device__ __forceinline__ float bf2f(uint32_t b) { return __uint_as_float(b << 16); }
+// two fp32 -> one word of two bf16 (lo, hi), one v_cvt_pk_bf16_f32
+__device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
+  f32x2 p = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(p, bf16x2));
+}
 __device__ __forceinline__ uint32_t f2bf(float v) {
   return __builtin_bit_cast(uint16_t, (__bf16)v);
 }
@@ -205,17 +210,89 @@ __global__ __launch_bounds__(kBlock) void cca_state_update(CcaArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// MFMA main kernel (hd = 128, t1 = 2, t0 = T0 <= 4), MT rows per workgroup
+// vectorised state update: 8 channels (16 bytes) per lane, history length N
 // ---------------------------------------------------------------------------
+template <int N>
+__global__ __launch_bounds__(kBlock) void cca_state_update_vec(CcaArgs a) {
+  const int C = (a.nq + a.nkv) * a.hd, qd = a.nq * a.hd;
+  const int vd = a.nkv * a.hd / 2;
+  const int req = blockIdx.x;
+  int64_t start;
+  int L;
+  int32_t slot;
+  bool h;
+  if (req < a.num_decodes) {
+    start = req;
+    L = 1;
+    slot = a.decode_slots[(int64_t)req * a.dslot_stride];
+    h = true;
+  } else {
+    const int r = req - a.num_decodes;
+    start = a.num_decodes + a.prefill_qsl[r];
+    L = a.prefill_qsl[r + 1] - a.prefill_qsl[r];
+    slot = a.prefill_slots[(int64_t)r * a.pslot_stride];
+    h = a.prefill_h[r] != 0;
+  }
+  if (slot < 0 || slot >= a.num_slots || L <= 0 || start + L > a.num_tokens) return;
+  const int ncv = C / 8, nvv = vd / 8;
+  for (int v = threadIdx.x; v < ncv + nvv; v += kBlock) {
+    if (v >= ncv) {
+      const int e8 = (v - ncv) * 8;
+      st16((uint16_t*)a.delayed_state + (int64_t)slot * vd + e8,
+           ld16((const uint16_t*)a.v_del + (start + L - 1) * a.vd_rs + e8));
+      continue;
+    }
+    const int c0 = v * 8;
+    const uint16_t* src = c0 < qd ? (const uint16_t*)a.q + c0 : (const uint16_t*)a.k + (c0 - qd);
+    const int64_t srs = c0 < qd ? a.q_rs : a.k_rs;
+    uint16_t* sp = (uint16_t*)a.conv_state + ((int64_t)slot * C + c0) * N;
+    u32x4 old[N], xr[N], nv[N];
+#pragma unroll
+    for (int jj = 0; jj < N; ++jj) {
+      old[jj] = (h && L < N) ? ld16(sp + jj * 8) : u32x4{0, 0, 0, 0};
+      const int pos = L - N + jj;
+      xr[jj] = pos >= 0 ? ld16(src + (start + pos) * srs) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int jj = 0; jj < N; ++jj)
+#pragma unroll
+      for (int ch = 0; ch < 8; ++ch) {
+        uint32_t val = BF16::get(xr[jj], ch);
+#pragma unroll
+        for (int m = 1; m < N; ++m)      // L = m < N: entry jj < N - m keeps old[m + jj]
+          if (m + jj < N && m == L) {
+            const int el = ch * N + m + jj;
+            val = BF16::get(old[el / 8], el % 8);
+          }
+        const int el = ch * N + jj;
+        BF16::set(nv[el / 8], el % 8, val);
+      }
+#pragma unroll
+    for (int jj = 0; jj < N; ++jj) st16(sp + jj * 8, nv[jj]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// MFMA main kernel (hd = 128, t1 = 2, t0 = T0 <= 4): MT rows per workgroup,
+// 8 waves per 64 rows (4 channel blocks x MT/32 token tiles)
+// ---------------------------------------------------------------------------
+template <int MT>
+constexpr int cca_threads() { return 256 * (MT / 32); }
+
 template <int T0, int MT>
-__global__ __launch_bounds__(kBlock) void cca_mfma_main(CcaArgs a) {
+__global__ __launch_bounds__(cca_threads<MT>(), SC_CCA_MIN_WAVES) void cca_mfma_main(CcaArgs a) {
   constexpr int HD = 128;
   constexpr int NV = HD / 8;           // 16-byte vectors per head row
   constexpr int N = T0;                // history length n = t0 + t1 - 2 with t1 = 2
   constexpr int AROW = 2 * HD + 8;     // LDS row of (prev, cur) pairs, padded (bf16)
+  constexpr int OROW = HD + 8;         // LDS row of staged outputs (bf16)
   constexpr int RROW = NV + 1;         // LDS raw row in 16-byte vectors, padded
-  constexpr int NT = MT / 32;          // 32-token MFMA tiles
-  static_assert(MT % 32 == 0 && MT <= 128, "tile rows");
+  constexpr int NTH = cca_threads<MT>();
+  constexpr int RPT = MT * NV / NTH;   // depthwise rows per lane (= 2)
+  constexpr int NR = RPT + T0;         // raw rows per lane: its rows plus the halo
+  constexpr int KS = 2 * HD / 16;      // MFMA K steps
+  static_assert(MT % 32 == 0 && MT <= 128 && RPT * NTH == MT * NV, "tile rows");
+  static_assert(MT * OROW <= MT * AROW, "output staging fits in the pair buffer");
 
   __shared__ __attribute__((aligned(16))) uint16_t act[MT * AROW];
   __shared__ u32x4 rawc[MT * RROW];    // current rows of the q head being processed
@@ -231,10 +308,12 @@ __global__ __launch_bounds__(kBlock) void cca_mfma_main(CcaArgs a) {
   const int tile = (int)blockIdx.x / nkv, g = (int)blockIdx.x - tile * nkv;
   const int64_t t0 = (int64_t)tile * MT;
   const int tid = (int)threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int cw = wave & 3, nt = wave >> 2;          // GEMM: channel block, token tile
+  const int v = tid % NV, i0 = (tid / NV) * RPT;    // depthwise: channel vector, first row
   const bool use_lds_qsl = a.num_prefills > 0 && a.num_prefills + 1 <= kQslCache;
 
   if (use_lds_qsl)
-    for (int i = tid; i <= a.num_prefills; i += kBlock) qsl_s[i] = a.prefill_qsl[i];
+    for (int i = tid; i <= a.num_prefills; i += NTH) qsl_s[i] = a.prefill_qsl[i];
   __syncthreads();
   if (tid < MT) {
     const RowInfo ri = row_info(a, t0 + tid, use_lds_qsl ? qsl_s : nullptr);
@@ -244,136 +323,145 @@ __global__ __launch_bounds__(kBlock) void cca_mfma_main(CcaArgs a) {
   }
   __syncthreads();
 
-  // k head rows of this bundle (residual of every group)
-  for (int it = tid; it < MT * NV; it += kBlock) {
-    const int i = it / NV, v = it - i * NV;
-    u32x4 val = {0, 0, 0, 0};
-    if (row_p[i] >= 0) val = ld16((const uint16_t*)a.k + (t0 + i) * a.k_rs + g * HD + v * 8);
-    rawk[i * RROW + v] = val;
-  }
-
-  f32x16 qsum[NT];
+  int rp[RPT];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) qsum[nt][r] = 0.f;
+  for (int r = 0; r < RPT; ++r) rp[r] = row_p[i0 + r];
 
-  for (int gi = 0; gi <= G; ++gi) {
+  // depthwise inputs of one head group: raw rows i0-T0 .. i0+RPT-1 (halo rows
+  // only when the first row's request reaches back to them), weights, bias
+  u32x4 xr[NR], wv[T0], bv;
+  auto issue_dw = [&](int gi) {
     const bool isk = gi == G;
-    const int grp = isk ? a.nq + g : g * G + gi;         // grouped-conv group index
-    const int cbase = grp * HD;                            // first raw channel of the group
+    const int cbase = isk ? (a.nq + g) * HD : (g * G + gi) * HD;
     const uint16_t* src = isk ? (const uint16_t*)a.k + g * HD
                               : (const uint16_t*)a.q + (int64_t)(g * G + gi) * HD;
     const int64_t srs = isk ? a.k_rs : a.q_rs;
+#pragma unroll
+    for (int s = 0; s < NR; ++s) {
+      const int i = i0 - T0 + s;
+      const bool need = s >= T0 ? rp[s - T0] >= 0 : rp[0] >= T0 - s;
+      xr[s] = need ? ld16(src + (t0 + i) * srs + v * 8) : u32x4{0, 0, 0, 0};
+    }
+    const uint16_t* wp = (const uint16_t*)a.w_dw + (int64_t)(cbase + v * 8) * T0;
+#pragma unroll
+    for (int s = 0; s < T0; ++s) wv[s] = ld16(wp + s * 8);
+    bv = ld16((const uint16_t*)a.b_dw + cbase + v * 8);
+  };
+  issue_dw(0);
 
-    __syncthreads();   // the previous group's GEMM and epilogue are done with act / rawc
-    // ---- depthwise stage: (prev, cur) bf16 pairs for 8 channels per item ----
-    for (int it = tid; it < MT * NV; it += kBlock) {
-      const int i = it / NV, v = it - i * NV;
-      const int p = row_p[i];
-      const int c0 = cbase + v * 8;
-      uint32_t pairs[8];
-      u32x4 cur = {0, 0, 0, 0};
-      if (p < 0) {
+  // the bundle's k head rows (residual of every group)
+  for (int it = tid; it < MT * NV; it += NTH) {
+    const int i = it / NV, vv = it - i * NV;
+    u32x4 val = {0, 0, 0, 0};
+    if (row_p[i] >= 0) val = ld16((const uint16_t*)a.k + (t0 + i) * a.k_rs + g * HD + vv * 8);
+    rawk[i * RROW + vv] = val;
+  }
+
+  f32x16 qsum;
 #pragma unroll
-        for (int ch = 0; ch < 8; ++ch) pairs[ch] = 0;
-      } else {
-        // ext(p - T0 .. p) for the 8 channels
-        float e[T0 + 1][8];
-        u32x4 hist[N];
-        const bool need_hist = p < T0;
-        if (need_hist && row_h[i]) {
-          const uint16_t* hp = (const uint16_t*)a.conv_state + ((int64_t)row_slot[i] * C + c0) * N;
+  for (int r = 0; r < 16; ++r) qsum[r] = 0.f;
+
+  for (int gi = 0; gi <= G; ++gi) {
+    const bool isk = gi == G;
+    const int cbase = isk ? (a.nq + g) * HD : (g * G + gi) * HD;
+#if !SC_CCA_XPREF
+    if (gi > 0) issue_dw(gi);
+#endif
+    const uint16_t* wrow = (const uint16_t*)a.w_gr +
+                           ((int64_t)(cbase + cw * 32 + (lane & 31)) * (2 * HD)) + 8 * (lane >> 5);
+    // history of rows that reach back before their request's first token
+    u32x4 hist[RPT][N];
 #pragma unroll
-          for (int vv = 0; vv < N; ++vv) hist[vv] = ld16(hp + vv * 8);
-        } else {
+    for (int r = 0; r < RPT; ++r) {
+      const bool need = rp[r] >= 0 && rp[r] < T0 && row_h[i0 + r];
+      const uint16_t* hp = (const uint16_t*)a.conv_state +
+                           ((int64_t)(need ? row_slot[i0 + r] : 0) * C + cbase + v * 8) * N;
 #pragma unroll
-          for (int vv = 0; vv < N; ++vv) hist[vv] = u32x4{0, 0, 0, 0};
+      for (int vv = 0; vv < N; ++vv) hist[r][vv] = need ? ld16(hp + vv * 8) : u32x4{0, 0, 0, 0};
+    }
+
+    __syncthreads();   // previous group's output staging has been stored
+    // ---- depthwise: (prev, cur) bf16 pairs for 8 channels of RPT rows ----
+    {
+      float wf32[T0][8], bs[8];
+#pragma unroll
+      for (int s = 0; s < T0; ++s) {
+        float f[8];
+        BF16::unpack(wv[s], f);
+        // wv[s] holds w_dw[(c0+ch)*T0 + tap] in element order ch*T0 + tap
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int flat = s * 8 + e, ch = flat / T0, tap = flat % T0;
+          wf32[tap][ch] = f[e];
         }
+      }
+      BF16::unpack(bv, bs);
 #pragma unroll
-        for (int s = 0; s <= T0; ++s) {
-          const int pos = p - T0 + s;
-          if (pos >= 0) {
-            const u32x4 xv = ld16(src + (t0 + i - p + pos) * srs + v * 8);
-            if (s == T0) cur = xv;
-            float f[8];
-            BF16::unpack(xv, f);
+      for (int r = 0; r < RPT; ++r) {
+        const int p = rp[r];
+        uint32_t pairs[8];
+        float e[T0 + 1][8];
 #pragma unroll
-            for (int ch = 0; ch < 8; ++ch) e[s][ch] = f[ch];
-          } else {
-            // history entry N + pos of channel ch (element ch*N + N + pos of
-            // hist), picked with compile-time indices
+        for (int s = 0; s <= T0; ++s) BF16::unpack(xr[r + s], e[s]);
+        if (p < T0) {
+          // the window reaches back before the request: history (or zeros)
+#pragma unroll
+          for (int s = 0; s < T0; ++s) {
+            const int pos = p - T0 + s;          // ext position of tap s
 #pragma unroll
             for (int ch = 0; ch < 8; ++ch) {
               float hv = 0.f;
 #pragma unroll
               for (int q = 1; q <= N; ++q) {
                 const int el = ch * N + N - q;
-                if (pos == -q) hv = bf2f(BF16::get(hist[el / 8], el % 8));
+                if (pos == -q) hv = bf2f(BF16::get(hist[r][el / 8], el % 8));
               }
-              e[s][ch] = hv;
+              if (pos < 0) e[s][ch] = hv;
             }
           }
-        }
-        float wv[8 * T0], bs[8];
-        {
-          const uint16_t* wp = (const uint16_t*)a.w_dw + (int64_t)c0 * T0;
-#pragma unroll
-          for (int vv = 0; vv < T0; ++vv) BF16::unpack(ld16(wp + vv * 8), wv + vv * 8);
-          BF16::unpack(ld16((const uint16_t*)a.b_dw + c0), bs);
         }
 #pragma unroll
         for (int ch = 0; ch < 8; ++ch) {
           float dp = bs[ch], dc = bs[ch];
 #pragma unroll
           for (int s = 0; s < T0; ++s) {
-            dp = __builtin_fmaf(wv[ch * T0 + s], e[s][ch], dp);
-            dc = __builtin_fmaf(wv[ch * T0 + s], e[s + 1][ch], dc);
+            dp = __builtin_fmaf(wf32[s][ch], e[s][ch], dp);
+            dc = __builtin_fmaf(wf32[s][ch], e[s + 1][ch], dc);
           }
-          pairs[ch] = f2bf(dp) | (f2bf(dc) << 16);
+          pairs[ch] = p >= 0 ? pk_bf16(dp, dc) : 0u;
         }
+        u32x4* ap = (u32x4*)(act + (i0 + r) * AROW + v * 16);
+        ap[0] = u32x4{pairs[0], pairs[1], pairs[2], pairs[3]};
+        ap[1] = u32x4{pairs[4], pairs[5], pairs[6], pairs[7]};
+        if (!isk) rawc[(i0 + r) * RROW + v] = p >= 0 ? xr[r + T0] : u32x4{0, 0, 0, 0};
       }
-      u32x4* ap = (u32x4*)(act + i * AROW + v * 16);
-      ap[0] = u32x4{pairs[0], pairs[1], pairs[2], pairs[3]};
-      ap[1] = u32x4{pairs[4], pairs[5], pairs[6], pairs[7]};
-      if (!isk) rawc[i * RROW + v] = cur;
     }
+#if SC_CCA_XPREF
+    if (gi < G) issue_dw(gi + 1);      // next group's inputs in flight during the GEMM
+#endif
     __syncthreads();
 
-    // ---- grouped conv on MFMA: wave owns output channels [32*wave, +32) ----
-    f32x16 acc[NT];
+    // ---- grouped conv on MFMA: out^T tile = W2 (32 ch x 256) . act^T (256 x 32 tok) ----
+    f32x16 acc;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[nt][r] = 0.f;
-    const uint16_t* wrow = (const uint16_t*)a.w_gr +
-                           ((int64_t)(cbase + wave * 32 + (lane & 31)) * (2 * HD)) + 8 * (lane >> 5);
-#pragma unroll 4
-    for (int ks = 0; ks < 2 * HD / 16; ++ks) {
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll SC_CCA_KUNROLL
+    for (int ks = 0; ks < KS; ++ks) {
       const bf16x8 af = __builtin_bit_cast(bf16x8, ld16(wrow + ks * 16));
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const u32x4 bv = *(const u32x4*)(act + (nt * 32 + (lane & 31)) * AROW + ks * 16 + 8 * (lane >> 5));
-        acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, __builtin_bit_cast(bf16x8, bv),
-                                                          acc[nt], 0, 0, 0);
-      }
+      const u32x4 bvv = *(const u32x4*)(act + (nt * 32 + (lane & 31)) * AROW + ks * 16 + 8 * (lane >> 5));
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, __builtin_bit_cast(bf16x8, bvv), acc, 0, 0, 0);
     }
 
-    // ---- epilogue: bias + residual, bf16 stores of 4 channels per lane ----
-    const int ocol = isk ? qd + g * HD : (g * G + gi) * HD;   // output column of the group
+    // ---- epilogue: bias + residual, bf16 staged in LDS (act is reused) ----
+    __syncthreads();   // every wave is done reading act (GEMM) before it is reused
+    uint16_t* ost = act;
+    {
+      const int i = nt * 32 + (lane & 31);
 #pragma unroll
-    for (int run = 0; run < 4; ++run) {
-      const int cl = wave * 32 + 8 * run + 4 * (lane >> 5);   // channel within the head
-      float b2[4];
-      {
-        const uint16_t* bp = (const uint16_t*)a.b_gr + cbase + cl;
-        const uint2 bb = *(const uint2*)bp;
-        b2[0] = bf2f(bb.x & 0xFFFFu); b2[1] = bf2f(bb.x >> 16);
-        b2[2] = bf2f(bb.y & 0xFFFFu); b2[3] = bf2f(bb.y >> 16);
-      }
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const int i = nt * 32 + (lane & 31);
+      for (int run = 0; run < 4; ++run) {
+        const int cl = cw * 32 + 8 * run + 4 * (lane >> 5);     // channel within the head
+        const uint2 bb = *(const uint2*)((const uint16_t*)a.b_gr + cbase + cl);
+        const float b2[4] = {bf2f(bb.x & 0xFFFFu), bf2f(bb.x >> 16), bf2f(bb.y & 0xFFFFu), bf2f(bb.y >> 16)};
         const int vsel = cl >> 3, half = (cl >> 2) & 1;
         const u32x4 kv4 = rawk[i * RROW + vsel];
         const uint32_t k01 = kv4[2 * half], k23 = kv4[2 * half + 1];
@@ -385,29 +473,35 @@ __global__ __launch_bounds__(kBlock) void cca_mfma_main(CcaArgs a) {
           const float qf[4] = {bf2f(q01 & 0xFFFFu), bf2f(q01 >> 16), bf2f(q23 & 0xFFFFu), bf2f(q23 >> 16)};
 #pragma unroll
           for (int s = 0; s < 4; ++s) {
-            qsum[nt][4 * run + s] += qf[s];
-            y[s] = acc[nt][4 * run + s] + b2[s] + 0.5f * (qf[s] + kf[s]);
+            qsum[4 * run + s] += qf[s];
+            y[s] = acc[4 * run + s] + b2[s] + 0.5f * (qf[s] + kf[s]);
           }
         } else {
 #pragma unroll
           for (int s = 0; s < 4; ++s)
-            y[s] = acc[nt][4 * run + s] + b2[s] +
-                   0.5f * (qsum[nt][4 * run + s] / (float)G + kf[s]);
+            y[s] = acc[4 * run + s] + b2[s] + 0.5f * (qsum[4 * run + s] / (float)G + kf[s]);
         }
-        if (row_p[i] >= 0) {
-          uint2 o;
-          o.x = f2bf(y[0]) | (f2bf(y[1]) << 16);
-          o.y = f2bf(y[2]) | (f2bf(y[3]) << 16);
-          *(uint2*)((uint16_t*)a.out + (t0 + i) * a.out_rs + ocol + cl) = o;
-        }
+        uint2 o;
+        o.x = pk_bf16(y[0], y[1]);
+        o.y = pk_bf16(y[2], y[3]);
+        *(uint2*)(ost + i * OROW + cl) = o;
       }
+    }
+    __syncthreads();
+    // full 256-byte row segments of the group's output columns
+    const int ocol = isk ? qd + g * HD : (g * G + gi) * HD;
+    for (int it = tid; it < MT * NV; it += NTH) {
+      const int ii = it / NV, vv = it - ii * NV;
+      if (row_p[ii] >= 0)
+        st16_stream((uint16_t*)a.out + (t0 + ii) * a.out_rs + ocol + vv * 8,
+                    *(const u32x4*)(ost + ii * OROW + vv * 8));
     }
   }
 
   // ---- value part: v_cur copied, v_del shifted by one token (this bundle's
   // share of the 16-byte vectors) ----
   const int nvv = vd / 8;   // vectors per value half
-  for (int it = tid; it < MT * 2 * nvv; it += kBlock) {
+  for (int it = tid; it < MT * 2 * nvv; it += NTH) {
     const int i = it / (2 * nvv), vv = it - i * (2 * nvv);
     if (vv % nkv != g) continue;
     const int p = row_p[i];
@@ -423,7 +517,7 @@ __global__ __launch_bounds__(kBlock) void cca_mfma_main(CcaArgs a) {
       else if (a.delayed_init) val = ld16((const uint16_t*)a.delayed_init + e8);
       else val = u32x4{0, 0, 0, 0};
     }
-    st16((uint16_t*)a.out + t * a.out_rs + C + vv * 8, val);
+    st16_stream((uint16_t*)a.out + t * a.out_rs + C + vv * 8, val);
   }
 }
 
@@ -446,11 +540,12 @@ hipError_t launch_cca(const CcaArgs& a, hipStream_t stream) {
     const int64_t blocks = tiles * a.nkv;
     if (blocks > 0x7FFFFFFFLL) return hipErrorInvalidValue;
     dim3 grid((unsigned)blocks);
+    const dim3 block(cca_threads<MT>());
     switch (a.t0) {
-      case 1: hipLaunchKernelGGL((cca_mfma_main<1, MT>), grid, dim3(kBlock), 0, stream, a); break;
-      case 2: hipLaunchKernelGGL((cca_mfma_main<2, MT>), grid, dim3(kBlock), 0, stream, a); break;
-      case 3: hipLaunchKernelGGL((cca_mfma_main<3, MT>), grid, dim3(kBlock), 0, stream, a); break;
-      default: hipLaunchKernelGGL((cca_mfma_main<4, MT>), grid, dim3(kBlock), 0, stream, a); break;
+      case 1: hipLaunchKernelGGL((cca_mfma_main<1, MT>), grid, block, 0, stream, a); break;
+      case 2: hipLaunchKernelGGL((cca_mfma_main<2, MT>), grid, block, 0, stream, a); break;
+      case 3: hipLaunchKernelGGL((cca_mfma_main<3, MT>), grid, block, 0, stream, a); break;
+      default: hipLaunchKernelGGL((cca_mfma_main<4, MT>), grid, block, 0, stream, a); break;
     }
   } else {
     if (a.t0 + a.t1 - 2 > 8) return hipErrorNotSupported;
@@ -463,7 +558,17 @@ hipError_t launch_cca(const CcaArgs& a, hipStream_t stream) {
   if (e != hipSuccess) return e;
   const int reqs = a.num_decodes + a.num_prefills;
   if (reqs > 0 && a.num_slots > 0) {
-    hipLaunchKernelGGL(cca_state_update, dim3((unsigned)reqs), dim3(kBlock), 0, stream, a);
+    const int n = a.t0 + a.t1 - 2;
+    if (mfma && n >= 1 && n <= 4) {
+      switch (n) {
+        case 1: hipLaunchKernelGGL((cca_state_update_vec<1>), dim3((unsigned)reqs), dim3(kBlock), 0, stream, a); break;
+        case 2: hipLaunchKernelGGL((cca_state_update_vec<2>), dim3((unsigned)reqs), dim3(kBlock), 0, stream, a); break;
+        case 3: hipLaunchKernelGGL((cca_state_update_vec<3>), dim3((unsigned)reqs), dim3(kBlock), 0, stream, a); break;
+        default: hipLaunchKernelGGL((cca_state_update_vec<4>), dim3((unsigned)reqs), dim3(kBlock), 0, stream, a); break;
+      }
+    } else {
+      hipLaunchKernelGGL(cca_state_update, dim3((unsigned)reqs), dim3(kBlock), 0, stream, a);
+    }
     e = hipGetLastError();
   }
   return e;

@@ -7,7 +7,19 @@
 namespace sc {
 
 #ifndef SC_CCA_TILE
-#define SC_CCA_TILE 64       // token rows per CCA workgroup (multiple of 32)
+#define SC_CCA_TILE 32       // token rows per CCA workgroup (multiple of 32)
+#endif
+#ifndef SC_CCA_WPREF
+#define SC_CCA_WPREF 0       // 1 = load a group's grouped-weight fragments up front
+#endif
+#ifndef SC_CCA_XPREF
+#define SC_CCA_XPREF 1       // 1 = issue the next group's raw rows before the GEMM
+#endif
+#ifndef SC_CCA_KUNROLL
+#define SC_CCA_KUNROLL 16    // MFMA K-loop unroll (weight loads in flight)
+#endif
+#ifndef SC_CCA_MIN_WAVES
+#define SC_CCA_MIN_WAVES 3   // waves per SIMD the main kernel is compiled for
 #endif
 #ifndef SC_CCA_GENERIC
 #define SC_CCA_GENERIC 0     // 1 = always use the scalar CCA kernel
