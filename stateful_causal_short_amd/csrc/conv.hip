@@ -33,7 +33,11 @@ namespace sc {
 // so consecutive chunks of the same channels (whose halos overlap) share an L2.
 __device__ __forceinline__ int logical_block(int n_logical, int per_xcd) {
   const int b = (int)blockIdx.x;
+#if SC_NO_XCD_REMAP
+  const int lb = b;
+#else
   const int lb = (b % kXcds) * per_xcd + b / kXcds;
+#endif
   return lb < n_logical ? lb : -1;
 }
 
@@ -416,7 +420,7 @@ __global__ __launch_bounds__(kBlock) void conv_pairs(ConvArgs a) {
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int t = UPDATE ? u : min(t0 + u, t1 - 1);
-    raw[H + u] = ld16(xb + (int64_t)t * xrs);
+    raw[H + u] = SC_NT_LOADS ? ld16_stream(xb + (int64_t)t * xrs) : ld16(xb + (int64_t)t * xrs);
   }
   // the slot is needed by the request's first chunk only (history and write-back)
   int32_t slot = -1;
@@ -554,7 +558,8 @@ __global__ __launch_bounds__(kBlock) void conv_update_pairs(ConvArgs a) {
 #pragma unroll
     for (int u = 0; u < Q; ++u)
       xr[rr][u] = (r < a.batch && lane_ok)
-                      ? ld16((const S*)a.x + ((int64_t)r * Q + u) * a.x_rs + c0)
+                      ? (SC_NT_LOADS ? ld16_stream((const S*)a.x + ((int64_t)r * Q + u) * a.x_rs + c0)
+                                     : ld16((const S*)a.x + ((int64_t)r * Q + u) * a.x_rs + c0))
                       : u32x4{0, 0, 0, 0};
   }
 #pragma unroll
@@ -570,7 +575,9 @@ __global__ __launch_bounds__(kBlock) void conv_update_pairs(ConvArgs a) {
 #pragma unroll
     for (int k = 0; k < H; ++k) {
       const int vi = tid + k * kBlock;
-      st[rr][k] = (hflag[rr] && vi < nvec) ? ld16(sp + vi * VEC) : u32x4{0, 0, 0, 0};
+      st[rr][k] = (hflag[rr] && vi < nvec)
+                      ? (SC_NT_LOADS ? ld16_stream(sp + vi * VEC) : ld16(sp + vi * VEC))
+                      : u32x4{0, 0, 0, 0};
     }
   }
   float bs[VEC];
@@ -628,7 +635,7 @@ __global__ __launch_bounds__(kBlock) void conv_update_pairs(ConvArgs a) {
 #pragma unroll
       for (int k = 0; k < H; ++k) {
         const int vi = tid + k * kBlock;
-        if (vi < nvec) st16(dp + vi * VEC, xch[vi]);
+        if (vi < nvec) st16_stream(dp + vi * VEC, xch[vi]);
       }
     }
   }

@@ -16,8 +16,11 @@ namespace sc {
 #ifndef SC_UNROLL_LARGE_H
 #define SC_UNROLL_LARGE_H 16
 #endif
+#ifndef SC_NO_XCD_REMAP
+#define SC_NO_XCD_REMAP 0
+#endif
 #ifndef SC_NT_LOADS
-#define SC_NT_LOADS 0
+#define SC_NT_LOADS 1   // streaming (non-temporal) loads of token rows read once
 #endif
 #ifndef SC_LDS_PAD
 #define SC_LDS_PAD 0
