@@ -30,8 +30,11 @@ def lib():
         P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
         L.oracle_conv.restype = I32
         L.oracle_conv.argtypes = [I32, I32, I32, I32, I32, I32, P, I64, P, I64, P,
-                                  P, P, P, I32, I32, I32, P, I64, P, I32, P, P,
+                                  P, P, P, I32, I32, I32, I32, P, I64, P, I32, P, P,
                                   I64, P, I32, P, P, P, I32]
+        L.oracle_conv_spec.restype = I32
+        L.oracle_conv_spec.argtypes = [I32, I32, I32, I32, I32, I32, I32, P, I64, P, I64,
+                                       P, P, P, P, I32, I32, I32, P, I64, P, P, I32]
         L.oracle_cca.restype = I32
         L.oracle_cca.argtypes = [I32, I32, I32, I32, I32, I32, I32, I32,
                                  P, I64, P, I64, P, I64, P, I64, P, I64, P,
@@ -97,11 +100,37 @@ def conv(case, *, out_dtype: Optional[str] = None, absum: bool = False,
     rc = lib().oracle_conv(
         C, case.K, case.d, 1 if case.act == "silu" else 0, _DT[case.dtype],
         _DT[odt], _p(x), C, _p(out), C, _p(ab), _p(w), _p(bias), _p(pool),
-        case.num_slots, case.num_decodes, case.q, _p(dsl), 1, _p(dh),
+        pool.shape[0], pool.shape[2], case.num_decodes, case.q, _p(dsl), 1, _p(dh),
         case.num_prefills, _p(qsl), _p(psl), 1, _p(ph), case.ckpt_grid,
         _p(cu), _p(cks), _p(rm), nthreads or default_threads())
     if rc != 0:
         raise RuntimeError(f"oracle_conv failed: {rc}")
+    return out, pool, ab
+
+
+def conv_spec(case, num_accepted, *, out_dtype: Optional[str] = None, absum: bool = False,
+              row_mask: Optional[np.ndarray] = None, nthreads: Optional[int] = None,
+              pool: Optional[np.ndarray] = None):
+    """Speculative update (rolling buffer) on a ConvCase whose decodes are the
+    spec requests (q tokens each) and whose pool is (num_slots, C, S), S >= H.
+    Returns (out, pool_after, absum_or_None)."""
+    odt = out_dtype or case.dtype
+    T, C = case.num_decode_tokens, case.C
+    x = _c(case.x[:T])
+    out = np.zeros((T, C), _NP[odt])
+    ab = np.zeros((T, C), np.float64) if absum else None
+    pool = np.array(case.pool, copy=True) if pool is None else pool
+    S = pool.shape[2]
+    dsl = _c(case.decode_slots, np.int32)
+    acc = _c(num_accepted, np.int32)
+    rm = _c(row_mask, np.uint8)
+    rc = lib().oracle_conv_spec(
+        C, case.K, case.d, S, 1 if case.act == "silu" else 0, _DT[case.dtype], _DT[odt],
+        _p(x), C, _p(out), C, _p(ab), _p(_c(case.w)), _p(_c(case.bias)), _p(pool),
+        pool.shape[0], case.num_decodes, case.q, _p(dsl), 1, _p(acc), _p(rm),
+        nthreads or default_threads())
+    if rc != 0:
+        raise RuntimeError(f"oracle_conv_spec failed: {rc}")
     return out, pool, ab
 
 

@@ -30,9 +30,14 @@
 // Parity pins: every function here is pinned by the CPU tests (zero-state vs.
 // a library convolution, a dense Toeplitz formulation, chunked == one-shot
 // state carry, checkpoint == one-shot prefix state, tiny brute force, CCA vs.
-// library depthwise+grouped convolutions and its special cases).
+// library depthwise+grouped convolutions and its special cases). The
+// speculative update is pinned by the library convolution of each request's
+// accepted token sequence across chains of steps, by its reduction to the
+// one-token decode, and by its padding and clamping rules; the wide-buffer
+// non-speculative steps by their reduction to the narrow buffer.
 #include <cmath>
 #include <cstdint>
+#include <algorithm>
 #include <cstring>
 #include <thread>
 #include <vector>
@@ -145,6 +150,7 @@ struct ConvArgs {
   const void* bias;
   void* pool;
   int32_t num_slots;
+  int32_t S;                 // state row length (>= H); the window is columns [0, H)
   int32_t ckpt_grid;
   const int32_t* cu_ckpt;
   const int32_t* ckpt_slots;
@@ -172,7 +178,7 @@ void conv_channels(const ConvArgs& a, const std::vector<Req>& reqs, int c0, int 
       ext.assign((size_t)(H + r.len), 0.0);
       for (int u = 0; u < H; ++u)
         ext[u] = (r.has_state && valid)
-                     ? ld(a.pool, a.io, ((int64_t)r.slot * a.C + c) * H + u)
+                     ? ld(a.pool, a.io, ((int64_t)r.slot * a.C + c) * a.S + u)
                      : 0.0;
       for (int64_t t = 0; t < r.len; ++t)
         ext[H + t] = ld(a.x, a.io, (r.start + t) * a.x_rs + c);
@@ -193,7 +199,7 @@ void conv_channels(const ConvArgs& a, const std::vector<Req>& reqs, int c0, int 
       }
       if (valid)
         for (int j = 0; j < H; ++j)
-          st(a.pool, a.io, ((int64_t)r.slot * a.C + c) * H + j, ext[r.len + j]);
+          st(a.pool, a.io, ((int64_t)r.slot * a.C + c) * a.S + j, ext[r.len + j]);
       if (a.ckpt_grid > 0 && (int)ri >= a.first_prefill && a.cu_ckpt) {
         const int pr = (int)ri - a.first_prefill;
         const int32_t cnt = a.cu_ckpt[pr + 1] - a.cu_ckpt[pr];
@@ -203,7 +209,7 @@ void conv_channels(const ConvArgs& a, const std::vector<Req>& reqs, int c0, int 
           const int32_t dst = a.ckpt_slots[a.cu_ckpt[pr] + m - 1];
           if (dst < 0 || dst >= a.num_slots) continue;
           for (int j = 0; j < H; ++j)
-            st(a.pool, a.io, ((int64_t)dst * a.C + c) * H + j, ext[p + j]);
+            st(a.pool, a.io, ((int64_t)dst * a.C + c) * a.S + j, ext[p + j]);
         }
       }
     }
@@ -221,13 +227,17 @@ uint16_t oracle_double_to_bf16(double v) { return double_to_bf16(v); }
 
 // Depthwise stateful causal conv over one batch (decode rows, then prefills).
 // x, w, bias and pool share io_dtype; out is written in out_dtype (F64 allowed
-// so that pins compare unrounded sums). pool is (num_slots, C, H), H=(K-1)*d.
+// so that pins compare unrounded sums). pool is (num_slots, C, S) with
+// S = state_len >= H = (K-1)*d (0 means H). When S > H (a buffer sized for
+// speculative rollback) the non-speculative steps keep their window in the
+// first H columns and leave the rest alone, as the GDN page's wide-buffer path
+// does ("only the first width-1 columns hold the real conv state").
 // absum (nullable, (T, C) doubles) receives |b| + sum_k |w*x| per output.
 // row_mask (nullable, T bytes): rows with mask 0 are not written.
 int oracle_conv(int32_t C, int32_t K, int32_t d, int32_t act, int32_t io_dtype,
                 int32_t out_dtype, const void* x, int64_t x_rs, void* out,
                 int64_t out_rs, double* absum, const void* w, const void* bias,
-                void* pool, int32_t num_slots, int32_t num_decodes, int32_t q,
+                void* pool, int32_t num_slots, int32_t state_len, int32_t num_decodes, int32_t q,
                 const int32_t* decode_slots, int64_t decode_slot_stride,
                 const uint8_t* decode_h, int32_t num_prefills,
                 const int32_t* qsl_p, const int32_t* prefill_slots,
@@ -237,14 +247,76 @@ int oracle_conv(int32_t C, int32_t K, int32_t d, int32_t act, int32_t io_dtype,
                 int32_t nthreads) {
   if (C <= 0 || K <= 0 || d <= 0 || q < 0 || num_decodes < 0 || num_prefills < 0)
     return -2;
+  const int32_t S = state_len > 0 ? state_len : (K - 1) * d;
+  if (S < (K - 1) * d) return -2;
   if (!dtype_ok(io_dtype) || !dtype_ok(out_dtype)) return -3;
   std::vector<Req> reqs =
       resolve(num_decodes, q, decode_slots, decode_slot_stride, decode_h,
               num_prefills, qsl_p, prefill_slots, prefill_slot_stride, prefill_h);
   ConvArgs a{C, K, d, act, io_dtype, out_dtype, x, x_rs, out, out_rs, absum, w,
-             bias, pool, num_slots, ckpt_grid, cu_ckpt, ckpt_slots, num_decodes,
+             bias, pool, num_slots, S, ckpt_grid, cu_ckpt, ckpt_slots, num_decodes,
              row_mask};
   parallel_for(C, nthreads, [&](int c0, int c1) { conv_channels(a, reqs, c0, c1); });
+  return 0;
+}
+
+// Speculative multi-token update with a rolling state buffer (GDN page,
+// _spec_forward: "roll the buffer: drop the accepted history from the front,
+// append the new draft tokens, keep total length == state_len").
+// pool is (num_slots, C, S), S >= H = (K-1)*d. Request r owns rows
+// [r*q, (r+1)*q) and has `a = num_accepted[r]` accepted tokens from the
+// previous step, clamped to [1, min(q, S-H+1)] (the range in which the
+// page's slices are well formed). Then
+//   ext      = [pool[s][c][a-1 : a-1+H], x_r]     (the window ending at the last accepted input)
+//   outputs  = the depthwise definition over ext
+//   pool[s]  = [pool[s][c][a : a+S-q], x_r]      (length S; q <= S required)
+// A slot outside the pool is a padding row: zero window, no write.
+int oracle_conv_spec(int32_t C, int32_t K, int32_t d, int32_t S, int32_t act,
+                     int32_t io_dtype, int32_t out_dtype, const void* x, int64_t x_rs,
+                     void* out, int64_t out_rs, double* absum, const void* w,
+                     const void* bias, void* pool, int32_t num_slots, int32_t B,
+                     int32_t q, const int32_t* slots, int64_t slot_stride,
+                     const int32_t* num_accepted, const uint8_t* row_mask,
+                     int32_t nthreads) {
+  const int H = (K - 1) * d;
+  if (C <= 0 || K <= 0 || d <= 0 || B < 0 || q < 1 || S < H || q > S) return -2;
+  if (!dtype_ok(io_dtype) || !dtype_ok(out_dtype)) return -3;
+  const int amax = std::min(q, S - H + 1);
+  auto body = [&](int c0, int c1) {
+    std::vector<double> ext((size_t)(H + q)), buf((size_t)S);
+    for (int r = 0; r < B; ++r) {
+      const int32_t slot = slots[r * slot_stride];
+      const bool valid = slot >= 0 && slot < num_slots;
+      const int a = std::min(std::max(num_accepted[r], 1), amax);
+      const int64_t start = (int64_t)r * q;
+      for (int c = c0; c < c1; ++c) {
+        for (int j = 0; j < S; ++j)
+          buf[j] = valid ? ld(pool, io_dtype, ((int64_t)slot * C + c) * S + j) : 0.0;
+        for (int u = 0; u < H; ++u) ext[u] = buf[a - 1 + u];
+        for (int t = 0; t < q; ++t) ext[H + t] = ld(x, io_dtype, (start + t) * x_rs + c);
+        const double b = bias ? ld(bias, io_dtype, c) : 0.0;
+        for (int t = 0; t < q; ++t) {
+          const int64_t row = start + t;
+          if (row_mask && !row_mask[row]) continue;
+          double z = b, A = std::fabs(b);
+          for (int k = 0; k < K; ++k) {
+            double term = ld(w, io_dtype, (int64_t)c * K + k) * ext[H + t - (int64_t)(K - 1 - k) * d];
+            z += term;
+            A += std::fabs(term);
+          }
+          st(out, out_dtype, row * out_rs + c, act ? z / (1.0 + std::exp(-z)) : z);
+          if (absum) absum[row * C + c] = A;
+        }
+        if (valid) {
+          for (int j = 0; j < S - q; ++j)
+            st(pool, io_dtype, ((int64_t)slot * C + c) * S + j, buf[a + j]);
+          for (int t = 0; t < q; ++t)
+            st(pool, io_dtype, ((int64_t)slot * C + c) * S + (S - q) + t, ext[H + t]);
+        }
+      }
+    }
+  };
+  parallel_for(C, nthreads, body);
   return 0;
 }
 

@@ -140,12 +140,13 @@ def conv_case(name: str, seed: int, *, C: int, K: int, d: int, dtype: str,
               prefill_lens=(), prefill_h_p: float = 0.5,
               prefill_h_all: Optional[int] = None, ckpt_grid: int = 0,
               x_std: float = 1.0, state_std: float = 1.0,
-              decode_h: Optional[np.ndarray] = None) -> ConvCase:
+              decode_h: Optional[np.ndarray] = None, num_spec: int = 0) -> ConvCase:
     """Build a depthwise case; slots are a random permutation of the pool.
 
     Slot assignment from one permutation: decodes first, then prefills, then
     checkpoint destinations, so every slot in one call is distinct and the
-    untouched slots act as canaries.
+    untouched slots act as canaries. ``num_spec`` > 0 widens each state row to
+    S = H + num_spec (a buffer sized for speculative rollback).
     """
     rng = np.random.default_rng(seed)
     H = (K - 1) * d
@@ -157,7 +158,8 @@ def conv_case(name: str, seed: int, *, C: int, K: int, d: int, dtype: str,
     x = _normal(rng, (T, C), x_std, dtype)
     w = _normal(rng, (C, K), w_std, dtype)
     bias = None if bias_std is None else _normal(rng, (C,), bias_std, dtype)
-    pool = _normal(rng, (num_slots, C, H), state_std, dtype)
+    S = H + num_spec
+    pool = _normal(rng, (num_slots, C, S), state_std, dtype)
     if prefill_h_all is not None:
         prefill_h = np.full(Bp, prefill_h_all, np.uint8)
     else:
@@ -176,7 +178,7 @@ def conv_case(name: str, seed: int, *, C: int, K: int, d: int, dtype: str,
     decode_slots = perm[:num_decodes].copy()
     prefill_slots = perm[num_decodes:num_decodes + Bp].copy()
     ckpt_slots = perm[num_decodes + Bp:need].copy() if ckpt_grid else None
-    return ConvCase(name=name, C=C, K=K, d=d, S=H, dtype=dtype, act=act, x=x,
+    return ConvCase(name=name, C=C, K=K, d=d, S=S, dtype=dtype, act=act, x=x,
                     w=w, bias=bias, pool=pool, num_decodes=num_decodes, q=q,
                     decode_slots=decode_slots, decode_h=decode_h, qsl_p=qsl_p,
                     prefill_slots=prefill_slots, prefill_h=prefill_h,
@@ -337,3 +339,11 @@ def config5(seed: int = SEED_BASE + 5, **kw) -> CcaCase:
     """CCA q/k conv: 16 q heads, 4 kv heads, head_dim 128, kernels 2 and 2,
     512 decodes + 64 prefills, 32768 tokens in all."""
     return cca_case("cfg5_cca_mixed", seed, **kw)
+
+
+def num_accepted(seed: int, batch: int, q: int, lo: int = 1, hi: Optional[int] = None) -> np.ndarray:
+    """Accepted-token counts of the previous speculative step, uniform in
+    [lo, hi] (hi defaults to q). Values outside the meaningful range can be
+    asked for on purpose (lo=0, hi > q) to exercise clamping."""
+    rng = np.random.default_rng(seed)
+    return rng.integers(lo, (q if hi is None else hi) + 1, size=batch).astype(np.int32)
