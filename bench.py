@@ -51,6 +51,7 @@ def conv_workload(name):
         "single": synthetic.config1,
         "decode": synthetic.config3a,
         "update_q4": synthetic.config3b,
+        "spec": synthetic.config3b_spec,
         "ple_mixed": synthetic.config4,
     }[name]()
 
@@ -75,6 +76,18 @@ def conv_alg_bytes(case):
     return b
 
 
+def spec_alg_bytes(case):
+    """Speculative update: x read + out write, every state row read and
+    written in full (S entries: the roll moves all of them), weights, bias and
+    the accepted counts read once."""
+    es, C = case.elsize, case.C
+    b = case.num_decode_tokens * C * es * 2
+    valid = sum(1 for s in case.decode_slots if 0 <= s < case.num_slots)
+    b += valid * 2 * C * case.S * es
+    b += C * case.K * es + (C * es if case.bias is not None else 0) + 4 * case.num_decodes
+    return b
+
+
 def conv_kernel_bytes(case):
     """Per-kernel split for mixed batches: (decode_update_bytes, prefill_bytes)."""
     from dataclasses import replace
@@ -91,7 +104,7 @@ def conv_kernel_bytes(case):
 
 
 class ConvRunner:
-    def __init__(self, case, nsets):
+    def __init__(self, case, nsets, num_accepted=None):
         import numpy as np
         import torch
         from tests._gpu import dev
@@ -106,6 +119,7 @@ class ConvRunner:
                     ck=None)
         if case.ckpt_grid:
             base["ck"] = (case.ckpt_grid, dev(case.cu_ckpt), dev(case.ckpt_slots))
+        self.acc = None if num_accepted is None else dev(num_accepted)
         self.base = base
         x0, p0 = dev(case.x), dev(case.pool)
         self.sets = []
@@ -114,7 +128,8 @@ class ConvRunner:
             out = torch.empty_like(x)
             pool = p0 if i == 0 else p0.clone()
             self.sets.append((x, out, pool))
-        self.kernels = (["decode_update"] if case.num_decodes else []) + \
+        dk = "spec_update" if self.acc is not None else "decode_update"
+        self.kernels = ([dk] if case.num_decodes else []) + \
                        (["prefill"] if case.num_prefills else [])
 
     def step(self, i, only=None):
@@ -123,7 +138,11 @@ class ConvRunner:
         import stateful_causal_short_amd as scs
         c, b = self.case, self.base
         x, out, pool = self.sets[i % len(self.sets)]
-        if c.num_decodes and only in (None, "decode_update"):
+        if c.num_decodes and self.acc is not None and only in (None, "spec_update"):
+            scs.sc_conv_update_spec(x[:self.nd], out[:self.nd], b["w"], b["b"], pool,
+                                    b["dslots"], self.acc, q=c.q, dilation=c.d,
+                                    activation=c.act)
+        elif c.num_decodes and only in (None, "decode_update"):
             scs.sc_conv_update(x[:self.nd], out[:self.nd], b["w"], b["b"], pool,
                                b["dslots"], b["dh"], q=c.q, dilation=c.d, activation=c.act)
         if c.num_prefills and only in (None, "prefill"):
@@ -177,13 +196,16 @@ class CcaRunner:
                            t0=c.t0, t1=c.t1)
 
 
-def cpu_baseline_conv(case, budget_s=10.0):
+def cpu_baseline_conv(case, budget_s=10.0, num_accepted=None):
     """The oracle, as it stands, on the same batch; repeated until ~budget_s."""
     import oracle
     threads = min(16, oracle.default_threads())
     runs, t0 = 0, time.perf_counter()
     while True:
-        oracle.conv(case, nthreads=threads)
+        if num_accepted is None:
+            oracle.conv(case, nthreads=threads)
+        else:
+            oracle.conv_spec(case, num_accepted, nthreads=threads)
         runs += 1
         el = time.perf_counter() - t0
         if el >= budget_s or runs >= 50:
@@ -194,7 +216,7 @@ def cpu_baseline_conv(case, budget_s=10.0):
                       f"oracle, {el:.1f} s wall on {threads} threads"}
 
 
-def source_sha(files=("conv.hip", "common.hpp", "kernels.hpp")):
+def source_sha(files=("conv.hip", "conv_device.hpp", "common.hpp", "kernels.hpp")):
     """Digest of the sources the depthwise kernels are built from."""
     h = hashlib.sha256()
     d = os.path.join(ROOT, "stateful_causal_short_amd", "csrc")
@@ -304,7 +326,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="varlen_prefill",
-                    choices=["varlen_prefill", "single", "decode", "update_q4",
+                    choices=["varlen_prefill", "single", "decode", "update_q4", "spec",
                              "ple_mixed", "cca", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
@@ -326,13 +348,20 @@ def main():
         return copy_calibration(args)
 
     case = conv_workload(args.workload)
-    alg = conv_alg_bytes(case)
-    dec_b, pre_b = conv_kernel_bytes(case)
+    acc = None
+    if args.workload == "spec":
+        import synthetic
+        acc = synthetic.num_accepted(synthetic.SEED_BASE + 0x36, case.num_decodes, case.q)
+        alg = dec_b = spec_alg_bytes(case)
+        pre_b = 0
+    else:
+        alg = conv_alg_bytes(case)
+        dec_b, pre_b = conv_kernel_bytes(case)
     set_bytes = case.T * case.C * case.elsize * 2 + case.pool.nbytes
     nsets = int(min(8, max(2, -(-ROTATE_BYTES // set_bytes))))
     log(f"T={case.T} C={case.C} K={case.K} d={case.d} {case.dtype} act={case.act}; "
         f"alg bytes/step={alg}; {nsets} rotating buffer sets")
-    run = ConvRunner(case, nsets)
+    run = ConvRunner(case, nsets, acc)
     for i in range(args.warmup):
         run.step(i)
     torch.cuda.synchronize()
@@ -402,6 +431,7 @@ def main():
             "prefills": case.num_prefills, "tokens": case.T, "channels": case.C,
             "width": case.K, "dilation": case.d, "activation": case.act,
             "state_slots": case.num_slots, "checkpoint_grid": case.ckpt_grid,
+            "state_len": case.S,
         },
         "hbm_gbps": alg / (ms_step * 1e-3) / 1e9,
         "pct_peak": 100.0 * alg / (ms_step * 1e-3) / 1e9 / PEAK_GBPS,
@@ -416,7 +446,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
-        result["cpu_baseline"] = cpu_baseline_conv(case)
+        result["cpu_baseline"] = cpu_baseline_conv(case, num_accepted=acc)
     print(json.dumps(result), flush=True)
 
 

@@ -62,7 +62,7 @@ typedef enum {
   SC_ERR_INVALID_ARG = -2,     /* a size, stride, enum or grid is out of range */
   SC_ERR_DTYPE = -3,           /* dtype not supported by this entry point */
   SC_ERR_STATE_CAPACITY = -4,  /* state_len < (width-1)*dilation */
-  SC_ERR_UNSUPPORTED = -5,     /* valid but not built here (e.g. state_len > H) */
+  SC_ERR_UNSUPPORTED = -5,     /* valid but not built here (e.g. width > 8) */
   SC_ERR_HIP = -6              /* the HIP runtime reported a launch error */
 } sc_status;
 
@@ -76,8 +76,13 @@ typedef struct {
   int32_t channels;       /* C >= 1 */
   int32_t width;          /* K in [1, 8] */
   int32_t dilation;       /* d >= 1 */
-  int32_t state_len;      /* S; S < (K-1)*d -> SC_ERR_STATE_CAPACITY,
-                             S > (K-1)*d (speculative rolling window) -> SC_ERR_UNSUPPORTED */
+  int32_t state_len;      /* S, entries per channel of a state row; S < H = (K-1)*d
+                             -> SC_ERR_STATE_CAPACITY; S > 2^20 -> SC_ERR_INVALID_ARG.
+                             S > H is a buffer sized for speculative rollback
+                             (GDN page, _spec_forward: width-1 + num_spec); the
+                             non-speculative calls keep their window in entries
+                             [0, H) of each row and leave [H, S) untouched (GDN
+                             page, _spec_aware_nonspec, first width-1 columns). */
   int32_t dtype;          /* sc_dtype */
   int32_t activation;     /* sc_activation */
   int64_t x_row_stride;   /* elements between token rows of x, >= C */
@@ -98,9 +103,9 @@ typedef struct {
 
 /* Varlen prefill: for request r (token rows [qsl[r], qsl[r+1]) of x), slot
  * s = state_indices[r*stride], flag h = has_initial_state[r]:
- *   ext = [h ? pool[s] : zeros (C x H, oldest first), x_r]
+ *   ext = [h ? pool[s][c][0 .. H) : zeros (oldest first), x_r]
  *   out[t, c] = act(bias[c] + sum_k weight[c, k] * ext[c, H + t - (K-1-k)*d])
- *   pool[s] = last H entries of ext (bit-exact copy of inputs/history)
+ *   pool[s][c][0 .. H) = last H entries of ext (bit-exact copies)
  * A zero-length request produces nothing and leaves its slot untouched.
  *   x                 (device) (num_tokens, C) rows of x_row_stride elements
  *   out               (device) (num_tokens, C) rows of out_row_stride
@@ -131,6 +136,29 @@ sc_status sc_conv_update(const sc_conv_desc* desc, const void* x, void* out,
                          int32_t num_slots, const int32_t* state_indices,
                          const uint8_t* has_initial_state, int32_t batch,
                          int32_t q, void* stream);
+
+/* Speculative multi-token update on a rolling buffer (GDN page
+ * "vllm.model_executor.layers.mamba.ops.cpu.gdn_attention", _spec_forward,
+ * per-sequence rolling buffer; PLE page "vllm.models.qwen4_exp.nvidia.ple_layer",
+ * ple_conv mode "spec" with num_accepted_tokens and spec_query_len).
+ * `batch` requests of exactly q tokens (request r owns rows [r*q, (r+1)*q)),
+ * pool rows of S = desc->state_len >= H entries. With slot s and
+ *   a = num_accepted_tokens[r] clamped to [1, min(q, S-H+1)]
+ * (the range in which the page's slices are well formed; values outside it
+ * act as the nearest bound):
+ *   ext      = [pool[s][c][a-1 .. a-1+H), x_r]
+ *   out[t,c] = act(bias[c] + sum_k weight[c,k] * ext[c, H + t - (K-1-k)*d])
+ *   pool[s]  = [pool[s][c][a .. a+S-q), x_r]   (length S, bit-exact copies)
+ * A slot outside [0, num_slots) is a padding row: zero history, no write.
+ * q > S -> SC_ERR_INVALID_ARG (the drafts would not fit the buffer).
+ *   num_accepted_tokens (device) int32 (batch), required.
+ * Other arguments as for sc_conv_update (no has_initial_state: speculative
+ * requests always continue their buffer). */
+sc_status sc_conv_update_spec(const sc_conv_desc* desc, const void* x, void* out,
+                              const void* weight, const void* bias, void* state_pool,
+                              int32_t num_slots, const int32_t* state_indices,
+                              const int32_t* num_accepted_tokens, int32_t batch,
+                              int32_t q, void* stream);
 
 /* Row copies between a slot pool and a dense buffer; each row is row_bytes.
  * gather: dense[i] = pool[idx[i*idx_stride]], or zeros when that index is

@@ -23,7 +23,7 @@ STATUS = {0: "SC_OK", -1: "SC_ERR_NULL_ARG", -2: "SC_ERR_INVALID_ARG",
 SC_DTYPE_F32, SC_DTYPE_BF16 = 0, 1
 SC_ACT_NONE, SC_ACT_SILU = 0, 1
 
-EXPORTS = ("sc_conv_prefill_varlen", "sc_conv_update", "sc_state_gather",
+EXPORTS = ("sc_conv_prefill_varlen", "sc_conv_update", "sc_conv_update_spec", "sc_state_gather",
            "sc_state_scatter", "sc_cca_qk_conv", "sc_status_string",
            "sc_abi_version")
 
@@ -78,6 +78,8 @@ def lib():
                                              ctypes.POINTER(sc_ckpt_desc), P]
         L.sc_conv_update.restype = I32
         L.sc_conv_update.argtypes = [D, P, P, P, P, P, I32, P, P, I32, I32, P]
+        L.sc_conv_update_spec.restype = I32
+        L.sc_conv_update_spec.argtypes = [D, P, P, P, P, P, I32, P, P, I32, I32, P]
         L.sc_state_gather.restype = I32
         L.sc_state_gather.argtypes = [P, I32, I64, P, I64, I32, P, P]
         L.sc_state_scatter.restype = I32
@@ -176,7 +178,8 @@ def sc_conv_prefill_varlen(x, out, weight, bias, state_pool, query_start_loc,
     """Varlen prefill conv; updates ``state_pool`` in place.
 
     x, out: (num_tokens, C); weight (C, K); bias (C) or None; state_pool
-    (num_slots, C, (K-1)*dilation); query_start_loc int32 (B+1);
+    (num_slots, C, S), S >= (K-1)*dilation (window in the first (K-1)*dilation
+    entries of each row); query_start_loc int32 (B+1);
     state_indices int32 (B) or (B, n) using column 0; has_initial_state
     bool/uint8 (B); ckpt = None or (grid, cu_ckpt int32 (B+1), ckpt_slots int32).
     """
@@ -208,6 +211,25 @@ def sc_conv_update(x, out, weight, bias, state_pool, state_indices,
         _ptr(state_pool), state_pool.shape[0], _index(state_indices, "state_indices")[0],
         _flags(has_initial_state, "has_initial_state"), B, q, _stream(stream))
     _check("sc_conv_update", st)
+
+
+def sc_conv_update_spec(x, out, weight, bias, state_pool, state_indices, num_accepted_tokens,
+                        *, q: int, dilation: int = 1, activation: Optional[str] = "silu",
+                        stream=None):
+    """Speculative update on a rolling buffer: x (B*q, C) rows, request r owns
+    rows [r*q, (r+1)*q); state_pool (num_slots, C, S) with S >= (K-1)*dilation;
+    num_accepted_tokens int32 (B). Updates ``state_pool`` in place."""
+    if q < 1 or x.shape[0] % q:
+        raise ValueError("x rows must be a positive multiple of q")
+    torch = _torch()
+    if num_accepted_tokens.dtype != torch.int32 or not num_accepted_tokens.is_contiguous():
+        raise ValueError("num_accepted_tokens: expected a contiguous int32 tensor")
+    desc = _conv_desc(x, out, weight, state_pool, dilation, activation, state_indices)
+    st = lib().sc_conv_update_spec(
+        ctypes.byref(desc), _ptr(x), _ptr(out), _ptr(weight), _ptr(bias),
+        _ptr(state_pool), state_pool.shape[0], _index(state_indices, "state_indices")[0],
+        _ptr(num_accepted_tokens), x.shape[0] // q, q, _stream(stream))
+    _check("sc_conv_update_spec", st)
 
 
 def sc_state_gather(state_pool, idx, dense, *, stream=None):
@@ -262,5 +284,6 @@ def sc_cca_qk_conv(q, k, v_cur, v_del, out, w_dw, b_dw, w_gr, b_gr, delayed_init
 
 
 __all__ = ["lib", "ScError", "LIB_PATH", "EXPORTS", "sc_conv_desc", "sc_ckpt_desc",
-           "sc_cca_desc", "sc_conv_prefill_varlen", "sc_conv_update", "sc_state_gather",
+           "sc_cca_desc", "sc_conv_prefill_varlen", "sc_conv_update", "sc_conv_update_spec",
+           "sc_state_gather",
            "sc_state_scatter", "sc_cca_qk_conv"]

@@ -13,7 +13,7 @@ bool al16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 // Descriptor checks shared by the depthwise entry points. The state-capacity
 // rule follows the PLE layer's _short_conv (cache narrower than the window
-// raises); a wider state is the speculative rolling window, not built here.
+// raises); a wider state is a buffer sized for speculative rollback.
 sc_status check_conv_desc(const sc_conv_desc* d, int* H) {
   if (d->dtype != SC_DTYPE_F32 && d->dtype != SC_DTYPE_BF16) return SC_ERR_DTYPE;
   if (d->channels < 1 || d->width < 1 || d->dilation < 1) return SC_ERR_INVALID_ARG;
@@ -24,7 +24,7 @@ sc_status check_conv_desc(const sc_conv_desc* d, int* H) {
   const int64_t h = (int64_t)(d->width - 1) * d->dilation;
   if (h > (1 << 20)) return SC_ERR_INVALID_ARG;
   if (d->state_len < h) return SC_ERR_STATE_CAPACITY;
-  if (d->state_len > h) return SC_ERR_UNSUPPORTED;
+  if (d->state_len > (1 << 20)) return SC_ERR_INVALID_ARG;
   *H = (int)h;
   return SC_OK;
 }
@@ -109,6 +109,7 @@ sc_status sc_conv_prefill_varlen(const sc_conv_desc* desc, const void* x, void* 
   a.batch = batch;
   a.q = 0;
   a.ckpt_grid = grid;
+  a.S = desc->state_len;
   const bool aligned = conv_aligned(desc, x, out, weight, bias, state_pool);
   return from_hip(sc::launch_conv(a, desc->dtype, desc->width, desc->dilation,
                                   desc->activation == SC_ACT_SILU, aligned,
@@ -149,10 +150,55 @@ sc_status sc_conv_update(const sc_conv_desc* desc, const void* x, void* out,
   a.batch = batch;
   a.q = q;
   a.ckpt_grid = 0;
+  a.S = desc->state_len;
   const bool aligned = conv_aligned(desc, x, out, weight, bias, state_pool);
   return from_hip(sc::launch_conv(a, desc->dtype, desc->width, desc->dilation,
                                   desc->activation == SC_ACT_SILU, aligned,
                                   (hipStream_t)stream, nullptr));
+}
+
+sc_status sc_conv_update_spec(const sc_conv_desc* desc, const void* x, void* out,
+                              const void* weight, const void* bias, void* state_pool,
+                              int32_t num_slots, const int32_t* state_indices,
+                              const int32_t* num_accepted_tokens, int32_t batch, int32_t q,
+                              void* stream) {
+  if (!desc) return SC_ERR_NULL_ARG;
+  int H = 0;
+  sc_status st = check_conv_desc(desc, &H);
+  if (st != SC_OK) return st;
+  if (batch < 0 || q < 0 || num_slots < 0) return SC_ERR_INVALID_ARG;
+  // the rolled buffer keeps S - q old entries: q drafts must fit in it
+  if (q > desc->state_len) return SC_ERR_INVALID_ARG;
+  if (batch == 0 || q == 0) return SC_OK;
+  if (!x || !out || !weight || !state_indices || !num_accepted_tokens) return SC_ERR_NULL_ARG;
+  if (!state_pool && num_slots > 0) return SC_ERR_NULL_ARG;
+  if (x == out) return SC_ERR_INVALID_ARG;
+  const int64_t T = (int64_t)batch * q;
+  if (T > 0x7FFFFFFFLL) return SC_ERR_UNSUPPORTED;
+  sc::ConvArgs a{};
+  a.x = x;
+  a.out = out;
+  a.w = weight;
+  a.bias = bias;
+  a.pool = state_pool;
+  a.qsl = nullptr;
+  a.slots = state_indices;
+  a.has_init = nullptr;
+  a.num_acc = num_accepted_tokens;
+  a.x_rs = desc->x_row_stride;
+  a.out_rs = desc->out_row_stride;
+  a.slot_stride = desc->state_indices_stride;
+  a.num_tokens = T;
+  a.C = desc->channels;
+  a.num_slots = num_slots;
+  a.batch = batch;
+  a.q = q;
+  a.ckpt_grid = 0;
+  a.S = desc->state_len;
+  const bool aligned = conv_aligned(desc, x, out, weight, bias, state_pool);
+  return from_hip(sc::launch_conv_spec(a, desc->dtype, desc->width, desc->dilation,
+                                       desc->activation == SC_ACT_SILU, aligned,
+                                       (hipStream_t)stream));
 }
 
 sc_status sc_state_gather(const void* pool, int32_t num_slots, int64_t row_bytes,

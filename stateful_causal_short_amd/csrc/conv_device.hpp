@@ -1,0 +1,180 @@
+// Device helpers shared by the depthwise kernels (conv.hip, spec.hip):
+// workgroup -> request/chunk resolution, register-window element access,
+// weight loading, the fp32 tap chain and the bf16 tap-pair dot product.
+#pragma once
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace sc {
+
+// ---------------------------------------------------------------------------
+// request / chunk resolution
+// ---------------------------------------------------------------------------
+
+// Logical workgroup index from the hardware one. Workgroups are dealt to the
+// 8 XCDs round-robin; this gives each XCD a contiguous run of logical blocks,
+// so consecutive chunks of the same channels (whose halos overlap) share an L2.
+__device__ __forceinline__ int logical_block(int n_logical, int per_xcd) {
+  const int b = (int)blockIdx.x;
+#if SC_NO_XCD_REMAP
+  const int lb = b;
+#else
+  const int lb = (b % kXcds) * per_xcd + b / kXcds;
+#endif
+  return lb < n_logical ? lb : -1;
+}
+
+// Chunk ids of request r are [base(r), base(r+1)) with
+// base(r) = floor(qsl[r] / chunk) + r, an upper bound on the chunks the request
+// needs that is monotone in r and computable per request. So the request owning
+// chunk id `id` is #{i in [1, B] : base(i) <= id}, counted wave-parallel.
+// Must be called by full waves (uses ballot).
+__device__ __forceinline__ int find_request(const int32_t* qsl, int B, int id, int chunk) {
+  const int lane = (int)(threadIdx.x & 63);
+  int cnt = 0;
+  for (int i0 = 1; i0 <= B; i0 += 64) {
+    const int i = i0 + lane;
+    bool p = false;
+    if (i <= B) p = (qsl[i] / chunk + i) <= id;
+    cnt += __popcll(__ballot(p));
+  }
+  return cnt;
+}
+
+// Request lookup that also returns qsl[r] and qsl[r+1]. With B < 64 every
+// needed entry is loaded once by one lane (lane l holds qsl[l]) and read back
+// with readlane; larger batches fall back to find_request plus two loads.
+// Must be called by full waves.
+__device__ __forceinline__ int find_request_bounds(const int32_t* qsl, int B, int id, int chunk,
+                                                   int& s0, int& s1) {
+  if (B < 64) {
+    const int lane = (int)(threadIdx.x & 63);
+    const int v = lane <= B ? qsl[lane] : 0x7FFFFFFF;
+    const bool p = lane >= 1 && lane <= B && (v / chunk + lane) <= id;
+    const int r = __popcll(__ballot(p));
+    s0 = __builtin_amdgcn_readlane(v, r);
+    s1 = __builtin_amdgcn_readlane(v, min(r + 1, 63));
+    return r;
+  }
+  const int r = find_request(qsl, B, id, chunk);
+  if (r < B) {
+    s0 = qsl[r];
+    s1 = qsl[r + 1];
+  }
+  return r;
+}
+
+struct Work {
+  int r, j, L, t0, t1;
+  int64_t start;
+  int32_t slot;
+  bool valid, h;
+};
+
+__device__ __forceinline__ bool resolve_work(const ConvArgs& a, int cid, Work& w) {
+  if (a.qsl == nullptr) {   // uniform update: batch x q rows
+    const int cpr = (a.q + a.chunk - 1) / a.chunk;
+    w.r = cid / cpr;
+    w.j = cid - w.r * cpr;
+    if (w.r >= a.batch) return false;
+    w.start = (int64_t)w.r * a.q;
+    w.L = a.q;
+  } else {
+    w.r = find_request(a.qsl, a.batch, cid, a.chunk);
+    if (w.r >= a.batch) return false;
+    const int s0 = a.qsl[w.r], s1 = a.qsl[w.r + 1];
+    if (s0 < 0) return false;
+    w.j = cid - (s0 / a.chunk + w.r);
+    w.start = s0;
+    w.L = s1 - s0;
+  }
+  if (w.j < 0 || w.L <= 0 || w.start >= a.num_tokens) return false;
+  if (w.start + w.L > a.num_tokens) w.L = (int)(a.num_tokens - w.start);
+  w.t0 = w.j * a.chunk;
+  if (w.t0 >= w.L) return false;
+  w.t1 = min(w.L, w.t0 + a.chunk);
+  w.slot = a.slots[(int64_t)w.r * a.slot_stride];
+  w.valid = w.slot >= 0 && w.slot < a.num_slots;
+  w.h = w.valid && (a.has_init ? a.has_init[w.r] != 0 : true);
+  return true;
+}
+
+// ---------------------------------------------------------------------------
+// register-window helpers (all indices compile-time after unrolling)
+// ---------------------------------------------------------------------------
+template <class E>
+__device__ __forceinline__ float widen(uint32_t b) {
+  if constexpr (E::VEC == 8) return __uint_as_float(b << 16);
+  else return __uint_as_float(b);
+}
+
+// element e of a flat array of 16-byte vectors
+template <class E>
+__device__ __forceinline__ uint32_t get_flat(const u32x4* v, int e) {
+  return E::get(v[e / E::VEC], e % E::VEC);
+}
+template <class E>
+__device__ __forceinline__ void set_flat(u32x4* v, int e, uint32_t val) {
+  E::set(v[e / E::VEC], e % E::VEC, val);
+}
+
+template <class E, int K>
+__device__ __forceinline__ void load_weights(const void* w, int c0, float (*wt)[E::VEC]) {
+  constexpr int VEC = E::VEC;
+  using S = typename E::S;
+  const S* wp = (const S*)w + (int64_t)c0 * K;
+  float flat[VEC * K];
+#pragma unroll
+  for (int v = 0; v < K; ++v) E::unpack(ld16(wp + v * VEC), flat + v * VEC);
+#pragma unroll
+  for (int ch = 0; ch < VEC; ++ch)
+#pragma unroll
+    for (int k = 0; k < K; ++k) wt[k][ch] = flat[ch * K + k];
+}
+
+// History vectors ((ch, u) order, as in the pool) to window rows 0..H-1.
+template <class E, int H>
+__device__ __forceinline__ void hist_to_win(const u32x4* old, float (*win)[E::VEC]) {
+#pragma unroll
+  for (int u = 0; u < H; ++u)
+#pragma unroll
+    for (int ch = 0; ch < E::VEC; ++ch) win[u][ch] = widen<E>(get_flat<E>(old, ch * H + u));
+}
+
+template <class E, int K, int D, bool SILU>
+__device__ __forceinline__ void conv_point(const float (*win)[E::VEC], int pos,
+                                           const float (*wt)[E::VEC], const float* bs,
+                                           float* z) {
+#pragma unroll
+  for (int ch = 0; ch < E::VEC; ++ch) {
+    float acc = bs[ch];
+#pragma unroll
+    for (int k = 0; k < K; ++k) acc = __builtin_fmaf(wt[k][ch], win[pos - (K - 1 - k) * D][ch], acc);
+    z[ch] = SILU ? silu(acc) : acc;
+  }
+}
+
+// Pair-of-taps dot product on bf16 data (v_dot2c_f32_bf16): acc + w.x over a
+// (older, newer) pair, fp32 accumulation.
+__device__ __forceinline__ float dot2_bf16(uint32_t w_pair, uint32_t x_pair, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w_pair),
+                                         __builtin_bit_cast(bf16x2, x_pair), acc, false);
+}
+
+// Pair of channel ch's values from rows a (older, low half) and b (newer).
+__device__ __forceinline__ uint32_t row_pair(const u32x4& ra, const u32x4& rb, int ch) {
+  return __builtin_amdgcn_perm(rb[ch >> 1], ra[ch >> 1], (ch & 1) ? 0x07060302u : 0x05040100u);
+}
+
+// Scalar element access for the one-channel-per-lane kernels.
+template <class E>
+__device__ __forceinline__ uint32_t ld_el(const typename E::S* p) { return (uint32_t)*p; }
+
+template <class E>
+__device__ __forceinline__ typename E::S narrow(float v) {
+  if constexpr (E::VEC == 8) return __builtin_bit_cast(uint16_t, (__bf16)v);
+  else return __float_as_uint(v);
+}
+
+}  // namespace sc

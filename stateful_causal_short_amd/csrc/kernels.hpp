@@ -49,8 +49,10 @@ struct ConvArgs {
   const int32_t* cu_ckpt;
   const int32_t* ckpt_slots;
   int64_t x_rs, out_rs, slot_stride;   // elements
+  const int32_t* num_acc;    // speculative update: accepted counts (batch), else nullptr
   int64_t num_tokens;
   int32_t C, num_slots, batch, q, ckpt_grid;
+  int32_t S;                 // state row length (>= H); the window is columns [0, H)
   // filled by launch_conv
   int32_t chunk, n_cblk, n_logical, per_xcd;
 };
@@ -64,6 +66,15 @@ struct ConvLaunchInfo {
 
 hipError_t launch_conv(ConvArgs a, int dtype, int K, int D, bool silu_act, bool aligned16,
                        hipStream_t stream, ConvLaunchInfo* info);
+
+// Speculative multi-token update on a rolling buffer of S >= H entries per
+// channel (requests of exactly a.q tokens, accepted counts in a.num_acc).
+hipError_t launch_conv_spec(ConvArgs a, int dtype, int K, int D, bool silu_act, bool aligned16,
+                            hipStream_t stream);
+// Plain decode / multi-token update on a buffer wider than H (the window in the
+// first H columns); nullptr-free fast path or hipErrorNotSupported.
+hipError_t launch_update_wide(ConvArgs a, int dtype, int K, int D, bool silu_act, bool aligned16,
+                              hipStream_t stream);
 
 hipError_t launch_state_copy(bool gather, const void* src, void* dst, int64_t row_bytes,
                              int32_t num_slots, const int32_t* idx, int64_t idx_stride,

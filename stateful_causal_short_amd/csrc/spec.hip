@@ -1,0 +1,309 @@
+// Depthwise conv updates on a state buffer widened for speculative rollback.
+//
+// Operation (GDN page "vllm.model_executor.layers.mamba.ops.cpu.gdn_attention",
+// _spec_forward, per-sequence rolling buffer; PLE page
+// "vllm.models.qwen4_exp.nvidia.ple_layer", spec mode with a state capacity of
+// conv_state_len + num_spec_tokens): each channel keeps S >= H = (K-1)*d
+// entries. A speculative request of q tokens whose previous step had `a`
+// accepted tokens (clamped to [1, min(q, S-H+1)], the range in which the
+// page's slices are well formed) reads the H entries starting at a-1 as its
+// history, produces out[t] = act(b + sum_k w[k] * ext[H + t - (K-1-k)*d]) over
+// ext = [history, x], and leaves its buffer as the entries from a on, cut to
+// S - q, followed by the q new tokens. A plain (non-speculative) update on such
+// a buffer uses the first H entries as the window and leaves the rest as they
+// were ("only the first width-1 columns hold the real conv state", GDN page,
+// _spec_aware_nonspec).
+//
+// Layout: pool (num_slots, C, S). A workgroup takes one request and 256
+// vectors of channels; their state rows form one contiguous region of 256 * S
+// vectors, which is loaded and stored with unit-stride lanes and staged in LDS.
+// Each lane then reads its own channels' entries at the runtime offset a-1 and
+// rolls them in place (its region is private to the lane), so a runtime
+// acceptance count costs only LDS addressing. The token arithmetic is that of
+// the narrow-buffer kernels (tap pairs on v_dot2c_f32_bf16 for the shapes the
+// prefill kernel pairs, an fp32 fused multiply-add chain otherwise), so a fully
+// accepted speculative chain reproduces the prefill outputs bit for bit.
+#include "conv_device.hpp"
+
+namespace sc {
+
+constexpr int kSpecQMax = 8;    // tokens per request on the register path
+constexpr int kSpecSMax = 16;   // state entries per channel staged in LDS
+
+template <class E, int K, int D, bool SILU, bool SPEC>
+__global__ __launch_bounds__(kBlock) void conv_rollbuf(ConvArgs a) {
+  using St = typename E::S;
+  constexpr int H = (K - 1) * D;
+  constexpr int VEC = E::VEC;
+  constexpr bool PAIRS = VEC == 8 && ((K == 4 && D <= 3) || (K == 2 && D == 1));
+  constexpr int NP = K / 2;
+  constexpr int QM = kSpecQMax;
+  extern __shared__ u32x4 region[];   // kBlock * S vectors
+
+  const int lb = logical_block(a.n_logical, a.per_xcd);
+  if (lb < 0) return;                       // uniform over the workgroup
+  const int r = lb / a.n_cblk, cb = lb - r * a.n_cblk;
+  if (r >= a.batch) return;
+  const int tid = (int)threadIdx.x;
+  const int cbase = cb * kBlock * VEC;
+  const int c0 = cbase + tid * VEC;
+  const bool lane_ok = c0 < a.C;
+  const int Sl = a.S, q = a.q;
+  const int nvec = (min(a.C - cbase, kBlock * VEC) / VEC) * Sl;
+
+  // weights and bias (independent of the request)
+  uint32_t wp[PAIRS ? NP : 1][VEC];
+  float wt[PAIRS ? 1 : K][VEC];
+  u32x4 bsv = u32x4{0, 0, 0, 0};
+  if (lane_ok) {
+    if constexpr (PAIRS) {
+      u32x4 wv[NP * 2];
+#pragma unroll
+      for (int v = 0; v < NP * 2; ++v) wv[v] = ld16((const St*)a.w + (int64_t)c0 * K + v * VEC);
+#pragma unroll
+      for (int ch = 0; ch < VEC; ++ch)
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+          const int word = ch * NP + p;
+          wp[p][ch] = wv[word >> 2][word & 3];
+        }
+    } else {
+      load_weights<E, K>(a.w, c0, wt);
+    }
+    if (a.bias) bsv = ld16((const St*)a.bias + c0);
+  }
+
+  // token rows, then the slot, then the state region (unit stride)
+  u32x4 xr[QM];
+#pragma unroll
+  for (int u = 0; u < QM; ++u)
+    xr[u] = (u < q && lane_ok) ? ld16_stream((const St*)a.x + ((int64_t)r * q + u) * a.x_rs + c0)
+                               : u32x4{0, 0, 0, 0};
+  const int32_t slot = a.slots[(int64_t)r * a.slot_stride];
+  const bool valid = slot >= 0 && slot < a.num_slots;
+  bool hist = valid;
+  int acc = 1;
+  if constexpr (SPEC) {
+    acc = min(max(a.num_acc[r], 1), min(q, Sl - H + 1));
+  } else {
+    hist = valid && (a.has_init ? a.has_init[r] != 0 : true);
+  }
+  if (valid) {
+    const St* sp = (const St*)a.pool + ((int64_t)slot * a.C + cbase) * Sl;
+    u32x4 sv[kSpecSMax];
+#pragma unroll
+    for (int k = 0; k < kSpecSMax; ++k) {
+      const int vi = tid + k * kBlock;
+      sv[k] = (k < Sl && vi < nvec) ? ld16_stream(sp + vi * VEC) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int k = 0; k < kSpecSMax; ++k) {
+      const int vi = tid + k * kBlock;
+      if (k < Sl && vi < nvec) region[vi] = sv[k];
+    }
+  }
+  __syncthreads();
+
+  St* le = (St*)region;
+  const int lbase = tid * VEC * Sl;          // channel c0, entry 0 of this lane
+  const int off = SPEC ? acc - 1 : 0;
+  u32x4 raw[H + QM];
+#pragma unroll
+  for (int u = 0; u < H; ++u) {
+    raw[u] = u32x4{0, 0, 0, 0};
+    if (hist && lane_ok) {
+#pragma unroll
+      for (int ch = 0; ch < VEC; ++ch) E::set(raw[u], ch, (uint32_t)le[lbase + ch * Sl + off + u]);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < QM; ++u) raw[H + u] = xr[u];
+
+  if (lane_ok) {
+    float bs[VEC];
+    E::unpack(bsv, bs);
+    float win[PAIRS ? 1 : H + QM][VEC];
+    if constexpr (!PAIRS) {
+#pragma unroll
+      for (int i = 0; i < H + QM; ++i) E::unpack(raw[i], win[i]);
+    }
+#pragma unroll
+    for (int u = 0; u < QM; ++u) {
+      if (u < q) {
+        float z[VEC];
+        if constexpr (PAIRS) {
+#pragma unroll
+          for (int ch = 0; ch < VEC; ++ch) {
+            float accf = bs[ch];
+#pragma unroll
+            for (int p = 0; p < NP; ++p) {
+              const int r0 = H + u - (K - 1 - 2 * p) * D;
+              accf = dot2_bf16(wp[p][ch], row_pair(raw[r0], raw[r0 + D], ch), accf);
+            }
+            z[ch] = SILU ? silu(accf) : accf;
+          }
+        } else {
+          conv_point<E, K, D, SILU>(win, H + u, wt, bs, z);
+        }
+        st16_stream((St*)a.out + ((int64_t)r * q + u) * a.out_rs + c0, E::pack(z));
+      }
+    }
+    // new buffer contents, in place in the lane's own entries
+    if (valid) {
+#pragma unroll
+      for (int ch = 0; ch < VEC; ++ch) {
+        St* row = le + lbase + ch * Sl;
+        if constexpr (SPEC) {
+          // ascending j reads entry acc + j > j before it is overwritten
+          for (int j = 0; j < Sl - q; ++j) row[j] = row[acc + j];
+#pragma unroll
+          for (int u = 0; u < QM; ++u)
+            if (u < q) row[Sl - q + u] = (St)E::get(xr[u], ch);
+        } else {
+          // window = ext[q .. q+H); entries H .. S-1 keep their values
+#pragma unroll
+          for (int j = 0; j < H; ++j) {
+            const int e = q + j;
+            uint32_t val = 0;
+            if (e < H) {
+              val = hist ? (uint32_t)row[e] : 0u;
+            } else {
+#pragma unroll
+              for (int u = 0; u < QM; ++u)
+                if (u == e - H) val = E::get(xr[u], ch);
+            }
+            row[j] = (St)val;
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();
+  if (valid) {
+    St* dp = (St*)a.pool + ((int64_t)slot * a.C + cbase) * Sl;
+#pragma unroll
+    for (int k = 0; k < kSpecSMax; ++k) {
+      const int vi = tid + k * kBlock;
+      if (k < Sl && vi < nvec) st16_stream(dp + vi * VEC, region[vi]);
+    }
+  }
+}
+
+// Any K <= 8, dilation, S, q and alignment: one channel a lane, entries read
+// and rolled in place in global memory.
+template <class E, bool SILU>
+__global__ __launch_bounds__(kBlock) void conv_spec_generic(ConvArgs a, int K, int D) {
+  using St = typename E::S;
+  const int lb = logical_block(a.n_logical, a.per_xcd);
+  if (lb < 0) return;
+  const int r = lb / a.n_cblk, cb = lb - r * a.n_cblk;
+  if (r >= a.batch) return;
+  const int c = cb * kBlock + (int)threadIdx.x;
+  if (c >= a.C) return;
+  const int H = (K - 1) * D, Sl = a.S, q = a.q;
+  float wt[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+    wt[k] = k < K ? widen<E>(ld_el<E>((const St*)a.w + (int64_t)c * K + k)) : 0.f;
+  const float b = a.bias ? widen<E>(ld_el<E>((const St*)a.bias + c)) : 0.f;
+  const int32_t slot = a.slots[(int64_t)r * a.slot_stride];
+  const bool valid = slot >= 0 && slot < a.num_slots;
+  const int acc = min(max(a.num_acc[r], 1), min(q, Sl - H + 1));
+  const St* xb = (const St*)a.x + (int64_t)r * q * a.x_rs + c;
+  St* ob = (St*)a.out + (int64_t)r * q * a.out_rs + c;
+  St* sp = (St*)a.pool + ((int64_t)(valid ? slot : 0) * a.C + c) * Sl;
+  for (int t = 0; t < q; ++t) {
+    float accf = b;
+    for (int k = 0; k < K; ++k) {
+      const int p = t - (K - 1 - k) * D;
+      float v = 0.f;
+      if (p >= 0) v = widen<E>(ld_el<E>(xb + (int64_t)p * a.x_rs));
+      else if (valid) v = widen<E>(ld_el<E>(sp + acc - 1 + H + p));
+      accf = __builtin_fmaf(wt[k], v, accf);
+    }
+    if (SILU) accf = silu(accf);
+    ob[(int64_t)t * a.out_rs] = narrow<E>(accf);
+  }
+  if (valid) {
+    for (int j = 0; j < Sl - q; ++j) sp[j] = sp[acc + j];
+    for (int u = 0; u < q; ++u) sp[Sl - q + u] = xb[(int64_t)u * a.x_rs];
+  }
+}
+
+namespace {
+
+bool rollbuf_shape(int K, int D) {
+  return (K == 4 && (D == 1 || D == 2 || D == 3)) || (D == 1 && (K == 2 || K == 3));
+}
+
+template <class E, bool SILU, bool SPEC>
+hipError_t launch_rollbuf(const ConvArgs& a, int K, int D, dim3 grid, hipStream_t s) {
+  const size_t lds = (size_t)kBlock * a.S * sizeof(u32x4);
+  const dim3 blk(kBlock);
+  if (K == 4 && D == 1) hipLaunchKernelGGL((conv_rollbuf<E, 4, 1, SILU, SPEC>), grid, blk, lds, s, a);
+  else if (K == 4 && D == 2) hipLaunchKernelGGL((conv_rollbuf<E, 4, 2, SILU, SPEC>), grid, blk, lds, s, a);
+  else if (K == 4 && D == 3) hipLaunchKernelGGL((conv_rollbuf<E, 4, 3, SILU, SPEC>), grid, blk, lds, s, a);
+  else if (K == 3) hipLaunchKernelGGL((conv_rollbuf<E, 3, 1, SILU, SPEC>), grid, blk, lds, s, a);
+  else hipLaunchKernelGGL((conv_rollbuf<E, 2, 1, SILU, SPEC>), grid, blk, lds, s, a);
+  return hipGetLastError();
+}
+
+template <bool SPEC>
+hipError_t launch_rollbuf_any(const ConvArgs& a, int dtype, int K, int D, bool silu_act,
+                              dim3 grid, hipStream_t s) {
+  if (dtype == 1)
+    return silu_act ? launch_rollbuf<BF16, true, SPEC>(a, K, D, grid, s)
+                    : launch_rollbuf<BF16, false, SPEC>(a, K, D, grid, s);
+  return silu_act ? launch_rollbuf<F32, true, SPEC>(a, K, D, grid, s)
+                  : launch_rollbuf<F32, false, SPEC>(a, K, D, grid, s);
+}
+
+bool use_rollbuf(const ConvArgs& a, int dtype, int K, int D, bool aligned16) {
+  const int vec = dtype == 1 ? 8 : 4;
+  return aligned16 && a.C % vec == 0 && rollbuf_shape(K, D) && a.q >= 1 && a.q <= kSpecQMax &&
+         a.S >= (K - 1) * D && a.S <= kSpecSMax;
+}
+
+// One workgroup per (request, block of channels); fills the grid fields.
+hipError_t set_grid(ConvArgs& a, int per_block_ch, dim3& grid) {
+  a.n_cblk = (a.C + per_block_ch - 1) / per_block_ch;
+  const int64_t n_logical = (int64_t)a.batch * a.n_cblk;
+  if (n_logical > 0x7FFFFFF0LL) return hipErrorInvalidValue;
+  a.n_logical = (int)n_logical;
+  a.per_xcd = (int)((n_logical + kXcds - 1) / kXcds);
+  grid = dim3((unsigned)(a.per_xcd * kXcds));
+  return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_conv_spec(ConvArgs a, int dtype, int K, int D, bool silu_act, bool aligned16,
+                            hipStream_t stream) {
+  dim3 grid;
+  if (use_rollbuf(a, dtype, K, D, aligned16)) {
+    const hipError_t e = set_grid(a, kBlock * (dtype == 1 ? 8 : 4), grid);
+    if (e != hipSuccess) return e;
+    return launch_rollbuf_any<true>(a, dtype, K, D, silu_act, grid, stream);
+  }
+  const hipError_t e = set_grid(a, kBlock, grid);
+  if (e != hipSuccess) return e;
+  if (dtype == 1) {
+    if (silu_act) hipLaunchKernelGGL((conv_spec_generic<BF16, true>), grid, dim3(kBlock), 0, stream, a, K, D);
+    else hipLaunchKernelGGL((conv_spec_generic<BF16, false>), grid, dim3(kBlock), 0, stream, a, K, D);
+  } else {
+    if (silu_act) hipLaunchKernelGGL((conv_spec_generic<F32, true>), grid, dim3(kBlock), 0, stream, a, K, D);
+    else hipLaunchKernelGGL((conv_spec_generic<F32, false>), grid, dim3(kBlock), 0, stream, a, K, D);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_update_wide(ConvArgs a, int dtype, int K, int D, bool silu_act, bool aligned16,
+                              hipStream_t stream) {
+  if (!use_rollbuf(a, dtype, K, D, aligned16)) return hipErrorNotSupported;
+  dim3 grid;
+  const hipError_t e = set_grid(a, kBlock * (dtype == 1 ? 8 : 4), grid);
+  if (e != hipSuccess) return e;
+  return launch_rollbuf_any<false>(a, dtype, K, D, silu_act, grid, stream);
+}
+
+}  // namespace sc

@@ -218,6 +218,15 @@ def config3b(seed: int = SEED_BASE + 0x33, *, C: int = 8192, B: int = 128,
                      num_decodes=B, q=q)
 
 
+def config3b_spec(seed: int = SEED_BASE + 0x35, *, C: int = 8192, B: int = 128,
+                  num_spec: int = 3, num_slots: int = 1024) -> ConvCase:
+    """Speculative update: B requests x (num_spec + 1) tokens on a rolling
+    buffer of (K-1) + num_spec entries (accepted counts from num_accepted)."""
+    return conv_case("cfg3b_spec_rollback", seed, C=C, K=4, d=1, dtype="bf16",
+                     act="silu", w_std=0.25, bias_std=0.1, num_slots=num_slots,
+                     num_decodes=B, q=num_spec + 1, num_spec=num_spec)
+
+
 def config4(seed: int = SEED_BASE + 4, *, C: int = 8192, num_decodes: int = 256,
             Bp: int = 16, min_len: int = 128, max_len: int = 4096,
             grid: int = 512, num_slots: int = 1024) -> ConvCase:

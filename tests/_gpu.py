@@ -81,6 +81,30 @@ def run_conv_case(case, *, pool=None, x_pad: int = 0, slot_2d: int = 0, stream=N
     return host(od.contiguous()), host(pd)
 
 
+def run_spec_case(case, num_accepted, *, pool=None, x_pad: int = 0, stream=None):
+    """Runs a ConvCase's decode requests (q rows each) as speculative requests
+    through sc_conv_update_spec with the given accepted counts. Returns
+    (out, pool_after) as NumPy arrays."""
+    import torch
+    import stateful_causal_short_amd as scs
+    T, C = case.num_decode_tokens, case.C
+    if x_pad:
+        xs = np.zeros((T, C + x_pad), case.x.dtype)
+        xs[:, :C] = case.x[:T]
+        xd = dev(xs)[:, :C]
+        od = dev(np.zeros((T, C + x_pad), case.x.dtype))[:, :C]
+    else:
+        xd = dev(case.x[:T])
+        od = dev(np.zeros((T, C), case.x.dtype))
+    pd = dev(case.pool if pool is None else pool)
+    scs.sc_conv_update_spec(xd, od, dev(case.w), None if case.bias is None else dev(case.bias),
+                            pd, dev(np.asarray(case.decode_slots, np.int32)),
+                            dev(np.asarray(num_accepted, np.int32)), q=case.q,
+                            dilation=case.d, activation=case.act, stream=stream)
+    torch.cuda.synchronize()
+    return host(od.contiguous()), host(pd)
+
+
 def ulp_bf16(ref: np.ndarray) -> np.ndarray:
     a = np.maximum(np.abs(ref), 2.0 ** -126)
     return np.exp2(np.floor(np.log2(a)) - 7)

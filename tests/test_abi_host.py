@@ -55,6 +55,11 @@ def update(d, *, x=P, out=P2, w=P, pool=P, num_slots=4, slots=P, h=None, batch=2
                                     None, pool, num_slots, slots, h, batch, q, None)
 
 
+def spec(d, *, x=P, out=P2, w=P, pool=P, num_slots=4, slots=P, acc=P, batch=2, q=2):
+    return scs.lib().sc_conv_update_spec(None if d is None else ctypes.byref(d), x, out, w,
+                                         None, pool, num_slots, slots, acc, batch, q, None)
+
+
 @pytest.mark.parametrize("kw,status", [
     (dict(dtype=7), DTYPE),
     (dict(channels=0), INVALID),
@@ -67,11 +72,35 @@ def update(d, *, x=P, out=P2, w=P, pool=P, num_slots=4, slots=P, h=None, batch=2
     (dict(state_indices_stride=0), INVALID),
     (dict(state_len=2), CAPACITY),                 # (4-1)*1 = 3 needed
     (dict(dilation=3, state_len=8), CAPACITY),     # 9 needed
-    (dict(state_len=7), UNSUPPORTED),              # speculative rolling window
+    (dict(state_len=(1 << 20) + 1), INVALID),
 ])
 def test_descriptor_validation(kw, status):
     assert prefill(desc(**kw)) == status
     assert update(desc(**kw)) == status
+    assert spec(desc(**kw)) == status
+
+
+def test_wide_state_rows_are_accepted():
+    # a buffer sized for speculative rollback (S = H + num_spec): zero-work calls succeed
+    d = desc(state_len=7)
+    assert prefill(d, batch=0) == OK
+    assert update(d, batch=0) == OK
+    assert spec(d, batch=0) == OK
+
+
+def test_spec_rules():
+    d = desc(state_len=6)
+    assert spec(None) == NULL
+    assert spec(d, acc=None) == NULL
+    assert spec(d, slots=None) == NULL
+    assert spec(d, pool=None) == NULL
+    assert spec(d, out=P) == INVALID            # out aliases x
+    assert spec(d, q=7) == INVALID              # 7 drafts do not fit 6 entries
+    assert spec(d, q=7, batch=0) == INVALID     # checked before the zero-work exit
+    assert spec(d, q=-1) == INVALID
+    assert spec(d, batch=-1) == INVALID
+    assert spec(d, x=None, out=None, w=None, slots=None, acc=None, pool=None, batch=0) == OK
+    assert spec(d, q=0) == OK
 
 
 def test_null_arguments():
