@@ -16,15 +16,11 @@
 // history another workgroup still has to read, and main-kernel tiles may mix
 // decode and prefill rows freely.
 //
-// Main kernel for hd = 128, t1 = 2 (the ZAYA shape): a workgroup owns MT token
-// rows of one kv bundle (the G q heads of kv head g plus k head g), so both
-// residuals stay inside the workgroup. For each of the bundle's G+1 head
-// groups it materialises the depthwise outputs in LDS as bf16 (prev, cur)
-// pairs, i.e. K ordered k = 2j + b, which makes each grouped-weight fragment a
-// contiguous 16-byte slice of the (C, hd, t1) weight; then the grouped conv is
-// the GEMM out^T (128 x MT) = W2_g (128 x 256) . act^T (256 x MT) on
-// v_mfma_f32_32x32x16_bf16 (each wave 32 output channels), and the epilogue adds
-// bias and residual and stores bf16.
+// The main kernel for hd = 128, t1 = 2 (the ZAYA shape) is cca_persist_main
+// below (persistent, weight-stationary, grouped conv on MFMA); other shapes
+// take the one-thread-per-output cca_generic_main.
+#include <algorithm>
+
 #include "common.hpp"
 #include "cca.hpp"
 
@@ -32,6 +28,7 @@ namespace sc {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 namespace {
 
@@ -96,6 +93,35 @@ __device__ __forceinline__ uint32_t raw_el(const CcaArgs& a, int64_t t, int c) {
   const uint16_t* src = c < qd ? (const uint16_t*)a.q + t * a.q_rs + c
                                : (const uint16_t*)a.k + t * a.k_rs + (c - qd);
   return *src;
+}
+
+// Logical workgroup index: workgroups are dealt to the 8 XCDs round-robin;
+// this gives each XCD a contiguous run of logical blocks, so the head groups
+// of one token chunk (which re-read each other's raw rows for the residuals)
+// share an L2.
+__device__ __forceinline__ int logical_block_cca(const CcaArgs& a) {
+  const int b = (int)blockIdx.x;
+  const int lb = (b % 8) * a.per_xcd + b / 8;
+  return lb < a.n_logical ? lb : -1;
+}
+
+// Raw buffer access (range-checked by the hardware): an offset at or beyond
+// `bytes` reads zeros and drops stores, so masked rows cost no branch.
+// Offsets are 32-bit; every resource below spans at most one token chunk.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kOff = 0x80000000u;   // an offset outside every resource
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int64_t b = bytes < 0 ? 0 : (bytes > 0x7FFFFFFF ? 0x7FFFFFFF : bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)b, 0x00020000);
+}
+__device__ __forceinline__ u32x4 bld16(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+__device__ __forceinline__ u32x4 bld16_stream(rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2);
+}
+__device__ __forceinline__ void bst16_stream(rsrc_t r, uint32_t off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 2);
 }
 
 }  // namespace
@@ -273,252 +299,403 @@ __global__ __launch_bounds__(kBlock) void cca_state_update_vec(CcaArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// MFMA main kernel (hd = 128, t1 = 2, t0 = T0 <= 4): MT rows per workgroup,
-// 8 waves per 64 rows (4 channel blocks x MT/32 token tiles)
+// MFMA main kernel (hd = 128, t1 = 2, t0 = T0 <= 4): persistent and
+// weight-stationary. The grid holds a multiple of NG = nq + nkv workgroups;
+// workgroup (head group grp, lane k0) walks the 32-row tiles k0, k0 + S,
+// k0 + 2S, ... (S = workgroups per group), so every tile is visited by the NG
+// workgroups of one S-slice at about the same time, and each workgroup loads
+// the 128 x 256 grouped weight of its head group once. Each of the 8 waves
+// keeps the slice of 16 output channels it multiplies in registers.
+//
+// Per tile: (A) the depthwise output of each row at its own position goes to
+// LDS row `act`; its value one position earlier is the previous LDS row when
+// both rows belong to one request, is computed into a side row `prv` when the
+// row starts a request (its window is then all history), and for the tile's
+// first row from the rows before the tile. The residual (plus grouped bias) is
+// computed alongside in fp32. (B) the grouped conv is the GEMM
+// out^T (128 x 32) = W2 (128 x 256) . act^T (256 x 32) with K ordered
+// k = b*128 + j (tap b, input channel j) on v_mfma_f32_16x16x32_bf16; the
+// epilogue adds the residual and stages bf16 rows, stored as 256-byte row
+// segments. The raw rows (and value columns) of the tile two ahead are in
+// flight meanwhile (one ahead for the k head, which also reads the bundle's
+// q rows). All row traffic uses range-checked buffer instructions: masked
+// rows read zeros and drop stores without a branch.
 // ---------------------------------------------------------------------------
-template <int MT>
-constexpr int cca_threads() { return 256 * (MT / 32); }
+constexpr int kCcaThreads = 512;   // 8 waves: 16 output channels each
+constexpr int kCcaMT = 32;         // token rows per tile
 
-template <int T0, int MT>
-__global__ __launch_bounds__(cca_threads<MT>(), SC_CCA_MIN_WAVES) void cca_mfma_main(CcaArgs a) {
-  constexpr int HD = 128;
-  constexpr int NV = HD / 8;           // 16-byte vectors per head row
-  constexpr int N = T0;                // history length n = t0 + t1 - 2 with t1 = 2
-  constexpr int AROW = 2 * HD + 8;     // LDS row of (prev, cur) pairs, padded (bf16)
-  constexpr int OROW = HD + 8;         // LDS row of staged outputs (bf16)
-  constexpr int RROW = NV + 1;         // LDS raw row in 16-byte vectors, padded
-  constexpr int NTH = cca_threads<MT>();
-  constexpr int RPT = MT * NV / NTH;   // depthwise rows per lane (= 2)
-  constexpr int NR = RPT + T0;         // raw rows per lane: its rows plus the halo
-  constexpr int KS = 2 * HD / 16;      // MFMA K steps
-  static_assert(MT % 32 == 0 && MT <= 128 && RPT * NTH == MT * NV, "tile rows");
-  static_assert(MT * OROW <= MT * AROW, "output staging fits in the pair buffer");
+template <int T0>
+struct CcaSmem {
+  static constexpr int HD = 128, MT = kCcaMT;
+  static constexpr int AROW = HD + 8;   // bf16 LDS rows (padded)
+  static constexpr int RROW = HD + 4;   // fp32 residual rows (padded)
+  uint16_t act[(MT + 1) * AROW];        // depthwise rows: row i+1 = token i, row 0 = token -1
+  uint16_t prv[MT * AROW];              // depthwise one position back, for request starts
+  uint16_t ost[MT * AROW];              // staged bf16 output rows
+  float res[MT * RROW];                 // residual + grouped bias, fp32
+  uint16_t w1[HD * T0];                 // depthwise weights of the group (c, tap)
+  uint16_t b1[HD], b2[HD];              // depthwise and grouped biases
+  int32_t qsl_s[kQslCache];
+  int row_p[2][MT];                     // position in the request (-1: no row), by tile parity
+  int row_src[2][MT];                   // prefill request index, or -2 - t for decode row t
+};
 
-  __shared__ __attribute__((aligned(16))) uint16_t act[MT * AROW];
-  __shared__ u32x4 rawc[MT * RROW];    // current rows of the q head being processed
-  __shared__ u32x4 rawk[MT * RROW];    // current rows of the bundle's k head
-  __shared__ int32_t qsl_s[kQslCache];
-  __shared__ int row_p[MT];
-  __shared__ int32_t row_slot[MT];
-  __shared__ uint8_t row_h[MT];
+// Waves per SIMD the main kernel is compiled for: 2 (one 8-wave workgroup per
+// CU). Phase A's fp32 working set keeps the kernel above the 128 registers
+// that a second resident workgroup would need.
+template <int T0>
+constexpr int cca_waves_per_simd() { return SC_CCA_MIN_WAVES; }
 
-  const int nkv = a.nkv, G = a.nq / a.nkv;
-  const int C = (a.nq + a.nkv) * HD;
-  const int qd = a.nq * HD, vd = a.nkv * HD / 2;
-  const int tile = (int)blockIdx.x / nkv, g = (int)blockIdx.x - tile * nkv;
-  const int64_t t0 = (int64_t)tile * MT;
-  const int tid = (int)threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int cw = wave & 3, nt = wave >> 2;          // GEMM: channel block, token tile
-  const int v = tid % NV, i0 = (tid / NV) * RPT;    // depthwise: channel vector, first row
-  const bool use_lds_qsl = a.num_prefills > 0 && a.num_prefills + 1 <= kQslCache;
-
-  if (use_lds_qsl)
-    for (int i = tid; i <= a.num_prefills; i += NTH) qsl_s[i] = a.prefill_qsl[i];
-  __syncthreads();
-  if (tid < MT) {
-    const RowInfo ri = row_info(a, t0 + tid, use_lds_qsl ? qsl_s : nullptr);
-    row_p[tid] = ri.p;
-    row_slot[tid] = ri.slot;
-    row_h[tid] = ri.h ? 1 : 0;
-  }
-  __syncthreads();
-
-  int rp[RPT];
-#pragma unroll
-  for (int r = 0; r < RPT; ++r) rp[r] = row_p[i0 + r];
-
-  // depthwise inputs of one head group: raw rows i0-T0 .. i0+RPT-1 (halo rows
-  // only when the first row's request reaches back to them), weights, bias
-  u32x4 xr[NR], wv[T0], bv;
-  auto issue_dw = [&](int gi) {
-    const bool isk = gi == G;
-    const int cbase = isk ? (a.nq + g) * HD : (g * G + gi) * HD;
-    const uint16_t* src = isk ? (const uint16_t*)a.k + g * HD
-                              : (const uint16_t*)a.q + (int64_t)(g * G + gi) * HD;
-    const int64_t srs = isk ? a.k_rs : a.q_rs;
-#pragma unroll
-    for (int s = 0; s < NR; ++s) {
-      const int i = i0 - T0 + s;
-      const bool need = s >= T0 ? rp[s - T0] >= 0 : rp[0] >= T0 - s;
-      xr[s] = need ? ld16(src + (t0 + i) * srs + v * 8) : u32x4{0, 0, 0, 0};
-    }
-    const uint16_t* wp = (const uint16_t*)a.w_dw + (int64_t)(cbase + v * 8) * T0;
-#pragma unroll
-    for (int s = 0; s < T0; ++s) wv[s] = ld16(wp + s * 8);
-    bv = ld16((const uint16_t*)a.b_dw + cbase + v * 8);
-  };
-  issue_dw(0);
-
-  // the bundle's k head rows (residual of every group)
-  for (int it = tid; it < MT * NV; it += NTH) {
-    const int i = it / NV, vv = it - i * NV;
-    u32x4 val = {0, 0, 0, 0};
-    if (row_p[i] >= 0) val = ld16((const uint16_t*)a.k + (t0 + i) * a.k_rs + g * HD + vv * 8);
-    rawk[i * RROW + vv] = val;
-  }
-
-  f32x16 qsum;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) qsum[r] = 0.f;
-
-  for (int gi = 0; gi <= G; ++gi) {
-    const bool isk = gi == G;
-    const int cbase = isk ? (a.nq + g) * HD : (g * G + gi) * HD;
-#if !SC_CCA_XPREF
-    if (gi > 0) issue_dw(gi);
-#endif
-    const uint16_t* wrow = (const uint16_t*)a.w_gr +
-                           ((int64_t)(cbase + cw * 32 + (lane & 31)) * (2 * HD)) + 8 * (lane >> 5);
-    // history of rows that reach back before their request's first token
-    u32x4 hist[RPT][N];
-#pragma unroll
-    for (int r = 0; r < RPT; ++r) {
-      const bool need = rp[r] >= 0 && rp[r] < T0 && row_h[i0 + r];
-      const uint16_t* hp = (const uint16_t*)a.conv_state +
-                           ((int64_t)(need ? row_slot[i0 + r] : 0) * C + cbase + v * 8) * N;
-#pragma unroll
-      for (int vv = 0; vv < N; ++vv) hist[r][vv] = need ? ld16(hp + vv * 8) : u32x4{0, 0, 0, 0};
-    }
-
-    __syncthreads();   // previous group's output staging has been stored
-    // ---- depthwise: (prev, cur) bf16 pairs for 8 channels of RPT rows ----
-    {
-      float wf32[T0][8], bs[8];
-#pragma unroll
-      for (int s = 0; s < T0; ++s) {
-        float f[8];
-        BF16::unpack(wv[s], f);
-        // wv[s] holds w_dw[(c0+ch)*T0 + tap] in element order ch*T0 + tap
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int flat = s * 8 + e, ch = flat / T0, tap = flat % T0;
-          wf32[tap][ch] = f[e];
-        }
+// Row info of the tile starting at token ta (threads 0 .. 31, one row each).
+// `cur` is the thread's prefill request index from its previous (earlier)
+// tile: the search gallops forward from it, then bisects.
+__device__ __forceinline__ void cca_tile_rows(const CcaArgs& a, int64_t ta, const int32_t* qsl,
+                                              int* rp, int* rs, int& cur) {
+  const int i = (int)threadIdx.x;
+  if (i >= kCcaMT) return;
+  const int64_t t = ta + i;
+  int p = -1, src = -1;
+  if (t < a.num_tokens) {
+    if (t < a.num_decodes) {
+      p = 0;
+      src = -2 - (int)t;
+    } else if (a.num_prefills > 0) {
+      const int B = a.num_prefills;
+      const int x = (int)(t - a.num_decodes);
+      int r = cur, step = 1;
+      while (r + step < B && qsl[r + step] <= x) {
+        r += step;
+        step <<= 1;
       }
-      BF16::unpack(bv, bs);
+      int lo = r, hi = min(r + step, B) - 1;      // largest index with qsl <= x
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (qsl[mid] <= x) lo = mid;
+        else hi = mid - 1;
+      }
+      cur = lo;
+      const int s0 = qsl[lo], s1 = qsl[lo + 1];
+      if (x >= s0 && x < s1) {
+        p = x - s0;
+        src = lo;
+      }
+    }
+  }
+  rp[i] = p;
+  rs[i] = src;
+}
+
+// Slot and has-state flag of a row's request (global reads: request starts only).
+__device__ __forceinline__ void cca_row_state(const CcaArgs& a, int src, int32_t& slot, bool& h) {
+  slot = -1;
+  h = false;
+  if (src <= -2) {
+    slot = a.decode_slots[(int64_t)(-2 - src) * a.dslot_stride];
+    h = slot >= 0 && slot < a.num_slots;
+  } else if (src >= 0) {
+    slot = a.prefill_slots[(int64_t)src * a.pslot_stride];
+    h = slot >= 0 && slot < a.num_slots && a.prefill_h[src] != 0;
+  }
+}
+
+template <int T0, int GMAX, bool ISK>
+__device__ __forceinline__ void cca_persist_body(const CcaArgs& a, CcaSmem<T0>& sm, int grp, int k0,
+                                                 int S, int my_tiles) {
+  using SM = CcaSmem<T0>;
+  constexpr int HD = 128;
+  constexpr int MT = kCcaMT;
+  constexpr int N = T0;                // history length n = t0 + t1 - 2 with t1 = 2
+  constexpr int AROW = SM::AROW;
+  constexpr int RROW = SM::RROW;
+  constexpr int NR = T0 + 1;           // raw rows per lane: i-T0 .. i
+  constexpr bool isk = ISK;
+
+  const int NG = a.nq + a.nkv, G = a.nq / a.nkv;
+  const int C = NG * HD, vd = a.nkv * HD / 2, nvv = vd / 8;
+  const int g = isk ? grp - a.nq : grp / G;       // kv head of the bundle
+  const int cbase = grp * HD;                      // raw / output channel base
+  const int tid = (int)threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int v = tid & 15, i = tid >> 4;            // depthwise: channel vector, tile row
+  const bool use_lds_qsl = a.num_prefills > 0 && a.num_prefills + 1 <= kQslCache;
+  // value columns of this group: vectors vv = grp + k * NG of 2 * nvv; item tid = (row, k)
+  const int mine = (2 * nvv - grp + NG - 1) / NG;
+  const int vr = tid / max(mine, 1), vk = tid - vr * max(mine, 1);
+  const bool vitem = tid < MT * mine;
+  const int vvv = grp + vk * NG;                   // this thread's value vector
+  const int64_t qrs = a.q_rs * 2, krs = a.k_rs * 2, ors = a.out_rs * 2;   // bytes
+  const int64_t vcb = a.vc_rs * 2, vdb = a.vd_rs * 2;
+  const int64_t srs = isk ? krs : qrs;
+  const int scol = ((isk ? g : grp) * HD + v * 8) * 2;    // byte column of the raw input
+
+  // ---- setup: parameters and prefill boundaries to LDS, weights to registers ----
+  if (use_lds_qsl)
+    for (int k = tid; k <= a.num_prefills; k += kCcaThreads) sm.qsl_s[k] = a.prefill_qsl[k];
+  if (tid < HD * T0 / 8)
+    *(u32x4*)(sm.w1 + tid * 8) = ld16((const uint16_t*)a.w_dw + (int64_t)cbase * T0 + tid * 8);
+  else if (tid < HD * T0 / 8 + 16)
+    *(u32x4*)(sm.b1 + (tid - HD * T0 / 8) * 8) =
+        ld16((const uint16_t*)a.b_dw + cbase + (tid - HD * T0 / 8) * 8);
+  else if (tid < HD * T0 / 8 + 32)
+    *(u32x4*)(sm.b2 + (tid - HD * T0 / 8 - 16) * 8) =
+        ld16((const uint16_t*)a.b_gr + cbase + (tid - HD * T0 / 8 - 16) * 8);
+  // grouped weights of this wave's 16 output channels, K ordered b*128 + j:
+  // one 32-byte run of a (C, hd, t1) row holds taps 0 and 1 of 8 channels
+  bf16x8 wf[8];
+  {
+    const uint16_t* wrow = (const uint16_t*)a.w_gr + (int64_t)(cbase + wv * 16 + (lane & 15)) * (2 * HD);
 #pragma unroll
-      for (int r = 0; r < RPT; ++r) {
-        const int p = rp[r];
-        uint32_t pairs[8];
-        float e[T0 + 1][8];
+    for (int kk = 0; kk < 4; ++kk) {
+      const int j = kk * 32 + 8 * (lane >> 4);
+      const u32x4 lo = ld16(wrow + 2 * j), hi = ld16(wrow + 2 * j + 8);
+      u32x4 t0v, t1v;
 #pragma unroll
-        for (int s = 0; s <= T0; ++s) BF16::unpack(xr[r + s], e[s]);
-        if (p < T0) {
-          // the window reaches back before the request: history (or zeros)
+      for (int w = 0; w < 2; ++w) {
+        t0v[w] = __builtin_amdgcn_perm(lo[2 * w + 1], lo[2 * w], 0x05040100u);
+        t1v[w] = __builtin_amdgcn_perm(lo[2 * w + 1], lo[2 * w], 0x07060302u);
+        t0v[w + 2] = __builtin_amdgcn_perm(hi[2 * w + 1], hi[2 * w], 0x05040100u);
+        t1v[w + 2] = __builtin_amdgcn_perm(hi[2 * w + 1], hi[2 * w], 0x07060302u);
+      }
+      wf[kk] = __builtin_bit_cast(bf16x8, t0v);
+      wf[kk + 4] = __builtin_bit_cast(bf16x8, t1v);
+    }
+  }
+
+  // whole-tensor buffer resources (the launcher keeps every tensor under
+  // 2 GiB, so all offsets are 32-bit); a row before the batch wraps to an
+  // offset outside the resource and reads zeros
+  const uint32_t T = (uint32_t)a.num_tokens;
+  const rsrc_t qbuf = make_rsrc(a.q, (int64_t)T * qrs);
+  const rsrc_t kbuf = make_rsrc(a.k, (int64_t)T * krs);
+  const rsrc_t obuf = make_rsrc(a.out, (int64_t)T * ors);
+  const rsrc_t vcbuf = make_rsrc(a.v_cur, (int64_t)T * vcb);
+  const rsrc_t vdbuf = make_rsrc(a.v_del, (int64_t)T * vdb);
+  const rsrc_t sbuf = isk ? kbuf : qbuf;
+  const uint32_t srs32 = (uint32_t)srs, krs32 = (uint32_t)krs, qrs32 = (uint32_t)qrs;
+  const uint32_t ors32 = (uint32_t)ors;
+  // per-lane parts of the offsets (row i of the tile; raw slot s is row i-T0+s)
+  const uint32_t x_lane = (uint32_t)(i - T0) * srs32 + (uint32_t)scol;
+  const uint32_t k_lane = (uint32_t)i * krs32 + (uint32_t)((g * HD + v * 8) * 2);
+  const uint32_t q_lane = (uint32_t)i * qrs32 + (uint32_t)((g * G * HD + v * 8) * 2);
+  const uint32_t v_lane = vvv < nvv ? (uint32_t)vr * (uint32_t)vcb + (uint32_t)(vvv * 16)
+                                    : (uint32_t)(vr - 1) * (uint32_t)vdb + (uint32_t)((vvv - nvv) * 16);
+  const uint32_t o_lane = (uint32_t)i * ors32 + (uint32_t)((cbase + v * 8) * 2);
+  const uint32_t ov_lane = (uint32_t)vr * ors32 + (uint32_t)((C + vvv * 8) * 2);
+
+  auto tile_ta = [&](int u) -> uint32_t { return (uint32_t)(k0 + u * S) * MT; };
+
+  // one tile's loads: raw rows i-T0 .. i of this lane's channel vector (rows
+  // of another request are loaded too and never used), the residual rows, and
+  // this thread's value item (v_cur row t, or v_del row t-1 for the shift)
+  struct Pref {
+    u32x4 x[NR], r[isk ? GMAX : 1], val;
+  };
+  auto issue = [&](int u, Pref& f) {
+    const uint32_t ta = tile_ta(u);
 #pragma unroll
-          for (int s = 0; s < T0; ++s) {
-            const int pos = p - T0 + s;          // ext position of tap s
+    for (int s = 0; s < NR; ++s) f.x[s] = bld16(sbuf, x_lane + (ta + s) * srs32);
+    if constexpr (!isk) {
+      f.r[0] = bld16(kbuf, k_lane + ta * krs32);
+    } else {
+#pragma unroll
+      for (int qi = 0; qi < GMAX; ++qi)
+        f.r[qi] = bld16(qbuf, qi < G ? q_lane + ta * qrs32 + (uint32_t)(qi * HD * 2) : kOff);
+    }
+    if (vvv < nvv) f.val = bld16_stream(vcbuf, vitem ? v_lane + ta * (uint32_t)vcb : kOff);
+    else f.val = bld16(vdbuf, vitem ? v_lane + ta * (uint32_t)vdb : kOff);
+  };
+
+  int rcur = 0;   // request cursor of this thread's row (threads 0 .. 31)
+  auto tile = [&](int u, Pref& f) {
+    const int cur = u & 1;
+    const uint32_t ta = tile_ta(u);
+    const int* rp = sm.row_p[cur];
+    const int* rsrc_ = sm.row_src[cur];
+    // ---- (A) depthwise rows, the request-start and tile-start side rows, residual ----
+    {
+      u32x4 wq[T0];
+#pragma unroll
+      for (int s = 0; s < T0; ++s) wq[s] = *(const u32x4*)(sm.w1 + (v * 8) * T0 + s * 8);
+      const u32x4 b1q = *(const u32x4*)(sm.b1 + v * 8), b2q = *(const u32x4*)(sm.b2 + v * 8);
+      auto w1 = [&](int tap, int ch) -> float {
+        const int el = ch * T0 + tap;
+        return bf2f(BF16::get(wq[el / 8], el % 8));
+      };
+      auto xe = [&](int s, int ch) -> float { return bf2f(BF16::get(f.x[s], ch)); };
+      const int p = rp[i];
+      // depthwise of this row's request at position pos; tap `tap` reads raw
+      // slot base + tap when its ext position is >= 0, else the request's
+      // history (zeros without state), taken only near a request's start
+      auto dw = [&](int pos, int base) -> u32x4 {
+        float d[8];
+#pragma unroll
+        for (int ch = 0; ch < 8; ++ch) d[ch] = bf2f(BF16::get(b1q, ch));
+        if (pos >= T0 - 1) {
+#pragma unroll
+          for (int tap = 0; tap < T0; ++tap)
+#pragma unroll
+            for (int ch = 0; ch < 8; ++ch) d[ch] = __builtin_fmaf(w1(tap, ch), xe(base + tap, ch), d[ch]);
+        } else {
+          int32_t slot;
+          bool hn;
+          cca_row_state(a, rsrc_[i], slot, hn);
+          const uint16_t* hp = (const uint16_t*)a.conv_state +
+                               ((int64_t)(hn ? slot : 0) * C + cbase + v * 8) * N;
+          u32x4 hist[N];
+#pragma unroll
+          for (int q = 0; q < N; ++q) hist[q] = hn ? ld16(hp + q * 8) : u32x4{0, 0, 0, 0};
+#pragma unroll
+          for (int tap = 0; tap < T0; ++tap) {
+            const int ep = pos - (T0 - 1) + tap;     // ext position of the tap
 #pragma unroll
             for (int ch = 0; ch < 8; ++ch) {
-              float hv = 0.f;
+              float x = 0.f;
+              if (ep >= 0) {
+                x = xe(base + tap, ch);
+              } else {
 #pragma unroll
-              for (int q = 1; q <= N; ++q) {
-                const int el = ch * N + N - q;
-                if (pos == -q) hv = bf2f(BF16::get(hist[r][el / 8], el % 8));
+                for (int q = 1; q <= N; ++q) {       // position -q = entry N - q
+                  const int el = ch * N + N - q;
+                  if (ep == -q) x = bf2f(BF16::get(hist[el / 8], el % 8));
+                }
               }
-              if (pos < 0) e[s][ch] = hv;
+              d[ch] = __builtin_fmaf(w1(tap, ch), x, d[ch]);
             }
           }
         }
+        return u32x4{pk_bf16(d[0], d[1]), pk_bf16(d[2], d[3]), pk_bf16(d[4], d[5]),
+                     pk_bf16(d[6], d[7])};
+      };
+      // residual + grouped bias, fp32
+      float y[8];
+      if constexpr (!isk) {
+#pragma unroll
+        for (int ch = 0; ch < 8; ++ch)
+          y[ch] = bf2f(BF16::get(b2q, ch)) + 0.5f * (xe(T0, ch) + bf2f(BF16::get(f.r[0], ch)));
+      } else {
+        // the mean over the bundle's q heads, summed in head order
 #pragma unroll
         for (int ch = 0; ch < 8; ++ch) {
-          float dp = bs[ch], dc = bs[ch];
+          float s = 0.f;
 #pragma unroll
-          for (int s = 0; s < T0; ++s) {
-            dp = __builtin_fmaf(wf32[s][ch], e[s][ch], dp);
-            dc = __builtin_fmaf(wf32[s][ch], e[s + 1][ch], dc);
-          }
-          pairs[ch] = p >= 0 ? pk_bf16(dp, dc) : 0u;
+          for (int qi = 0; qi < GMAX; ++qi)
+            if (qi < G) s += bf2f(BF16::get(f.r[qi], ch));
+          y[ch] = bf2f(BF16::get(b2q, ch)) + 0.5f * (s / (float)G + xe(T0, ch));
         }
-        u32x4* ap = (u32x4*)(act + (i0 + r) * AROW + v * 16);
-        ap[0] = u32x4{pairs[0], pairs[1], pairs[2], pairs[3]};
-        ap[1] = u32x4{pairs[4], pairs[5], pairs[6], pairs[7]};
-        if (!isk) rawc[(i0 + r) * RROW + v] = p >= 0 ? xr[r + T0] : u32x4{0, 0, 0, 0};
       }
+      u32x4 cur_dw = {0, 0, 0, 0};
+      if (p >= 0) {
+        cur_dw = dw(p, 1);
+        if (p == 0) *(u32x4*)(sm.prv + i * AROW + v * 8) = dw(-1, 0);
+      }
+      *(u32x4*)(sm.act + (i + 1) * AROW + v * 8) = cur_dw;
+      float* rq = sm.res + i * RROW + v * 8;
+      *(float4*)rq = float4{y[0], y[1], y[2], y[3]};
+      *(float4*)(rq + 4) = float4{y[4], y[5], y[6], y[7]};
+      // the tile's first row continues a request: its previous position
+      if (i == 0 && p >= 1) *(u32x4*)(sm.act + v * 8) = dw(p - 1, 0);
     }
-#if SC_CCA_XPREF
-    if (gi < G) issue_dw(gi + 1);      // next group's inputs in flight during the GEMM
-#endif
+    // value item of this tile, then the next tiles' rows and loads
+    u32x4 val = f.val;
+    const int vp = vitem ? rp[vr] : -1;
+    const int vsrc = vitem ? rsrc_[vr] : -1;
+    if (u + 1 < my_tiles) cca_tile_rows(a, tile_ta(u + 1), use_lds_qsl ? sm.qsl_s : a.prefill_qsl,
+                                        sm.row_p[cur ^ 1], sm.row_src[cur ^ 1], rcur);
+    if (u + SC_CCA_AHEAD < my_tiles) issue(u + SC_CCA_AHEAD, f);
+    // store offsets of this tile (row info is rewritten by the next tile)
+    const uint32_t ooff = rp[i] >= 0 ? o_lane + ta * ors32 : kOff;
+    const uint32_t voff = vp >= 0 ? ov_lane + ta * ors32 : kOff;
     __syncthreads();
 
-    // ---- grouped conv on MFMA: out^T tile = W2 (32 ch x 256) . act^T (256 x 32 tok) ----
-    f32x16 acc;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-#pragma unroll SC_CCA_KUNROLL
-    for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 af = __builtin_bit_cast(bf16x8, ld16(wrow + ks * 16));
-      const u32x4 bvv = *(const u32x4*)(act + (nt * 32 + (lane & 31)) * AROW + ks * 16 + 8 * (lane >> 5));
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, __builtin_bit_cast(bf16x8, bvv), acc, 0, 0, 0);
-    }
-
-    // ---- epilogue: bias + residual, bf16 staged in LDS (act is reused) ----
-    __syncthreads();   // every wave is done reading act (GEMM) before it is reused
-    uint16_t* ost = act;
+    // ---- (B) grouped conv on MFMA: this wave's 16 channels x 32 tokens ----
+    f32x4 acc[2];
     {
-      const int i = nt * 32 + (lane & 31);
+      const uint16_t* bp[2][2];
 #pragma unroll
-      for (int run = 0; run < 4; ++run) {
-        const int cl = cw * 32 + 8 * run + 4 * (lane >> 5);     // channel within the head
-        const uint2 bb = *(const uint2*)((const uint16_t*)a.b_gr + cbase + cl);
-        const float b2[4] = {bf2f(bb.x & 0xFFFFu), bf2f(bb.x >> 16), bf2f(bb.y & 0xFFFFu), bf2f(bb.y >> 16)};
-        const int vsel = cl >> 3, half = (cl >> 2) & 1;
-        const u32x4 kv4 = rawk[i * RROW + vsel];
-        const uint32_t k01 = kv4[2 * half], k23 = kv4[2 * half + 1];
-        const float kf[4] = {bf2f(k01 & 0xFFFFu), bf2f(k01 >> 16), bf2f(k23 & 0xFFFFu), bf2f(k23 >> 16)};
-        float y[4];
-        if (!isk) {
-          const u32x4 qv4 = rawc[i * RROW + vsel];
-          const uint32_t q01 = qv4[2 * half], q23 = qv4[2 * half + 1];
-          const float qf[4] = {bf2f(q01 & 0xFFFFu), bf2f(q01 >> 16), bf2f(q23 & 0xFFFFu), bf2f(q23 >> 16)};
+      for (int th = 0; th < 2; ++th) {
+        const int n = th * 16 + (lane & 15);
+        bp[th][0] = (rp[n] >= 1 ? sm.act + n * AROW : sm.prv + n * AROW) + 8 * (lane >> 4);
+        bp[th][1] = sm.act + (n + 1) * AROW + 8 * (lane >> 4);
+        acc[th] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+      // B fragments in two batches of 8 LDS reads, each read ahead of its MFMAs
 #pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            qsum[4 * run + s] += qf[s];
-            y[s] = acc[4 * run + s] + b2[s] + 0.5f * (qf[s] + kf[s]);
-          }
-        } else {
+      for (int half = 0; half < 2; ++half) {
+        u32x4 bv[2][4];
 #pragma unroll
-          for (int s = 0; s < 4; ++s)
-            y[s] = acc[4 * run + s] + b2[s] + 0.5f * (qsum[4 * run + s] / (float)G + kf[s]);
-        }
-        uint2 o;
-        o.x = pk_bf16(y[0], y[1]);
-        o.y = pk_bf16(y[2], y[3]);
-        *(uint2*)(ost + i * OROW + cl) = o;
+        for (int k4 = 0; k4 < 4; ++k4)
+#pragma unroll
+          for (int th = 0; th < 2; ++th) bv[th][k4] = *(const u32x4*)(bp[th][half] + k4 * 32);
+#pragma unroll
+        for (int k4 = 0; k4 < 4; ++k4)
+#pragma unroll
+          for (int th = 0; th < 2; ++th)
+            acc[th] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[half * 4 + k4],
+                                                              __builtin_bit_cast(bf16x8, bv[th][k4]),
+                                                              acc[th], 0, 0, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
       }
     }
-    __syncthreads();
-    // full 256-byte row segments of the group's output columns
-    const int ocol = isk ? qd + g * HD : (g * G + gi) * HD;
-    for (int it = tid; it < MT * NV; it += NTH) {
-      const int ii = it / NV, vv = it - ii * NV;
-      if (row_p[ii] >= 0)
-        st16_stream((uint16_t*)a.out + (t0 + ii) * a.out_rs + ocol + vv * 8,
-                    *(const u32x4*)(ost + ii * OROW + vv * 8));
+#pragma unroll
+    for (int th = 0; th < 2; ++th) {
+      const int n = th * 16 + (lane & 15);
+      const int cl = wv * 16 + 4 * (lane >> 4);
+      const float4 rr = *(const float4*)(sm.res + n * RROW + cl);
+      uint2 o;
+      o.x = pk_bf16(acc[th][0] + rr.x, acc[th][1] + rr.y);
+      o.y = pk_bf16(acc[th][2] + rr.z, acc[th][3] + rr.w);
+      *(uint2*)(sm.ost + n * AROW + cl) = o;
     }
-  }
-
-  // ---- value part: v_cur copied, v_del shifted by one token (this bundle's
-  // share of the 16-byte vectors) ----
-  const int nvv = vd / 8;   // vectors per value half
-  for (int it = tid; it < MT * 2 * nvv; it += NTH) {
-    const int i = it / (2 * nvv), vv = it - i * (2 * nvv);
-    if (vv % nkv != g) continue;
-    const int p = row_p[i];
-    if (p < 0) continue;
-    const int64_t t = t0 + i;
-    u32x4 val;
-    if (vv < nvv) {
-      val = ld16((const uint16_t*)a.v_cur + t * a.vc_rs + vv * 8);
-    } else {
-      const int e8 = (vv - nvv) * 8;
-      if (p >= 1) val = ld16((const uint16_t*)a.v_del + (t - 1) * a.vd_rs + e8);
-      else if (row_h[i]) val = ld16((const uint16_t*)a.delayed_state + (int64_t)row_slot[i] * vd + e8);
+    // value item: a request's first token takes the saved delayed value (or
+    // delayed_init, or zeros) instead of the previous row
+    if (vitem && vvv >= nvv && vp == 0) {
+      int32_t slot;
+      bool hs;
+      cca_row_state(a, vsrc, slot, hs);
+      const int e8 = (vvv - nvv) * 8;
+      if (hs) val = ld16((const uint16_t*)a.delayed_state + (int64_t)slot * vd + e8);
       else if (a.delayed_init) val = ld16((const uint16_t*)a.delayed_init + e8);
       else val = u32x4{0, 0, 0, 0};
     }
-    st16_stream((uint16_t*)a.out + t * a.out_rs + C + vv * 8, val);
+    __syncthreads();
+    // full 256-byte row segments of the group's output columns, and the value item
+    bst16_stream(obuf, ooff, *(const u32x4*)(sm.ost + i * AROW + v * 8));
+    bst16_stream(obuf, voff, val);
+  };
+
+#if SC_CCA_AHEAD == 1
+  Pref fa;
+  issue(0, fa);
+  __syncthreads();   // qsl and parameters visible
+  cca_tile_rows(a, tile_ta(0), use_lds_qsl ? sm.qsl_s : a.prefill_qsl, sm.row_p[0], sm.row_src[0], rcur);
+  __syncthreads();
+  for (int u = 0; u < my_tiles; ++u) tile(u, fa);
+#else
+  Pref fa, fb;
+  issue(0, fa);
+  if (my_tiles > 1) issue(1, fb);
+  __syncthreads();   // qsl and parameters visible
+  cca_tile_rows(a, tile_ta(0), use_lds_qsl ? sm.qsl_s : a.prefill_qsl, sm.row_p[0], sm.row_src[0], rcur);
+  __syncthreads();
+  for (int u = 0; u < my_tiles; u += 2) {
+    tile(u, fa);
+    if (u + 1 < my_tiles) tile(u + 1, fb);
   }
+#endif
+}
+
+template <int T0, int GMAX>
+__global__ __launch_bounds__(kCcaThreads, cca_waves_per_simd<T0>()) void cca_persist_main(CcaArgs a) {
+  __shared__ __attribute__((aligned(16))) CcaSmem<T0> sm;
+  const int lb = logical_block_cca(a);
+  if (lb < 0) return;
+  const int NG = a.nq + a.nkv;
+  const int grp = lb % NG, k0 = lb / NG, S = a.n_logical / NG;
+  const int64_t ntiles = (a.num_tokens + kCcaMT - 1) / kCcaMT;
+  if (k0 >= ntiles) return;
+  const int my_tiles = (int)((ntiles - 1 - k0) / S + 1);
+  if (grp >= a.nq) cca_persist_body<T0, GMAX, true>(a, sm, grp, k0, S, my_tiles);
+  else cca_persist_body<T0, GMAX, false>(a, sm, grp, k0, S, my_tiles);
 }
 
 // ---------------------------------------------------------------------------
@@ -532,20 +709,44 @@ hipError_t launch_cca(const CcaArgs& a, hipStream_t stream) {
   const bool strides16 = (a.q_rs * 2) % 16 == 0 && (a.k_rs * 2) % 16 == 0 &&
                          (a.vc_rs * 2) % 16 == 0 && (a.vd_rs * 2) % 16 == 0 &&
                          (a.out_rs * 2) % 16 == 0;
+  // the MFMA kernel addresses every token tensor with 32-bit offsets
+  const int64_t max_rs = std::max(std::max(a.q_rs, a.k_rs), std::max(std::max(a.vc_rs, a.vd_rs), a.out_rs));
+  const bool fits32 = a.num_tokens * max_rs * 2 <= 0x7FFFFFFFLL;
   const bool mfma = a.hd == 128 && a.t1 == 2 && a.t0 >= 1 && a.t0 <= 4 && (al & 15) == 0 &&
-                    strides16 && vd % 8 == 0 && !SC_CCA_GENERIC;
+                    strides16 && vd % 8 == 0 && a.nq / a.nkv <= 8 && fits32 && !SC_CCA_GENERIC;
   if (mfma) {
-    constexpr int MT = SC_CCA_TILE;
-    const int64_t tiles = (a.num_tokens + MT - 1) / MT;
-    const int64_t blocks = tiles * a.nkv;
-    if (blocks > 0x7FFFFFFFLL) return hipErrorInvalidValue;
-    dim3 grid((unsigned)blocks);
-    const dim3 block(cca_threads<MT>());
-    switch (a.t0) {
-      case 1: hipLaunchKernelGGL((cca_mfma_main<1, MT>), grid, block, 0, stream, a); break;
-      case 2: hipLaunchKernelGGL((cca_mfma_main<2, MT>), grid, block, 0, stream, a); break;
-      case 3: hipLaunchKernelGGL((cca_mfma_main<3, MT>), grid, block, 0, stream, a); break;
-      default: hipLaunchKernelGGL((cca_mfma_main<4, MT>), grid, block, 0, stream, a); break;
+    // persistent grid: a multiple of the head-group count, as many workgroups
+    // as fit on the device at once, never more than there are tiles to share
+    static int cu_count[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    if (cu_count[dev] == 0) {
+      int n = 0;
+      if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+        n = 256;
+      cu_count[dev] = n;
+    }
+    const int NG = a.nq + a.nkv;
+    const int per_cu = SC_CCA_MIN_WAVES / 2;   // 8-wave workgroups resident per CU
+    const int64_t ntiles = (a.num_tokens + kCcaMT - 1) / kCcaMT;
+    int64_t S = (int64_t)cu_count[dev] * per_cu / NG;
+    if (S < 1) S = 1;
+    if (S > ntiles) S = ntiles;
+    CcaArgs b = a;
+    b.n_logical = (int)(S * NG);
+    b.per_xcd = (b.n_logical + 7) / 8;
+    dim3 grid((unsigned)(b.per_xcd * 8));
+    const dim3 block(kCcaThreads);
+    const bool g8 = a.nq / a.nkv > 4;
+    switch (a.t0 * 2 + (g8 ? 1 : 0)) {
+      case 2: hipLaunchKernelGGL((cca_persist_main<1, 4>), grid, block, 0, stream, b); break;
+      case 3: hipLaunchKernelGGL((cca_persist_main<1, 8>), grid, block, 0, stream, b); break;
+      case 4: hipLaunchKernelGGL((cca_persist_main<2, 4>), grid, block, 0, stream, b); break;
+      case 5: hipLaunchKernelGGL((cca_persist_main<2, 8>), grid, block, 0, stream, b); break;
+      case 6: hipLaunchKernelGGL((cca_persist_main<3, 4>), grid, block, 0, stream, b); break;
+      case 7: hipLaunchKernelGGL((cca_persist_main<3, 8>), grid, block, 0, stream, b); break;
+      case 8: hipLaunchKernelGGL((cca_persist_main<4, 4>), grid, block, 0, stream, b); break;
+      default: hipLaunchKernelGGL((cca_persist_main<4, 8>), grid, block, 0, stream, b); break;
     }
   } else {
     if (a.t0 + a.t1 - 2 > 8) return hipErrorNotSupported;

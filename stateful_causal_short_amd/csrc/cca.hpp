@@ -6,20 +6,11 @@
 
 namespace sc {
 
-#ifndef SC_CCA_TILE
-#define SC_CCA_TILE 32       // token rows per CCA workgroup (multiple of 32)
-#endif
-#ifndef SC_CCA_WPREF
-#define SC_CCA_WPREF 0       // 1 = load a group's grouped-weight fragments up front
-#endif
-#ifndef SC_CCA_XPREF
-#define SC_CCA_XPREF 1       // 1 = issue the next group's raw rows before the GEMM
-#endif
-#ifndef SC_CCA_KUNROLL
-#define SC_CCA_KUNROLL 16    // MFMA K-loop unroll (weight loads in flight)
+#ifndef SC_CCA_AHEAD
+#define SC_CCA_AHEAD 2       // tiles of raw rows in flight ahead of the one being computed (1 or 2)
 #endif
 #ifndef SC_CCA_MIN_WAVES
-#define SC_CCA_MIN_WAVES 3   // waves per SIMD the main kernel is compiled for
+#define SC_CCA_MIN_WAVES 2   // waves per SIMD the main kernel is compiled for (2 or 4)
 #endif
 #ifndef SC_CCA_GENERIC
 #define SC_CCA_GENERIC 0     // 1 = always use the scalar CCA kernel
@@ -46,6 +37,7 @@ struct CcaArgs {
   int64_t q_rs, k_rs, vc_rs, vd_rs, out_rs, dslot_stride, pslot_stride;
   int64_t num_tokens;
   int32_t nq, nkv, hd, t0, t1, num_slots, num_decodes, num_prefills;
+  int32_t n_logical, per_xcd;   // filled by launch_cca
 };
 
 hipError_t launch_cca(const CcaArgs& a, hipStream_t stream);
