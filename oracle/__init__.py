@@ -31,10 +31,11 @@ def lib():
         L.oracle_conv.restype = I32
         L.oracle_conv.argtypes = [I32, I32, I32, I32, I32, I32, P, I64, P, I64, P,
                                   P, P, P, I32, I32, I32, I32, P, I64, P, I32, P, P,
-                                  I64, P, I32, P, P, P, I32]
+                                  I64, P, I32, P, P, P, P, P, I64, P, I64, I32]
         L.oracle_conv_spec.restype = I32
         L.oracle_conv_spec.argtypes = [I32, I32, I32, I32, I32, I32, I32, P, I64, P, I64,
-                                       P, P, P, P, I32, I32, I32, P, I64, P, P, I32]
+                                       P, P, P, P, I32, I32, I32, P, I64, P, P, P, P, I64,
+                                       P, I64, I32]
         L.oracle_cca.restype = I32
         L.oracle_cca.argtypes = [I32, I32, I32, I32, I32, I32, I32, I32,
                                  P, I64, P, I64, P, I64, P, I64, P, I64, P,
@@ -71,19 +72,31 @@ def double_to_bf16(v: float) -> int:
     return int(lib().oracle_double_to_bf16(float(v)))
 
 
+def _fuse_args(x, token_indices, resid, outer):
+    ti = _c(token_indices, np.int32)
+    rs = _c(resid)
+    ou = _c(outer)
+    return (_p(ti), _p(rs), 0 if rs is None else rs.shape[1],
+            _p(ou), 0 if ou is None else ou.shape[1])
+
+
 def conv(case, *, out_dtype: Optional[str] = None, absum: bool = False,
          row_mask: Optional[np.ndarray] = None, nthreads: Optional[int] = None,
-         pool: Optional[np.ndarray] = None):
+         pool: Optional[np.ndarray] = None, x: Optional[np.ndarray] = None,
+         token_indices: Optional[np.ndarray] = None, resid: Optional[np.ndarray] = None,
+         outer: Optional[np.ndarray] = None):
     """Run the depthwise oracle on a :class:`synthetic.ConvCase`.
 
     Returns ``(out, pool_after, absum_or_None)``; the case's arrays are not
     modified (the pool is copied unless ``pool`` is passed, which is then
-    updated in place and returned).
+    updated in place and returned). ``x`` overrides the case's rows (a
+    physical batch tensor addressed through ``token_indices``); ``resid`` and
+    ``outer`` (physical rows) are added to the result; ``out`` has x's rows.
     """
     odt = out_dtype or case.dtype
     T, C = case.T, case.C
-    x = _c(case.x)
-    out = np.zeros((T, C), _NP[odt])
+    x = _c(case.x if x is None else x)
+    out = np.zeros((x.shape[0], C), _NP[odt])
     ab = np.zeros((T, C), np.float64) if absum else None
     pool = np.array(case.pool, copy=True) if pool is None else pool
     assert pool.flags.c_contiguous
@@ -102,7 +115,8 @@ def conv(case, *, out_dtype: Optional[str] = None, absum: bool = False,
         _DT[odt], _p(x), C, _p(out), C, _p(ab), _p(w), _p(bias), _p(pool),
         pool.shape[0], pool.shape[2], case.num_decodes, case.q, _p(dsl), 1, _p(dh),
         case.num_prefills, _p(qsl), _p(psl), 1, _p(ph), case.ckpt_grid,
-        _p(cu), _p(cks), _p(rm), nthreads or default_threads())
+        _p(cu), _p(cks), _p(rm), *_fuse_args(x, token_indices, resid, outer),
+        nthreads or default_threads())
     if rc != 0:
         raise RuntimeError(f"oracle_conv failed: {rc}")
     return out, pool, ab
@@ -110,14 +124,16 @@ def conv(case, *, out_dtype: Optional[str] = None, absum: bool = False,
 
 def conv_spec(case, num_accepted, *, out_dtype: Optional[str] = None, absum: bool = False,
               row_mask: Optional[np.ndarray] = None, nthreads: Optional[int] = None,
-              pool: Optional[np.ndarray] = None):
+              pool: Optional[np.ndarray] = None, x: Optional[np.ndarray] = None,
+              token_indices: Optional[np.ndarray] = None, resid: Optional[np.ndarray] = None,
+              outer: Optional[np.ndarray] = None):
     """Speculative update (rolling buffer) on a ConvCase whose decodes are the
     spec requests (q tokens each) and whose pool is (num_slots, C, S), S >= H.
-    Returns (out, pool_after, absum_or_None)."""
+    Returns (out, pool_after, absum_or_None); fusion arguments as in conv()."""
     odt = out_dtype or case.dtype
     T, C = case.num_decode_tokens, case.C
-    x = _c(case.x[:T])
-    out = np.zeros((T, C), _NP[odt])
+    x = _c(case.x[:T] if x is None else x)
+    out = np.zeros((x.shape[0], C), _NP[odt])
     ab = np.zeros((T, C), np.float64) if absum else None
     pool = np.array(case.pool, copy=True) if pool is None else pool
     S = pool.shape[2]
@@ -128,7 +144,7 @@ def conv_spec(case, num_accepted, *, out_dtype: Optional[str] = None, absum: boo
         C, case.K, case.d, S, 1 if case.act == "silu" else 0, _DT[case.dtype], _DT[odt],
         _p(x), C, _p(out), C, _p(ab), _p(_c(case.w)), _p(_c(case.bias)), _p(pool),
         pool.shape[0], case.num_decodes, case.q, _p(dsl), 1, _p(acc), _p(rm),
-        nthreads or default_threads())
+        *_fuse_args(x, token_indices, resid, outer), nthreads or default_threads())
     if rc != 0:
         raise RuntimeError(f"oracle_conv_spec failed: {rc}")
     return out, pool, ab

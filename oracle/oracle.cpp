@@ -139,6 +139,36 @@ void parallel_for(int n, int nthreads, F f) {
   for (auto& t : th) t.join();
 }
 
+// Row mapping and residual fusion shared by the depthwise entry points (PLE
+// page, `_short_conv`: the conv result is accumulated into `residual`, and
+// `outer_residual` is added in the same pass; `token_indices` maps the call's
+// logical rows to rows of the full batch tensors, for batches that mix
+// speculative and non-speculative requests).
+struct Fuse {
+  const int32_t* idx;    // logical row -> physical row of x / out / resid / outer (nullable)
+  const void* resid;     // residual added to the result (io dtype, nullable)
+  int64_t resid_rs;
+  const void* outer;     // outer residual added to the result (io dtype, nullable)
+  int64_t outer_rs;
+  int64_t row(int64_t logical) const { return idx ? (int64_t)idx[logical] : logical; }
+};
+
+// The value stored for one output: act(z) plus the residuals, in double; the
+// residual magnitudes join the sum of |terms|.
+double fuse_value(const Fuse& f, int io, int64_t prow, int c, double y, double* A) {
+  if (f.resid) {
+    const double r = ld(f.resid, io, prow * f.resid_rs + c);
+    y += r;
+    *A += std::fabs(r);
+  }
+  if (f.outer) {
+    const double o = ld(f.outer, io, prow * f.outer_rs + c);
+    y += o;
+    *A += std::fabs(o);
+  }
+  return y;
+}
+
 struct ConvArgs {
   int32_t C, K, d, act, io, odt;
   const void* x;
@@ -156,6 +186,7 @@ struct ConvArgs {
   const int32_t* ckpt_slots;
   int32_t first_prefill;     // index in the request list of prefill 0
   const uint8_t* row_mask;
+  Fuse fz;
 };
 
 // Depthwise causal conv of one channel range over every request.
@@ -181,7 +212,7 @@ void conv_channels(const ConvArgs& a, const std::vector<Req>& reqs, int c0, int 
                      ? ld(a.pool, a.io, ((int64_t)r.slot * a.C + c) * a.S + u)
                      : 0.0;
       for (int64_t t = 0; t < r.len; ++t)
-        ext[H + t] = ld(a.x, a.io, (r.start + t) * a.x_rs + c);
+        ext[H + t] = ld(a.x, a.io, a.fz.row(r.start + t) * a.x_rs + c);
       const double b = a.bias ? ld(a.bias, a.io, c) : 0.0;
       for (int64_t t = 0; t < r.len; ++t) {
         const int64_t row = r.start + t;
@@ -193,8 +224,10 @@ void conv_channels(const ConvArgs& a, const std::vector<Req>& reqs, int c0, int 
           z += term;
           A += std::fabs(term);
         }
+        const int64_t prow = a.fz.row(row);
         double y = a.act ? z / (1.0 + std::exp(-z)) : z;
-        st(a.out, a.odt, row * a.out_rs + c, y);
+        y = fuse_value(a.fz, a.io, prow, c, y, &A);
+        st(a.out, a.odt, prow * a.out_rs + c, y);
         if (a.absum) a.absum[row * a.C + c] = A;
       }
       if (valid)
@@ -232,8 +265,11 @@ uint16_t oracle_double_to_bf16(double v) { return double_to_bf16(v); }
 // speculative rollback) the non-speculative steps keep their window in the
 // first H columns and leave the rest alone, as the GDN page's wide-buffer path
 // does ("only the first width-1 columns hold the real conv state").
-// absum (nullable, (T, C) doubles) receives |b| + sum_k |w*x| per output.
-// row_mask (nullable, T bytes): rows with mask 0 are not written.
+// absum (nullable, (T, C) doubles, by logical row) receives |b| + sum_k |w*x|
+// (+ |resid| + |outer|) per output.
+// row_mask (nullable, T bytes, by logical row): rows with mask 0 are not written.
+// token_indices (nullable): logical row -> physical row of x, out, resid and
+// outer. resid / outer (nullable): added to the result (see Fuse).
 int oracle_conv(int32_t C, int32_t K, int32_t d, int32_t act, int32_t io_dtype,
                 int32_t out_dtype, const void* x, int64_t x_rs, void* out,
                 int64_t out_rs, double* absum, const void* w, const void* bias,
@@ -244,7 +280,8 @@ int oracle_conv(int32_t C, int32_t K, int32_t d, int32_t act, int32_t io_dtype,
                 int64_t prefill_slot_stride, const uint8_t* prefill_h,
                 int32_t ckpt_grid, const int32_t* cu_ckpt,
                 const int32_t* ckpt_slots, const uint8_t* row_mask,
-                int32_t nthreads) {
+                const int32_t* token_indices, const void* resid, int64_t resid_rs,
+                const void* outer, int64_t outer_rs, int32_t nthreads) {
   if (C <= 0 || K <= 0 || d <= 0 || q < 0 || num_decodes < 0 || num_prefills < 0)
     return -2;
   const int32_t S = state_len > 0 ? state_len : (K - 1) * d;
@@ -255,7 +292,7 @@ int oracle_conv(int32_t C, int32_t K, int32_t d, int32_t act, int32_t io_dtype,
               num_prefills, qsl_p, prefill_slots, prefill_slot_stride, prefill_h);
   ConvArgs a{C, K, d, act, io_dtype, out_dtype, x, x_rs, out, out_rs, absum, w,
              bias, pool, num_slots, S, ckpt_grid, cu_ckpt, ckpt_slots, num_decodes,
-             row_mask};
+             row_mask, Fuse{token_indices, resid, resid_rs, outer, outer_rs}};
   parallel_for(C, nthreads, [&](int c0, int c1) { conv_channels(a, reqs, c0, c1); });
   return 0;
 }
@@ -277,7 +314,9 @@ int oracle_conv_spec(int32_t C, int32_t K, int32_t d, int32_t S, int32_t act,
                      const void* bias, void* pool, int32_t num_slots, int32_t B,
                      int32_t q, const int32_t* slots, int64_t slot_stride,
                      const int32_t* num_accepted, const uint8_t* row_mask,
-                     int32_t nthreads) {
+                     const int32_t* token_indices, const void* resid, int64_t resid_rs,
+                     const void* outer, int64_t outer_rs, int32_t nthreads) {
+  const Fuse fz{token_indices, resid, resid_rs, outer, outer_rs};
   const int H = (K - 1) * d;
   if (C <= 0 || K <= 0 || d <= 0 || B < 0 || q < 1 || S < H || q > S) return -2;
   if (!dtype_ok(io_dtype) || !dtype_ok(out_dtype)) return -3;
@@ -293,7 +332,7 @@ int oracle_conv_spec(int32_t C, int32_t K, int32_t d, int32_t S, int32_t act,
         for (int j = 0; j < S; ++j)
           buf[j] = valid ? ld(pool, io_dtype, ((int64_t)slot * C + c) * S + j) : 0.0;
         for (int u = 0; u < H; ++u) ext[u] = buf[a - 1 + u];
-        for (int t = 0; t < q; ++t) ext[H + t] = ld(x, io_dtype, (start + t) * x_rs + c);
+        for (int t = 0; t < q; ++t) ext[H + t] = ld(x, io_dtype, fz.row(start + t) * x_rs + c);
         const double b = bias ? ld(bias, io_dtype, c) : 0.0;
         for (int t = 0; t < q; ++t) {
           const int64_t row = start + t;
@@ -304,7 +343,9 @@ int oracle_conv_spec(int32_t C, int32_t K, int32_t d, int32_t S, int32_t act,
             z += term;
             A += std::fabs(term);
           }
-          st(out, out_dtype, row * out_rs + c, act ? z / (1.0 + std::exp(-z)) : z);
+          const int64_t prow = fz.row(row);
+          const double y = fuse_value(fz, io_dtype, prow, c, act ? z / (1.0 + std::exp(-z)) : z, &A);
+          st(out, out_dtype, prow * out_rs + c, y);
           if (absum) absum[row * C + c] = A;
         }
         if (valid) {
