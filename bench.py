@@ -53,6 +53,7 @@ def conv_workload(name):
         "update_q4": synthetic.config3b,
         "spec": synthetic.config3b_spec,
         "ple_mixed": synthetic.config4,
+        "ple_fused": synthetic.config4,
     }[name]()
 
 
@@ -103,8 +104,14 @@ def conv_kernel_bytes(case):
     return dec, pre
 
 
+def fused_extra_bytes(case):
+    """PLE residual fusion: the residual (out) is read before it is written,
+    and the outer residual is read, once per output element."""
+    return 2 * case.T * case.C * case.elsize
+
+
 class ConvRunner:
-    def __init__(self, case, nsets, num_accepted=None):
+    def __init__(self, case, nsets, num_accepted=None, fused=False):
         import numpy as np
         import torch
         from tests._gpu import dev
@@ -122,12 +129,14 @@ class ConvRunner:
         self.acc = None if num_accepted is None else dev(num_accepted)
         self.base = base
         x0, p0 = dev(case.x), dev(case.pool)
+        self.fused = fused
         self.sets = []
         for i in range(nsets):
             x = x0 if i == 0 else x0.clone()
-            out = torch.empty_like(x)
+            out = torch.randn_like(x) if fused else torch.empty_like(x)
             pool = p0 if i == 0 else p0.clone()
-            self.sets.append((x, out, pool))
+            outer = torch.randn_like(x) if fused else None
+            self.sets.append((x, out, pool, outer))
         dk = "spec_update" if self.acc is not None else "decode_update"
         self.kernels = ([dk] if case.num_decodes else []) + \
                        (["prefill"] if case.num_prefills else [])
@@ -137,18 +146,22 @@ class ConvRunner:
         layer dispatches them); `only` restricts it to one kernel for timing."""
         import stateful_causal_short_amd as scs
         c, b = self.case, self.base
-        x, out, pool = self.sets[i % len(self.sets)]
+        x, out, pool, outer = self.sets[i % len(self.sets)]
+        fz = dict(accumulate=True, outer_residual=outer) if self.fused else {}
         if c.num_decodes and self.acc is not None and only in (None, "spec_update"):
             scs.sc_conv_update_spec(x[:self.nd], out[:self.nd], b["w"], b["b"], pool,
                                     b["dslots"], self.acc, q=c.q, dilation=c.d,
                                     activation=c.act)
         elif c.num_decodes and only in (None, "decode_update"):
+            fd = dict(fz, outer_residual=outer[:self.nd]) if self.fused else {}
             scs.sc_conv_update(x[:self.nd], out[:self.nd], b["w"], b["b"], pool,
-                               b["dslots"], b["dh"], q=c.q, dilation=c.d, activation=c.act)
+                               b["dslots"], b["dh"], q=c.q, dilation=c.d, activation=c.act,
+                               **fd)
         if c.num_prefills and only in (None, "prefill"):
+            fp = dict(fz, outer_residual=outer[self.nd:]) if self.fused else {}
             scs.sc_conv_prefill_varlen(x[self.nd:], out[self.nd:], b["w"], b["b"], pool,
                                        b["qsl"], b["pslots"], b["ph"], dilation=c.d,
-                                       activation=c.act, ckpt=b["ck"])
+                                       activation=c.act, ckpt=b["ck"], **fp)
 
 
 def cca_alg_bytes(case):
@@ -196,14 +209,16 @@ class CcaRunner:
                            t0=c.t0, t1=c.t1)
 
 
-def cpu_baseline_conv(case, budget_s=10.0, num_accepted=None):
+def cpu_baseline_conv(case, budget_s=10.0, num_accepted=None, fused=False):
     """The oracle, as it stands, on the same batch; repeated until ~budget_s."""
+    import numpy as np
     import oracle
     threads = min(16, oracle.default_threads())
+    fz = dict(resid=case.x, outer=case.x) if fused else {}
     runs, t0 = 0, time.perf_counter()
     while True:
         if num_accepted is None:
-            oracle.conv(case, nthreads=threads)
+            oracle.conv(case, nthreads=threads, **fz)
         else:
             oracle.conv_spec(case, num_accepted, nthreads=threads)
         runs += 1
@@ -327,7 +342,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="varlen_prefill",
                     choices=["varlen_prefill", "single", "decode", "update_q4", "spec",
-                             "ple_mixed", "cca", "copy"])
+                             "ple_mixed", "ple_fused", "cca", "copy"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -357,11 +372,17 @@ def main():
     else:
         alg = conv_alg_bytes(case)
         dec_b, pre_b = conv_kernel_bytes(case)
+    fused = args.workload == "ple_fused"
+    if fused:
+        # every output element also reads its residual and outer residual
+        alg += fused_extra_bytes(case)
+        dec_b += 2 * case.num_decode_tokens * case.C * case.elsize
+        pre_b += 2 * (case.T - case.num_decode_tokens) * case.C * case.elsize
     set_bytes = case.T * case.C * case.elsize * 2 + case.pool.nbytes
     nsets = int(min(8, max(2, -(-ROTATE_BYTES // set_bytes))))
     log(f"T={case.T} C={case.C} K={case.K} d={case.d} {case.dtype} act={case.act}; "
         f"alg bytes/step={alg}; {nsets} rotating buffer sets")
-    run = ConvRunner(case, nsets, acc)
+    run = ConvRunner(case, nsets, acc, fused=fused)
     for i in range(args.warmup):
         run.step(i)
     torch.cuda.synchronize()
@@ -431,7 +452,7 @@ def main():
             "prefills": case.num_prefills, "tokens": case.T, "channels": case.C,
             "width": case.K, "dilation": case.d, "activation": case.act,
             "state_slots": case.num_slots, "checkpoint_grid": case.ckpt_grid,
-            "state_len": case.S,
+            "state_len": case.S, "fused_residuals": fused,
         },
         "hbm_gbps": alg / (ms_step * 1e-3) / 1e9,
         "pct_peak": 100.0 * alg / (ms_step * 1e-3) / 1e9 / PEAK_GBPS,
@@ -446,7 +467,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
-        result["cpu_baseline"] = cpu_baseline_conv(case, num_accepted=acc)
+        result["cpu_baseline"] = cpu_baseline_conv(case, num_accepted=acc, fused=fused)
     print(json.dumps(result), flush=True)
 
 

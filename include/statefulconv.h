@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define SC_ABI_VERSION 1
+#define SC_ABI_VERSION 2
 
 typedef enum {
   SC_OK = 0,
@@ -101,6 +101,32 @@ typedef struct {
   const int32_t* ckpt_slots; /* (device) destination slots, flat */
 } sc_ckpt_desc;
 
+/* Residual fusion and row mapping, optional on every depthwise call (PLE page
+ * "vllm.models.qwen4_exp.nvidia.ple_layer", _short_conv: the conv result is
+ * accumulated into `residual`, optionally adding `outer_residual` in the same
+ * pass; the dispatch's token_indices let the calls address the speculative and
+ * non-speculative rows of a mixed batch in place). NULL = plain call
+ * (out = conv). With a descriptor, logical row j of the call (the row the
+ * plain call would use) lives at physical row
+ *   p = token_indices ? token_indices[j] : j
+ * of x, out and outer_residual, and the stored value is, in fp32,
+ *   out[p] = (accumulate ? out[p] : 0) + conv_j (+ outer_residual[p])
+ * with one final rounding (the additions follow the conv's activation).
+ *   token_indices     (device) int32 per logical row, or NULL; entries must be
+ *                     distinct rows in [0, num_physical_rows) (an entry outside
+ *                     is clamped: no memory fault, that row's results unspecified)
+ *   num_physical_rows rows of x / out / outer_residual; required with token_indices
+ *   accumulate        0 or 1: out holds the residual on entry (read, then written)
+ *   outer_residual    (device) rows like out, or NULL; must not alias out
+ *   outer_row_stride  elements between its rows (>= C) */
+typedef struct {
+  const int32_t* token_indices;
+  int64_t num_physical_rows;
+  int32_t accumulate;
+  const void* outer_residual;
+  int64_t outer_row_stride;
+} sc_conv_fuse;
+
 /* Varlen prefill: for request r (token rows [qsl[r], qsl[r+1]) of x), slot
  * s = state_indices[r*stride], flag h = has_initial_state[r]:
  *   ext = [h ? pool[s][c][0 .. H) : zeros (oldest first), x_r]
@@ -124,7 +150,7 @@ sc_status sc_conv_prefill_varlen(const sc_conv_desc* desc, const void* x, void* 
                                  const int32_t* state_indices,
                                  const uint8_t* has_initial_state, int32_t batch,
                                  int64_t num_tokens, const sc_ckpt_desc* ckpt,
-                                 void* stream);
+                                 const sc_conv_fuse* fuse, void* stream);
 
 /* Decode / multi-token update: `batch` requests of exactly q tokens each,
  * request r owning rows [r*q, (r+1)*q) of x (x viewed as (batch, q, C)), all q
@@ -135,7 +161,7 @@ sc_status sc_conv_update(const sc_conv_desc* desc, const void* x, void* out,
                          const void* weight, const void* bias, void* state_pool,
                          int32_t num_slots, const int32_t* state_indices,
                          const uint8_t* has_initial_state, int32_t batch,
-                         int32_t q, void* stream);
+                         int32_t q, const sc_conv_fuse* fuse, void* stream);
 
 /* Speculative multi-token update on a rolling buffer (GDN page
  * "vllm.model_executor.layers.mamba.ops.cpu.gdn_attention", _spec_forward,
@@ -158,7 +184,7 @@ sc_status sc_conv_update_spec(const sc_conv_desc* desc, const void* x, void* out
                               const void* weight, const void* bias, void* state_pool,
                               int32_t num_slots, const int32_t* state_indices,
                               const int32_t* num_accepted_tokens, int32_t batch,
-                              int32_t q, void* stream);
+                              int32_t q, const sc_conv_fuse* fuse, void* stream);
 
 /* Row copies between a slot pool and a dense buffer; each row is row_bytes.
  * gather: dense[i] = pool[idx[i*idx_stride]], or zeros when that index is

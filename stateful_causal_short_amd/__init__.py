@@ -48,6 +48,12 @@ class sc_ckpt_desc(ctypes.Structure):
                 ("ckpt_slots", ctypes.c_void_p)]
 
 
+class sc_conv_fuse(ctypes.Structure):
+    _fields_ = [("token_indices", ctypes.c_void_p), ("num_physical_rows", ctypes.c_int64),
+                ("accumulate", ctypes.c_int32), ("outer_residual", ctypes.c_void_p),
+                ("outer_row_stride", ctypes.c_int64)]
+
+
 class sc_cca_desc(ctypes.Structure):
     _fields_ = [("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("t0", ctypes.c_int32),
@@ -74,12 +80,13 @@ def lib():
         P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
         D = ctypes.POINTER(sc_conv_desc)
         L.sc_conv_prefill_varlen.restype = I32
+        F = ctypes.POINTER(sc_conv_fuse)
         L.sc_conv_prefill_varlen.argtypes = [D, P, P, P, P, P, I32, P, P, P, I32, I64,
-                                             ctypes.POINTER(sc_ckpt_desc), P]
+                                             ctypes.POINTER(sc_ckpt_desc), F, P]
         L.sc_conv_update.restype = I32
-        L.sc_conv_update.argtypes = [D, P, P, P, P, P, I32, P, P, I32, I32, P]
+        L.sc_conv_update.argtypes = [D, P, P, P, P, P, I32, P, P, I32, I32, F, P]
         L.sc_conv_update_spec.restype = I32
-        L.sc_conv_update_spec.argtypes = [D, P, P, P, P, P, I32, P, P, I32, I32, P]
+        L.sc_conv_update_spec.argtypes = [D, P, P, P, P, P, I32, P, P, I32, I32, F, P]
         L.sc_state_gather.restype = I32
         L.sc_state_gather.argtypes = [P, I32, I64, P, I64, I32, P, P]
         L.sc_state_scatter.restype = I32
@@ -154,6 +161,24 @@ def _check(fn: str, status: int):
         raise ScError(fn, status)
 
 
+def _fuse(x, out, token_indices, accumulate, outer_residual):
+    """The optional residual-fusion / row-map descriptor (None = plain call)."""
+    if token_indices is None and not accumulate and outer_residual is None:
+        return None
+    torch = _torch()
+    if token_indices is not None and (token_indices.dtype != torch.int32 or
+                                      not token_indices.is_contiguous()):
+        raise ValueError("token_indices: expected a contiguous int32 tensor")
+    if outer_residual is not None and outer_residual.shape[0] != out.shape[0]:
+        raise ValueError("outer_residual: expected as many rows as out")
+    if token_indices is not None and out.shape[0] != x.shape[0]:
+        raise ValueError("with token_indices, x and out are the full batch tensors")
+    return ctypes.byref(sc_conv_fuse(
+        token_indices=_ptr(token_indices), num_physical_rows=x.shape[0],
+        accumulate=1 if accumulate else 0, outer_residual=_ptr(outer_residual),
+        outer_row_stride=0 if outer_residual is None else _rows(outer_residual, "outer_residual")))
+
+
 def _conv_desc(x, out, weight, state_pool, dilation, activation, state_indices):
     C = x.shape[1]
     K = weight.shape[-1]
@@ -174,7 +199,8 @@ def _conv_desc(x, out, weight, state_pool, dilation, activation, state_indices):
 # ---------------------------------------------------------------------------
 def sc_conv_prefill_varlen(x, out, weight, bias, state_pool, query_start_loc,
                            state_indices, has_initial_state, *, dilation: int = 1,
-                           activation: Optional[str] = "silu", ckpt=None, stream=None):
+                           activation: Optional[str] = "silu", ckpt=None, token_indices=None,
+                           accumulate: bool = False, outer_residual=None, stream=None):
     """Varlen prefill conv; updates ``state_pool`` in place.
 
     x, out: (num_tokens, C); weight (C, K); bias (C) or None; state_pool
@@ -182,6 +208,9 @@ def sc_conv_prefill_varlen(x, out, weight, bias, state_pool, query_start_loc,
     entries of each row); query_start_loc int32 (B+1);
     state_indices int32 (B) or (B, n) using column 0; has_initial_state
     bool/uint8 (B); ckpt = None or (grid, cu_ckpt int32 (B+1), ckpt_slots int32).
+    token_indices (int32, one per logical row) maps the call's rows to rows of
+    x / out / outer_residual; accumulate adds the result to out's contents;
+    outer_residual is added too.
     """
     desc = _conv_desc(x, out, weight, state_pool, dilation, activation, state_indices)
     cd = None
@@ -193,34 +222,42 @@ def sc_conv_prefill_varlen(x, out, weight, bias, state_pool, query_start_loc,
         _ptr(state_pool), state_pool.shape[0], _ptr(query_start_loc),
         _index(state_indices, "state_indices")[0],
         _flags(has_initial_state, "has_initial_state"),
-        query_start_loc.shape[0] - 1, x.shape[0], cd, _stream(stream))
+        query_start_loc.shape[0] - 1,
+        x.shape[0] if token_indices is None else token_indices.shape[0], cd,
+        _fuse(x, out, token_indices, accumulate, outer_residual), _stream(stream))
     _check("sc_conv_prefill_varlen", st)
 
 
 def sc_conv_update(x, out, weight, bias, state_pool, state_indices,
                    has_initial_state=None, *, q: int = 1, dilation: int = 1,
-                   activation: Optional[str] = "silu", stream=None):
+                   activation: Optional[str] = "silu", token_indices=None,
+                   accumulate: bool = False, outer_residual=None, stream=None):
     """Decode / multi-token update: x (B*q, C) rows, request r owns rows
-    [r*q, (r+1)*q); updates ``state_pool`` in place."""
-    if x.shape[0] % max(q, 1):
-        raise ValueError("x rows must be a multiple of q")
+    [r*q, (r+1)*q) (logical rows, mapped by token_indices when given);
+    updates ``state_pool`` in place."""
+    rows = x.shape[0] if token_indices is None else token_indices.shape[0]
+    if rows % max(q, 1):
+        raise ValueError("rows must be a multiple of q")
     desc = _conv_desc(x, out, weight, state_pool, dilation, activation, state_indices)
-    B = x.shape[0] // q if q else 0
+    B = rows // q if q else 0
     st = lib().sc_conv_update(
         ctypes.byref(desc), _ptr(x), _ptr(out), _ptr(weight), _ptr(bias),
         _ptr(state_pool), state_pool.shape[0], _index(state_indices, "state_indices")[0],
-        _flags(has_initial_state, "has_initial_state"), B, q, _stream(stream))
+        _flags(has_initial_state, "has_initial_state"), B, q,
+        _fuse(x, out, token_indices, accumulate, outer_residual), _stream(stream))
     _check("sc_conv_update", st)
 
 
 def sc_conv_update_spec(x, out, weight, bias, state_pool, state_indices, num_accepted_tokens,
                         *, q: int, dilation: int = 1, activation: Optional[str] = "silu",
+                        token_indices=None, accumulate: bool = False, outer_residual=None,
                         stream=None):
     """Speculative update on a rolling buffer: x (B*q, C) rows, request r owns
     rows [r*q, (r+1)*q); state_pool (num_slots, C, S) with S >= (K-1)*dilation;
     num_accepted_tokens int32 (B). Updates ``state_pool`` in place."""
-    if q < 1 or x.shape[0] % q:
-        raise ValueError("x rows must be a positive multiple of q")
+    rows = x.shape[0] if token_indices is None else token_indices.shape[0]
+    if q < 1 or rows % q:
+        raise ValueError("rows must be a positive multiple of q")
     torch = _torch()
     if num_accepted_tokens.dtype != torch.int32 or not num_accepted_tokens.is_contiguous():
         raise ValueError("num_accepted_tokens: expected a contiguous int32 tensor")
@@ -228,7 +265,8 @@ def sc_conv_update_spec(x, out, weight, bias, state_pool, state_indices, num_acc
     st = lib().sc_conv_update_spec(
         ctypes.byref(desc), _ptr(x), _ptr(out), _ptr(weight), _ptr(bias),
         _ptr(state_pool), state_pool.shape[0], _index(state_indices, "state_indices")[0],
-        _ptr(num_accepted_tokens), x.shape[0] // q, q, _stream(stream))
+        _ptr(num_accepted_tokens), rows // q, q,
+        _fuse(x, out, token_indices, accumulate, outer_residual), _stream(stream))
     _check("sc_conv_update_spec", st)
 
 
@@ -284,6 +322,6 @@ def sc_cca_qk_conv(q, k, v_cur, v_del, out, w_dw, b_dw, w_gr, b_gr, delayed_init
 
 
 __all__ = ["lib", "ScError", "LIB_PATH", "EXPORTS", "sc_conv_desc", "sc_ckpt_desc",
-           "sc_cca_desc", "sc_conv_prefill_varlen", "sc_conv_update", "sc_conv_update_spec",
+           "sc_cca_desc", "sc_conv_fuse", "sc_conv_prefill_varlen", "sc_conv_update", "sc_conv_update_spec",
            "sc_state_gather",
            "sc_state_scatter", "sc_cca_qk_conv"]

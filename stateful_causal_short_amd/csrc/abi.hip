@@ -37,6 +37,28 @@ bool conv_aligned(const sc_conv_desc* d, const void* x, const void* out, const v
          (d->x_row_stride * es) % 16 == 0 && (d->out_row_stride * es) % 16 == 0;
 }
 
+// Descriptor checks of the optional residual fusion / row map.
+sc_status check_fuse(const sc_conv_fuse* f, const sc_conv_desc* d) {
+  if (!f) return SC_OK;
+  if (f->accumulate != 0 && f->accumulate != 1) return SC_ERR_INVALID_ARG;
+  if (f->token_indices && f->num_physical_rows < 1) return SC_ERR_INVALID_ARG;
+  if (f->outer_residual && f->outer_row_stride < d->channels) return SC_ERR_INVALID_ARG;
+  return SC_OK;
+}
+
+// Copies the fusion descriptor into the kernel arguments; out must not be the
+// outer residual.
+sc_status apply_fuse(const sc_conv_fuse* f, const void* out, sc::ConvArgs& a) {
+  if (!f) return SC_OK;
+  if (f->outer_residual && f->outer_residual == out) return SC_ERR_INVALID_ARG;
+  a.tok = f->token_indices;
+  a.phys_rows = f->num_physical_rows;
+  a.accumulate = f->accumulate;
+  a.outer = f->outer_residual;
+  a.outer_rs = f->outer_row_stride;
+  return SC_OK;
+}
+
 sc_status from_hip(hipError_t e) {
   if (e == hipSuccess) return SC_OK;
   if (e == hipErrorNotSupported) return SC_ERR_UNSUPPORTED;
@@ -68,11 +90,12 @@ sc_status sc_conv_prefill_varlen(const sc_conv_desc* desc, const void* x, void* 
                                  const int32_t* state_indices,
                                  const uint8_t* has_initial_state, int32_t batch,
                                  int64_t num_tokens, const sc_ckpt_desc* ckpt,
-                                 void* stream) {
+                                 const sc_conv_fuse* fuse, void* stream) {
   if (!desc) return SC_ERR_NULL_ARG;
   int H = 0;
   sc_status st = check_conv_desc(desc, &H);
   if (st != SC_OK) return st;
+  if ((st = check_fuse(fuse, desc)) != SC_OK) return st;
   if (batch < 0 || num_tokens < 0 || num_slots < 0) return SC_ERR_INVALID_ARG;
   int32_t grid = 0;
   if (ckpt && ckpt->grid != 0) {
@@ -110,7 +133,9 @@ sc_status sc_conv_prefill_varlen(const sc_conv_desc* desc, const void* x, void* 
   a.q = 0;
   a.ckpt_grid = grid;
   a.S = desc->state_len;
-  const bool aligned = conv_aligned(desc, x, out, weight, bias, state_pool);
+  if ((st = apply_fuse(fuse, out, a)) != SC_OK) return st;
+  const bool aligned = conv_aligned(desc, x, out, weight, bias, state_pool) &&
+                       (!a.outer || al16(a.outer));
   return from_hip(sc::launch_conv(a, desc->dtype, desc->width, desc->dilation,
                                   desc->activation == SC_ACT_SILU, aligned,
                                   (hipStream_t)stream, nullptr));
@@ -120,11 +145,12 @@ sc_status sc_conv_update(const sc_conv_desc* desc, const void* x, void* out,
                          const void* weight, const void* bias, void* state_pool,
                          int32_t num_slots, const int32_t* state_indices,
                          const uint8_t* has_initial_state, int32_t batch, int32_t q,
-                         void* stream) {
+                         const sc_conv_fuse* fuse, void* stream) {
   if (!desc) return SC_ERR_NULL_ARG;
   int H = 0;
   sc_status st = check_conv_desc(desc, &H);
   if (st != SC_OK) return st;
+  if ((st = check_fuse(fuse, desc)) != SC_OK) return st;
   if (batch < 0 || q < 0 || num_slots < 0) return SC_ERR_INVALID_ARG;
   if (batch == 0 || q == 0) return SC_OK;
   if (!x || !out || !weight || !state_indices) return SC_ERR_NULL_ARG;
@@ -151,7 +177,9 @@ sc_status sc_conv_update(const sc_conv_desc* desc, const void* x, void* out,
   a.q = q;
   a.ckpt_grid = 0;
   a.S = desc->state_len;
-  const bool aligned = conv_aligned(desc, x, out, weight, bias, state_pool);
+  if ((st = apply_fuse(fuse, out, a)) != SC_OK) return st;
+  const bool aligned = conv_aligned(desc, x, out, weight, bias, state_pool) &&
+                       (!a.outer || al16(a.outer));
   return from_hip(sc::launch_conv(a, desc->dtype, desc->width, desc->dilation,
                                   desc->activation == SC_ACT_SILU, aligned,
                                   (hipStream_t)stream, nullptr));
@@ -161,11 +189,12 @@ sc_status sc_conv_update_spec(const sc_conv_desc* desc, const void* x, void* out
                               const void* weight, const void* bias, void* state_pool,
                               int32_t num_slots, const int32_t* state_indices,
                               const int32_t* num_accepted_tokens, int32_t batch, int32_t q,
-                              void* stream) {
+                              const sc_conv_fuse* fuse, void* stream) {
   if (!desc) return SC_ERR_NULL_ARG;
   int H = 0;
   sc_status st = check_conv_desc(desc, &H);
   if (st != SC_OK) return st;
+  if ((st = check_fuse(fuse, desc)) != SC_OK) return st;
   if (batch < 0 || q < 0 || num_slots < 0) return SC_ERR_INVALID_ARG;
   // the rolled buffer keeps S - q old entries: q drafts must fit in it
   if (q > desc->state_len) return SC_ERR_INVALID_ARG;
@@ -195,7 +224,9 @@ sc_status sc_conv_update_spec(const sc_conv_desc* desc, const void* x, void* out
   a.q = q;
   a.ckpt_grid = 0;
   a.S = desc->state_len;
-  const bool aligned = conv_aligned(desc, x, out, weight, bias, state_pool);
+  if ((st = apply_fuse(fuse, out, a)) != SC_OK) return st;
+  const bool aligned = conv_aligned(desc, x, out, weight, bias, state_pool) &&
+                       (!a.outer || al16(a.outer));
   return from_hip(sc::launch_conv_spec(a, desc->dtype, desc->width, desc->dilation,
                                        desc->activation == SC_ACT_SILU, aligned,
                                        (hipStream_t)stream));

@@ -24,14 +24,13 @@
 namespace sc {
 
 
-// Store the window x rows [p-H, p) (all >= 0) as a (ch, jj) state row.
-template <class E, int H>
-__device__ __forceinline__ void store_window_from_x(typename E::S* dst,
-                                                    const typename E::S* xb,
-                                                    int64_t xrs, int p) {
+// Store the window of request rows [p-H, p) (all >= 0) as a (ch, jj) state
+// row; xrow(t) is the lane's channel vector in the request's row t.
+template <class E, int H, class XRow>
+__device__ __forceinline__ void store_window_from_x(typename E::S* dst, XRow xrow, int p) {
   u32x4 xr[H], nv[H];
 #pragma unroll
-  for (int jj = 0; jj < H; ++jj) xr[jj] = ld16(xb + (int64_t)(p - H + jj) * xrs);
+  for (int jj = 0; jj < H; ++jj) xr[jj] = ld16(xrow(p - H + jj));
 #pragma unroll
   for (int jj = 0; jj < H; ++jj)
 #pragma unroll
@@ -41,11 +40,11 @@ __device__ __forceinline__ void store_window_from_x(typename E::S* dst,
 }
 
 // New state = ext[L .. L+H) for a request of runtime length L.
-template <class E, int H>
+template <class E, int H, class XRow>
 __device__ __forceinline__ void write_state(typename E::S* sp, const u32x4* old, int L,
-                                            const typename E::S* xb, int64_t xrs) {
+                                            XRow xrow) {
   if (L >= H) {
-    store_window_from_x<E, H>(sp, xb, xrs, L);
+    store_window_from_x<E, H>(sp, xrow, L);
     return;
   }
   // 1 <= L < H: entries jj < H-L keep old[L + jj], the rest are the L tokens.
@@ -53,7 +52,7 @@ __device__ __forceinline__ void write_state(typename E::S* sp, const u32x4* old,
 #pragma unroll
   for (int jj = 0; jj < H; ++jj) {
     const int p = L - H + jj;
-    xr[jj] = p >= 0 ? ld16(xb + (int64_t)p * xrs) : u32x4{0, 0, 0, 0};
+    xr[jj] = p >= 0 ? ld16(xrow(p)) : u32x4{0, 0, 0, 0};
   }
 #pragma unroll
   for (int jj = 0; jj < H; ++jj)
@@ -171,7 +170,8 @@ __global__ __launch_bounds__(kBlock) void conv_fast(ConvArgs a) {
 #pragma unroll
         for (int ch = 0; ch < VEC; ++ch) win[i][ch] = win[i + U][ch];
     }
-    if (w.j == 0 && w.valid) write_state<E, H>(sp, old, w.L, xb, xrs);
+    auto xrow = [&](int t) { return xb + (int64_t)t * xrs; };
+    if (w.j == 0 && w.valid) write_state<E, H>(sp, old, w.L, xrow);
     if (a.ckpt_grid > 0 && a.qsl != nullptr) {
       // checkpoints at p = m*g with t0 < p <= t1: the chunk holding token p-1
       const int g = a.ckpt_grid;
@@ -179,7 +179,7 @@ __global__ __launch_bounds__(kBlock) void conv_fast(ConvArgs a) {
       for (int m = w.t0 / g + 1; m <= cnt && (int64_t)m * g <= w.t1; ++m) {
         const int32_t dst = a.ckpt_slots[cu0 + m - 1];
         if (dst < 0 || dst >= a.num_slots) continue;
-        store_window_from_x<E, H>((S*)a.pool + ((int64_t)dst * a.C + c0) * H, xb, xrs, m * g);
+        store_window_from_x<E, H>((S*)a.pool + ((int64_t)dst * a.C + c0) * H, xrow, m * g);
       }
     }
   }
@@ -193,7 +193,7 @@ __global__ __launch_bounds__(kBlock) void conv_fast(ConvArgs a) {
 // reused by every output that needs it. UPDATE: requests of exactly U tokens.
 // ---------------------------------------------------------------------------
 
-template <int K, int D, int U, bool SILU, bool UPDATE>
+template <int K, int D, int U, bool SILU, bool UPDATE, bool FUSE>
 __global__ __launch_bounds__(kBlock) void conv_pairs(ConvArgs a) {
 #if SC_LDS_PAD > 0
   __shared__ uint8_t occupancy_pad[SC_LDS_PAD];
@@ -255,16 +255,21 @@ __global__ __launch_bounds__(kBlock) void conv_pairs(ConvArgs a) {
   const int64_t xrs = a.x_rs, ors = a.out_rs;
   const S* xb = (const S*)a.x + (int64_t)s0 * xrs + c0;
   S* ob = (S*)a.out + (int64_t)s0 * ors + c0;
+  // request row t of x / out (through the row map when fused)
+  auto xrow = [&](int t) -> const S* {
+    if constexpr (FUSE) return (const S*)a.x + phys_row(a, (int64_t)s0 + t) * xrs + c0;
+    else return xb + (int64_t)t * xrs;
+  };
 
   u32x4 raw[H + U];
   if (j > 0) {
 #pragma unroll
-    for (int u = 0; u < H; ++u) raw[u] = ld16(xb + (int64_t)(t0 - H + u) * xrs);
+    for (int u = 0; u < H; ++u) raw[u] = ld16(xrow(t0 - H + u));
   }
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int t = UPDATE ? u : min(t0 + u, t1 - 1);
-    raw[H + u] = SC_NT_LOADS ? ld16_stream(xb + (int64_t)t * xrs) : ld16(xb + (int64_t)t * xrs);
+    raw[H + u] = SC_NT_LOADS ? ld16_stream(xrow(t)) : ld16(xrow(t));
   }
   // the slot is needed by the request's first chunk only (history and write-back)
   int32_t slot = -1;
@@ -292,6 +297,17 @@ __global__ __launch_bounds__(kBlock) void conv_pairs(ConvArgs a) {
   w.slot = slot;
   w.valid = valid;
   w.h = hflag;
+  // fused residuals of the chunk's rows, issued before the arithmetic
+  u32x4 rres[FUSE ? U : 1], rout[FUSE ? U : 1];
+  if constexpr (FUSE) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int t = UPDATE ? u : min(t0 + u, t1 - 1);
+      const int64_t pr = phys_row(a, (int64_t)s0 + t);
+      rres[u] = a.accumulate ? ld16((const S*)a.out + pr * ors + c0) : u32x4{0, 0, 0, 0};
+      rout[u] = a.outer ? ld16((const S*)a.outer + pr * a.outer_rs + c0) : u32x4{0, 0, 0, 0};
+    }
+  }
   float bs[VEC];
   E::unpack(bsv, bs);
   if (w.j == 0) {
@@ -319,7 +335,20 @@ __global__ __launch_bounds__(kBlock) void conv_pairs(ConvArgs a) {
         }
         z[ch] = SILU ? silu(acc) : acc;
       }
-      st16_stream(ob + (int64_t)(w.t0 + u) * ors, E::pack(z));
+      if constexpr (FUSE) {
+        const int64_t pr = phys_row(a, (int64_t)s0 + w.t0 + u);
+        float rr[VEC], ro[VEC];
+        E::unpack(rres[u], rr);
+        E::unpack(rout[u], ro);
+#pragma unroll
+        for (int ch = 0; ch < VEC; ++ch) {
+          if (a.accumulate) z[ch] += rr[ch];
+          if (a.outer) z[ch] += ro[ch];
+        }
+        st16_stream((S*)a.out + pr * ors + c0, E::pack(z));
+      } else {
+        st16_stream(ob + (int64_t)(w.t0 + u) * ors, E::pack(z));
+      }
     }
   }
 
@@ -334,7 +363,7 @@ __global__ __launch_bounds__(kBlock) void conv_pairs(ConvArgs a) {
 #pragma unroll
       for (int v = 0; v < H; ++v) st16(sp + v * VEC, nv[v]);
     } else {
-      write_state<E, H>(sp, old, w.L, xb, xrs);
+      write_state<E, H>(sp, old, w.L, xrow);
     }
   }
   if (!UPDATE && a.ckpt_grid > 0 && a.qsl != nullptr) {
@@ -343,7 +372,7 @@ __global__ __launch_bounds__(kBlock) void conv_pairs(ConvArgs a) {
     for (int m = w.t0 / g + 1; m <= cnt && (int64_t)m * g <= w.t1; ++m) {
       const int32_t dst = a.ckpt_slots[cu0 + m - 1];
       if (dst < 0 || dst >= a.num_slots) continue;
-      store_window_from_x<E, H>((S*)a.pool + ((int64_t)dst * a.C + c0) * H, xb, xrs, m * g);
+      store_window_from_x<E, H>((S*)a.pool + ((int64_t)dst * a.C + c0) * H, xrow, m * g);
     }
   }
 }
@@ -356,7 +385,7 @@ __global__ __launch_bounds__(kBlock) void conv_pairs(ConvArgs a) {
 // weights are loaded once for the R requests. Same tap pairing and dot2 order
 // as conv_pairs, so a decode step equals the matching prefill token bit for bit.
 // ---------------------------------------------------------------------------
-template <int K, int D, int Q, int R, bool SILU>
+template <int K, int D, int Q, int R, bool SILU, bool FUSE>
 __global__ __launch_bounds__(kBlock) void conv_update_pairs(ConvArgs a) {
   using E = BF16;
   using S = E::S;
@@ -396,15 +425,36 @@ __global__ __launch_bounds__(kBlock) void conv_update_pairs(ConvArgs a) {
   int32_t slot[R];
   bool valid[R], hflag[R];
   u32x4 st[R][H], xr[R][Q];
+  // physical row of request r's token u (through the row map when fused)
+  auto prow = [&](int r, int u) -> int64_t {
+    if constexpr (FUSE) return phys_row(a, (int64_t)r * Q + u);
+    else return (int64_t)r * Q + u;
+  };
 #pragma unroll
   for (int rr = 0; rr < R; ++rr) {
     const int r = grp * R + rr;
 #pragma unroll
     for (int u = 0; u < Q; ++u)
       xr[rr][u] = (r < a.batch && lane_ok)
-                      ? (SC_NT_LOADS ? ld16_stream((const S*)a.x + ((int64_t)r * Q + u) * a.x_rs + c0)
-                                     : ld16((const S*)a.x + ((int64_t)r * Q + u) * a.x_rs + c0))
+                      ? (SC_NT_LOADS ? ld16_stream((const S*)a.x + prow(r, u) * a.x_rs + c0)
+                                     : ld16((const S*)a.x + prow(r, u) * a.x_rs + c0))
                       : u32x4{0, 0, 0, 0};
+  }
+  // fused residuals, issued with the token rows
+  u32x4 rres[FUSE ? R : 1][FUSE ? Q : 1], rout[FUSE ? R : 1][FUSE ? Q : 1];
+  if constexpr (FUSE) {
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) {
+      const int r = grp * R + rr;
+#pragma unroll
+      for (int u = 0; u < Q; ++u) {
+        const bool ok = r < a.batch && lane_ok;
+        rres[rr][u] = (ok && a.accumulate) ? ld16((const S*)a.out + prow(r, u) * a.out_rs + c0)
+                                           : u32x4{0, 0, 0, 0};
+        rout[rr][u] = (ok && a.outer) ? ld16((const S*)a.outer + prow(r, u) * a.outer_rs + c0)
+                                      : u32x4{0, 0, 0, 0};
+      }
+    }
   }
 #pragma unroll
   for (int rr = 0; rr < R; ++rr) {
@@ -461,7 +511,18 @@ __global__ __launch_bounds__(kBlock) void conv_update_pairs(ConvArgs a) {
           }
           z[ch] = SILU ? silu(acc) : acc;
         }
-        st16_stream((S*)a.out + ((int64_t)r * Q + u) * a.out_rs + c0, E::pack(z));
+        const int64_t pr = prow(r, u);
+        if constexpr (FUSE) {
+          float fr[VEC], fo[VEC];
+          E::unpack(rres[rr][u], fr);
+          E::unpack(rout[rr][u], fo);
+#pragma unroll
+          for (int ch = 0; ch < VEC; ++ch) {
+            if (a.accumulate) z[ch] += fr[ch];
+            if (a.outer) z[ch] += fo[ch];
+          }
+        }
+        st16_stream((S*)a.out + pr * a.out_rs + c0, E::pack(z));
       }
     }
     // new state = ext[Q .. Q+H) in (channel, tap) order -> region order
@@ -509,26 +570,32 @@ __global__ __launch_bounds__(kBlock) void conv_generic(ConvArgs a, int K, int D)
   const float b = a.bias ? widen<E>(ld_el<E>((const S*)a.bias + c)) : 0.f;
   const int64_t xrs = a.x_rs, ors = a.out_rs;
   const S* xb = (const S*)a.x + w.start * xrs + c;
-  S* ob = (S*)a.out + w.start * ors + c;
   S* sp = (S*)a.pool + ((int64_t)(w.valid ? w.slot : 0) * a.C + c) * a.S;
+  // request row p of x (through the row map when one is given)
+  auto xg = [&](int p) -> const S* {
+    return a.tok ? (const S*)a.x + phys_row(a, w.start + p) * xrs + c : xb + (int64_t)p * xrs;
+  };
   for (int t = w.t0; t < w.t1; ++t) {
     float acc = b;
     for (int k = 0; k < K; ++k) {
       const int p = t - (K - 1 - k) * D;
       float v = 0.f;
-      if (p >= 0) v = widen<E>(ld_el<E>(xb + (int64_t)p * xrs));
+      if (p >= 0) v = widen<E>(ld_el<E>(xg(p)));
       else if (w.h) v = widen<E>(ld_el<E>(sp + H + p));
       acc = __builtin_fmaf(wt[k], v, acc);
     }
     if (SILU) acc = silu(acc);
-    ob[(int64_t)t * ors] = narrow<E>(acc);
+    const int64_t pr = a.tok ? phys_row(a, w.start + t) : w.start + t;
+    if (a.accumulate) acc += widen<E>(ld_el<E>((const S*)a.out + pr * ors + c));
+    if (a.outer) acc += widen<E>(ld_el<E>((const S*)a.outer + pr * a.outer_rs + c));
+    ((S*)a.out)[pr * ors + c] = narrow<E>(acc);
   }
   if (w.j == 0 && w.valid) {
     // ascending jj reads old entry L + jj > jj before it is overwritten
     for (int jj = 0; jj < H; ++jj) {
       const int p = w.L - H + jj;
       S v = 0;
-      if (p >= 0) v = xb[(int64_t)p * xrs];
+      if (p >= 0) v = *xg(p);
       else if (w.h) v = sp[w.L + jj];
       sp[jj] = v;
     }
@@ -540,7 +607,7 @@ __global__ __launch_bounds__(kBlock) void conv_generic(ConvArgs a, int K, int D)
       const int32_t dst = a.ckpt_slots[cu0 + m - 1];
       if (dst < 0 || dst >= a.num_slots) continue;
       S* dp = (S*)a.pool + ((int64_t)dst * a.C + c) * a.S;
-      for (int jj = 0; jj < H; ++jj) dp[jj] = xb[(int64_t)(m * g - H + jj) * xrs];
+      for (int jj = 0; jj < H; ++jj) dp[jj] = *xg(m * g - H + jj);
     }
   }
 }
@@ -574,33 +641,34 @@ constexpr int pairs_chunk(int H) { return H <= 4 ? SC_PAIRS_CHUNK_SMALL : (H <= 
 // requests per update workgroup
 constexpr int update_reqs(int H, int Q) { return (H <= 4 && Q == 1) ? SC_UPDATE_REQS : (H <= 4 ? 2 : (Q == 1 ? 2 : 1)); }
 
-template <int K, int D, bool SILU>
+template <int K, int D, bool SILU, bool FUSE>
 hipError_t launch_pairs_kd(const ConvArgs& a, int qc, dim3 grid, hipStream_t s) {
   constexpr int H = (K - 1) * D;
   switch (qc) {
-    case 1: hipLaunchKernelGGL((conv_update_pairs<K, D, 1, update_reqs(H, 1), SILU>), grid, dim3(kBlock), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((conv_update_pairs<K, D, 2, update_reqs(H, 2), SILU>), grid, dim3(kBlock), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((conv_update_pairs<K, D, 4, update_reqs(H, 4), SILU>), grid, dim3(kBlock), 0, s, a); break;
-    default: hipLaunchKernelGGL((conv_pairs<K, D, pairs_chunk(H), SILU, false>), grid, dim3(kBlock), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((conv_update_pairs<K, D, 1, update_reqs(H, 1), SILU, FUSE>), grid, dim3(kBlock), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((conv_update_pairs<K, D, 2, update_reqs(H, 2), SILU, FUSE>), grid, dim3(kBlock), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((conv_update_pairs<K, D, 4, update_reqs(H, 4), SILU, FUSE>), grid, dim3(kBlock), 0, s, a); break;
+    default: hipLaunchKernelGGL((conv_pairs<K, D, pairs_chunk(H), SILU, false, FUSE>), grid, dim3(kBlock), 0, s, a); break;
   }
   return hipGetLastError();
 }
 
-template <bool SILU>
+template <bool SILU, bool FUSE>
 hipError_t launch_pairs(const ConvArgs& a, int K, int D, int qc, dim3 grid, hipStream_t s) {
-  if (K == 4 && D == 1) return launch_pairs_kd<4, 1, SILU>(a, qc, grid, s);
-  if (K == 4 && D == 2) return launch_pairs_kd<4, 2, SILU>(a, qc, grid, s);
-  if (K == 4 && D == 3) return launch_pairs_kd<4, 3, SILU>(a, qc, grid, s);
-  return launch_pairs_kd<2, 1, SILU>(a, qc, grid, s);
+  if (K == 4 && D == 1) return launch_pairs_kd<4, 1, SILU, FUSE>(a, qc, grid, s);
+  if (K == 4 && D == 2) return launch_pairs_kd<4, 2, SILU, FUSE>(a, qc, grid, s);
+  if (K == 4 && D == 3) return launch_pairs_kd<4, 3, SILU, FUSE>(a, qc, grid, s);
+  return launch_pairs_kd<2, 1, SILU, FUSE>(a, qc, grid, s);
 }
 
 template <class E, bool SILU>
 hipError_t launch_typed(const ConvArgs& a, int K, int D, bool fast, int qc, dim3 grid,
-                        hipStream_t s) {
+                        hipStream_t s, bool fuse) {
   if (a.chunk == pairs_chunk((K - 1) * D) && fast && E::VEC == 8 && pairs_shape(K, D) &&
       !SC_NO_PAIRS)
-    return launch_pairs<SILU>(a, K, D, qc, grid, s);
-  if (fast) {
+    return fuse ? launch_pairs<SILU, true>(a, K, D, qc, grid, s)
+                : launch_pairs<SILU, false>(a, K, D, qc, grid, s);
+  if (fast && !fuse) {
     if (K == 4 && D == 1) return launch_kd<E, 4, 1, SILU>(a, qc, grid, s);
     if (K == 4 && D == 3) return launch_kd<E, 4, 3, SILU>(a, qc, grid, s);
     if (K == 4 && D == 2) return launch_kd<E, 4, 2, SILU>(a, qc, grid, s);
@@ -627,10 +695,17 @@ hipError_t launch_conv(ConvArgs a, int dtype, int K, int D, bool silu_act, bool 
     const hipError_t e = launch_update_wide(a, dtype, K, D, silu_act, aligned16, stream);
     if (e != hipErrorNotSupported) return e;
   }
-  // the register-window kernels assume S == H (the lane's state is H vectors)
-  const bool fast = a.S == H && aligned16 && (a.C % vec == 0) && fast_shape(K, D);
+  // the register-window kernels assume S == H (the lane's state is H vectors);
+  // residual fusion and row maps are built into the bf16 pair kernels and the
+  // generic one
+  const bool fuse = a.tok != nullptr || a.outer != nullptr || a.accumulate != 0;
+  const bool pairs_ok = a.S == H && aligned16 && (a.C % vec == 0) && dtype == 1 &&
+                        pairs_shape(K, D) && !SC_NO_PAIRS &&
+                        (!a.outer || (a.outer_rs * 2) % 16 == 0);
+  const bool fast = a.S == H && aligned16 && (a.C % vec == 0) && fast_shape(K, D) &&
+                    (!fuse || pairs_ok);
   // the one-pass kernel takes its halo from x: its chunk covers H by construction
-  const bool pairs = fast && dtype == 1 && pairs_shape(K, D) && !SC_NO_PAIRS;
+  const bool pairs = fast && pairs_ok;
   a.chunk = pairs ? pairs_chunk(H) : fast ? kChunk : (H > kChunk ? H : kChunk);
   int qc = 0;
   if (fast && uniform && (a.q == 1 || a.q == 2 || a.q == 4) && a.q <= a.chunk) qc = a.q;
@@ -657,10 +732,10 @@ hipError_t launch_conv(ConvArgs a, int dtype, int K, int D, bool silu_act, bool 
     info->chunk = a.chunk;
   }
   if (dtype == 1)
-    return silu_act ? launch_typed<BF16, true>(a, K, D, fast, qc, grid, stream)
-                    : launch_typed<BF16, false>(a, K, D, fast, qc, grid, stream);
-  return silu_act ? launch_typed<F32, true>(a, K, D, fast, qc, grid, stream)
-                  : launch_typed<F32, false>(a, K, D, fast, qc, grid, stream);
+    return silu_act ? launch_typed<BF16, true>(a, K, D, fast, qc, grid, stream, fuse)
+                    : launch_typed<BF16, false>(a, K, D, fast, qc, grid, stream, fuse);
+  return silu_act ? launch_typed<F32, true>(a, K, D, fast, qc, grid, stream, fuse)
+                  : launch_typed<F32, false>(a, K, D, fast, qc, grid, stream, fuse);
 }
 
 }  // namespace sc

@@ -155,6 +155,38 @@ __device__ __forceinline__ void conv_point(const float (*win)[E::VEC], int pos,
   }
 }
 
+// ---------------------------------------------------------------------------
+// row mapping and residual fusion (PLE page, _short_conv / ple_conv)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ bool fused(const ConvArgs& a) {
+  return a.tok != nullptr || a.outer != nullptr || a.accumulate != 0;
+}
+// physical row of logical row r; a map entry outside [0, phys_rows) is a
+// caller error and is clamped so that no access leaves the tensors
+__device__ __forceinline__ int64_t phys_row(const ConvArgs& a, int64_t r) {
+  if (!a.tok) return r;
+  const int64_t p = a.tok[r];
+  return p < 0 ? 0 : (p >= a.phys_rows ? a.phys_rows - 1 : p);
+}
+// z (one vector of channels at physical row pr, channel c0) plus the residual
+// held in out (accumulate) and the outer residual, in that order, in fp32
+template <class E>
+__device__ __forceinline__ void add_residuals(const ConvArgs& a, int64_t pr, int c0, float* z) {
+  using S = typename E::S;
+  if (a.accumulate) {
+    float r[E::VEC];
+    E::unpack(ld16((const S*)a.out + pr * a.out_rs + c0), r);
+#pragma unroll
+    for (int ch = 0; ch < E::VEC; ++ch) z[ch] += r[ch];
+  }
+  if (a.outer) {
+    float o[E::VEC];
+    E::unpack(ld16((const S*)a.outer + pr * a.outer_rs + c0), o);
+#pragma unroll
+    for (int ch = 0; ch < E::VEC; ++ch) z[ch] += o[ch];
+  }
+}
+
 // Pair-of-taps dot product on bf16 data (v_dot2c_f32_bf16): acc + w.x over a
 // (older, newer) pair, fp32 accumulation.
 __device__ __forceinline__ float dot2_bf16(uint32_t w_pair, uint32_t x_pair, float acc) {

@@ -50,6 +50,11 @@ struct ConvArgs {
   const int32_t* ckpt_slots;
   int64_t x_rs, out_rs, slot_stride;   // elements
   const int32_t* num_acc;    // speculative update: accepted counts (batch), else nullptr
+  const int32_t* tok;        // logical row -> physical row of x / out / outer, or nullptr
+  const void* outer;         // added to each result at its physical row, or nullptr
+  int64_t outer_rs;          // elements
+  int32_t accumulate;        // 1: out rows hold a residual on entry; the result is added to it
+  int64_t phys_rows;         // rows of x / out / outer when tok is given (indices are clamped)
   int64_t num_tokens;
   int32_t C, num_slots, batch, q, ckpt_grid;
   int32_t S;                 // state row length (>= H); the window is columns [0, H)

@@ -30,7 +30,7 @@ namespace sc {
 constexpr int kSpecQMax = 8;    // tokens per request on the register path
 constexpr int kSpecSMax = 16;   // state entries per channel staged in LDS
 
-template <class E, int K, int D, bool SILU, bool SPEC>
+template <class E, int K, int D, bool SILU, bool SPEC, bool FUSE>
 __global__ __launch_bounds__(kBlock) void conv_rollbuf(ConvArgs a) {
   using St = typename E::S;
   constexpr int H = (K - 1) * D;
@@ -73,12 +73,27 @@ __global__ __launch_bounds__(kBlock) void conv_rollbuf(ConvArgs a) {
     if (a.bias) bsv = ld16((const St*)a.bias + c0);
   }
 
-  // token rows, then the slot, then the state region (unit stride)
-  u32x4 xr[QM];
+  // physical row of the request's token u (through the row map when fused)
+  auto prow = [&](int u) -> int64_t {
+    if constexpr (FUSE) return phys_row(a, (int64_t)r * q + u);
+    else return (int64_t)r * q + u;
+  };
+  // token rows (and fused residuals), then the slot, then the state region
+  u32x4 xr[QM], rres[FUSE ? QM : 1], rout[FUSE ? QM : 1];
 #pragma unroll
   for (int u = 0; u < QM; ++u)
-    xr[u] = (u < q && lane_ok) ? ld16_stream((const St*)a.x + ((int64_t)r * q + u) * a.x_rs + c0)
+    xr[u] = (u < q && lane_ok) ? ld16_stream((const St*)a.x + prow(u) * a.x_rs + c0)
                                : u32x4{0, 0, 0, 0};
+  if constexpr (FUSE) {
+#pragma unroll
+    for (int u = 0; u < QM; ++u) {
+      const bool ok = u < q && lane_ok;
+      rres[u] = (ok && a.accumulate) ? ld16((const St*)a.out + prow(u) * a.out_rs + c0)
+                                     : u32x4{0, 0, 0, 0};
+      rout[u] = (ok && a.outer) ? ld16((const St*)a.outer + prow(u) * a.outer_rs + c0)
+                                : u32x4{0, 0, 0, 0};
+    }
+  }
   const int32_t slot = a.slots[(int64_t)r * a.slot_stride];
   const bool valid = slot >= 0 && slot < a.num_slots;
   bool hist = valid;
@@ -145,7 +160,17 @@ __global__ __launch_bounds__(kBlock) void conv_rollbuf(ConvArgs a) {
         } else {
           conv_point<E, K, D, SILU>(win, H + u, wt, bs, z);
         }
-        st16_stream((St*)a.out + ((int64_t)r * q + u) * a.out_rs + c0, E::pack(z));
+        if constexpr (FUSE) {
+          float fr[VEC], fo[VEC];
+          E::unpack(rres[u], fr);
+          E::unpack(rout[u], fo);
+#pragma unroll
+          for (int ch = 0; ch < VEC; ++ch) {
+            if (a.accumulate) z[ch] += fr[ch];
+            if (a.outer) z[ch] += fo[ch];
+          }
+        }
+        st16_stream((St*)a.out + prow(u) * a.out_rs + c0, E::pack(z));
       }
     }
     // new buffer contents, in place in the lane's own entries
@@ -209,24 +234,27 @@ __global__ __launch_bounds__(kBlock) void conv_spec_generic(ConvArgs a, int K, i
   const int32_t slot = a.slots[(int64_t)r * a.slot_stride];
   const bool valid = slot >= 0 && slot < a.num_slots;
   const int acc = min(max(a.num_acc[r], 1), min(q, Sl - H + 1));
-  const St* xb = (const St*)a.x + (int64_t)r * q * a.x_rs + c;
-  St* ob = (St*)a.out + (int64_t)r * q * a.out_rs + c;
   St* sp = (St*)a.pool + ((int64_t)(valid ? slot : 0) * a.C + c) * Sl;
+  // the request's token u in x / out (through the row map when one is given)
+  auto pr = [&](int u) -> int64_t { return phys_row(a, (int64_t)r * q + u); };
   for (int t = 0; t < q; ++t) {
     float accf = b;
     for (int k = 0; k < K; ++k) {
       const int p = t - (K - 1 - k) * D;
       float v = 0.f;
-      if (p >= 0) v = widen<E>(ld_el<E>(xb + (int64_t)p * a.x_rs));
+      if (p >= 0) v = widen<E>(ld_el<E>((const St*)a.x + pr(p) * a.x_rs + c));
       else if (valid) v = widen<E>(ld_el<E>(sp + acc - 1 + H + p));
       accf = __builtin_fmaf(wt[k], v, accf);
     }
     if (SILU) accf = silu(accf);
-    ob[(int64_t)t * a.out_rs] = narrow<E>(accf);
+    const int64_t ot = pr(t);
+    if (a.accumulate) accf += widen<E>(ld_el<E>((const St*)a.out + ot * a.out_rs + c));
+    if (a.outer) accf += widen<E>(ld_el<E>((const St*)a.outer + ot * a.outer_rs + c));
+    ((St*)a.out)[ot * a.out_rs + c] = narrow<E>(accf);
   }
   if (valid) {
     for (int j = 0; j < Sl - q; ++j) sp[j] = sp[acc + j];
-    for (int u = 0; u < q; ++u) sp[Sl - q + u] = xb[(int64_t)u * a.x_rs];
+    for (int u = 0; u < q; ++u) sp[Sl - q + u] = *((const St*)a.x + pr(u) * a.x_rs + c);
   }
 }
 
@@ -236,32 +264,41 @@ bool rollbuf_shape(int K, int D) {
   return (K == 4 && (D == 1 || D == 2 || D == 3)) || (D == 1 && (K == 2 || K == 3));
 }
 
-template <class E, bool SILU, bool SPEC>
+template <class E, bool SILU, bool SPEC, bool FUSE>
 hipError_t launch_rollbuf(const ConvArgs& a, int K, int D, dim3 grid, hipStream_t s) {
   const size_t lds = (size_t)kBlock * a.S * sizeof(u32x4);
   const dim3 blk(kBlock);
-  if (K == 4 && D == 1) hipLaunchKernelGGL((conv_rollbuf<E, 4, 1, SILU, SPEC>), grid, blk, lds, s, a);
-  else if (K == 4 && D == 2) hipLaunchKernelGGL((conv_rollbuf<E, 4, 2, SILU, SPEC>), grid, blk, lds, s, a);
-  else if (K == 4 && D == 3) hipLaunchKernelGGL((conv_rollbuf<E, 4, 3, SILU, SPEC>), grid, blk, lds, s, a);
-  else if (K == 3) hipLaunchKernelGGL((conv_rollbuf<E, 3, 1, SILU, SPEC>), grid, blk, lds, s, a);
-  else hipLaunchKernelGGL((conv_rollbuf<E, 2, 1, SILU, SPEC>), grid, blk, lds, s, a);
+  if (K == 4 && D == 1) hipLaunchKernelGGL((conv_rollbuf<E, 4, 1, SILU, SPEC, FUSE>), grid, blk, lds, s, a);
+  else if (K == 4 && D == 2) hipLaunchKernelGGL((conv_rollbuf<E, 4, 2, SILU, SPEC, FUSE>), grid, blk, lds, s, a);
+  else if (K == 4 && D == 3) hipLaunchKernelGGL((conv_rollbuf<E, 4, 3, SILU, SPEC, FUSE>), grid, blk, lds, s, a);
+  else if (K == 3) hipLaunchKernelGGL((conv_rollbuf<E, 3, 1, SILU, SPEC, FUSE>), grid, blk, lds, s, a);
+  else hipLaunchKernelGGL((conv_rollbuf<E, 2, 1, SILU, SPEC, FUSE>), grid, blk, lds, s, a);
   return hipGetLastError();
 }
 
 template <bool SPEC>
 hipError_t launch_rollbuf_any(const ConvArgs& a, int dtype, int K, int D, bool silu_act,
                               dim3 grid, hipStream_t s) {
+  const bool fuse = a.tok != nullptr || a.outer != nullptr || a.accumulate != 0;
+  if (fuse) {
+    if (dtype == 1)
+      return silu_act ? launch_rollbuf<BF16, true, SPEC, true>(a, K, D, grid, s)
+                      : launch_rollbuf<BF16, false, SPEC, true>(a, K, D, grid, s);
+    return silu_act ? launch_rollbuf<F32, true, SPEC, true>(a, K, D, grid, s)
+                    : launch_rollbuf<F32, false, SPEC, true>(a, K, D, grid, s);
+  }
   if (dtype == 1)
-    return silu_act ? launch_rollbuf<BF16, true, SPEC>(a, K, D, grid, s)
-                    : launch_rollbuf<BF16, false, SPEC>(a, K, D, grid, s);
-  return silu_act ? launch_rollbuf<F32, true, SPEC>(a, K, D, grid, s)
-                  : launch_rollbuf<F32, false, SPEC>(a, K, D, grid, s);
+    return silu_act ? launch_rollbuf<BF16, true, SPEC, false>(a, K, D, grid, s)
+                    : launch_rollbuf<BF16, false, SPEC, false>(a, K, D, grid, s);
+  return silu_act ? launch_rollbuf<F32, true, SPEC, false>(a, K, D, grid, s)
+                  : launch_rollbuf<F32, false, SPEC, false>(a, K, D, grid, s);
 }
 
 bool use_rollbuf(const ConvArgs& a, int dtype, int K, int D, bool aligned16) {
   const int vec = dtype == 1 ? 8 : 4;
+  const int es = dtype == 1 ? 2 : 4;
   return aligned16 && a.C % vec == 0 && rollbuf_shape(K, D) && a.q >= 1 && a.q <= kSpecQMax &&
-         a.S >= (K - 1) * D && a.S <= kSpecSMax;
+         a.S >= (K - 1) * D && a.S <= kSpecSMax && (!a.outer || (a.outer_rs * es) % 16 == 0);
 }
 
 // One workgroup per (request, block of channels); fills the grid fields.

@@ -177,3 +177,43 @@ def cca_floor_rel(case) -> float:
     residual terms (2 per query head, 2G per key head), gamma_n = n * 2^-24."""
     G = case.nq // case.nkv
     return (case.hd * case.t1 + 2 * G + 4) * 2.0 ** -24
+
+
+def run_fused_case(case, xp, perm, *, resid=None, outer=None, pool=None, num_accepted=None):
+    """Runs a ConvCase through the fused calls on physical tensors: x rows at
+    xp[perm[j]] for logical row j, out initialised with `resid` (accumulate)
+    or zeros, `outer` added. Decode rows go through sc_conv_update (or
+    sc_conv_update_spec when num_accepted is given), prefill rows through
+    sc_conv_prefill_varlen, each with its slice of the row map. Returns
+    (out, pool_after) as NumPy arrays (physical rows)."""
+    import torch
+    import stateful_causal_short_amd as scs
+    xd = dev(xp)
+    od = dev(resid if resid is not None else np.zeros_like(xp))
+    ou = None if outer is None else dev(outer)
+    pd = dev(case.pool if pool is None else pool)
+    wd = dev(case.w)
+    bd = None if case.bias is None else dev(case.bias)
+    tok = dev(np.asarray(perm, np.int32))
+    nd = case.num_decode_tokens
+    kw = dict(accumulate=resid is not None, outer_residual=ou, dilation=case.d,
+              activation=case.act)
+    if case.num_decodes:
+        if num_accepted is not None:
+            scs.sc_conv_update_spec(xd, od, wd, bd, pd, dev(np.asarray(case.decode_slots, np.int32)),
+                                    dev(np.asarray(num_accepted, np.int32)), q=case.q,
+                                    token_indices=tok[:nd], **kw)
+        else:
+            dh = None if case.decode_h is None else dev(np.asarray(case.decode_h, np.uint8))
+            scs.sc_conv_update(xd, od, wd, bd, pd, dev(np.asarray(case.decode_slots, np.int32)), dh,
+                               q=case.q, token_indices=tok[:nd], **kw)
+    if case.num_prefills:
+        ck = None
+        if case.ckpt_grid:
+            ck = (case.ckpt_grid, dev(case.cu_ckpt), dev(case.ckpt_slots))
+        scs.sc_conv_prefill_varlen(xd, od, wd, bd, pd, dev(case.qsl_p),
+                                   dev(np.asarray(case.prefill_slots, np.int32)),
+                                   dev(np.asarray(case.prefill_h, np.uint8)), ckpt=ck,
+                                   token_indices=tok[nd:], **kw)
+    torch.cuda.synchronize()
+    return host(od), host(pd)

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_function():
     assert set(names) == set(scs.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.sc_abi_version() == 1
+    assert lib.sc_abi_version() == 2
     for s in (0, -1, -2, -3, -4, -5, -6):
         assert lib.sc_status_string(s)
 
@@ -44,20 +44,25 @@ def desc(**kw):
 
 
 def prefill(d, *, x=P, out=P2, w=P, bias=None, pool=P, num_slots=4, qsl=P, slots=P,
-            h=P, batch=2, T=10, ckpt=None):
+            h=P, batch=2, T=10, ckpt=None, fuse=None):
     return scs.lib().sc_conv_prefill_varlen(
         None if d is None else ctypes.byref(d), x, out, w, bias, pool, num_slots, qsl,
-        slots, h, batch, T, None if ckpt is None else ctypes.byref(ckpt), None)
+        slots, h, batch, T, None if ckpt is None else ctypes.byref(ckpt),
+        None if fuse is None else ctypes.byref(fuse), None)
 
 
-def update(d, *, x=P, out=P2, w=P, pool=P, num_slots=4, slots=P, h=None, batch=2, q=1):
+def update(d, *, x=P, out=P2, w=P, pool=P, num_slots=4, slots=P, h=None, batch=2, q=1,
+           fuse=None):
     return scs.lib().sc_conv_update(None if d is None else ctypes.byref(d), x, out, w,
-                                    None, pool, num_slots, slots, h, batch, q, None)
+                                    None, pool, num_slots, slots, h, batch, q,
+                                    None if fuse is None else ctypes.byref(fuse), None)
 
 
-def spec(d, *, x=P, out=P2, w=P, pool=P, num_slots=4, slots=P, acc=P, batch=2, q=2):
+def spec(d, *, x=P, out=P2, w=P, pool=P, num_slots=4, slots=P, acc=P, batch=2, q=2,
+         fuse=None):
     return scs.lib().sc_conv_update_spec(None if d is None else ctypes.byref(d), x, out, w,
-                                         None, pool, num_slots, slots, acc, batch, q, None)
+                                         None, pool, num_slots, slots, acc, batch, q,
+                                         None if fuse is None else ctypes.byref(fuse), None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -194,3 +199,17 @@ def test_cca_null_and_empty():
     assert cca(d, T=1) == INVALID                 # fewer rows than decodes
     assert cca(d, nd=0, npf=0, T=0) == OK
     assert cca(d, nd=0, npf=1, T=0, dslots=None) == OK
+
+
+def test_fuse_descriptor_rules():
+    from stateful_causal_short_amd import sc_conv_fuse
+    d = desc()
+    for call in (prefill, update, spec):
+        dd = desc(state_len=6) if call is spec else d
+        assert call(dd, fuse=sc_conv_fuse(accumulate=2), batch=0) == INVALID
+        assert call(dd, fuse=sc_conv_fuse(token_indices=P, num_physical_rows=0), batch=0) == INVALID
+        assert call(dd, fuse=sc_conv_fuse(outer_residual=P, outer_row_stride=63), batch=0) == INVALID
+        assert call(dd, fuse=sc_conv_fuse(accumulate=1, outer_residual=P, outer_row_stride=64),
+                    batch=0) == OK
+        # the outer residual must not be the output
+        assert call(dd, fuse=sc_conv_fuse(outer_residual=P2, outer_row_stride=64)) == INVALID
