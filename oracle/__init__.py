@@ -30,10 +30,10 @@ def lib():
         P, I32, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
         L.oracle_conv.restype = I32
         L.oracle_conv.argtypes = [I32, I32, I32, I32, I32, I32, P, I64, P, I64, P,
-                                  P, P, P, I32, I32, I32, I32, P, I64, P, I32, P, P,
+                                  P, P, P, I32, I32, I32, I32, I32, P, I64, P, I32, P, P,
                                   I64, P, I32, P, P, P, P, P, I64, P, I64, I32]
         L.oracle_conv_spec.restype = I32
-        L.oracle_conv_spec.argtypes = [I32, I32, I32, I32, I32, I32, I32, P, I64, P, I64,
+        L.oracle_conv_spec.argtypes = [I32, I32, I32, I32, I32, I32, I32, I32, P, I64, P, I64,
                                        P, P, P, P, I32, I32, I32, P, I64, P, P, P, P, I64,
                                        P, I64, I32]
         L.oracle_cca.restype = I32
@@ -70,6 +70,15 @@ def default_threads() -> int:
 
 def double_to_bf16(v: float) -> int:
     return int(lib().oracle_double_to_bf16(float(v)))
+
+
+def _layout(case) -> int:
+    return 1 if getattr(case, "layout", "ds") == "sd" else 0
+
+
+def _state_len(case, pool) -> int:
+    """S of a (num_slots, C, S) pool, or of a (num_slots, S, C) one in SD layout."""
+    return pool.shape[1] if _layout(case) else pool.shape[2]
 
 
 def _fuse_args(x, token_indices, resid, outer):
@@ -113,7 +122,8 @@ def conv(case, *, out_dtype: Optional[str] = None, absum: bool = False,
     rc = lib().oracle_conv(
         C, case.K, case.d, 1 if case.act == "silu" else 0, _DT[case.dtype],
         _DT[odt], _p(x), C, _p(out), C, _p(ab), _p(w), _p(bias), _p(pool),
-        pool.shape[0], pool.shape[2], case.num_decodes, case.q, _p(dsl), 1, _p(dh),
+        pool.shape[0], _state_len(case, pool), _layout(case), case.num_decodes, case.q,
+        _p(dsl), 1, _p(dh),
         case.num_prefills, _p(qsl), _p(psl), 1, _p(ph), case.ckpt_grid,
         _p(cu), _p(cks), _p(rm), *_fuse_args(x, token_indices, resid, outer),
         nthreads or default_threads())
@@ -136,12 +146,13 @@ def conv_spec(case, num_accepted, *, out_dtype: Optional[str] = None, absum: boo
     out = np.zeros((x.shape[0], C), _NP[odt])
     ab = np.zeros((T, C), np.float64) if absum else None
     pool = np.array(case.pool, copy=True) if pool is None else pool
-    S = pool.shape[2]
+    S = _state_len(case, pool)
     dsl = _c(case.decode_slots, np.int32)
     acc = _c(num_accepted, np.int32)
     rm = _c(row_mask, np.uint8)
     rc = lib().oracle_conv_spec(
-        C, case.K, case.d, S, 1 if case.act == "silu" else 0, _DT[case.dtype], _DT[odt],
+        C, case.K, case.d, S, _layout(case), 1 if case.act == "silu" else 0, _DT[case.dtype],
+        _DT[odt],
         _p(x), C, _p(out), C, _p(ab), _p(_c(case.w)), _p(_c(case.bias)), _p(pool),
         pool.shape[0], case.num_decodes, case.q, _p(dsl), 1, _p(acc), _p(rm),
         *_fuse_args(x, token_indices, resid, outer), nthreads or default_threads())

@@ -169,6 +169,14 @@ double fuse_value(const Fuse& f, int io, int64_t prow, int c, double y, double* 
   return y;
 }
 
+// Index of state entry u (oldest first) of channel c in slot `slot`: the pool
+// is (num_slots, C, S) ("DS", channel-major; GDN `_conv_buffer_view`) or
+// (num_slots, S, C) ("SD", the cache viewed transposed when the conv state is
+// not dim-first; GDN and PLE pages, `is_conv_state_dim_first`).
+int64_t sidx(int sd, int64_t slot, int64_t C, int64_t S, int64_t c, int64_t u) {
+  return sd ? (slot * S + u) * C + c : (slot * C + c) * S + u;
+}
+
 struct ConvArgs {
   int32_t C, K, d, act, io, odt;
   const void* x;
@@ -181,6 +189,7 @@ struct ConvArgs {
   void* pool;
   int32_t num_slots;
   int32_t S;                 // state row length (>= H); the window is columns [0, H)
+  int32_t sd;                // 1: pool is (num_slots, S, C)
   int32_t ckpt_grid;
   const int32_t* cu_ckpt;
   const int32_t* ckpt_slots;
@@ -209,7 +218,7 @@ void conv_channels(const ConvArgs& a, const std::vector<Req>& reqs, int c0, int 
       ext.assign((size_t)(H + r.len), 0.0);
       for (int u = 0; u < H; ++u)
         ext[u] = (r.has_state && valid)
-                     ? ld(a.pool, a.io, ((int64_t)r.slot * a.C + c) * a.S + u)
+                     ? ld(a.pool, a.io, sidx(a.sd, r.slot, a.C, a.S, c, u))
                      : 0.0;
       for (int64_t t = 0; t < r.len; ++t)
         ext[H + t] = ld(a.x, a.io, a.fz.row(r.start + t) * a.x_rs + c);
@@ -232,7 +241,7 @@ void conv_channels(const ConvArgs& a, const std::vector<Req>& reqs, int c0, int 
       }
       if (valid)
         for (int j = 0; j < H; ++j)
-          st(a.pool, a.io, ((int64_t)r.slot * a.C + c) * a.S + j, ext[r.len + j]);
+          st(a.pool, a.io, sidx(a.sd, r.slot, a.C, a.S, c, j), ext[r.len + j]);
       if (a.ckpt_grid > 0 && (int)ri >= a.first_prefill && a.cu_ckpt) {
         const int pr = (int)ri - a.first_prefill;
         const int32_t cnt = a.cu_ckpt[pr + 1] - a.cu_ckpt[pr];
@@ -242,7 +251,7 @@ void conv_channels(const ConvArgs& a, const std::vector<Req>& reqs, int c0, int 
           const int32_t dst = a.ckpt_slots[a.cu_ckpt[pr] + m - 1];
           if (dst < 0 || dst >= a.num_slots) continue;
           for (int j = 0; j < H; ++j)
-            st(a.pool, a.io, ((int64_t)dst * a.C + c) * a.S + j, ext[p + j]);
+            st(a.pool, a.io, sidx(a.sd, dst, a.C, a.S, c, j), ext[p + j]);
         }
       }
     }
@@ -260,7 +269,8 @@ uint16_t oracle_double_to_bf16(double v) { return double_to_bf16(v); }
 
 // Depthwise stateful causal conv over one batch (decode rows, then prefills).
 // x, w, bias and pool share io_dtype; out is written in out_dtype (F64 allowed
-// so that pins compare unrounded sums). pool is (num_slots, C, S) with
+// so that pins compare unrounded sums). pool is (num_slots, C, S), or
+// (num_slots, S, C) with state_layout = 1, with
 // S = state_len >= H = (K-1)*d (0 means H). When S > H (a buffer sized for
 // speculative rollback) the non-speculative steps keep their window in the
 // first H columns and leave the rest alone, as the GDN page's wide-buffer path
@@ -273,7 +283,8 @@ uint16_t oracle_double_to_bf16(double v) { return double_to_bf16(v); }
 int oracle_conv(int32_t C, int32_t K, int32_t d, int32_t act, int32_t io_dtype,
                 int32_t out_dtype, const void* x, int64_t x_rs, void* out,
                 int64_t out_rs, double* absum, const void* w, const void* bias,
-                void* pool, int32_t num_slots, int32_t state_len, int32_t num_decodes, int32_t q,
+                void* pool, int32_t num_slots, int32_t state_len, int32_t state_layout,
+                int32_t num_decodes, int32_t q,
                 const int32_t* decode_slots, int64_t decode_slot_stride,
                 const uint8_t* decode_h, int32_t num_prefills,
                 const int32_t* qsl_p, const int32_t* prefill_slots,
@@ -291,7 +302,7 @@ int oracle_conv(int32_t C, int32_t K, int32_t d, int32_t act, int32_t io_dtype,
       resolve(num_decodes, q, decode_slots, decode_slot_stride, decode_h,
               num_prefills, qsl_p, prefill_slots, prefill_slot_stride, prefill_h);
   ConvArgs a{C, K, d, act, io_dtype, out_dtype, x, x_rs, out, out_rs, absum, w,
-             bias, pool, num_slots, S, ckpt_grid, cu_ckpt, ckpt_slots, num_decodes,
+             bias, pool, num_slots, S, state_layout ? 1 : 0, ckpt_grid, cu_ckpt, ckpt_slots, num_decodes,
              row_mask, Fuse{token_indices, resid, resid_rs, outer, outer_rs}};
   parallel_for(C, nthreads, [&](int c0, int c1) { conv_channels(a, reqs, c0, c1); });
   return 0;
@@ -308,7 +319,7 @@ int oracle_conv(int32_t C, int32_t K, int32_t d, int32_t act, int32_t io_dtype,
 //   outputs  = the depthwise definition over ext
 //   pool[s]  = [pool[s][c][a : a+S-q], x_r]      (length S; q <= S required)
 // A slot outside the pool is a padding row: zero window, no write.
-int oracle_conv_spec(int32_t C, int32_t K, int32_t d, int32_t S, int32_t act,
+int oracle_conv_spec(int32_t C, int32_t K, int32_t d, int32_t S, int32_t state_layout, int32_t act,
                      int32_t io_dtype, int32_t out_dtype, const void* x, int64_t x_rs,
                      void* out, int64_t out_rs, double* absum, const void* w,
                      const void* bias, void* pool, int32_t num_slots, int32_t B,
@@ -330,7 +341,7 @@ int oracle_conv_spec(int32_t C, int32_t K, int32_t d, int32_t S, int32_t act,
       const int64_t start = (int64_t)r * q;
       for (int c = c0; c < c1; ++c) {
         for (int j = 0; j < S; ++j)
-          buf[j] = valid ? ld(pool, io_dtype, ((int64_t)slot * C + c) * S + j) : 0.0;
+          buf[j] = valid ? ld(pool, io_dtype, sidx(state_layout, slot, C, S, c, j)) : 0.0;
         for (int u = 0; u < H; ++u) ext[u] = buf[a - 1 + u];
         for (int t = 0; t < q; ++t) ext[H + t] = ld(x, io_dtype, fz.row(start + t) * x_rs + c);
         const double b = bias ? ld(bias, io_dtype, c) : 0.0;
@@ -350,9 +361,9 @@ int oracle_conv_spec(int32_t C, int32_t K, int32_t d, int32_t S, int32_t act,
         }
         if (valid) {
           for (int j = 0; j < S - q; ++j)
-            st(pool, io_dtype, ((int64_t)slot * C + c) * S + j, buf[a + j]);
+            st(pool, io_dtype, sidx(state_layout, slot, C, S, c, j), buf[a + j]);
           for (int t = 0; t < q; ++t)
-            st(pool, io_dtype, ((int64_t)slot * C + c) * S + (S - q) + t, ext[H + t]);
+            st(pool, io_dtype, sidx(state_layout, slot, C, S, c, (S - q) + t), ext[H + t]);
         }
       }
     }

@@ -93,7 +93,7 @@ class ConvCase:
     x: np.ndarray                  # (T, C)
     w: np.ndarray                  # (C, K)
     bias: Optional[np.ndarray]     # (C,) or None
-    pool: np.ndarray               # (num_slots, C, S)
+    pool: np.ndarray               # (num_slots, C, S), or (num_slots, S, C) when layout == "sd"
     num_decodes: int = 0
     q: int = 1                     # tokens per decode request
     decode_slots: np.ndarray = field(default_factory=lambda: np.zeros(0, np.int32))
@@ -104,6 +104,7 @@ class ConvCase:
     ckpt_grid: int = 0
     cu_ckpt: Optional[np.ndarray] = None    # (B_p + 1,) exclusive prefix
     ckpt_slots: Optional[np.ndarray] = None
+    layout: str = "ds"                      # state pool layout: "ds" (slot, C, S) | "sd" (slot, S, C)
 
     @property
     def H(self) -> int:
@@ -356,3 +357,10 @@ def num_accepted(seed: int, batch: int, q: int, lo: int = 1, hi: Optional[int] =
     asked for on purpose (lo=0, hi > q) to exercise clamping."""
     rng = np.random.default_rng(seed)
     return rng.integers(lo, (q if hi is None else hi) + 1, size=batch).astype(np.int32)
+
+
+def as_sd(case: ConvCase) -> ConvCase:
+    """The same case with its state pool stored (num_slots, S, C)."""
+    from dataclasses import replace
+    assert case.layout == "ds"
+    return replace(case, pool=np.ascontiguousarray(case.pool.transpose(0, 2, 1)), layout="sd")
