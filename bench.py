@@ -148,20 +148,21 @@ class ConvRunner:
         c, b = self.case, self.base
         x, out, pool, outer = self.sets[i % len(self.sets)]
         fz = dict(accumulate=True, outer_residual=outer) if self.fused else {}
+        lay = dict(state_layout=c.layout)
         if c.num_decodes and self.acc is not None and only in (None, "spec_update"):
             scs.sc_conv_update_spec(x[:self.nd], out[:self.nd], b["w"], b["b"], pool,
                                     b["dslots"], self.acc, q=c.q, dilation=c.d,
-                                    activation=c.act)
+                                    activation=c.act, **lay)
         elif c.num_decodes and only in (None, "decode_update"):
             fd = dict(fz, outer_residual=outer[:self.nd]) if self.fused else {}
             scs.sc_conv_update(x[:self.nd], out[:self.nd], b["w"], b["b"], pool,
                                b["dslots"], b["dh"], q=c.q, dilation=c.d, activation=c.act,
-                               **fd)
+                               **fd, **lay)
         if c.num_prefills and only in (None, "prefill"):
             fp = dict(fz, outer_residual=outer[self.nd:]) if self.fused else {}
             scs.sc_conv_prefill_varlen(x[self.nd:], out[self.nd:], b["w"], b["b"], pool,
                                        b["qsl"], b["pslots"], b["ph"], dilation=c.d,
-                                       activation=c.act, ckpt=b["ck"], **fp)
+                                       activation=c.act, ckpt=b["ck"], **fp, **lay)
 
 
 def cca_alg_bytes(case):
@@ -343,6 +344,8 @@ def main():
     ap.add_argument("--workload", default="varlen_prefill",
                     choices=["varlen_prefill", "single", "decode", "update_q4", "spec",
                              "ple_mixed", "ple_fused", "cca", "copy"])
+    ap.add_argument("--state-layout", default="ds", choices=["ds", "sd"],
+                    help="state pool layout: (slots, C, S) or (slots, S, C)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -363,6 +366,9 @@ def main():
         return copy_calibration(args)
 
     case = conv_workload(args.workload)
+    if args.state_layout == "sd":
+        import synthetic
+        case = synthetic.as_sd(case)
     acc = None
     if args.workload == "spec":
         import synthetic
@@ -452,7 +458,7 @@ def main():
             "prefills": case.num_prefills, "tokens": case.T, "channels": case.C,
             "width": case.K, "dilation": case.d, "activation": case.act,
             "state_slots": case.num_slots, "checkpoint_grid": case.ckpt_grid,
-            "state_len": case.S, "fused_residuals": fused,
+            "state_len": case.S, "state_layout": case.layout, "fused_residuals": fused,
         },
         "hbm_gbps": alg / (ms_step * 1e-3) / 1e9,
         "pct_peak": 100.0 * alg / (ms_step * 1e-3) / 1e9 / PEAK_GBPS,

@@ -68,6 +68,11 @@ typedef enum {
 
 typedef enum { SC_DTYPE_F32 = 0, SC_DTYPE_BF16 = 1 } sc_dtype;
 typedef enum { SC_ACT_NONE = 0, SC_ACT_SILU = 1 } sc_activation;
+/* State pool layout (GDN and PLE pages, `is_conv_state_dim_first`): DS =
+ * (num_slots, C, S), a channel's entries adjacent (GDN `_conv_buffer_view`);
+ * SD = (num_slots, S, C), the cache viewed transposed. Entries are oldest
+ * first in both. */
+typedef enum { SC_STATE_DS = 0, SC_STATE_SD = 1 } sc_state_layout;
 
 /* Depthwise conv descriptor (host struct, read during the call only).
  * x, out, weight, bias and the state pool share `dtype` (the PLE layer casts
@@ -89,6 +94,7 @@ typedef struct {
   int64_t out_row_stride; /* elements between token rows of out, >= C */
   int64_t state_indices_stride; /* >= 1; row stride of a 2-D index tensor whose
                                    column 0 holds the slot */
+  int32_t state_layout;   /* sc_state_layout of every state pool the call touches */
 } sc_conv_desc;
 
 /* Prefill checkpoint export (optional). For prefill request r, the m-th

@@ -22,6 +22,7 @@ STATUS = {0: "SC_OK", -1: "SC_ERR_NULL_ARG", -2: "SC_ERR_INVALID_ARG",
           -5: "SC_ERR_UNSUPPORTED", -6: "SC_ERR_HIP"}
 SC_DTYPE_F32, SC_DTYPE_BF16 = 0, 1
 SC_ACT_NONE, SC_ACT_SILU = 0, 1
+SC_STATE_DS, SC_STATE_SD = 0, 1
 
 EXPORTS = ("sc_conv_prefill_varlen", "sc_conv_update", "sc_conv_update_spec", "sc_state_gather",
            "sc_state_scatter", "sc_cca_qk_conv", "sc_status_string",
@@ -40,7 +41,7 @@ class sc_conv_desc(ctypes.Structure):
                 ("dilation", ctypes.c_int32), ("state_len", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("activation", ctypes.c_int32),
                 ("x_row_stride", ctypes.c_int64), ("out_row_stride", ctypes.c_int64),
-                ("state_indices_stride", ctypes.c_int64)]
+                ("state_indices_stride", ctypes.c_int64), ("state_layout", ctypes.c_int32)]
 
 
 class sc_ckpt_desc(ctypes.Structure):
@@ -179,19 +180,24 @@ def _fuse(x, out, token_indices, accumulate, outer_residual):
         outer_row_stride=0 if outer_residual is None else _rows(outer_residual, "outer_residual")))
 
 
-def _conv_desc(x, out, weight, state_pool, dilation, activation, state_indices):
+def _conv_desc(x, out, weight, state_pool, dilation, activation, state_indices,
+               state_layout="ds"):
     C = x.shape[1]
     K = weight.shape[-1]
     act = {"silu": SC_ACT_SILU, "none": SC_ACT_NONE, None: SC_ACT_NONE}[activation]
     if weight.numel() != C * K or not weight.is_contiguous():
         raise ValueError("weight: expected a contiguous (C, K) or (C, 1, K) tensor")
-    if not state_pool.is_contiguous() or state_pool.dim() != 3:
-        raise ValueError("state_pool: expected a contiguous (num_slots, C, S) tensor")
+    sd = {"ds": False, "sd": True}[state_layout]
+    if not state_pool.is_contiguous() or state_pool.dim() != 3 or \
+            state_pool.shape[2 if sd else 1] != C:
+        raise ValueError("state_pool: expected a contiguous (num_slots, C, S) tensor, or "
+                         "(num_slots, S, C) with state_layout='sd'")
     _, sst = _index(state_indices, "state_indices")
     return sc_conv_desc(channels=C, width=K, dilation=dilation,
-                        state_len=state_pool.shape[2], dtype=_dtype_code(x),
+                        state_len=state_pool.shape[1 if sd else 2], dtype=_dtype_code(x),
                         activation=act, x_row_stride=_rows(x, "x"),
-                        out_row_stride=_rows(out, "out"), state_indices_stride=sst)
+                        out_row_stride=_rows(out, "out"), state_indices_stride=sst,
+                        state_layout=SC_STATE_SD if sd else SC_STATE_DS)
 
 
 # ---------------------------------------------------------------------------
@@ -200,7 +206,8 @@ def _conv_desc(x, out, weight, state_pool, dilation, activation, state_indices):
 def sc_conv_prefill_varlen(x, out, weight, bias, state_pool, query_start_loc,
                            state_indices, has_initial_state, *, dilation: int = 1,
                            activation: Optional[str] = "silu", ckpt=None, token_indices=None,
-                           accumulate: bool = False, outer_residual=None, stream=None):
+                           accumulate: bool = False, outer_residual=None,
+                           state_layout: str = "ds", stream=None):
     """Varlen prefill conv; updates ``state_pool`` in place.
 
     x, out: (num_tokens, C); weight (C, K); bias (C) or None; state_pool
@@ -212,7 +219,8 @@ def sc_conv_prefill_varlen(x, out, weight, bias, state_pool, query_start_loc,
     x / out / outer_residual; accumulate adds the result to out's contents;
     outer_residual is added too.
     """
-    desc = _conv_desc(x, out, weight, state_pool, dilation, activation, state_indices)
+    desc = _conv_desc(x, out, weight, state_pool, dilation, activation, state_indices,
+                      state_layout)
     cd = None
     if ckpt is not None:
         grid, cu, slots = ckpt
@@ -231,14 +239,16 @@ def sc_conv_prefill_varlen(x, out, weight, bias, state_pool, query_start_loc,
 def sc_conv_update(x, out, weight, bias, state_pool, state_indices,
                    has_initial_state=None, *, q: int = 1, dilation: int = 1,
                    activation: Optional[str] = "silu", token_indices=None,
-                   accumulate: bool = False, outer_residual=None, stream=None):
+                   accumulate: bool = False, outer_residual=None, state_layout: str = "ds",
+                   stream=None):
     """Decode / multi-token update: x (B*q, C) rows, request r owns rows
     [r*q, (r+1)*q) (logical rows, mapped by token_indices when given);
     updates ``state_pool`` in place."""
     rows = x.shape[0] if token_indices is None else token_indices.shape[0]
     if rows % max(q, 1):
         raise ValueError("rows must be a multiple of q")
-    desc = _conv_desc(x, out, weight, state_pool, dilation, activation, state_indices)
+    desc = _conv_desc(x, out, weight, state_pool, dilation, activation, state_indices,
+                      state_layout)
     B = rows // q if q else 0
     st = lib().sc_conv_update(
         ctypes.byref(desc), _ptr(x), _ptr(out), _ptr(weight), _ptr(bias),
@@ -251,7 +261,7 @@ def sc_conv_update(x, out, weight, bias, state_pool, state_indices,
 def sc_conv_update_spec(x, out, weight, bias, state_pool, state_indices, num_accepted_tokens,
                         *, q: int, dilation: int = 1, activation: Optional[str] = "silu",
                         token_indices=None, accumulate: bool = False, outer_residual=None,
-                        stream=None):
+                        state_layout: str = "ds", stream=None):
     """Speculative update on a rolling buffer: x (B*q, C) rows, request r owns
     rows [r*q, (r+1)*q); state_pool (num_slots, C, S) with S >= (K-1)*dilation;
     num_accepted_tokens int32 (B). Updates ``state_pool`` in place."""
@@ -261,7 +271,8 @@ def sc_conv_update_spec(x, out, weight, bias, state_pool, state_indices, num_acc
     torch = _torch()
     if num_accepted_tokens.dtype != torch.int32 or not num_accepted_tokens.is_contiguous():
         raise ValueError("num_accepted_tokens: expected a contiguous int32 tensor")
-    desc = _conv_desc(x, out, weight, state_pool, dilation, activation, state_indices)
+    desc = _conv_desc(x, out, weight, state_pool, dilation, activation, state_indices,
+                      state_layout)
     st = lib().sc_conv_update_spec(
         ctypes.byref(desc), _ptr(x), _ptr(out), _ptr(weight), _ptr(bias),
         _ptr(state_pool), state_pool.shape[0], _index(state_indices, "state_indices")[0],

@@ -25,6 +25,7 @@ sc_status check_conv_desc(const sc_conv_desc* d, int* H) {
   if (h > (1 << 20)) return SC_ERR_INVALID_ARG;
   if (d->state_len < h) return SC_ERR_STATE_CAPACITY;
   if (d->state_len > (1 << 20)) return SC_ERR_INVALID_ARG;
+  if (d->state_layout != SC_STATE_DS && d->state_layout != SC_STATE_SD) return SC_ERR_INVALID_ARG;
   *H = (int)h;
   return SC_OK;
 }
@@ -133,6 +134,7 @@ sc_status sc_conv_prefill_varlen(const sc_conv_desc* desc, const void* x, void* 
   a.q = 0;
   a.ckpt_grid = grid;
   a.S = desc->state_len;
+  a.sd = desc->state_layout == SC_STATE_SD ? 1 : 0;
   if ((st = apply_fuse(fuse, out, a)) != SC_OK) return st;
   const bool aligned = conv_aligned(desc, x, out, weight, bias, state_pool) &&
                        (!a.outer || al16(a.outer));
@@ -177,6 +179,7 @@ sc_status sc_conv_update(const sc_conv_desc* desc, const void* x, void* out,
   a.q = q;
   a.ckpt_grid = 0;
   a.S = desc->state_len;
+  a.sd = desc->state_layout == SC_STATE_SD ? 1 : 0;
   if ((st = apply_fuse(fuse, out, a)) != SC_OK) return st;
   const bool aligned = conv_aligned(desc, x, out, weight, bias, state_pool) &&
                        (!a.outer || al16(a.outer));
@@ -224,6 +227,7 @@ sc_status sc_conv_update_spec(const sc_conv_desc* desc, const void* x, void* out
   a.q = q;
   a.ckpt_grid = 0;
   a.S = desc->state_len;
+  a.sd = desc->state_layout == SC_STATE_SD ? 1 : 0;
   if ((st = apply_fuse(fuse, out, a)) != SC_OK) return st;
   const bool aligned = conv_aligned(desc, x, out, weight, bias, state_pool) &&
                        (!a.outer || al16(a.outer));

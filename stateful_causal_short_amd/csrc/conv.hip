@@ -24,48 +24,85 @@
 namespace sc {
 
 
-// Store the window of request rows [p-H, p) (all >= 0) as a (ch, jj) state
-// row; xrow(t) is the lane's channel vector in the request's row t.
-template <class E, int H, class XRow>
-__device__ __forceinline__ void store_window_from_x(typename E::S* dst, XRow xrow, int p) {
-  u32x4 xr[H], nv[H];
+// State I/O in "rows": rows[u] is entry u (oldest first) of the lane's VEC
+// channels. In the SD pool (num_slots, S, C) a row is one 16-byte vector
+// (coalesced across lanes); in the DS pool (num_slots, C, S) with S == H the
+// lane's entries are H contiguous vectors in (channel, entry) order and are
+// transposed in registers.
+template <class E, int H>
+__device__ __forceinline__ void load_state_rows(const ConvArgs& a, int32_t slot, int c0,
+                                                u32x4* rows) {
+  using S = typename E::S;
+  if (a.sd) {
+    const S* base = (const S*)a.pool + (int64_t)slot * a.S * a.C + c0;
 #pragma unroll
-  for (int jj = 0; jj < H; ++jj) xr[jj] = ld16(xrow(p - H + jj));
+    for (int u = 0; u < H; ++u) rows[u] = ld16(base + (int64_t)u * a.C);
+  } else {
+    const S* sp = (const S*)a.pool + ((int64_t)slot * a.C + c0) * H;
+    u32x4 old[H];
 #pragma unroll
-  for (int jj = 0; jj < H; ++jj)
+    for (int v = 0; v < H; ++v) old[v] = ld16(sp + v * E::VEC);
 #pragma unroll
-    for (int ch = 0; ch < E::VEC; ++ch) set_flat<E>(nv, ch * H + jj, E::get(xr[jj], ch));
+    for (int u = 0; u < H; ++u) {
+      rows[u] = u32x4{0, 0, 0, 0};
 #pragma unroll
-  for (int v = 0; v < H; ++v) st16(dst + v * E::VEC, nv[v]);
+      for (int ch = 0; ch < E::VEC; ++ch) E::set(rows[u], ch, get_flat<E>(old, ch * H + u));
+    }
+  }
 }
 
-// New state = ext[L .. L+H) for a request of runtime length L.
+template <class E, int H>
+__device__ __forceinline__ void store_state_rows(const ConvArgs& a, int32_t slot, int c0,
+                                                 const u32x4* rows) {
+  using S = typename E::S;
+  if (a.sd) {
+    S* base = (S*)a.pool + (int64_t)slot * a.S * a.C + c0;
+#pragma unroll
+    for (int u = 0; u < H; ++u) st16(base + (int64_t)u * a.C, rows[u]);
+  } else {
+    S* sp = (S*)a.pool + ((int64_t)slot * a.C + c0) * H;
+    u32x4 nv[H];
+#pragma unroll
+    for (int u = 0; u < H; ++u)
+#pragma unroll
+      for (int ch = 0; ch < E::VEC; ++ch) set_flat<E>(nv, ch * H + u, E::get(rows[u], ch));
+#pragma unroll
+    for (int v = 0; v < H; ++v) st16(sp + v * E::VEC, nv[v]);
+  }
+}
+
+// Store the window of request rows [p-H, p) (all >= 0) into `slot`; xrow(t) is
+// the lane's channel vector in the request's row t.
 template <class E, int H, class XRow>
-__device__ __forceinline__ void write_state(typename E::S* sp, const u32x4* old, int L,
-                                            XRow xrow) {
+__device__ __forceinline__ void store_window_rows(const ConvArgs& a, int32_t slot, int c0,
+                                                  XRow xrow, int p) {
+  u32x4 r[H];
+#pragma unroll
+  for (int jj = 0; jj < H; ++jj) r[jj] = ld16(xrow(p - H + jj));
+  store_state_rows<E, H>(a, slot, c0, r);
+}
+
+// New state = ext[L .. L+H) for a request of runtime length L >= 1, where ext
+// is [old rows (H), x rows].
+template <class E, int H, class XRow>
+__device__ __forceinline__ void write_state_rows(const ConvArgs& a, int32_t slot, int c0,
+                                                 const u32x4* old, int L, XRow xrow) {
   if (L >= H) {
-    store_window_from_x<E, H>(sp, xrow, L);
+    store_window_rows<E, H>(a, slot, c0, xrow, L);
     return;
   }
-  // 1 <= L < H: entries jj < H-L keep old[L + jj], the rest are the L tokens.
-  u32x4 xr[H], nv[H];
+  // 1 <= L < H: entries jj < H-L keep old[L + jj], the rest are the L tokens
+  u32x4 r[H];
 #pragma unroll
   for (int jj = 0; jj < H; ++jj) {
     const int p = L - H + jj;
-    xr[jj] = p >= 0 ? ld16(xrow(p)) : u32x4{0, 0, 0, 0};
+    u32x4 val = p >= 0 ? ld16(xrow(p)) : u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int m = 1; m < H; ++m)
+      if (m + jj < H && m == L) val = old[m + jj];
+    r[jj] = val;
   }
-#pragma unroll
-  for (int jj = 0; jj < H; ++jj)
-#pragma unroll
-    for (int ch = 0; ch < E::VEC; ++ch) {
-      uint32_t val = E::get(xr[jj], ch);
-#pragma unroll
-      for (int m = 1; m < H; ++m)
-        if (m + jj < H && m == L) val = get_flat<E>(old, ch * H + m + jj);
-      set_flat<E>(nv, ch * H + jj, val);
-    }
-#pragma unroll
-  for (int v = 0; v < H; ++v) st16(sp + v * E::VEC, nv[v]);
+  store_state_rows<E, H>(a, slot, c0, r);
 }
 
 // ---------------------------------------------------------------------------
@@ -102,15 +139,10 @@ __global__ __launch_bounds__(kBlock) void conv_fast(ConvArgs a) {
   const int64_t xrs = a.x_rs, ors = a.out_rs;
   const S* xb = (const S*)a.x + w.start * xrs + c0;
   S* ob = (S*)a.out + w.start * ors + c0;
-  S* sp = (S*)a.pool + ((int64_t)(w.valid ? w.slot : 0) * a.C + c0) * H;
-
-  u32x4 old[H];
+  u32x4 old[H];   // history rows (entry u of this lane's channels)
 #pragma unroll
   for (int v = 0; v < H; ++v) old[v] = u32x4{0, 0, 0, 0};
-  if (w.j == 0 && w.h) {
-#pragma unroll
-    for (int v = 0; v < H; ++v) old[v] = ld16(sp + v * VEC);
-  }
+  if (w.j == 0 && w.h) load_state_rows<E, H>(a, w.slot, c0, old);
 
   if constexpr (QC > 0) {
     // Update of exactly QC tokens (the host launches this only when q == QC).
@@ -118,7 +150,8 @@ __global__ __launch_bounds__(kBlock) void conv_fast(ConvArgs a) {
 #pragma unroll
     for (int u = 0; u < QC; ++u) xr[u] = ld16(xb + (int64_t)u * xrs);
     float win[H + QC][VEC];
-    hist_to_win<E, H>(old, win);
+#pragma unroll
+    for (int u = 0; u < H; ++u) E::unpack(old[u], win[u]);
 #pragma unroll
     for (int u = 0; u < QC; ++u) E::unpack(xr[u], win[H + u]);
 #pragma unroll
@@ -128,22 +161,19 @@ __global__ __launch_bounds__(kBlock) void conv_fast(ConvArgs a) {
       st16_stream(ob + (int64_t)u * ors, E::pack(z));
     }
     if (w.valid) {
-      u32x4 nv[H];
+      u32x4 nr[H];
 #pragma unroll
-      for (int jj = 0; jj < H; ++jj)
-#pragma unroll
-        for (int ch = 0; ch < VEC; ++ch) {
-          const int e = QC + jj;   // ext index of new-state entry jj
-          const uint32_t val = e < H ? get_flat<E>(old, ch * H + e) : E::get(xr[e - H], ch);
-          set_flat<E>(nv, ch * H + jj, val);
-        }
-#pragma unroll
-      for (int v = 0; v < H; ++v) st16(sp + v * VEC, nv[v]);
+      for (int jj = 0; jj < H; ++jj) {
+        const int e = QC + jj;   // ext index of new-state entry jj
+        nr[jj] = e < H ? old[e] : xr[e - H];
+      }
+      store_state_rows<E, H>(a, w.slot, c0, nr);
     }
   } else {
     float win[H + U][VEC];
     if (w.j == 0) {
-      hist_to_win<E, H>(old, win);
+#pragma unroll
+      for (int u = 0; u < H; ++u) E::unpack(old[u], win[u]);
     } else {
 #pragma unroll
       for (int u = 0; u < H; ++u) E::unpack(ld16(xb + (int64_t)(w.t0 - H + u) * xrs), win[u]);
@@ -171,7 +201,7 @@ __global__ __launch_bounds__(kBlock) void conv_fast(ConvArgs a) {
         for (int ch = 0; ch < VEC; ++ch) win[i][ch] = win[i + U][ch];
     }
     auto xrow = [&](int t) { return xb + (int64_t)t * xrs; };
-    if (w.j == 0 && w.valid) write_state<E, H>(sp, old, w.L, xrow);
+    if (w.j == 0 && w.valid) write_state_rows<E, H>(a, w.slot, c0, old, w.L, xrow);
     if (a.ckpt_grid > 0 && a.qsl != nullptr) {
       // checkpoints at p = m*g with t0 < p <= t1: the chunk holding token p-1
       const int g = a.ckpt_grid;
@@ -179,7 +209,7 @@ __global__ __launch_bounds__(kBlock) void conv_fast(ConvArgs a) {
       for (int m = w.t0 / g + 1; m <= cnt && (int64_t)m * g <= w.t1; ++m) {
         const int32_t dst = a.ckpt_slots[cu0 + m - 1];
         if (dst < 0 || dst >= a.num_slots) continue;
-        store_window_from_x<E, H>((S*)a.pool + ((int64_t)dst * a.C + c0) * H, xrow, m * g);
+        store_window_rows<E, H>(a, dst, c0, xrow, m * g);
       }
     }
   }
@@ -282,11 +312,7 @@ __global__ __launch_bounds__(kBlock) void conv_pairs(ConvArgs a) {
     valid = slot >= 0 && slot < a.num_slots;
     hflag = valid && (a.has_init ? a.has_init[r] != 0 : true);
   }
-  S* sp = (S*)a.pool + ((int64_t)(valid ? slot : 0) * a.C + c0) * H;
-  if (hflag) {
-#pragma unroll
-    for (int v = 0; v < H; ++v) old[v] = ld16(sp + v * VEC);
-  }
+  if (hflag) load_state_rows<E, H>(a, slot, c0, old);   // history rows
   Work w;
   w.r = r;
   w.j = j;
@@ -311,13 +337,8 @@ __global__ __launch_bounds__(kBlock) void conv_pairs(ConvArgs a) {
   float bs[VEC];
   E::unpack(bsv, bs);
   if (w.j == 0) {
-    // history (ch, u) layout -> rows
 #pragma unroll
-    for (int u = 0; u < H; ++u) {
-      raw[u] = u32x4{0, 0, 0, 0};
-#pragma unroll
-      for (int ch = 0; ch < VEC; ++ch) E::set(raw[u], ch, get_flat<E>(old, ch * H + u));
-    }
+    for (int u = 0; u < H; ++u) raw[u] = old[u];
   }
 
 #pragma unroll
@@ -354,16 +375,9 @@ __global__ __launch_bounds__(kBlock) void conv_pairs(ConvArgs a) {
 
   if (w.j == 0 && w.valid) {
     if constexpr (UPDATE) {
-      // new state = ext[U .. U+H), all in registers
-      u32x4 nv[H];
-#pragma unroll
-      for (int jj = 0; jj < H; ++jj)
-#pragma unroll
-        for (int ch = 0; ch < VEC; ++ch) set_flat<E>(nv, ch * H + jj, E::get(raw[U + jj], ch));
-#pragma unroll
-      for (int v = 0; v < H; ++v) st16(sp + v * VEC, nv[v]);
+      store_state_rows<E, H>(a, slot, c0, raw + U);   // new state = ext[U .. U+H)
     } else {
-      write_state<E, H>(sp, old, w.L, xrow);
+      write_state_rows<E, H>(a, slot, c0, old, w.L, xrow);
     }
   }
   if (!UPDATE && a.ckpt_grid > 0 && a.qsl != nullptr) {
@@ -372,7 +386,7 @@ __global__ __launch_bounds__(kBlock) void conv_pairs(ConvArgs a) {
     for (int m = w.t0 / g + 1; m <= cnt && (int64_t)m * g <= w.t1; ++m) {
       const int32_t dst = a.ckpt_slots[cu0 + m - 1];
       if (dst < 0 || dst >= a.num_slots) continue;
-      store_window_from_x<E, H>((S*)a.pool + ((int64_t)dst * a.C + c0) * H, xrow, m * g);
+      store_window_rows<E, H>(a, dst, c0, xrow, m * g);
     }
   }
 }
@@ -463,15 +477,26 @@ __global__ __launch_bounds__(kBlock) void conv_update_pairs(ConvArgs a) {
     valid[rr] = slot[rr] >= 0 && slot[rr] < a.num_slots;
     hflag[rr] = valid[rr] && (a.has_init ? a.has_init[r] != 0 : true);
   }
+  if (a.sd) {
+    // SD pool: entry k of the lane's channels is one vector, unit stride across lanes
 #pragma unroll
-  for (int rr = 0; rr < R; ++rr) {
-    const S* sp = (const S*)a.pool + ((int64_t)(valid[rr] ? slot[rr] : 0) * a.C + cbase) * H;
+    for (int rr = 0; rr < R; ++rr) {
+      const S* sp = (const S*)a.pool + (int64_t)(valid[rr] ? slot[rr] : 0) * a.S * a.C + c0;
 #pragma unroll
-    for (int k = 0; k < H; ++k) {
-      const int vi = tid + k * kBlock;
-      st[rr][k] = (hflag[rr] && vi < nvec)
-                      ? (SC_NT_LOADS ? ld16_stream(sp + vi * VEC) : ld16(sp + vi * VEC))
-                      : u32x4{0, 0, 0, 0};
+      for (int k = 0; k < H; ++k)
+        st[rr][k] = (hflag[rr] && lane_ok) ? ld16_stream(sp + (int64_t)k * a.C) : u32x4{0, 0, 0, 0};
+    }
+  } else {
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) {
+      const S* sp = (const S*)a.pool + ((int64_t)(valid[rr] ? slot[rr] : 0) * a.C + cbase) * H;
+#pragma unroll
+      for (int k = 0; k < H; ++k) {
+        const int vi = tid + k * kBlock;
+        st[rr][k] = (hflag[rr] && vi < nvec)
+                        ? (SC_NT_LOADS ? ld16_stream(sp + vi * VEC) : ld16(sp + vi * VEC))
+                        : u32x4{0, 0, 0, 0};
+      }
     }
   }
   float bs[VEC];
@@ -480,20 +505,25 @@ __global__ __launch_bounds__(kBlock) void conv_update_pairs(ConvArgs a) {
 #pragma unroll
   for (int rr = 0; rr < R; ++rr) {
     const int r = grp * R + rr;
-    // state region -> per-lane (channel, tap) order
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < H; ++k) xch[tid + k * kBlock] = st[rr][k];
-    __syncthreads();
-    u32x4 old[H];
-#pragma unroll
-    for (int k = 0; k < H; ++k) old[k] = xch[tid * H + k];
     u32x4 raw[H + Q];
+    if (a.sd) {
 #pragma unroll
-    for (int u = 0; u < H; ++u) {
-      raw[u] = u32x4{0, 0, 0, 0};
+      for (int u = 0; u < H; ++u) raw[u] = st[rr][u];
+    } else {
+      // state region -> per-lane (channel, tap) order
+      __syncthreads();
 #pragma unroll
-      for (int ch = 0; ch < VEC; ++ch) E::set(raw[u], ch, get_flat<E>(old, ch * H + u));
+      for (int k = 0; k < H; ++k) xch[tid + k * kBlock] = st[rr][k];
+      __syncthreads();
+      u32x4 old[H];
+#pragma unroll
+      for (int k = 0; k < H; ++k) old[k] = xch[tid * H + k];
+#pragma unroll
+      for (int u = 0; u < H; ++u) {
+        raw[u] = u32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int ch = 0; ch < VEC; ++ch) E::set(raw[u], ch, get_flat<E>(old, ch * H + u));
+      }
     }
 #pragma unroll
     for (int u = 0; u < Q; ++u) raw[H + u] = xr[rr][u];
@@ -525,22 +555,31 @@ __global__ __launch_bounds__(kBlock) void conv_update_pairs(ConvArgs a) {
         st16_stream((S*)a.out + pr * a.out_rs + c0, E::pack(z));
       }
     }
-    // new state = ext[Q .. Q+H) in (channel, tap) order -> region order
-    u32x4 nv[H];
+    // new state = ext[Q .. Q+H)
+    if (a.sd) {
+      if (valid[rr] && lane_ok) {
+        S* dp = (S*)a.pool + (int64_t)slot[rr] * a.S * a.C + c0;
 #pragma unroll
-    for (int jj = 0; jj < H; ++jj)
+        for (int k = 0; k < H; ++k) st16_stream(dp + (int64_t)k * a.C, raw[Q + k]);
+      }
+    } else {
+      // (channel, tap) order -> region order
+      u32x4 nv[H];
 #pragma unroll
-      for (int ch = 0; ch < VEC; ++ch) set_flat<E>(nv, ch * H + jj, E::get(raw[Q + jj], ch));
-    __syncthreads();
+      for (int jj = 0; jj < H; ++jj)
 #pragma unroll
-    for (int k = 0; k < H; ++k) xch[tid * H + k] = nv[k];
-    __syncthreads();
-    if (valid[rr]) {
-      S* dp = (S*)a.pool + ((int64_t)slot[rr] * a.C + cbase) * H;
+        for (int ch = 0; ch < VEC; ++ch) set_flat<E>(nv, ch * H + jj, E::get(raw[Q + jj], ch));
+      __syncthreads();
 #pragma unroll
-      for (int k = 0; k < H; ++k) {
-        const int vi = tid + k * kBlock;
-        if (vi < nvec) st16_stream(dp + vi * VEC, xch[vi]);
+      for (int k = 0; k < H; ++k) xch[tid * H + k] = nv[k];
+      __syncthreads();
+      if (valid[rr]) {
+        S* dp = (S*)a.pool + ((int64_t)slot[rr] * a.C + cbase) * H;
+#pragma unroll
+        for (int k = 0; k < H; ++k) {
+          const int vi = tid + k * kBlock;
+          if (vi < nvec) st16_stream(dp + vi * VEC, xch[vi]);
+        }
       }
     }
   }
@@ -570,7 +609,12 @@ __global__ __launch_bounds__(kBlock) void conv_generic(ConvArgs a, int K, int D)
   const float b = a.bias ? widen<E>(ld_el<E>((const S*)a.bias + c)) : 0.f;
   const int64_t xrs = a.x_rs, ors = a.out_rs;
   const S* xb = (const S*)a.x + w.start * xrs + c;
-  S* sp = (S*)a.pool + ((int64_t)(w.valid ? w.slot : 0) * a.C + c) * a.S;
+  // state entry u of this channel in slot s (DS or SD pool)
+  auto sref = [&](int32_t s, int u) -> S& {
+    S* pool = (S*)a.pool;
+    return a.sd ? pool[((int64_t)s * a.S + u) * a.C + c] : pool[((int64_t)s * a.C + c) * a.S + u];
+  };
+  const int32_t wslot = w.valid ? w.slot : 0;
   // request row p of x (through the row map when one is given)
   auto xg = [&](int p) -> const S* {
     return a.tok ? (const S*)a.x + phys_row(a, w.start + p) * xrs + c : xb + (int64_t)p * xrs;
@@ -581,7 +625,7 @@ __global__ __launch_bounds__(kBlock) void conv_generic(ConvArgs a, int K, int D)
       const int p = t - (K - 1 - k) * D;
       float v = 0.f;
       if (p >= 0) v = widen<E>(ld_el<E>(xg(p)));
-      else if (w.h) v = widen<E>(ld_el<E>(sp + H + p));
+      else if (w.h) v = widen<E>((uint32_t)sref(wslot, H + p));
       acc = __builtin_fmaf(wt[k], v, acc);
     }
     if (SILU) acc = silu(acc);
@@ -596,8 +640,8 @@ __global__ __launch_bounds__(kBlock) void conv_generic(ConvArgs a, int K, int D)
       const int p = w.L - H + jj;
       S v = 0;
       if (p >= 0) v = *xg(p);
-      else if (w.h) v = sp[w.L + jj];
-      sp[jj] = v;
+      else if (w.h) v = sref(wslot, w.L + jj);
+      sref(wslot, jj) = v;
     }
   }
   if (a.ckpt_grid > 0 && a.qsl != nullptr) {
@@ -606,8 +650,7 @@ __global__ __launch_bounds__(kBlock) void conv_generic(ConvArgs a, int K, int D)
     for (int m = w.t0 / g + 1; m <= cnt && (int64_t)m * g <= w.t1; ++m) {
       const int32_t dst = a.ckpt_slots[cu0 + m - 1];
       if (dst < 0 || dst >= a.num_slots) continue;
-      S* dp = (S*)a.pool + ((int64_t)dst * a.C + c) * a.S;
-      for (int jj = 0; jj < H; ++jj) dp[jj] = *xg(m * g - H + jj);
+      for (int jj = 0; jj < H; ++jj) sref(dst, jj) = *xg(m * g - H + jj);
     }
   }
 }
@@ -690,7 +733,7 @@ hipError_t launch_conv(ConvArgs a, int dtype, int K, int D, bool silu_act, bool 
   const int H = (K - 1) * D;
   if (a.S <= 0) a.S = H;
   const bool uniform = a.qsl == nullptr;
-  if (a.S != H && uniform) {
+  if (a.S != H && !a.sd && uniform) {
     // a buffer widened for speculative rollback: plain update on its first H columns
     const hipError_t e = launch_update_wide(a, dtype, K, D, silu_act, aligned16, stream);
     if (e != hipErrorNotSupported) return e;
@@ -699,10 +742,12 @@ hipError_t launch_conv(ConvArgs a, int dtype, int K, int D, bool silu_act, bool 
   // residual fusion and row maps are built into the bf16 pair kernels and the
   // generic one
   const bool fuse = a.tok != nullptr || a.outer != nullptr || a.accumulate != 0;
-  const bool pairs_ok = a.S == H && aligned16 && (a.C % vec == 0) && dtype == 1 &&
+  // (an SD pool keeps a lane's entries as vectors at any S; a DS one only at S == H)
+  const bool rows_ok = a.S == H || a.sd;
+  const bool pairs_ok = rows_ok && aligned16 && (a.C % vec == 0) && dtype == 1 &&
                         pairs_shape(K, D) && !SC_NO_PAIRS &&
                         (!a.outer || (a.outer_rs * 2) % 16 == 0);
-  const bool fast = a.S == H && aligned16 && (a.C % vec == 0) && fast_shape(K, D) &&
+  const bool fast = rows_ok && aligned16 && (a.C % vec == 0) && fast_shape(K, D) &&
                     (!fuse || pairs_ok);
   // the one-pass kernel takes its halo from x: its chunk covers H by construction
   const bool pairs = fast && pairs_ok;

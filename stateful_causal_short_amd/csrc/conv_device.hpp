@@ -133,15 +133,6 @@ __device__ __forceinline__ void load_weights(const void* w, int c0, float (*wt)[
     for (int k = 0; k < K; ++k) wt[k][ch] = flat[ch * K + k];
 }
 
-// History vectors ((ch, u) order, as in the pool) to window rows 0..H-1.
-template <class E, int H>
-__device__ __forceinline__ void hist_to_win(const u32x4* old, float (*win)[E::VEC]) {
-#pragma unroll
-  for (int u = 0; u < H; ++u)
-#pragma unroll
-    for (int ch = 0; ch < E::VEC; ++ch) win[u][ch] = widen<E>(get_flat<E>(old, ch * H + u));
-}
-
 template <class E, int K, int D, bool SILU>
 __device__ __forceinline__ void conv_point(const float (*win)[E::VEC], int pos,
                                            const float (*wt)[E::VEC], const float* bs,

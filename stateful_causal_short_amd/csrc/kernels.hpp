@@ -57,7 +57,8 @@ struct ConvArgs {
   int64_t phys_rows;         // rows of x / out / outer when tok is given (indices are clamped)
   int64_t num_tokens;
   int32_t C, num_slots, batch, q, ckpt_grid;
-  int32_t S;                 // state row length (>= H); the window is columns [0, H)
+  int32_t S;                 // state entries per channel (>= H); the window is entries [0, H)
+  int32_t sd;                // 1: pool is (num_slots, S, C) ("SD"), else (num_slots, C, S)
   // filled by launch_conv
   int32_t chunk, n_cblk, n_logical, per_xcd;
 };

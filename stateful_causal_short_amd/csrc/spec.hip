@@ -103,32 +103,50 @@ __global__ __launch_bounds__(kBlock) void conv_rollbuf(ConvArgs a) {
   } else {
     hist = valid && (a.has_init ? a.has_init[r] != 0 : true);
   }
+  // SD pool (num_slots, S, C): entry k of the lane's channels is one vector;
+  // the lane keeps its own column region[k * kBlock + tid] (no other lane
+  // touches it). DS pool: the workgroup's rows are one contiguous region.
+  const bool sd = a.sd != 0;
   if (valid) {
-    const St* sp = (const St*)a.pool + ((int64_t)slot * a.C + cbase) * Sl;
     u32x4 sv[kSpecSMax];
+    if (sd) {
+      const St* sp = (const St*)a.pool + (int64_t)slot * Sl * a.C + c0;
 #pragma unroll
-    for (int k = 0; k < kSpecSMax; ++k) {
-      const int vi = tid + k * kBlock;
-      sv[k] = (k < Sl && vi < nvec) ? ld16_stream(sp + vi * VEC) : u32x4{0, 0, 0, 0};
-    }
+      for (int k = 0; k < kSpecSMax; ++k)
+        sv[k] = (k < Sl && lane_ok) ? ld16_stream(sp + (int64_t)k * a.C) : u32x4{0, 0, 0, 0};
 #pragma unroll
-    for (int k = 0; k < kSpecSMax; ++k) {
-      const int vi = tid + k * kBlock;
-      if (k < Sl && vi < nvec) region[vi] = sv[k];
+      for (int k = 0; k < kSpecSMax; ++k)
+        if (k < Sl) region[k * kBlock + tid] = sv[k];
+    } else {
+      const St* sp = (const St*)a.pool + ((int64_t)slot * a.C + cbase) * Sl;
+#pragma unroll
+      for (int k = 0; k < kSpecSMax; ++k) {
+        const int vi = tid + k * kBlock;
+        sv[k] = (k < Sl && vi < nvec) ? ld16_stream(sp + vi * VEC) : u32x4{0, 0, 0, 0};
+      }
+#pragma unroll
+      for (int k = 0; k < kSpecSMax; ++k) {
+        const int vi = tid + k * kBlock;
+        if (k < Sl && vi < nvec) region[vi] = sv[k];
+      }
     }
   }
   __syncthreads();
 
   St* le = (St*)region;
-  const int lbase = tid * VEC * Sl;          // channel c0, entry 0 of this lane
+  const int lbase = tid * VEC * Sl;          // DS: channel c0, entry 0 of this lane
   const int off = SPEC ? acc - 1 : 0;
   u32x4 raw[H + QM];
 #pragma unroll
   for (int u = 0; u < H; ++u) {
     raw[u] = u32x4{0, 0, 0, 0};
     if (hist && lane_ok) {
+      if (sd) {
+        raw[u] = region[(off + u) * kBlock + tid];
+      } else {
 #pragma unroll
-      for (int ch = 0; ch < VEC; ++ch) E::set(raw[u], ch, (uint32_t)le[lbase + ch * Sl + off + u]);
+        for (int ch = 0; ch < VEC; ++ch) E::set(raw[u], ch, (uint32_t)le[lbase + ch * Sl + off + u]);
+      }
     }
   }
 #pragma unroll
@@ -174,7 +192,25 @@ __global__ __launch_bounds__(kBlock) void conv_rollbuf(ConvArgs a) {
       }
     }
     // new buffer contents, in place in the lane's own entries
-    if (valid) {
+    if (valid && sd) {
+      if constexpr (SPEC) {
+        // ascending j reads entry acc + j > j before it is overwritten
+        for (int j = 0; j < Sl - q; ++j) region[j * kBlock + tid] = region[(acc + j) * kBlock + tid];
+#pragma unroll
+        for (int u = 0; u < QM; ++u)
+          if (u < q) region[(Sl - q + u) * kBlock + tid] = xr[u];
+      } else {
+        // window = ext[q .. q+H) = raw[q .. q+H); entries H .. S-1 keep their values
+#pragma unroll
+        for (int j = 0; j < H; ++j) {
+          u32x4 val = u32x4{0, 0, 0, 0};
+#pragma unroll
+          for (int e = 0; e < H + QM; ++e)
+            if (e == q + j) val = raw[e];
+          region[j * kBlock + tid] = val;
+        }
+      }
+    } else if (valid) {
 #pragma unroll
       for (int ch = 0; ch < VEC; ++ch) {
         St* row = le + lbase + ch * Sl;
@@ -204,7 +240,12 @@ __global__ __launch_bounds__(kBlock) void conv_rollbuf(ConvArgs a) {
     }
   }
   __syncthreads();
-  if (valid) {
+  if (valid && sd) {
+    St* dp = (St*)a.pool + (int64_t)slot * Sl * a.C + c0;
+#pragma unroll
+    for (int k = 0; k < kSpecSMax; ++k)
+      if (k < Sl && lane_ok) st16_stream(dp + (int64_t)k * a.C, region[k * kBlock + tid]);
+  } else if (valid) {
     St* dp = (St*)a.pool + ((int64_t)slot * a.C + cbase) * Sl;
 #pragma unroll
     for (int k = 0; k < kSpecSMax; ++k) {
@@ -234,7 +275,12 @@ __global__ __launch_bounds__(kBlock) void conv_spec_generic(ConvArgs a, int K, i
   const int32_t slot = a.slots[(int64_t)r * a.slot_stride];
   const bool valid = slot >= 0 && slot < a.num_slots;
   const int acc = min(max(a.num_acc[r], 1), min(q, Sl - H + 1));
-  St* sp = (St*)a.pool + ((int64_t)(valid ? slot : 0) * a.C + c) * Sl;
+  // state entry u of this channel (DS or SD pool)
+  const int32_t vs = valid ? slot : 0;
+  auto sref = [&](int u) -> St& {
+    St* pool = (St*)a.pool;
+    return a.sd ? pool[((int64_t)vs * Sl + u) * a.C + c] : pool[((int64_t)vs * a.C + c) * Sl + u];
+  };
   // the request's token u in x / out (through the row map when one is given)
   auto pr = [&](int u) -> int64_t { return phys_row(a, (int64_t)r * q + u); };
   for (int t = 0; t < q; ++t) {
@@ -243,7 +289,7 @@ __global__ __launch_bounds__(kBlock) void conv_spec_generic(ConvArgs a, int K, i
       const int p = t - (K - 1 - k) * D;
       float v = 0.f;
       if (p >= 0) v = widen<E>(ld_el<E>((const St*)a.x + pr(p) * a.x_rs + c));
-      else if (valid) v = widen<E>(ld_el<E>(sp + acc - 1 + H + p));
+      else if (valid) v = widen<E>((uint32_t)sref(acc - 1 + H + p));
       accf = __builtin_fmaf(wt[k], v, accf);
     }
     if (SILU) accf = silu(accf);
@@ -253,8 +299,8 @@ __global__ __launch_bounds__(kBlock) void conv_spec_generic(ConvArgs a, int K, i
     ((St*)a.out)[ot * a.out_rs + c] = narrow<E>(accf);
   }
   if (valid) {
-    for (int j = 0; j < Sl - q; ++j) sp[j] = sp[acc + j];
-    for (int u = 0; u < q; ++u) sp[Sl - q + u] = *((const St*)a.x + pr(u) * a.x_rs + c);
+    for (int j = 0; j < Sl - q; ++j) sref(j) = sref(acc + j);
+    for (int u = 0; u < q; ++u) sref(Sl - q + u) = *((const St*)a.x + pr(u) * a.x_rs + c);
   }
 }
 

@@ -67,7 +67,8 @@ def run_conv_case(case, *, pool=None, x_pad: int = 0, slot_2d: int = 0, stream=N
     if case.num_decodes:
         dh = None if case.decode_h is None else dev(np.asarray(case.decode_h, np.uint8))
         scs.sc_conv_update(xd[:nd], od[:nd], wd, bd, pd, slots(case.decode_slots), dh,
-                           q=case.q, dilation=case.d, activation=case.act, stream=stream)
+                           q=case.q, dilation=case.d, activation=case.act,
+                           state_layout=case.layout, stream=stream)
     if case.num_prefills:
         ck = None
         if case.ckpt_grid:
@@ -76,7 +77,7 @@ def run_conv_case(case, *, pool=None, x_pad: int = 0, slot_2d: int = 0, stream=N
                                    slots(case.prefill_slots),
                                    dev(np.asarray(case.prefill_h, np.uint8)),
                                    dilation=case.d, activation=case.act, ckpt=ck,
-                                   stream=stream)
+                                   state_layout=case.layout, stream=stream)
     torch.cuda.synchronize()
     return host(od.contiguous()), host(pd)
 
@@ -100,7 +101,8 @@ def run_spec_case(case, num_accepted, *, pool=None, x_pad: int = 0, stream=None)
     scs.sc_conv_update_spec(xd, od, dev(case.w), None if case.bias is None else dev(case.bias),
                             pd, dev(np.asarray(case.decode_slots, np.int32)),
                             dev(np.asarray(num_accepted, np.int32)), q=case.q,
-                            dilation=case.d, activation=case.act, stream=stream)
+                            dilation=case.d, activation=case.act, state_layout=case.layout,
+                            stream=stream)
     torch.cuda.synchronize()
     return host(od.contiguous()), host(pd)
 
@@ -197,7 +199,7 @@ def run_fused_case(case, xp, perm, *, resid=None, outer=None, pool=None, num_acc
     tok = dev(np.asarray(perm, np.int32))
     nd = case.num_decode_tokens
     kw = dict(accumulate=resid is not None, outer_residual=ou, dilation=case.d,
-              activation=case.act)
+              activation=case.act, state_layout=case.layout)
     if case.num_decodes:
         if num_accepted is not None:
             scs.sc_conv_update_spec(xd, od, wd, bd, pd, dev(np.asarray(case.decode_slots, np.int32)),

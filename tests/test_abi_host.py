@@ -78,6 +78,7 @@ def spec(d, *, x=P, out=P2, w=P, pool=P, num_slots=4, slots=P, acc=P, batch=2, q
     (dict(state_len=2), CAPACITY),                 # (4-1)*1 = 3 needed
     (dict(dilation=3, state_len=8), CAPACITY),     # 9 needed
     (dict(state_len=(1 << 20) + 1), INVALID),
+    (dict(state_layout=2), INVALID),
 ])
 def test_descriptor_validation(kw, status):
     assert prefill(desc(**kw)) == status
