@@ -106,28 +106,38 @@ def lib():
 # ---------------------------------------------------------------------------
 # marshalling helpers
 # ---------------------------------------------------------------------------
+_torch_mod = None
+_dtype_codes = None
+
+
 def _torch():
-    import torch
-    return torch
+    global _torch_mod
+    if _torch_mod is None:
+        import torch
+        _torch_mod = torch
+    return _torch_mod
 
 
 def _ptr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
-def _stream(stream) -> Optional[int]:
+def _stream(stream, like=None) -> Optional[int]:
+    """Raw HIP stream: the given one, else torch's current stream on the device
+    of tensor `like` (or the current device)."""
+    if stream is not None:
+        return stream.cuda_stream
     torch = _torch()
-    s = stream if stream is not None else torch.cuda.current_stream()
-    return s.cuda_stream
+    dev = like.get_device() if like is not None else torch.cuda.current_device()
+    return torch._C._cuda_getCurrentRawStream(dev)
 
 
 def _dtype_code(t) -> int:
-    torch = _torch()
-    if t.dtype == torch.bfloat16:
-        return SC_DTYPE_BF16
-    if t.dtype == torch.float32:
-        return SC_DTYPE_F32
-    return -1
+    global _dtype_codes
+    if _dtype_codes is None:
+        torch = _torch()
+        _dtype_codes = {torch.bfloat16: SC_DTYPE_BF16, torch.float32: SC_DTYPE_F32}
+    return _dtype_codes.get(t.dtype, -1)
 
 
 def _rows(t, name):
@@ -232,7 +242,7 @@ def sc_conv_prefill_varlen(x, out, weight, bias, state_pool, query_start_loc,
         _flags(has_initial_state, "has_initial_state"),
         query_start_loc.shape[0] - 1,
         x.shape[0] if token_indices is None else token_indices.shape[0], cd,
-        _fuse(x, out, token_indices, accumulate, outer_residual), _stream(stream))
+        _fuse(x, out, token_indices, accumulate, outer_residual), _stream(stream, x))
     _check("sc_conv_prefill_varlen", st)
 
 
@@ -254,7 +264,7 @@ def sc_conv_update(x, out, weight, bias, state_pool, state_indices,
         ctypes.byref(desc), _ptr(x), _ptr(out), _ptr(weight), _ptr(bias),
         _ptr(state_pool), state_pool.shape[0], _index(state_indices, "state_indices")[0],
         _flags(has_initial_state, "has_initial_state"), B, q,
-        _fuse(x, out, token_indices, accumulate, outer_residual), _stream(stream))
+        _fuse(x, out, token_indices, accumulate, outer_residual), _stream(stream, x))
     _check("sc_conv_update", st)
 
 
@@ -277,7 +287,7 @@ def sc_conv_update_spec(x, out, weight, bias, state_pool, state_indices, num_acc
         ctypes.byref(desc), _ptr(x), _ptr(out), _ptr(weight), _ptr(bias),
         _ptr(state_pool), state_pool.shape[0], _index(state_indices, "state_indices")[0],
         _ptr(num_accepted_tokens), rows // q, q,
-        _fuse(x, out, token_indices, accumulate, outer_residual), _stream(stream))
+        _fuse(x, out, token_indices, accumulate, outer_residual), _stream(stream, x))
     _check("sc_conv_update_spec", st)
 
 
@@ -287,7 +297,7 @@ def sc_state_gather(state_pool, idx, dense, *, stream=None):
         dense[0].numel() * dense.element_size()
     p, s = _index(idx, "idx")
     st = lib().sc_state_gather(_ptr(state_pool), state_pool.shape[0], row, p, s,
-                               idx.shape[0], _ptr(dense), _stream(stream))
+                               idx.shape[0], _ptr(dense), _stream(stream, dense))
     _check("sc_state_gather", st)
 
 
@@ -296,7 +306,7 @@ def sc_state_scatter(dense, idx, state_pool, *, stream=None):
     row = dense[0].numel() * dense.element_size() if dense.shape[0] else 1
     p, s = _index(idx, "idx")
     st = lib().sc_state_scatter(_ptr(dense), row, p, s, idx.shape[0], _ptr(state_pool),
-                                state_pool.shape[0], _stream(stream))
+                                state_pool.shape[0], _stream(stream, dense))
     _check("sc_state_scatter", st)
 
 
@@ -328,7 +338,7 @@ def sc_cca_qk_conv(q, k, v_cur, v_del, out, w_dw, b_dw, w_gr, b_gr, delayed_init
         _ptr(w_dw), _ptr(b_dw), _ptr(w_gr), _ptr(b_gr), _ptr(delayed_init),
         _ptr(conv_state), _ptr(delayed_state), conv_state.shape[0], nd, dp, npf,
         _ptr(prefill_qsl), pp, _flags(prefill_has_initial_state, "prefill_has_initial_state"),
-        q.shape[0], _stream(stream))
+        q.shape[0], _stream(stream, q))
     _check("sc_cca_qk_conv", st)
 
 

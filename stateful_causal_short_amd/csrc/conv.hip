@@ -29,11 +29,11 @@ namespace sc {
 // (coalesced across lanes); in the DS pool (num_slots, C, S) with S == H the
 // lane's entries are H contiguous vectors in (channel, entry) order and are
 // transposed in registers.
-template <class E, int H>
+template <class E, int H, bool SD>
 __device__ __forceinline__ void load_state_rows(const ConvArgs& a, int32_t slot, int c0,
                                                 u32x4* rows) {
   using S = typename E::S;
-  if (a.sd) {
+  if constexpr (SD) {
     const S* base = (const S*)a.pool + (int64_t)slot * a.S * a.C + c0;
 #pragma unroll
     for (int u = 0; u < H; ++u) rows[u] = ld16(base + (int64_t)u * a.C);
@@ -51,11 +51,11 @@ __device__ __forceinline__ void load_state_rows(const ConvArgs& a, int32_t slot,
   }
 }
 
-template <class E, int H>
+template <class E, int H, bool SD>
 __device__ __forceinline__ void store_state_rows(const ConvArgs& a, int32_t slot, int c0,
                                                  const u32x4* rows) {
   using S = typename E::S;
-  if (a.sd) {
+  if constexpr (SD) {
     S* base = (S*)a.pool + (int64_t)slot * a.S * a.C + c0;
 #pragma unroll
     for (int u = 0; u < H; ++u) st16(base + (int64_t)u * a.C, rows[u]);
@@ -73,22 +73,22 @@ __device__ __forceinline__ void store_state_rows(const ConvArgs& a, int32_t slot
 
 // Store the window of request rows [p-H, p) (all >= 0) into `slot`; xrow(t) is
 // the lane's channel vector in the request's row t.
-template <class E, int H, class XRow>
+template <class E, int H, bool SD, class XRow>
 __device__ __forceinline__ void store_window_rows(const ConvArgs& a, int32_t slot, int c0,
                                                   XRow xrow, int p) {
   u32x4 r[H];
 #pragma unroll
   for (int jj = 0; jj < H; ++jj) r[jj] = ld16(xrow(p - H + jj));
-  store_state_rows<E, H>(a, slot, c0, r);
+  store_state_rows<E, H, SD>(a, slot, c0, r);
 }
 
 // New state = ext[L .. L+H) for a request of runtime length L >= 1, where ext
 // is [old rows (H), x rows].
-template <class E, int H, class XRow>
+template <class E, int H, bool SD, class XRow>
 __device__ __forceinline__ void write_state_rows(const ConvArgs& a, int32_t slot, int c0,
                                                  const u32x4* old, int L, XRow xrow) {
   if (L >= H) {
-    store_window_rows<E, H>(a, slot, c0, xrow, L);
+    store_window_rows<E, H, SD>(a, slot, c0, xrow, L);
     return;
   }
   // 1 <= L < H: entries jj < H-L keep old[L + jj], the rest are the L tokens
@@ -102,13 +102,13 @@ __device__ __forceinline__ void write_state_rows(const ConvArgs& a, int32_t slot
       if (m + jj < H && m == L) val = old[m + jj];
     r[jj] = val;
   }
-  store_state_rows<E, H>(a, slot, c0, r);
+  store_state_rows<E, H, SD>(a, slot, c0, r);
 }
 
 // ---------------------------------------------------------------------------
 // fast kernel: compile-time K, D; QC > 0 is a compile-time update length
 // ---------------------------------------------------------------------------
-template <class E, int K, int D, int U, bool SILU, int QC>
+template <class E, int K, int D, int U, bool SILU, int QC, bool SD>
 __global__ __launch_bounds__(kBlock) void conv_fast(ConvArgs a) {
 #if SC_LDS_PAD > 0
   __shared__ uint8_t occupancy_pad[SC_LDS_PAD];
@@ -142,7 +142,7 @@ __global__ __launch_bounds__(kBlock) void conv_fast(ConvArgs a) {
   u32x4 old[H];   // history rows (entry u of this lane's channels)
 #pragma unroll
   for (int v = 0; v < H; ++v) old[v] = u32x4{0, 0, 0, 0};
-  if (w.j == 0 && w.h) load_state_rows<E, H>(a, w.slot, c0, old);
+  if (w.j == 0 && w.h) load_state_rows<E, H, SD>(a, w.slot, c0, old);
 
   if constexpr (QC > 0) {
     // Update of exactly QC tokens (the host launches this only when q == QC).
@@ -167,7 +167,7 @@ __global__ __launch_bounds__(kBlock) void conv_fast(ConvArgs a) {
         const int e = QC + jj;   // ext index of new-state entry jj
         nr[jj] = e < H ? old[e] : xr[e - H];
       }
-      store_state_rows<E, H>(a, w.slot, c0, nr);
+      store_state_rows<E, H, SD>(a, w.slot, c0, nr);
     }
   } else {
     float win[H + U][VEC];
@@ -201,7 +201,7 @@ __global__ __launch_bounds__(kBlock) void conv_fast(ConvArgs a) {
         for (int ch = 0; ch < VEC; ++ch) win[i][ch] = win[i + U][ch];
     }
     auto xrow = [&](int t) { return xb + (int64_t)t * xrs; };
-    if (w.j == 0 && w.valid) write_state_rows<E, H>(a, w.slot, c0, old, w.L, xrow);
+    if (w.j == 0 && w.valid) write_state_rows<E, H, SD>(a, w.slot, c0, old, w.L, xrow);
     if (a.ckpt_grid > 0 && a.qsl != nullptr) {
       // checkpoints at p = m*g with t0 < p <= t1: the chunk holding token p-1
       const int g = a.ckpt_grid;
@@ -209,7 +209,7 @@ __global__ __launch_bounds__(kBlock) void conv_fast(ConvArgs a) {
       for (int m = w.t0 / g + 1; m <= cnt && (int64_t)m * g <= w.t1; ++m) {
         const int32_t dst = a.ckpt_slots[cu0 + m - 1];
         if (dst < 0 || dst >= a.num_slots) continue;
-        store_window_rows<E, H>(a, dst, c0, xrow, m * g);
+        store_window_rows<E, H, SD>(a, dst, c0, xrow, m * g);
       }
     }
   }
@@ -223,7 +223,7 @@ __global__ __launch_bounds__(kBlock) void conv_fast(ConvArgs a) {
 // reused by every output that needs it. UPDATE: requests of exactly U tokens.
 // ---------------------------------------------------------------------------
 
-template <int K, int D, int U, bool SILU, bool UPDATE, bool FUSE>
+template <int K, int D, int U, bool SILU, bool UPDATE, bool FUSE, bool SD>
 __global__ __launch_bounds__(kBlock) void conv_pairs(ConvArgs a) {
 #if SC_LDS_PAD > 0
   __shared__ uint8_t occupancy_pad[SC_LDS_PAD];
@@ -312,7 +312,7 @@ __global__ __launch_bounds__(kBlock) void conv_pairs(ConvArgs a) {
     valid = slot >= 0 && slot < a.num_slots;
     hflag = valid && (a.has_init ? a.has_init[r] != 0 : true);
   }
-  if (hflag) load_state_rows<E, H>(a, slot, c0, old);   // history rows
+  if (hflag) load_state_rows<E, H, SD>(a, slot, c0, old);   // history rows
   Work w;
   w.r = r;
   w.j = j;
@@ -375,9 +375,9 @@ __global__ __launch_bounds__(kBlock) void conv_pairs(ConvArgs a) {
 
   if (w.j == 0 && w.valid) {
     if constexpr (UPDATE) {
-      store_state_rows<E, H>(a, slot, c0, raw + U);   // new state = ext[U .. U+H)
+      store_state_rows<E, H, SD>(a, slot, c0, raw + U);   // new state = ext[U .. U+H)
     } else {
-      write_state_rows<E, H>(a, slot, c0, old, w.L, xrow);
+      write_state_rows<E, H, SD>(a, slot, c0, old, w.L, xrow);
     }
   }
   if (!UPDATE && a.ckpt_grid > 0 && a.qsl != nullptr) {
@@ -386,7 +386,7 @@ __global__ __launch_bounds__(kBlock) void conv_pairs(ConvArgs a) {
     for (int m = w.t0 / g + 1; m <= cnt && (int64_t)m * g <= w.t1; ++m) {
       const int32_t dst = a.ckpt_slots[cu0 + m - 1];
       if (dst < 0 || dst >= a.num_slots) continue;
-      store_window_rows<E, H>(a, dst, c0, xrow, m * g);
+      store_window_rows<E, H, SD>(a, dst, c0, xrow, m * g);
     }
   }
 }
@@ -399,7 +399,7 @@ __global__ __launch_bounds__(kBlock) void conv_pairs(ConvArgs a) {
 // weights are loaded once for the R requests. Same tap pairing and dot2 order
 // as conv_pairs, so a decode step equals the matching prefill token bit for bit.
 // ---------------------------------------------------------------------------
-template <int K, int D, int Q, int R, bool SILU, bool FUSE>
+template <int K, int D, int Q, int R, bool SILU, bool FUSE, bool SD>
 __global__ __launch_bounds__(kBlock) void conv_update_pairs(ConvArgs a) {
   using E = BF16;
   using S = E::S;
@@ -477,7 +477,7 @@ __global__ __launch_bounds__(kBlock) void conv_update_pairs(ConvArgs a) {
     valid[rr] = slot[rr] >= 0 && slot[rr] < a.num_slots;
     hflag[rr] = valid[rr] && (a.has_init ? a.has_init[r] != 0 : true);
   }
-  if (a.sd) {
+  if constexpr (SD) {
     // SD pool: entry k of the lane's channels is one vector, unit stride across lanes
 #pragma unroll
     for (int rr = 0; rr < R; ++rr) {
@@ -506,7 +506,7 @@ __global__ __launch_bounds__(kBlock) void conv_update_pairs(ConvArgs a) {
   for (int rr = 0; rr < R; ++rr) {
     const int r = grp * R + rr;
     u32x4 raw[H + Q];
-    if (a.sd) {
+    if constexpr (SD) {
 #pragma unroll
       for (int u = 0; u < H; ++u) raw[u] = st[rr][u];
     } else {
@@ -556,7 +556,7 @@ __global__ __launch_bounds__(kBlock) void conv_update_pairs(ConvArgs a) {
       }
     }
     // new state = ext[Q .. Q+H)
-    if (a.sd) {
+    if constexpr (SD) {
       if (valid[rr] && lane_ok) {
         S* dp = (S*)a.pool + (int64_t)slot[rr] * a.S * a.C + c0;
 #pragma unroll
@@ -667,16 +667,22 @@ bool pairs_shape(int K, int D) {
   return (K == 4 && (D == 1 || D == 2 || D == 3)) || (K == 2 && D == 1);
 }
 
-template <class E, int K, int D, bool SILU>
-hipError_t launch_kd(const ConvArgs& a, int qc, dim3 grid, hipStream_t s) {
+template <class E, int K, int D, bool SILU, bool SD>
+hipError_t launch_kd_l(const ConvArgs& a, int qc, dim3 grid, hipStream_t s) {
   constexpr int U = ((K - 1) * D <= 4) ? SC_UNROLL_SMALL_H : SC_UNROLL_LARGE_H;
   switch (qc) {
-    case 1: hipLaunchKernelGGL((conv_fast<E, K, D, U, SILU, 1>), grid, dim3(kBlock), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((conv_fast<E, K, D, U, SILU, 2>), grid, dim3(kBlock), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((conv_fast<E, K, D, U, SILU, 4>), grid, dim3(kBlock), 0, s, a); break;
-    default: hipLaunchKernelGGL((conv_fast<E, K, D, U, SILU, 0>), grid, dim3(kBlock), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((conv_fast<E, K, D, U, SILU, 1, SD>), grid, dim3(kBlock), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((conv_fast<E, K, D, U, SILU, 2, SD>), grid, dim3(kBlock), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((conv_fast<E, K, D, U, SILU, 4, SD>), grid, dim3(kBlock), 0, s, a); break;
+    default: hipLaunchKernelGGL((conv_fast<E, K, D, U, SILU, 0, SD>), grid, dim3(kBlock), 0, s, a); break;
   }
   return hipGetLastError();
+}
+
+template <class E, int K, int D, bool SILU>
+hipError_t launch_kd(const ConvArgs& a, int qc, dim3 grid, hipStream_t s) {
+  return a.sd ? launch_kd_l<E, K, D, SILU, true>(a, qc, grid, s)
+              : launch_kd_l<E, K, D, SILU, false>(a, qc, grid, s);
 }
 
 // tokens per one-pass prefill chunk for history length H (must be >= H)
@@ -684,16 +690,22 @@ constexpr int pairs_chunk(int H) { return H <= 4 ? SC_PAIRS_CHUNK_SMALL : (H <= 
 // requests per update workgroup
 constexpr int update_reqs(int H, int Q) { return (H <= 4 && Q == 1) ? SC_UPDATE_REQS : (H <= 4 ? 2 : (Q == 1 ? 2 : 1)); }
 
-template <int K, int D, bool SILU, bool FUSE>
-hipError_t launch_pairs_kd(const ConvArgs& a, int qc, dim3 grid, hipStream_t s) {
+template <int K, int D, bool SILU, bool FUSE, bool SD>
+hipError_t launch_pairs_l(const ConvArgs& a, int qc, dim3 grid, hipStream_t s) {
   constexpr int H = (K - 1) * D;
   switch (qc) {
-    case 1: hipLaunchKernelGGL((conv_update_pairs<K, D, 1, update_reqs(H, 1), SILU, FUSE>), grid, dim3(kBlock), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((conv_update_pairs<K, D, 2, update_reqs(H, 2), SILU, FUSE>), grid, dim3(kBlock), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((conv_update_pairs<K, D, 4, update_reqs(H, 4), SILU, FUSE>), grid, dim3(kBlock), 0, s, a); break;
-    default: hipLaunchKernelGGL((conv_pairs<K, D, pairs_chunk(H), SILU, false, FUSE>), grid, dim3(kBlock), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((conv_update_pairs<K, D, 1, update_reqs(H, 1), SILU, FUSE, SD>), grid, dim3(kBlock), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((conv_update_pairs<K, D, 2, update_reqs(H, 2), SILU, FUSE, SD>), grid, dim3(kBlock), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((conv_update_pairs<K, D, 4, update_reqs(H, 4), SILU, FUSE, SD>), grid, dim3(kBlock), 0, s, a); break;
+    default: hipLaunchKernelGGL((conv_pairs<K, D, pairs_chunk(H), SILU, false, FUSE, SD>), grid, dim3(kBlock), 0, s, a); break;
   }
   return hipGetLastError();
+}
+
+template <int K, int D, bool SILU, bool FUSE>
+hipError_t launch_pairs_kd(const ConvArgs& a, int qc, dim3 grid, hipStream_t s) {
+  return a.sd ? launch_pairs_l<K, D, SILU, FUSE, true>(a, qc, grid, s)
+              : launch_pairs_l<K, D, SILU, FUSE, false>(a, qc, grid, s);
 }
 
 template <bool SILU, bool FUSE>
