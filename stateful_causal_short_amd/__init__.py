@@ -17,6 +17,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libstatefulconv.so")
 
 SC_OK = 0
+SC_ABI_VERSION = 2   # the struct layouts and signatures below
 STATUS = {0: "SC_OK", -1: "SC_ERR_NULL_ARG", -2: "SC_ERR_INVALID_ARG",
           -3: "SC_ERR_DTYPE", -4: "SC_ERR_STATE_CAPACITY",
           -5: "SC_ERR_UNSUPPORTED", -6: "SC_ERR_HIP"}
@@ -99,6 +100,9 @@ def lib():
         L.sc_status_string.argtypes = [I32]
         L.sc_abi_version.restype = I32
         L.sc_abi_version.argtypes = []
+        if L.sc_abi_version() != SC_ABI_VERSION:
+            raise RuntimeError(f"{LIB_PATH} has ABI version {L.sc_abi_version()}, the binding "
+                               f"expects {SC_ABI_VERSION}: rebuild the library")
         _lib = L
     return _lib
 

@@ -340,11 +340,14 @@ struct CcaSmem {
   int row_src[2][MT];                   // prefill request index, or -2 - t for decode row t
 };
 
-// Waves per SIMD the main kernel is compiled for: 2 (one 8-wave workgroup per
-// CU). Phase A's fp32 working set keeps the kernel above the 128 registers
-// that a second resident workgroup would need.
-template <int T0>
-constexpr int cca_waves_per_simd() { return SC_CCA_MIN_WAVES; }
+// Waves per SIMD the main kernel is compiled for: 4 (two resident 8-wave
+// workgroups per CU, so one's phase A overlaps the other's MFMA and stores)
+// for depthwise widths up to 2 and at most 4 q heads per kv head; wider
+// windows and larger groups need more than 128 registers and run one
+// workgroup per CU.
+__host__ __device__ constexpr int cca_waves_per_simd(int t0, int gmax) {
+  return (t0 <= 2 && gmax <= 4) ? SC_CCA_MIN_WAVES : 2;
+}
 
 // Row info of the tile starting at token ta (threads 0 .. 31, one row each).
 // `cur` is the thread's prefill request index from its previous (earlier)
@@ -409,6 +412,9 @@ __device__ __forceinline__ void cca_persist_body(const CcaArgs& a, CcaSmem<T0>& 
   constexpr int RROW = SM::RROW;
   constexpr int NR = T0 + 1;           // raw rows per lane: i-T0 .. i
   constexpr bool isk = ISK;
+  // tiles of loads in flight ahead of the one computed: the k head also
+  // holds the bundle's q rows per tile, so it keeps one tile in flight
+  constexpr int AHEAD = ISK ? 1 : SC_CCA_AHEAD;
 
   const int NG = a.nq + a.nkv, G = a.nq / a.nkv;
   const int C = NG * HD, vd = a.nkv * HD / 2, nvv = vd / 8;
@@ -417,11 +423,13 @@ __device__ __forceinline__ void cca_persist_body(const CcaArgs& a, CcaSmem<T0>& 
   const int tid = (int)threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int v = tid & 15, i = tid >> 4;            // depthwise: channel vector, tile row
   const bool use_lds_qsl = a.num_prefills > 0 && a.num_prefills + 1 <= kQslCache;
-  // value columns of this group: vectors vv = grp + k * NG of 2 * nvv; item tid = (row, k)
-  const int mine = (2 * nvv - grp + NG - 1) / NG;
+  // value columns of this group: vectors vv = grp + k * nq of 2 * nvv; item tid = (row, k)
+  // (dealt over the nq q-head groups only; the k head's workgroups carry the
+  // bundle's q rows instead)
+  const int mine = isk ? 0 : (2 * nvv - grp + a.nq - 1) / a.nq;
   const int vr = tid / max(mine, 1), vk = tid - vr * max(mine, 1);
   const bool vitem = tid < MT * mine;
-  const int vvv = grp + vk * NG;                   // this thread's value vector
+  const int vvv = grp + vk * a.nq;                 // this thread's value vector
   const int64_t qrs = a.q_rs * 2, krs = a.k_rs * 2, ors = a.out_rs * 2;   // bytes
   const int64_t vcb = a.vc_rs * 2, vdb = a.vd_rs * 2;
   const int64_t srs = isk ? krs : qrs;
@@ -500,8 +508,10 @@ __device__ __forceinline__ void cca_persist_body(const CcaArgs& a, CcaSmem<T0>& 
       for (int qi = 0; qi < GMAX; ++qi)
         f.r[qi] = bld16(qbuf, qi < G ? q_lane + ta * qrs32 + (uint32_t)(qi * HD * 2) : kOff);
     }
-    if (vvv < nvv) f.val = bld16_stream(vcbuf, vitem ? v_lane + ta * (uint32_t)vcb : kOff);
-    else f.val = bld16(vdbuf, vitem ? v_lane + ta * (uint32_t)vdb : kOff);
+    if constexpr (!isk) {
+      if (vvv < nvv) f.val = bld16_stream(vcbuf, vitem ? v_lane + ta * (uint32_t)vcb : kOff);
+      else f.val = bld16(vdbuf, vitem ? v_lane + ta * (uint32_t)vdb : kOff);
+    }
   };
 
   int rcur = 0;   // request cursor of this thread's row (threads 0 .. 31)
@@ -511,88 +521,101 @@ __device__ __forceinline__ void cca_persist_body(const CcaArgs& a, CcaSmem<T0>& 
     const int* rp = sm.row_p[cur];
     const int* rsrc_ = sm.row_src[cur];
     // ---- (A) depthwise rows, the request-start and tile-start side rows, residual ----
+    // The lane's 8 channels are done in two halves of 4, one after the other,
+    // which halves the fp32 working set of this phase.
     {
-      u32x4 wq[T0];
-#pragma unroll
-      for (int s = 0; s < T0; ++s) wq[s] = *(const u32x4*)(sm.w1 + (v * 8) * T0 + s * 8);
-      const u32x4 b1q = *(const u32x4*)(sm.b1 + v * 8), b2q = *(const u32x4*)(sm.b2 + v * 8);
-      auto w1 = [&](int tap, int ch) -> float {
-        const int el = ch * T0 + tap;
-        return bf2f(BF16::get(wq[el / 8], el % 8));
-      };
-      auto xe = [&](int s, int ch) -> float { return bf2f(BF16::get(f.x[s], ch)); };
       const int p = rp[i];
-      // depthwise of this row's request at position pos; tap `tap` reads raw
-      // slot base + tap when its ext position is >= 0, else the request's
-      // history (zeros without state), taken only near a request's start
-      auto dw = [&](int pos, int base) -> u32x4 {
-        float d[8];
 #pragma unroll
-        for (int ch = 0; ch < 8; ++ch) d[ch] = bf2f(BF16::get(b1q, ch));
-        if (pos >= T0 - 1) {
+      for (int hf = 0; hf < 2; ++hf) {
+        const int c4 = 4 * hf;                        // first channel of the half
+        // depthwise weights (ch * T0 + tap), biases of the half
+        uint16_t wl[4 * T0];
 #pragma unroll
-          for (int tap = 0; tap < T0; ++tap)
+        for (int k = 0; k < 4 * T0; k += 4) {
+          const uint2 w4 = *(const uint2*)(sm.w1 + (v * 8 + c4) * T0 + k);
+          wl[k] = (uint16_t)(w4.x & 0xFFFFu);
+          wl[k + 1] = (uint16_t)(w4.x >> 16);
+          wl[k + 2] = (uint16_t)(w4.y & 0xFFFFu);
+          wl[k + 3] = (uint16_t)(w4.y >> 16);
+        }
+        const uint2 b1h = *(const uint2*)(sm.b1 + v * 8 + c4);
+        const uint2 b2h = *(const uint2*)(sm.b2 + v * 8 + c4);
+        auto half_el = [&](uint2 w, int ch) -> float {
+          const uint32_t word = ch < 2 ? w.x : w.y;
+          return bf2f((ch & 1) ? (word >> 16) : (word & 0xFFFFu));
+        };
+        auto w1 = [&](int tap, int ch) -> float { return bf2f(wl[ch * T0 + tap]); };
+        auto xe = [&](int s, int ch) -> float { return bf2f(BF16::get(f.x[s], c4 + ch)); };
+        // depthwise of this row's request at position pos for the half; tap
+        // `tap` reads raw slot base + tap when its ext position is >= 0, else
+        // the request's history (zeros without state)
+        auto dw = [&](int pos, int base) -> uint2 {
+          float d[4];
 #pragma unroll
-            for (int ch = 0; ch < 8; ++ch) d[ch] = __builtin_fmaf(w1(tap, ch), xe(base + tap, ch), d[ch]);
-        } else {
-          int32_t slot;
-          bool hn;
-          cca_row_state(a, rsrc_[i], slot, hn);
-          const uint16_t* hp = (const uint16_t*)a.conv_state +
-                               ((int64_t)(hn ? slot : 0) * C + cbase + v * 8) * N;
-          u32x4 hist[N];
+          for (int ch = 0; ch < 4; ++ch) d[ch] = half_el(b1h, ch);
+          if (pos >= T0 - 1) {
 #pragma unroll
-          for (int q = 0; q < N; ++q) hist[q] = hn ? ld16(hp + q * 8) : u32x4{0, 0, 0, 0};
+            for (int tap = 0; tap < T0; ++tap)
 #pragma unroll
-          for (int tap = 0; tap < T0; ++tap) {
-            const int ep = pos - (T0 - 1) + tap;     // ext position of the tap
+              for (int ch = 0; ch < 4; ++ch) d[ch] = __builtin_fmaf(w1(tap, ch), xe(base + tap, ch), d[ch]);
+          } else {
+            // near a request's start: the saved history (global reads, rare)
+            int32_t hslot;
+            bool hn;
+            cca_row_state(a, rsrc_[i], hslot, hn);
+            const uint16_t* hp = (const uint16_t*)a.conv_state +
+                                 ((int64_t)(hn ? hslot : 0) * C + cbase + v * 8) * N;
+            u32x4 hist[N];
 #pragma unroll
-            for (int ch = 0; ch < 8; ++ch) {
-              float x = 0.f;
-              if (ep >= 0) {
-                x = xe(base + tap, ch);
-              } else {
+            for (int q = 0; q < N; ++q) hist[q] = hn ? ld16(hp + q * 8) : u32x4{0, 0, 0, 0};
 #pragma unroll
-                for (int q = 1; q <= N; ++q) {       // position -q = entry N - q
-                  const int el = ch * N + N - q;
-                  if (ep == -q) x = bf2f(BF16::get(hist[el / 8], el % 8));
+            for (int tap = 0; tap < T0; ++tap) {
+              const int ep = pos - (T0 - 1) + tap;   // ext position of the tap
+#pragma unroll
+              for (int ch = 0; ch < 4; ++ch) {
+                float x = xe(base + tap, ch);
+                if (ep < 0) {
+                  x = 0.f;
+#pragma unroll
+                  for (int q = 1; q <= N; ++q) {     // position -q = entry N - q
+                    const int el = (c4 + ch) * N + N - q;
+                    if (ep == -q) x = bf2f(BF16::get(hist[el / 8], el % 8));
+                  }
                 }
+                d[ch] = __builtin_fmaf(w1(tap, ch), x, d[ch]);
               }
-              d[ch] = __builtin_fmaf(w1(tap, ch), x, d[ch]);
             }
           }
+          return uint2{pk_bf16(d[0], d[1]), pk_bf16(d[2], d[3])};
+        };
+        // residual + grouped bias, fp32
+        float y[4];
+        if constexpr (!isk) {
+#pragma unroll
+          for (int ch = 0; ch < 4; ++ch)
+            y[ch] = half_el(b2h, ch) + 0.5f * (xe(T0, ch) + bf2f(BF16::get(f.r[0], c4 + ch)));
+        } else {
+          // the mean over the bundle's q heads, summed in head order
+#pragma unroll
+          for (int ch = 0; ch < 4; ++ch) {
+            float s = 0.f;
+#pragma unroll
+            for (int qi = 0; qi < GMAX; ++qi)
+              if (qi < G) s += bf2f(BF16::get(f.r[qi], c4 + ch));
+            y[ch] = half_el(b2h, ch) + 0.5f * (s / (float)G + xe(T0, ch));
+          }
         }
-        return u32x4{pk_bf16(d[0], d[1]), pk_bf16(d[2], d[3]), pk_bf16(d[4], d[5]),
-                     pk_bf16(d[6], d[7])};
-      };
-      // residual + grouped bias, fp32
-      float y[8];
-      if constexpr (!isk) {
-#pragma unroll
-        for (int ch = 0; ch < 8; ++ch)
-          y[ch] = bf2f(BF16::get(b2q, ch)) + 0.5f * (xe(T0, ch) + bf2f(BF16::get(f.r[0], ch)));
-      } else {
-        // the mean over the bundle's q heads, summed in head order
-#pragma unroll
-        for (int ch = 0; ch < 8; ++ch) {
-          float s = 0.f;
-#pragma unroll
-          for (int qi = 0; qi < GMAX; ++qi)
-            if (qi < G) s += bf2f(BF16::get(f.r[qi], ch));
-          y[ch] = bf2f(BF16::get(b2q, ch)) + 0.5f * (s / (float)G + xe(T0, ch));
+        uint2 cur_dw = {0u, 0u};
+        if (p >= 0) {
+          cur_dw = dw(p, 1);
+          if (p == 0) *(uint2*)(sm.prv + i * AROW + v * 8 + c4) = dw(-1, 0);
         }
+        *(uint2*)(sm.act + (i + 1) * AROW + v * 8 + c4) = cur_dw;
+        *(float4*)(sm.res + i * RROW + v * 8 + c4) = float4{y[0], y[1], y[2], y[3]};
+        // the tile's first row continues a request: its previous position
+        if (i == 0 && p >= 1) *(uint2*)(sm.act + v * 8 + c4) = dw(p - 1, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      u32x4 cur_dw = {0, 0, 0, 0};
-      if (p >= 0) {
-        cur_dw = dw(p, 1);
-        if (p == 0) *(u32x4*)(sm.prv + i * AROW + v * 8) = dw(-1, 0);
-      }
-      *(u32x4*)(sm.act + (i + 1) * AROW + v * 8) = cur_dw;
-      float* rq = sm.res + i * RROW + v * 8;
-      *(float4*)rq = float4{y[0], y[1], y[2], y[3]};
-      *(float4*)(rq + 4) = float4{y[4], y[5], y[6], y[7]};
-      // the tile's first row continues a request: its previous position
-      if (i == 0 && p >= 1) *(u32x4*)(sm.act + v * 8) = dw(p - 1, 0);
     }
     // value item of this tile, then the next tiles' rows and loads
     u32x4 val = f.val;
@@ -600,7 +623,7 @@ __device__ __forceinline__ void cca_persist_body(const CcaArgs& a, CcaSmem<T0>& 
     const int vsrc = vitem ? rsrc_[vr] : -1;
     if (u + 1 < my_tiles) cca_tile_rows(a, tile_ta(u + 1), use_lds_qsl ? sm.qsl_s : a.prefill_qsl,
                                         sm.row_p[cur ^ 1], sm.row_src[cur ^ 1], rcur);
-    if (u + SC_CCA_AHEAD < my_tiles) issue(u + SC_CCA_AHEAD, f);
+    if (u + AHEAD < my_tiles) issue(u + AHEAD, f);
     // store offsets of this tile (row info is rewritten by the next tile)
     const uint32_t ooff = rp[i] >= 0 ? o_lane + ta * ors32 : kOff;
     const uint32_t voff = vp >= 0 ? ov_lane + ta * ors32 : kOff;
@@ -617,23 +640,25 @@ __device__ __forceinline__ void cca_persist_body(const CcaArgs& a, CcaSmem<T0>& 
         bp[th][1] = sm.act + (n + 1) * AROW + 8 * (lane >> 4);
         acc[th] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
-      // B fragments in two batches of 8 LDS reads, each read ahead of its MFMAs
+      // B fragments in batches of 4 LDS reads (2 K steps), each batch read
+      // ahead of its MFMAs
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        u32x4 bv[2][4];
+      for (int kb = 0; kb < 4; ++kb) {
+        u32x4 bv[2][2];
 #pragma unroll
-        for (int k4 = 0; k4 < 4; ++k4)
-#pragma unroll
-          for (int th = 0; th < 2; ++th) bv[th][k4] = *(const u32x4*)(bp[th][half] + k4 * 32);
-#pragma unroll
-        for (int k4 = 0; k4 < 4; ++k4)
+        for (int k2 = 0; k2 < 2; ++k2)
 #pragma unroll
           for (int th = 0; th < 2; ++th)
-            acc[th] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[half * 4 + k4],
-                                                              __builtin_bit_cast(bf16x8, bv[th][k4]),
+            bv[th][k2] = *(const u32x4*)(bp[th][kb >> 1] + ((kb & 1) * 2 + k2) * 32);
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+          for (int th = 0; th < 2; ++th)
+            acc[th] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[kb * 2 + k2],
+                                                              __builtin_bit_cast(bf16x8, bv[th][k2]),
                                                               acc[th], 0, 0, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
       }
     }
 #pragma unroll
@@ -660,32 +685,34 @@ __device__ __forceinline__ void cca_persist_body(const CcaArgs& a, CcaSmem<T0>& 
     __syncthreads();
     // full 256-byte row segments of the group's output columns, and the value item
     bst16_stream(obuf, ooff, *(const u32x4*)(sm.ost + i * AROW + v * 8));
-    bst16_stream(obuf, voff, val);
+    if constexpr (!isk) bst16_stream(obuf, voff, val);
   };
 
-#if SC_CCA_AHEAD == 1
-  Pref fa;
-  issue(0, fa);
-  __syncthreads();   // qsl and parameters visible
-  cca_tile_rows(a, tile_ta(0), use_lds_qsl ? sm.qsl_s : a.prefill_qsl, sm.row_p[0], sm.row_src[0], rcur);
-  __syncthreads();
-  for (int u = 0; u < my_tiles; ++u) tile(u, fa);
-#else
-  Pref fa, fb;
-  issue(0, fa);
-  if (my_tiles > 1) issue(1, fb);
-  __syncthreads();   // qsl and parameters visible
-  cca_tile_rows(a, tile_ta(0), use_lds_qsl ? sm.qsl_s : a.prefill_qsl, sm.row_p[0], sm.row_src[0], rcur);
-  __syncthreads();
-  for (int u = 0; u < my_tiles; u += 2) {
-    tile(u, fa);
-    if (u + 1 < my_tiles) tile(u + 1, fb);
+  if constexpr (AHEAD == 1) {
+    Pref fa;
+    issue(0, fa);
+    __syncthreads();   // qsl and parameters visible
+    cca_tile_rows(a, tile_ta(0), use_lds_qsl ? sm.qsl_s : a.prefill_qsl, sm.row_p[0],
+                  sm.row_src[0], rcur);
+    __syncthreads();
+    for (int u = 0; u < my_tiles; ++u) tile(u, fa);
+  } else {
+    Pref fa, fb;
+    issue(0, fa);
+    if (my_tiles > 1) issue(1, fb);
+    __syncthreads();   // qsl and parameters visible
+    cca_tile_rows(a, tile_ta(0), use_lds_qsl ? sm.qsl_s : a.prefill_qsl, sm.row_p[0],
+                  sm.row_src[0], rcur);
+    __syncthreads();
+    for (int u = 0; u < my_tiles; u += 2) {
+      tile(u, fa);
+      if (u + 1 < my_tiles) tile(u + 1, fb);
+    }
   }
-#endif
 }
 
 template <int T0, int GMAX>
-__global__ __launch_bounds__(kCcaThreads, cca_waves_per_simd<T0>()) void cca_persist_main(CcaArgs a) {
+__global__ __launch_bounds__(kCcaThreads, cca_waves_per_simd(T0, GMAX)) void cca_persist_main(CcaArgs a) {
   __shared__ __attribute__((aligned(16))) CcaSmem<T0> sm;
   const int lb = logical_block_cca(a);
   if (lb < 0) return;
@@ -727,7 +754,8 @@ hipError_t launch_cca(const CcaArgs& a, hipStream_t stream) {
       cu_count[dev] = n;
     }
     const int NG = a.nq + a.nkv;
-    const int per_cu = SC_CCA_MIN_WAVES / 2;   // 8-wave workgroups resident per CU
+    const bool g8 = a.nq / a.nkv > 4;
+    const int per_cu = cca_waves_per_simd(a.t0, g8 ? 8 : 4) / 2;   // resident 8-wave workgroups per CU
     const int64_t ntiles = (a.num_tokens + kCcaMT - 1) / kCcaMT;
     int64_t S = (int64_t)cu_count[dev] * per_cu / NG;
     if (S < 1) S = 1;
@@ -737,7 +765,6 @@ hipError_t launch_cca(const CcaArgs& a, hipStream_t stream) {
     b.per_xcd = (b.n_logical + 7) / 8;
     dim3 grid((unsigned)(b.per_xcd * 8));
     const dim3 block(kCcaThreads);
-    const bool g8 = a.nq / a.nkv > 4;
     switch (a.t0 * 2 + (g8 ? 1 : 0)) {
       case 2: hipLaunchKernelGGL((cca_persist_main<1, 4>), grid, block, 0, stream, b); break;
       case 3: hipLaunchKernelGGL((cca_persist_main<1, 8>), grid, block, 0, stream, b); break;
