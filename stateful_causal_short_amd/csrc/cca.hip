@@ -33,6 +33,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 namespace {
 
 constexpr int kQslCache = 1024;   // prefill boundaries cached in LDS (else searched in HBM)
+template <typename T>
+using gptr = const __attribute__((address_space(1))) T*;
 
 __device__ __forceinline__ float bf2f(uint32_t b) { return __uint_as_float(b << 16); }
 // two fp32 -> one word of two bf16 (lo, hi), one v_cvt_pk_bf16_f32
@@ -332,13 +334,18 @@ struct CcaSmem {
   uint16_t act[(MT + 1) * AROW];        // depthwise rows: row i+1 = token i, row 0 = token -1
   uint16_t prv[MT * AROW];              // depthwise one position back, for request starts
   uint16_t ost[MT * AROW];              // staged bf16 output rows
-  float res[MT * RROW];                 // residual + grouped bias, fp32
-  uint16_t w1[HD * T0];                 // depthwise weights of the group (c, tap)
-  uint16_t b1[HD], b2[HD];              // depthwise and grouped biases
+  float res[MT * RROW];                 // residual + grouped bias, fp32, half-major (cca_hslot)
+  uint16_t w1[HD * T0];                 // depthwise weights: (cca_hslot(c), c % 4, tap)
+  uint16_t bb[2 * HD];                  // (cca_hslot(c)): depthwise biases of 4 channels, then grouped
   int32_t qsl_s[kQslCache];
   int row_p[2][MT];                     // position in the request (-1: no row), by tile parity
   int row_src[2][MT];                   // prefill request index, or -2 - t for decode row t
 };
+
+// Phase A gives a lane 8 channels v*8 .. v*8+7 of a row and computes them as
+// two halves of 4. Its LDS parameters and residual rows are stored by block
+// (half, v), so that the 16 lanes of a row touch one contiguous run per half.
+__device__ __forceinline__ constexpr int cca_hslot(int c) { return ((c >> 2) & 1) * 16 + (c >> 3); }
 
 // Waves per SIMD the main kernel is compiled for: 4 (two resident 8-wave
 // workgroups per CU, so one's phase A overlaps the other's MFMA and stores)
@@ -352,7 +359,8 @@ __host__ __device__ constexpr int cca_waves_per_simd(int t0, int gmax) {
 // Row info of the tile starting at token ta (threads 0 .. 31, one row each).
 // `cur` is the thread's prefill request index from its previous (earlier)
 // tile: the search gallops forward from it, then bisects.
-__device__ __forceinline__ void cca_tile_rows(const CcaArgs& a, int64_t ta, const int32_t* qsl,
+template <typename QP>
+__device__ __forceinline__ void cca_tile_rows(const CcaArgs& a, int64_t ta, QP qsl,
                                               int* rp, int* rs, int& cur) {
   const int i = (int)threadIdx.x;
   if (i >= kCcaMT) return;
@@ -417,6 +425,7 @@ __device__ __forceinline__ void cca_persist_body(const CcaArgs& a, CcaSmem<T0>& 
   constexpr int AHEAD = ISK ? 1 : SC_CCA_AHEAD;
 
   const int NG = a.nq + a.nkv, G = a.nq / a.nkv;
+  const float inv_g = 1.0f / (float)G;           // exact when G is a power of two
   const int C = NG * HD, vd = a.nkv * HD / 2, nvv = vd / 8;
   const int g = isk ? grp - a.nq : grp / G;       // kv head of the bundle
   const int cbase = grp * HD;                      // raw / output channel base
@@ -438,14 +447,14 @@ __device__ __forceinline__ void cca_persist_body(const CcaArgs& a, CcaSmem<T0>& 
   // ---- setup: parameters and prefill boundaries to LDS, weights to registers ----
   if (use_lds_qsl)
     for (int k = tid; k <= a.num_prefills; k += kCcaThreads) sm.qsl_s[k] = a.prefill_qsl[k];
-  if (tid < HD * T0 / 8)
-    *(u32x4*)(sm.w1 + tid * 8) = ld16((const uint16_t*)a.w_dw + (int64_t)cbase * T0 + tid * 8);
-  else if (tid < HD * T0 / 8 + 16)
-    *(u32x4*)(sm.b1 + (tid - HD * T0 / 8) * 8) =
-        ld16((const uint16_t*)a.b_dw + cbase + (tid - HD * T0 / 8) * 8);
-  else if (tid < HD * T0 / 8 + 32)
-    *(u32x4*)(sm.b2 + (tid - HD * T0 / 8 - 16) * 8) =
-        ld16((const uint16_t*)a.b_gr + cbase + (tid - HD * T0 / 8 - 16) * 8);
+  for (int k = tid; k < HD * T0; k += kCcaThreads) {
+    const int cc = k / T0, tap = k - cc * T0;
+    sm.w1[(cca_hslot(cc) * 4 + (cc & 3)) * T0 + tap] = ((const uint16_t*)a.w_dw)[(int64_t)cbase * T0 + k];
+  }
+  if (tid < HD) {
+    sm.bb[cca_hslot(tid) * 8 + (tid & 3)] = ((const uint16_t*)a.b_dw)[cbase + tid];
+    sm.bb[cca_hslot(tid) * 8 + 4 + (tid & 3)] = ((const uint16_t*)a.b_gr)[cbase + tid];
+  }
   // grouped weights of this wave's 16 output channels, K ordered b*128 + j:
   // one 32-byte run of a (C, hd, t1) row holds taps 0 and 1 of 8 channels
   bf16x8 wf[8];
@@ -514,7 +523,12 @@ __device__ __forceinline__ void cca_persist_body(const CcaArgs& a, CcaSmem<T0>& 
     }
   };
 
-  int rcur = 0;   // request cursor of this thread's row (threads 0 .. 31)
+  int rcur = 0;
+  const gptr<int32_t> qsl_g = (gptr<int32_t>)a.prefill_qsl;
+  auto rows = [&](int64_t ta, int* rp, int* rs) {
+    if (use_lds_qsl) cca_tile_rows(a, ta, sm.qsl_s, rp, rs, rcur);
+    else cca_tile_rows(a, ta, qsl_g, rp, rs, rcur);
+  };
   auto tile = [&](int u, Pref& f) {
     const int cur = u & 1;
     const uint32_t ta = tile_ta(u);
@@ -525,21 +539,23 @@ __device__ __forceinline__ void cca_persist_body(const CcaArgs& a, CcaSmem<T0>& 
     // which halves the fp32 working set of this phase.
     {
       const int p = rp[i];
+      uint2 dwh[2];
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
         const int c4 = 4 * hf;                        // first channel of the half
+        const int hs = hf * 16 + v;                   // the half's parameter / residual block
         // depthwise weights (ch * T0 + tap), biases of the half
         uint16_t wl[4 * T0];
 #pragma unroll
         for (int k = 0; k < 4 * T0; k += 4) {
-          const uint2 w4 = *(const uint2*)(sm.w1 + (v * 8 + c4) * T0 + k);
+          const uint2 w4 = *(const uint2*)(sm.w1 + hs * 4 * T0 + k);
           wl[k] = (uint16_t)(w4.x & 0xFFFFu);
           wl[k + 1] = (uint16_t)(w4.x >> 16);
           wl[k + 2] = (uint16_t)(w4.y & 0xFFFFu);
           wl[k + 3] = (uint16_t)(w4.y >> 16);
         }
-        const uint2 b1h = *(const uint2*)(sm.b1 + v * 8 + c4);
-        const uint2 b2h = *(const uint2*)(sm.b2 + v * 8 + c4);
+        const u32x4 bbv = *(const u32x4*)(sm.bb + hs * 8);
+        const uint2 b1h = {bbv[0], bbv[1]}, b2h = {bbv[2], bbv[3]};
         auto half_el = [&](uint2 w, int ch) -> float {
           const uint32_t word = ch < 2 ? w.x : w.y;
           return bf2f((ch & 1) ? (word >> 16) : (word & 0xFFFFu));
@@ -595,14 +611,14 @@ __device__ __forceinline__ void cca_persist_body(const CcaArgs& a, CcaSmem<T0>& 
           for (int ch = 0; ch < 4; ++ch)
             y[ch] = half_el(b2h, ch) + 0.5f * (xe(T0, ch) + bf2f(BF16::get(f.r[0], c4 + ch)));
         } else {
-          // the mean over the bundle's q heads, summed in head order
+          // the mean over the bundle's q heads, summed in head order (the
+          // rows of heads G .. GMAX-1 were read as zeros)
 #pragma unroll
           for (int ch = 0; ch < 4; ++ch) {
             float s = 0.f;
 #pragma unroll
-            for (int qi = 0; qi < GMAX; ++qi)
-              if (qi < G) s += bf2f(BF16::get(f.r[qi], c4 + ch));
-            y[ch] = half_el(b2h, ch) + 0.5f * (s / (float)G + xe(T0, ch));
+            for (int qi = 0; qi < GMAX; ++qi) s += bf2f(BF16::get(f.r[qi], c4 + ch));
+            y[ch] = half_el(b2h, ch) + 0.5f * __builtin_fmaf(s, inv_g, xe(T0, ch));
           }
         }
         uint2 cur_dw = {0u, 0u};
@@ -610,19 +626,19 @@ __device__ __forceinline__ void cca_persist_body(const CcaArgs& a, CcaSmem<T0>& 
           cur_dw = dw(p, 1);
           if (p == 0) *(uint2*)(sm.prv + i * AROW + v * 8 + c4) = dw(-1, 0);
         }
-        *(uint2*)(sm.act + (i + 1) * AROW + v * 8 + c4) = cur_dw;
-        *(float4*)(sm.res + i * RROW + v * 8 + c4) = float4{y[0], y[1], y[2], y[3]};
+        dwh[hf] = cur_dw;
+        *(float4*)(sm.res + i * RROW + hs * 4) = float4{y[0], y[1], y[2], y[3]};
         // the tile's first row continues a request: its previous position
         if (i == 0 && p >= 1) *(uint2*)(sm.act + v * 8 + c4) = dw(p - 1, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
+      *(u32x4*)(sm.act + (i + 1) * AROW + v * 8) = u32x4{dwh[0].x, dwh[0].y, dwh[1].x, dwh[1].y};
     }
     // value item of this tile, then the next tiles' rows and loads
     u32x4 val = f.val;
     const int vp = vitem ? rp[vr] : -1;
     const int vsrc = vitem ? rsrc_[vr] : -1;
-    if (u + 1 < my_tiles) cca_tile_rows(a, tile_ta(u + 1), use_lds_qsl ? sm.qsl_s : a.prefill_qsl,
-                                        sm.row_p[cur ^ 1], sm.row_src[cur ^ 1], rcur);
+    if (u + 1 < my_tiles) rows(tile_ta(u + 1), sm.row_p[cur ^ 1], sm.row_src[cur ^ 1]);
     if (u + AHEAD < my_tiles) issue(u + AHEAD, f);
     // store offsets of this tile (row info is rewritten by the next tile)
     const uint32_t ooff = rp[i] >= 0 ? o_lane + ta * ors32 : kOff;
@@ -665,7 +681,7 @@ __device__ __forceinline__ void cca_persist_body(const CcaArgs& a, CcaSmem<T0>& 
     for (int th = 0; th < 2; ++th) {
       const int n = th * 16 + (lane & 15);
       const int cl = wv * 16 + 4 * (lane >> 4);
-      const float4 rr = *(const float4*)(sm.res + n * RROW + cl);
+      const float4 rr = *(const float4*)(sm.res + n * RROW + cca_hslot(cl) * 4);
       uint2 o;
       o.x = pk_bf16(acc[th][0] + rr.x, acc[th][1] + rr.y);
       o.y = pk_bf16(acc[th][2] + rr.z, acc[th][3] + rr.w);
@@ -692,8 +708,7 @@ __device__ __forceinline__ void cca_persist_body(const CcaArgs& a, CcaSmem<T0>& 
     Pref fa;
     issue(0, fa);
     __syncthreads();   // qsl and parameters visible
-    cca_tile_rows(a, tile_ta(0), use_lds_qsl ? sm.qsl_s : a.prefill_qsl, sm.row_p[0],
-                  sm.row_src[0], rcur);
+    rows(tile_ta(0), sm.row_p[0], sm.row_src[0]);
     __syncthreads();
     for (int u = 0; u < my_tiles; ++u) tile(u, fa);
   } else {
@@ -701,8 +716,7 @@ __device__ __forceinline__ void cca_persist_body(const CcaArgs& a, CcaSmem<T0>& 
     issue(0, fa);
     if (my_tiles > 1) issue(1, fb);
     __syncthreads();   // qsl and parameters visible
-    cca_tile_rows(a, tile_ta(0), use_lds_qsl ? sm.qsl_s : a.prefill_qsl, sm.row_p[0],
-                  sm.row_src[0], rcur);
+    rows(tile_ta(0), sm.row_p[0], sm.row_src[0]);
     __syncthreads();
     for (int u = 0; u < my_tiles; u += 2) {
       tile(u, fa);

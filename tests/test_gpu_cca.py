@@ -84,6 +84,21 @@ def test_generic_shapes(hd, t0, t1):
     parity(case)
 
 
+@pytest.mark.parametrize("nq,nkv", [(16, 4), (8, 1)])
+def test_many_short_and_empty_prefills(nq, nkv):
+    """Hundreds of requests of 0 to 2 tokens: a tile crosses more than 64
+    request boundaries (a run of 90 empty requests), and with more tiles than
+    a 256-CU grid has workgroups per head group (2 per CU / (nq + nkv)), a
+    workgroup's next tile lies hundreds of requests after its previous one."""
+    rng = np.random.default_rng(950 + nq)
+    lens = np.concatenate([[3, 1], np.zeros(90, np.int64), rng.integers(0, 3, 900),
+                           [100, 40, 0, 0, 65], rng.integers(0, 2, 70), [1000]])
+    case = synthetic.cca_case("cca_many", 951 + nq, nq=nq, nkv=nkv, hd=128, num_decodes=37,
+                              prefill_lens=lens, num_slots=1200)
+    assert (case.T + 31) // 32 > 2 * 256 // (nq + nkv)
+    parity(case)
+
+
 def test_padding_slots_fused_rows_and_no_delayed_init():
     case = synthetic.cca_case("cca_pad", 801, num_decodes=6, prefill_lens=[4, 80, 1],
                               num_slots=16)
