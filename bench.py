@@ -335,6 +335,60 @@ def copy_calibration(args):
                       "GBps": 2 * nbytes / (ms * 1e-3) / 1e9}), flush=True)
 
 
+def traffic_from(d):
+    """Rewrite profiles/traffic.json from four rocprofv3 --pmc runs (one counter
+    each) under directory d: pmc_{varlen_prefill,copy}_{FETCH_SIZE,WRITE_SIZE}/
+    run_counter_collection.csv. Each counter of the prefill kernel (the non-copy
+    kernel with the most bytes) is scaled by the factor that maps the same counter
+    of the row copy to its known bytes. CPU only; prints a summary."""
+    import csv
+    import statistics
+
+    def per_kernel(workload, counter):
+        path = os.path.join(d, f"pmc_{workload}_{counter}", "run_counter_collection.csv")
+        vals = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] == counter:
+                    vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return vals
+
+    copy_bytes = ((1 << 30) // (48 * 1024)) * 48 * 1024     # copy_calibration's launch
+    factors, kib, names = {}, {}, {}
+    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+        cp = per_kernel("copy", counter)
+        ck = [k for k in cp if "row_copy" in k]
+        if len(ck) != 1:
+            raise SystemExit(f"copy run: expected one row_copy kernel, found {ck}")
+        med = statistics.median(cp[ck[0]])
+        factors[counter] = copy_bytes / 1024.0 / med
+        pv = per_kernel("varlen_prefill", counter)
+        cand = {k: statistics.median(v) for k, v in pv.items() if not k.startswith("__amd")}
+        name = max(cand, key=cand.get)
+        kib[counter], names[counter] = cand[name], name
+        print(f"{counter}: copy median {med:,.1f} KiB ({len(cp[ck[0]])} dispatches) -> factor "
+              f"{factors[counter]:.5f}; {name}: median {cand[name]:,.2f} KiB ({len(pv[name])} "
+              f"dispatches) -> {cand[name] * factors[counter]:,.0f} KiB")
+    if names["FETCH_SIZE"] != names["WRITE_SIZE"]:
+        raise SystemExit(f"different dominant kernels: {names}")
+    _, pre_b = conv_kernel_bytes(conv_workload("varlen_prefill"))
+    total = int(round(1024 * sum(kib[c] * factors[c] for c in kib)))
+    print(f"total {total:,} bytes per launch vs {pre_b:,} algorithmic: ratio {total / pre_b:.4f}; "
+          f"source digest {source_sha()}")
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    with open(path) as f:
+        t = json.load(f)
+    t["varlen_prefill:prefill"] = {
+        "bytes_per_launch": total, "alg_bytes_per_launch": pre_b,
+        "fetch_kib": kib["FETCH_SIZE"], "write_kib": kib["WRITE_SIZE"],
+        "fetch_factor": factors["FETCH_SIZE"], "write_factor": factors["WRITE_SIZE"],
+        "kernel": names["FETCH_SIZE"], "source_sha": source_sha(),
+    }
+    with open(path, "w") as f:
+        json.dump(t, f, indent=1)
+        f.write("\n")
+
+
 # ---------------------------------------------------------------------------
 def main():
     ap = argparse.ArgumentParser()
@@ -347,7 +401,12 @@ def main():
     ap.add_argument("--state-layout", default="ds", choices=["ds", "sd"],
                     help="state pool layout: (slots, C, S) or (slots, S, C)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic-from", metavar="DIR",
+                    help="rewrite profiles/traffic.json from rocprofv3 --pmc runs under DIR "
+                         "and exit (CPU only)")
     args = ap.parse_args()
+    if args.traffic_from:
+        return traffic_from(args.traffic_from)
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (this path has no multi-GPU leg); "
               f"--gpus {args.gpus} is not supported", file=sys.stderr)

@@ -225,9 +225,9 @@ __global__ __launch_bounds__(kBlock) void conv_fast(ConvArgs a) {
 
 template <int K, int D, int U, bool SILU, bool UPDATE, bool FUSE, bool SD>
 __global__ __launch_bounds__(kBlock) void conv_pairs(ConvArgs a) {
-#if SC_LDS_PAD > 0
-  __shared__ uint8_t occupancy_pad[SC_LDS_PAD];
-  if (a.C < 0) occupancy_pad[threadIdx.x] = 0;
+#if SC_PAIRS_LDS_RESERVE > 0
+  __shared__ uint8_t residency_cap[SC_PAIRS_LDS_RESERVE];
+  if (a.C < 0) residency_cap[threadIdx.x] = 0;   // never taken: keeps the reservation
 #endif
   using E = BF16;
   using S = E::S;

@@ -25,6 +25,13 @@ namespace sc {
 #ifndef SC_LDS_PAD
 #define SC_LDS_PAD 0
 #endif
+#ifndef SC_PAIRS_LDS_RESERVE
+// LDS each one-pass prefill workgroup reserves only to cap residency (the
+// kernel itself uses none): a gfx950 CU has 160 KiB, so 48 KiB admits three
+// 4-wave workgroups per CU. Three measured faster than the five the register
+// count allows (and than two or four): fewer streams contend for HBM.
+#define SC_PAIRS_LDS_RESERVE 49152
+#endif
 #ifndef SC_NO_PAIRS
 #define SC_NO_PAIRS 0
 #endif
