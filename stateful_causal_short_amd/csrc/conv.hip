@@ -688,7 +688,9 @@ hipError_t launch_kd(const ConvArgs& a, int qc, dim3 grid, hipStream_t s) {
 // tokens per one-pass prefill chunk for history length H (must be >= H)
 constexpr int pairs_chunk(int H) { return H <= 4 ? SC_PAIRS_CHUNK_SMALL : (H <= 8 ? 8 : 16); }
 // requests per update workgroup
-constexpr int update_reqs(int H, int Q) { return (H <= 4 && Q == 1) ? SC_UPDATE_REQS : (H <= 4 ? 2 : (Q == 1 ? 2 : 1)); }
+constexpr int update_reqs(int H, int Q) {
+  return (H <= 4 && Q == 1) ? SC_UPDATE_REQS : (H <= 4 ? SC_UPDATE_REQS_MULTI : (Q == 1 ? 2 : 1));
+}
 
 template <int K, int D, bool SILU, bool FUSE, bool SD>
 hipError_t launch_pairs_l(const ConvArgs& a, int qc, dim3 grid, hipStream_t s) {

@@ -41,6 +41,9 @@ namespace sc {
 #ifndef SC_UPDATE_REQS
 #define SC_UPDATE_REQS 4
 #endif
+#ifndef SC_UPDATE_REQS_MULTI
+#define SC_UPDATE_REQS_MULTI 1   // requests per update workgroup for q = 2, 4 (H <= 4)
+#endif
 constexpr int kChunk = SC_PREFILL_CHUNK;   // tokens per prefill chunk (>= H for the fast kernels)
 
 // Depthwise conv launch arguments (by value into the kernel).

@@ -30,6 +30,14 @@ namespace sc {
 constexpr int kSpecQMax = 8;    // tokens per request on the register path
 constexpr int kSpecSMax = 16;   // state entries per channel staged in LDS
 
+// DS pool in LDS: a lane's channels hold 4*S words (S vectors); with one pad
+// word per lane the lane stride is odd, so the element-wise window and roll
+// accesses of a wave fall in distinct banks. Without room for the pad (S = 16)
+// the stride stays 4*S.
+__host__ __device__ constexpr int ds_lane_words(int S, int block) {
+  return (size_t)block * (4 * S + 1) * 4 <= 65536 ? 4 * S + 1 : 4 * S;
+}
+
 template <class E, int K, int D, bool SILU, bool SPEC, bool FUSE>
 __global__ __launch_bounds__(kBlock) void conv_rollbuf(ConvArgs a) {
   using St = typename E::S;
@@ -38,7 +46,7 @@ __global__ __launch_bounds__(kBlock) void conv_rollbuf(ConvArgs a) {
   constexpr bool PAIRS = VEC == 8 && ((K == 4 && D <= 3) || (K == 2 && D == 1));
   constexpr int NP = K / 2;
   constexpr int QM = kSpecQMax;
-  extern __shared__ u32x4 region[];   // kBlock * S vectors
+  extern __shared__ u32x4 region[];   // SD: kBlock * S vectors; DS: kBlock lanes of ds_lane_words
 
   const int lb = logical_block(a.n_logical, a.per_xcd);
   if (lb < 0) return;                       // uniform over the workgroup
@@ -50,6 +58,8 @@ __global__ __launch_bounds__(kBlock) void conv_rollbuf(ConvArgs a) {
   const bool lane_ok = c0 < a.C;
   const int Sl = a.S, q = a.q;
   const int nvec = (min(a.C - cbase, kBlock * VEC) / VEC) * Sl;
+  const int lw = ds_lane_words(Sl, kBlock);  // DS: words per lane in LDS
+  uint32_t* rw = (uint32_t*)region;
 
   // weights and bias (independent of the request)
   uint32_t wp[PAIRS ? NP : 1][VEC];
@@ -118,6 +128,8 @@ __global__ __launch_bounds__(kBlock) void conv_rollbuf(ConvArgs a) {
       for (int k = 0; k < kSpecSMax; ++k)
         if (k < Sl) region[k * kBlock + tid] = sv[k];
     } else {
+      // coalesced loads of the workgroup's contiguous rows; vector vi is entry
+      // group vi % S of lane vi / S, stored at that lane's padded offset
       const St* sp = (const St*)a.pool + ((int64_t)slot * a.C + cbase) * Sl;
 #pragma unroll
       for (int k = 0; k < kSpecSMax; ++k) {
@@ -127,14 +139,19 @@ __global__ __launch_bounds__(kBlock) void conv_rollbuf(ConvArgs a) {
 #pragma unroll
       for (int k = 0; k < kSpecSMax; ++k) {
         const int vi = tid + k * kBlock;
-        if (k < Sl && vi < nvec) region[vi] = sv[k];
+        if (k < Sl && vi < nvec) {
+          const int ln = vi / Sl;
+          uint32_t* wd = rw + ln * lw + 4 * (vi - ln * Sl);
+#pragma unroll
+          for (int d = 0; d < 4; ++d) wd[d] = sv[k][d];
+        }
       }
     }
   }
   __syncthreads();
 
   St* le = (St*)region;
-  const int lbase = tid * VEC * Sl;          // DS: channel c0, entry 0 of this lane
+  const int lbase = tid * lw * (int)(4 / sizeof(St));   // DS: channel c0, entry 0 of this lane
   const int off = SPEC ? acc - 1 : 0;
   u32x4 raw[H + QM];
 #pragma unroll
@@ -211,12 +228,21 @@ __global__ __launch_bounds__(kBlock) void conv_rollbuf(ConvArgs a) {
         }
       }
     } else if (valid) {
+      if constexpr (SPEC) {
+        // ascending j reads entry acc + j > j before it is overwritten; the
+        // lane's channels go together, so each step's reads are independent
+        for (int j = 0; j < Sl - q; ++j) {
+          St v8[VEC];
+#pragma unroll
+          for (int ch = 0; ch < VEC; ++ch) v8[ch] = le[lbase + ch * Sl + acc + j];
+#pragma unroll
+          for (int ch = 0; ch < VEC; ++ch) le[lbase + ch * Sl + j] = v8[ch];
+        }
+      }
 #pragma unroll
       for (int ch = 0; ch < VEC; ++ch) {
         St* row = le + lbase + ch * Sl;
         if constexpr (SPEC) {
-          // ascending j reads entry acc + j > j before it is overwritten
-          for (int j = 0; j < Sl - q; ++j) row[j] = row[acc + j];
 #pragma unroll
           for (int u = 0; u < QM; ++u)
             if (u < q) row[Sl - q + u] = (St)E::get(xr[u], ch);
@@ -250,7 +276,11 @@ __global__ __launch_bounds__(kBlock) void conv_rollbuf(ConvArgs a) {
 #pragma unroll
     for (int k = 0; k < kSpecSMax; ++k) {
       const int vi = tid + k * kBlock;
-      if (k < Sl && vi < nvec) st16_stream(dp + vi * VEC, region[vi]);
+      if (k < Sl && vi < nvec) {
+        const int ln = vi / Sl;
+        const uint32_t* wd = rw + ln * lw + 4 * (vi - ln * Sl);
+        st16_stream(dp + vi * VEC, u32x4{wd[0], wd[1], wd[2], wd[3]});
+      }
     }
   }
 }
@@ -312,7 +342,8 @@ bool rollbuf_shape(int K, int D) {
 
 template <class E, bool SILU, bool SPEC, bool FUSE>
 hipError_t launch_rollbuf(const ConvArgs& a, int K, int D, dim3 grid, hipStream_t s) {
-  const size_t lds = (size_t)kBlock * a.S * sizeof(u32x4);
+  const size_t lds = a.sd ? (size_t)kBlock * a.S * sizeof(u32x4)
+                          : (size_t)kBlock * ds_lane_words(a.S, kBlock) * 4;
   const dim3 blk(kBlock);
   if (K == 4 && D == 1) hipLaunchKernelGGL((conv_rollbuf<E, 4, 1, SILU, SPEC, FUSE>), grid, blk, lds, s, a);
   else if (K == 4 && D == 2) hipLaunchKernelGGL((conv_rollbuf<E, 4, 2, SILU, SPEC, FUSE>), grid, blk, lds, s, a);
