@@ -226,14 +226,40 @@ def cpu_baseline_conv(case, budget_s=10.0, num_accepted=None, fused=False):
         el = time.perf_counter() - t0
         if el >= budget_s or runs >= 50:
             break
-    return {"value": case.T * runs / el, "unit": "tokens/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"the full batch ({case.T} tokens) run {runs}x through the fp64 "
-                      f"oracle, {el:.1f} s wall on {threads} threads"}
+    res = {"value": case.T * runs / el, "unit": "tokens/s", "cores": threads,
+           "kind": "oracle",
+           "sample": f"the full batch ({case.T} tokens) run {runs}x through the fp64 "
+                     f"oracle, {el:.1f} s wall on {threads} threads"}
+    # one thread, one run of the batch, when that stays within the budget
+    if threads > 1 and el / runs * threads <= budget_s:
+        t1 = time.perf_counter()
+        if num_accepted is None:
+            oracle.conv(case, nthreads=1, **fz)
+        else:
+            oracle.conv_spec(case, num_accepted, nthreads=1)
+        res["one_thread_value"] = case.T / (time.perf_counter() - t1)
+    res["cpu_model"] = cpu_model()
+    return res
 
 
-def source_sha(files=("conv.hip", "conv_device.hpp", "common.hpp", "kernels.hpp")):
-    """Digest of the sources the depthwise kernels are built from."""
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+DW_SOURCES = ("conv.hip", "conv_device.hpp", "common.hpp", "kernels.hpp")
+CCA_SOURCES = ("cca.hip", "cca.hpp", "common.hpp")
+
+
+def source_sha(files=DW_SOURCES):
+    """Digest of the sources a kernel family is built from (depthwise by default)."""
     h = hashlib.sha256()
     d = os.path.join(ROOT, "stateful_causal_short_amd", "csrc")
     for f in files:
@@ -242,7 +268,7 @@ def source_sha(files=("conv.hip", "conv_device.hpp", "common.hpp", "kernels.hpp"
     return h.hexdigest()[:16]
 
 
-def traffic_for(kernel_key):
+def traffic_for(kernel_key, files=DW_SOURCES):
     """HBM bytes per launch from the committed PMC summary, if it was taken on
     the current kernel sources (else null)."""
     p = os.path.join(ROOT, "profiles", "traffic.json")
@@ -252,7 +278,7 @@ def traffic_for(kernel_key):
     except (OSError, ValueError):
         return None
     e = t.get(kernel_key)
-    if not e or e.get("source_sha") != source_sha():
+    if not e or e.get("source_sha") != source_sha(files):
         return None
     return e.get("bytes_per_launch")
 
@@ -297,10 +323,32 @@ def cca_bench(args):
         "roofline": {"kernel": "cca_main+state", "bound": "hbm",
                      "achieved": (main_b + upd_b) / (ms * 1e-3) / 1e9, "peak": PEAK_GBPS,
                      "unit": "GB/s", "frac": (main_b + upd_b) / (ms * 1e-3) / 1e9 / PEAK_GBPS,
-                     "traffic": None, "alg_bytes_per_launch": main_b + upd_b},
+                     "traffic": traffic_for("cca:cca_main+state", CCA_SOURCES),
+                     "alg_bytes_per_launch": main_b + upd_b},
         "cpu_baseline": None,
     }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        result["cpu_baseline"] = cpu_baseline_cca(case)
     print(json.dumps(result), flush=True)
+
+
+def cpu_baseline_cca(case, budget_s=10.0):
+    """The CCA oracle, as it stands, on the same batch; repeated until ~budget_s."""
+    import oracle
+    threads = min(16, oracle.default_threads())
+    runs, t0 = 0, time.perf_counter()
+    while True:
+        oracle.cca(case, nthreads=threads)
+        runs += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or runs >= 20:
+            break
+    return {"value": case.T * runs / el, "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"the full batch ({case.T} tokens) run {runs}x through the fp64 "
+                      f"oracle, {el:.1f} s wall on {threads} threads",
+            "cpu_model": cpu_model()}
 
 
 def copy_calibration(args):
@@ -336,11 +384,13 @@ def copy_calibration(args):
 
 
 def traffic_from(d):
-    """Rewrite profiles/traffic.json from four rocprofv3 --pmc runs (one counter
-    each) under directory d: pmc_{varlen_prefill,copy}_{FETCH_SIZE,WRITE_SIZE}/
-    run_counter_collection.csv. Each counter of the prefill kernel (the non-copy
-    kernel with the most bytes) is scaled by the factor that maps the same counter
-    of the row copy to its known bytes. CPU only; prints a summary."""
+    """Rewrite the entries of profiles/traffic.json whose rocprofv3 --pmc runs
+    (one counter each) are under directory d: pmc_<workload>_<COUNTER>/
+    run_counter_collection.csv for COUNTER in FETCH_SIZE, WRITE_SIZE and
+    workload varlen_prefill (the prefill kernel: the non-copy kernel with the
+    most bytes) and/or cca (the CCA kernels together), plus the row-copy
+    calibration pmc_copy_*. Each counter is scaled by the factor that maps the
+    same counter of the row copy to its known bytes. CPU only; prints a summary."""
     import csv
     import statistics
 
@@ -354,7 +404,7 @@ def traffic_from(d):
         return vals
 
     copy_bytes = ((1 << 30) // (48 * 1024)) * 48 * 1024     # copy_calibration's launch
-    factors, kib, names = {}, {}, {}
+    factors = {}
     for counter in ("FETCH_SIZE", "WRITE_SIZE"):
         cp = per_kernel("copy", counter)
         ck = [k for k in cp if "row_copy" in k]
@@ -362,28 +412,49 @@ def traffic_from(d):
             raise SystemExit(f"copy run: expected one row_copy kernel, found {ck}")
         med = statistics.median(cp[ck[0]])
         factors[counter] = copy_bytes / 1024.0 / med
-        pv = per_kernel("varlen_prefill", counter)
-        cand = {k: statistics.median(v) for k, v in pv.items() if not k.startswith("__amd")}
-        name = max(cand, key=cand.get)
-        kib[counter], names[counter] = cand[name], name
         print(f"{counter}: copy median {med:,.1f} KiB ({len(cp[ck[0]])} dispatches) -> factor "
-              f"{factors[counter]:.5f}; {name}: median {cand[name]:,.2f} KiB ({len(pv[name])} "
-              f"dispatches) -> {cand[name] * factors[counter]:,.0f} KiB")
-    if names["FETCH_SIZE"] != names["WRITE_SIZE"]:
-        raise SystemExit(f"different dominant kernels: {names}")
-    _, pre_b = conv_kernel_bytes(conv_workload("varlen_prefill"))
-    total = int(round(1024 * sum(kib[c] * factors[c] for c in kib)))
-    print(f"total {total:,} bytes per launch vs {pre_b:,} algorithmic: ratio {total / pre_b:.4f}; "
-          f"source digest {source_sha()}")
+              f"{factors[counter]:.5f}")
+
+    def have(workload):
+        return all(os.path.exists(os.path.join(d, f"pmc_{workload}_{c}", "run_counter_collection.csv"))
+                   for c in ("FETCH_SIZE", "WRITE_SIZE"))
+
+    entries = {}
+    if have("varlen_prefill"):
+        kib, names = {}, {}
+        for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+            pv = per_kernel("varlen_prefill", counter)
+            cand = {k: statistics.median(v) for k, v in pv.items() if not k.startswith("__amd")}
+            names[counter] = max(cand, key=cand.get)
+            kib[counter] = cand[names[counter]]
+        if names["FETCH_SIZE"] != names["WRITE_SIZE"]:
+            raise SystemExit(f"different dominant kernels: {names}")
+        _, alg = conv_kernel_bytes(conv_workload("varlen_prefill"))
+        entries["varlen_prefill:prefill"] = (kib, names["FETCH_SIZE"], alg, source_sha())
+    if have("cca"):
+        import synthetic
+        kib, kern = {}, []
+        for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+            pv = per_kernel("cca", counter)
+            ks = sorted(k for k in pv if "cca_" in k)
+            kern = ks
+            kib[counter] = sum(statistics.median(pv[k]) for k in ks)
+        main_b, upd_b = cca_alg_bytes(synthetic.config5())
+        entries["cca:cca_main+state"] = (kib, " + ".join(kern), main_b + upd_b,
+                                         source_sha(CCA_SOURCES))
     path = os.path.join(ROOT, "profiles", "traffic.json")
     with open(path) as f:
         t = json.load(f)
-    t["varlen_prefill:prefill"] = {
-        "bytes_per_launch": total, "alg_bytes_per_launch": pre_b,
-        "fetch_kib": kib["FETCH_SIZE"], "write_kib": kib["WRITE_SIZE"],
-        "fetch_factor": factors["FETCH_SIZE"], "write_factor": factors["WRITE_SIZE"],
-        "kernel": names["FETCH_SIZE"], "source_sha": source_sha(),
-    }
+    for key, (kib, kernel, alg, sha) in entries.items():
+        total = int(round(1024 * sum(kib[c] * factors[c] for c in kib)))
+        for c in kib:
+            print(f"{key}: {c} median {kib[c]:,.2f} KiB -> {kib[c] * factors[c]:,.0f} KiB")
+        print(f"{key}: total {total:,} bytes per launch vs {alg:,} algorithmic: ratio "
+              f"{total / alg:.4f}; kernels {kernel}; source digest {sha}")
+        t[key] = {"bytes_per_launch": total, "alg_bytes_per_launch": alg,
+                  "fetch_kib": kib["FETCH_SIZE"], "write_kib": kib["WRITE_SIZE"],
+                  "fetch_factor": factors["FETCH_SIZE"], "write_factor": factors["WRITE_SIZE"],
+                  "kernel": kernel, "source_sha": sha}
     with open(path, "w") as f:
         json.dump(t, f, indent=1)
         f.write("\n")

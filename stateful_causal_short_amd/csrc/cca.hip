@@ -432,13 +432,17 @@ __device__ __forceinline__ void cca_persist_body(const CcaArgs& a, CcaSmem<T0>& 
   const int tid = (int)threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int v = tid & 15, i = tid >> 4;            // depthwise: channel vector, tile row
   const bool use_lds_qsl = a.num_prefills > 0 && a.num_prefills + 1 <= kQslCache;
-  // value columns of this group: vectors vv = grp + k * nq of 2 * nvv; item tid = (row, k)
-  // (dealt over the nq q-head groups only; the k head's workgroups carry the
-  // bundle's q rows instead)
-  const int mine = isk ? 0 : (2 * nvv - grp + a.nq - 1) / a.nq;
+  // Value columns (v_cur copied, v_del shifted one token) are dealt over the
+  // nq q-head groups only (the k head's workgroups carry the bundle's q rows
+  // instead); item tid = (row vr, vector vk). A row's value columns are 2*nvv/8 lines of 128 bytes (8 vectors); line l
+  // goes to q group l % nq, so each line is read and written whole by 8
+  // consecutive lanes of one workgroup (16-byte pieces from different
+  // workgroups would each cost a partial-line transfer).
+  const int vlines = 2 * nvv / 8;
+  const int mine = (isk || grp >= vlines) ? 0 : 8 * ((vlines - grp + a.nq - 1) / a.nq);
   const int vr = tid / max(mine, 1), vk = tid - vr * max(mine, 1);
   const bool vitem = tid < MT * mine;
-  const int vvv = grp + vk * a.nq;                 // this thread's value vector
+  const int vvv = (grp + (vk >> 3) * a.nq) * 8 + (vk & 7);   // this thread's value vector
   const int64_t qrs = a.q_rs * 2, krs = a.k_rs * 2, ors = a.out_rs * 2;   // bytes
   const int64_t vcb = a.vc_rs * 2, vdb = a.vd_rs * 2;
   const int64_t srs = isk ? krs : qrs;
