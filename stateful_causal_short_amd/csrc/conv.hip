@@ -406,7 +406,11 @@ __global__ __launch_bounds__(kBlock) void conv_update_pairs(ConvArgs a) {
   constexpr int H = (K - 1) * D;
   constexpr int NP = K / 2;
   constexpr int VEC = 8;
-  __shared__ u32x4 xch[H * kBlock];
+  // DS pool: requests whose state regions are transposed through LDS together
+  // (at most 48 KiB of LDS), so the workgroup passes 4 barriers per batch
+  constexpr int RB = (SD || R * H * kBlock * 16 > 49152) ? 1 : R;
+  static_assert(R % RB == 0, "whole batches");
+  __shared__ u32x4 xch[RB * H * kBlock];
 
   const int lb = logical_block(a.n_logical, a.per_xcd);
   if (lb < 0) return;                       // uniform over the workgroup
@@ -503,82 +507,98 @@ __global__ __launch_bounds__(kBlock) void conv_update_pairs(ConvArgs a) {
   E::unpack(bsv, bs);
 
 #pragma unroll
-  for (int rr = 0; rr < R; ++rr) {
-    const int r = grp * R + rr;
-    u32x4 raw[H + Q];
-    if constexpr (SD) {
-#pragma unroll
-      for (int u = 0; u < H; ++u) raw[u] = st[rr][u];
-    } else {
-      // state region -> per-lane (channel, tap) order
+  for (int rb = 0; rb < R; rb += RB) {
+    if constexpr (!SD) {
+      // the batch's state regions -> per-lane (channel, tap) order
       __syncthreads();
 #pragma unroll
-      for (int k = 0; k < H; ++k) xch[tid + k * kBlock] = st[rr][k];
+      for (int j = 0; j < RB; ++j)
+#pragma unroll
+        for (int k = 0; k < H; ++k) xch[j * H * kBlock + tid + k * kBlock] = st[rb + j][k];
       __syncthreads();
-      u32x4 old[H];
-#pragma unroll
-      for (int k = 0; k < H; ++k) old[k] = xch[tid * H + k];
-#pragma unroll
-      for (int u = 0; u < H; ++u) {
-        raw[u] = u32x4{0, 0, 0, 0};
-#pragma unroll
-        for (int ch = 0; ch < VEC; ++ch) E::set(raw[u], ch, get_flat<E>(old, ch * H + u));
-      }
     }
+    u32x4 nvb[RB][SD ? 1 : H];   // new state of the batch, (channel, tap) order
 #pragma unroll
-    for (int u = 0; u < Q; ++u) raw[H + u] = xr[rr][u];
-    if (r < a.batch && lane_ok) {
+    for (int j = 0; j < RB; ++j) {
+      const int rr = rb + j;
+      const int r = grp * R + rr;
+      u32x4 raw[H + Q];
+      if constexpr (SD) {
 #pragma unroll
-      for (int u = 0; u < Q; ++u) {
-        float z[VEC];
+        for (int u = 0; u < H; ++u) raw[u] = st[rr][u];
+      } else {
+        u32x4 old[H];
 #pragma unroll
-        for (int ch = 0; ch < VEC; ++ch) {
-          float acc = bs[ch];
+        for (int k = 0; k < H; ++k) old[k] = xch[j * H * kBlock + tid * H + k];
 #pragma unroll
-          for (int p = 0; p < NP; ++p) {
-            const int r0 = H + u - (K - 1 - 2 * p) * D;
-            acc = dot2_bf16(wp[p][ch], row_pair(raw[r0], raw[r0 + D], ch), acc);
-          }
-          z[ch] = SILU ? silu(acc) : acc;
+        for (int u = 0; u < H; ++u) {
+          raw[u] = u32x4{0, 0, 0, 0};
+#pragma unroll
+          for (int ch = 0; ch < VEC; ++ch) E::set(raw[u], ch, get_flat<E>(old, ch * H + u));
         }
-        const int64_t pr = prow(r, u);
-        if constexpr (FUSE) {
-          float fr[VEC], fo[VEC];
-          E::unpack(rres[rr][u], fr);
-          E::unpack(rout[rr][u], fo);
+      }
+#pragma unroll
+      for (int u = 0; u < Q; ++u) raw[H + u] = xr[rr][u];
+      if (r < a.batch && lane_ok) {
+#pragma unroll
+        for (int u = 0; u < Q; ++u) {
+          float z[VEC];
 #pragma unroll
           for (int ch = 0; ch < VEC; ++ch) {
-            if (a.accumulate) z[ch] += fr[ch];
-            if (a.outer) z[ch] += fo[ch];
+            float acc = bs[ch];
+#pragma unroll
+            for (int p = 0; p < NP; ++p) {
+              const int r0 = H + u - (K - 1 - 2 * p) * D;
+              acc = dot2_bf16(wp[p][ch], row_pair(raw[r0], raw[r0 + D], ch), acc);
+            }
+            z[ch] = SILU ? silu(acc) : acc;
           }
+          const int64_t pr = prow(r, u);
+          if constexpr (FUSE) {
+            float fr[VEC], fo[VEC];
+            E::unpack(rres[rr][u], fr);
+            E::unpack(rout[rr][u], fo);
+#pragma unroll
+            for (int ch = 0; ch < VEC; ++ch) {
+              if (a.accumulate) z[ch] += fr[ch];
+              if (a.outer) z[ch] += fo[ch];
+            }
+          }
+          st16_stream((S*)a.out + pr * a.out_rs + c0, E::pack(z));
         }
-        st16_stream((S*)a.out + pr * a.out_rs + c0, E::pack(z));
+      }
+      // new state = ext[Q .. Q+H)
+      if constexpr (SD) {
+        if (valid[rr] && lane_ok) {
+          S* dp = (S*)a.pool + (int64_t)slot[rr] * a.S * a.C + c0;
+#pragma unroll
+          for (int k = 0; k < H; ++k) st16_stream(dp + (int64_t)k * a.C, raw[Q + k]);
+        }
+      } else {
+#pragma unroll
+        for (int jj = 0; jj < H; ++jj)
+#pragma unroll
+          for (int ch = 0; ch < VEC; ++ch) set_flat<E>(nvb[j], ch * H + jj, E::get(raw[Q + jj], ch));
       }
     }
-    // new state = ext[Q .. Q+H)
-    if constexpr (SD) {
-      if (valid[rr] && lane_ok) {
-        S* dp = (S*)a.pool + (int64_t)slot[rr] * a.S * a.C + c0;
-#pragma unroll
-        for (int k = 0; k < H; ++k) st16_stream(dp + (int64_t)k * a.C, raw[Q + k]);
-      }
-    } else {
-      // (channel, tap) order -> region order
-      u32x4 nv[H];
-#pragma unroll
-      for (int jj = 0; jj < H; ++jj)
-#pragma unroll
-        for (int ch = 0; ch < VEC; ++ch) set_flat<E>(nv, ch * H + jj, E::get(raw[Q + jj], ch));
+    if constexpr (!SD) {
+      // (channel, tap) order -> region order, then unit-stride stores
       __syncthreads();
 #pragma unroll
-      for (int k = 0; k < H; ++k) xch[tid * H + k] = nv[k];
-      __syncthreads();
-      if (valid[rr]) {
-        S* dp = (S*)a.pool + ((int64_t)slot[rr] * a.C + cbase) * H;
+      for (int j = 0; j < RB; ++j)
 #pragma unroll
-        for (int k = 0; k < H; ++k) {
-          const int vi = tid + k * kBlock;
-          if (vi < nvec) st16_stream(dp + vi * VEC, xch[vi]);
+        for (int k = 0; k < H; ++k) xch[j * H * kBlock + tid * H + k] = nvb[j][k];
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < RB; ++j) {
+        const int rr = rb + j;
+        if (valid[rr]) {
+          S* dp = (S*)a.pool + ((int64_t)slot[rr] * a.C + cbase) * H;
+#pragma unroll
+          for (int k = 0; k < H; ++k) {
+            const int vi = tid + k * kBlock;
+            if (vi < nvec) st16_stream(dp + vi * VEC, xch[j * H * kBlock + vi]);
+          }
         }
       }
     }
