@@ -530,11 +530,16 @@ def main():
         """Average GPU time per launch of K back-to-back launches, measured two
         ways with HIP events on the launch stream: eager launches, and one
         replay of the K launches captured in a HIP graph (no host launch cost).
-        Small kernels can outrun the host's launch rate eagerly; graph replay
-        adds a few us between nodes on large ones. The faster is reported and
-        both are kept."""
+        Graph replay adds a few us between nodes on large kernels. The faster
+        is reported and both are kept. Either way the average includes the
+        gaps between back-to-back launches (an event pair around each launch
+        would add the events' own cost, which is larger)."""
         s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
+        # a GPU spin ahead of the region lets the host queue all K launches
+        # before the first runs, so small kernels are not timed at the host's
+        # launch rate
+        torch.cuda._sleep(5_000_000)
         s.record()
         fn_steps()
         e.record()
