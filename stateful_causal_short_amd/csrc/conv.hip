@@ -323,17 +323,23 @@ __global__ __launch_bounds__(kBlock) void conv_pairs(ConvArgs a) {
   w.slot = slot;
   w.valid = valid;
   w.h = hflag;
-  // fused residuals of the chunk's rows, issued before the arithmetic
-  u32x4 rres[FUSE ? U : 1], rout[FUSE ? U : 1];
-  if constexpr (FUSE) {
+  // fused residuals, FG rows at a time, one group ahead of the rows computed
+  // (all U rows at once would hold 2*U vectors; physical rows are distinct,
+  // so a row's residual is read before that row is written)
+  constexpr int FG = FUSE ? (U < 4 ? U : 4) : 1;
+  static_assert(!FUSE || U % FG == 0, "whole residual groups");
+  u32x4 rres[2][FG], rout[2][FG];
+  auto load_res = [&](int g) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
+    for (int k = 0; k < FG; ++k) {
+      const int u = g * FG + k;
       const int t = UPDATE ? u : min(t0 + u, t1 - 1);
       const int64_t pr = phys_row(a, (int64_t)s0 + t);
-      rres[u] = a.accumulate ? ld16((const S*)a.out + pr * ors + c0) : u32x4{0, 0, 0, 0};
-      rout[u] = a.outer ? ld16((const S*)a.outer + pr * a.outer_rs + c0) : u32x4{0, 0, 0, 0};
+      rres[g & 1][k] = a.accumulate ? ld16((const S*)a.out + pr * ors + c0) : u32x4{0, 0, 0, 0};
+      rout[g & 1][k] = a.outer ? ld16((const S*)a.outer + pr * a.outer_rs + c0) : u32x4{0, 0, 0, 0};
     }
-  }
+  };
+  if constexpr (FUSE) load_res(0);
   float bs[VEC];
   E::unpack(bsv, bs);
   if (w.j == 0) {
@@ -343,6 +349,9 @@ __global__ __launch_bounds__(kBlock) void conv_pairs(ConvArgs a) {
 
 #pragma unroll
   for (int u = 0; u < U; ++u) {
+    if constexpr (FUSE) {
+      if (u % FG == 0 && u + FG < U) load_res(u / FG + 1);
+    }
     if (UPDATE || w.t0 + u < w.t1) {
       float z[VEC];
 #pragma unroll
@@ -359,8 +368,8 @@ __global__ __launch_bounds__(kBlock) void conv_pairs(ConvArgs a) {
       if constexpr (FUSE) {
         const int64_t pr = phys_row(a, (int64_t)s0 + w.t0 + u);
         float rr[VEC], ro[VEC];
-        E::unpack(rres[u], rr);
-        E::unpack(rout[u], ro);
+        E::unpack(rres[(u / FG) & 1][u % FG], rr);
+        E::unpack(rout[(u / FG) & 1][u % FG], ro);
 #pragma unroll
         for (int ch = 0; ch < VEC; ++ch) {
           if (a.accumulate) z[ch] += rr[ch];
