@@ -408,6 +408,14 @@ __global__ __launch_bounds__(kBlock) void conv_pairs(ConvArgs a) {
 // weights are loaded once for the R requests. Same tap pairing and dot2 order
 // as conv_pairs, so a decode step equals the matching prefill token bit for bit.
 // ---------------------------------------------------------------------------
+// Requests of a DS update workgroup transposed through LDS together: the
+// largest divisor of R whose state regions fit in 48 KiB.
+constexpr int ds_batch(int R, int H) {
+  int b = R;
+  while (b > 1 && (R % b != 0 || b * H * kBlock * 16 > 49152)) --b;
+  return b;
+}
+
 template <int K, int D, int Q, int R, bool SILU, bool FUSE, bool SD>
 __global__ __launch_bounds__(kBlock) void conv_update_pairs(ConvArgs a) {
   using E = BF16;
@@ -417,7 +425,7 @@ __global__ __launch_bounds__(kBlock) void conv_update_pairs(ConvArgs a) {
   constexpr int VEC = 8;
   // DS pool: requests whose state regions are transposed through LDS together
   // (at most 48 KiB of LDS), so the workgroup passes 4 barriers per batch
-  constexpr int RB = (SD || R * H * kBlock * 16 > 49152) ? 1 : R;
+  constexpr int RB = SD ? 1 : ds_batch(R, H);
   static_assert(R % RB == 0, "whole batches");
   __shared__ u32x4 xch[RB * H * kBlock];
 
@@ -717,17 +725,18 @@ hipError_t launch_kd(const ConvArgs& a, int qc, dim3 grid, hipStream_t s) {
 // tokens per one-pass prefill chunk for history length H (must be >= H)
 constexpr int pairs_chunk(int H) { return H <= 4 ? SC_PAIRS_CHUNK_SMALL : (H <= 8 ? 8 : 16); }
 // requests per update workgroup
-constexpr int update_reqs(int H, int Q) {
-  return (H <= 4 && Q == 1) ? SC_UPDATE_REQS : (H <= 4 ? SC_UPDATE_REQS_MULTI : (Q == 1 ? 2 : 1));
+constexpr int update_reqs(int H, int Q, bool sd) {
+  if (H <= 4) return Q == 1 ? (sd ? SC_UPDATE_REQS_SD : SC_UPDATE_REQS) : SC_UPDATE_REQS_MULTI;
+  return Q == 1 ? 2 : 1;
 }
 
 template <int K, int D, bool SILU, bool FUSE, bool SD>
 hipError_t launch_pairs_l(const ConvArgs& a, int qc, dim3 grid, hipStream_t s) {
   constexpr int H = (K - 1) * D;
   switch (qc) {
-    case 1: hipLaunchKernelGGL((conv_update_pairs<K, D, 1, update_reqs(H, 1), SILU, FUSE, SD>), grid, dim3(kBlock), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((conv_update_pairs<K, D, 2, update_reqs(H, 2), SILU, FUSE, SD>), grid, dim3(kBlock), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((conv_update_pairs<K, D, 4, update_reqs(H, 4), SILU, FUSE, SD>), grid, dim3(kBlock), 0, s, a); break;
+    case 1: hipLaunchKernelGGL((conv_update_pairs<K, D, 1, update_reqs(H, 1, SD), SILU, FUSE, SD>), grid, dim3(kBlock), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((conv_update_pairs<K, D, 2, update_reqs(H, 2, SD), SILU, FUSE, SD>), grid, dim3(kBlock), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((conv_update_pairs<K, D, 4, update_reqs(H, 4, SD), SILU, FUSE, SD>), grid, dim3(kBlock), 0, s, a); break;
     default: hipLaunchKernelGGL((conv_pairs<K, D, pairs_chunk(H), SILU, false, FUSE, SD>), grid, dim3(kBlock), 0, s, a); break;
   }
   return hipGetLastError();
@@ -801,7 +810,7 @@ hipError_t launch_conv(ConvArgs a, int dtype, int K, int D, bool silu_act, bool 
   a.n_cblk = (int)((a.C + per_block_ch - 1) / per_block_ch);
   int64_t n_chunks;
   if (pairs && qc) {
-    const int R = update_reqs(H, qc);
+    const int R = update_reqs(H, qc, a.sd != 0);
     n_chunks = (a.batch + R - 1) / R;     // workgroup groups of R requests
   } else if (uniform) {
     n_chunks = (int64_t)a.batch * ((a.q + a.chunk - 1) / a.chunk);

@@ -41,6 +41,9 @@ namespace sc {
 #ifndef SC_UPDATE_REQS
 #define SC_UPDATE_REQS 4
 #endif
+#ifndef SC_UPDATE_REQS_SD
+#define SC_UPDATE_REQS_SD 8   // requests per q = 1 update workgroup on an SD pool (H <= 4)
+#endif
 #ifndef SC_UPDATE_REQS_MULTI
 #define SC_UPDATE_REQS_MULTI 1   // requests per update workgroup for q = 2, 4 (H <= 4)
 #endif
