@@ -36,7 +36,7 @@ namespace sc {
 #define SC_NO_PAIRS 0
 #endif
 #ifndef SC_PAIRS_CHUNK_SMALL
-#define SC_PAIRS_CHUNK_SMALL 8
+#define SC_PAIRS_CHUNK_SMALL 12
 #endif
 #ifndef SC_UPDATE_REQS
 #define SC_UPDATE_REQS 4
