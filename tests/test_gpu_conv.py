@@ -89,7 +89,9 @@ def test_config4_full():
 # ----------------------------------------------------------------------------
 @pytest.mark.parametrize("d", [1, 3])
 def test_chunk_edges_and_short_requests(d):
-    lens = [1, 2, 3, 8, 9, 10, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 200]
+    # around multiples of the one-pass chunk lengths (12 for H <= 4, 16 for H = 9)
+    lens = [1, 2, 3, 8, 9, 10, 11, 12, 13, 15, 16, 17, 23, 24, 25, 31, 32, 33, 35, 36, 37,
+            47, 48, 49, 63, 64, 65, 127, 128, 129, 200]
     case = conv_case("edges", 500 + d, C=256, K=4, d=d, dtype="bf16", act="silu",
                      w_std=0.25, bias_std=0.1, num_slots=128, prefill_lens=lens,
                      prefill_h_p=0.5, ckpt_grid=max(16, 3 * d))
