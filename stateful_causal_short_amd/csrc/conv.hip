@@ -263,24 +263,25 @@ __global__ __launch_bounds__(kBlock) void conv_pairs(ConvArgs a) {
   }
 
   // chunk -> request (one round of loads), bounds and chunk range
+  // (the launcher sets a.chunk = U for this kernel; U as a constant turns the
+  // divisions below into multiplies)
   int r, s0 = 0, s1 = 0;
   if (UPDATE || a.qsl == nullptr) {
-    const int cpr = (a.q + a.chunk - 1) / a.chunk;
+    const int cpr = (a.q + U - 1) / U;
     r = cid / cpr;
     s0 = r * a.q;
     s1 = s0 + a.q;
   } else {
-    r = find_request_bounds(a.qsl, a.batch, cid, a.chunk, s0, s1);
+    r = find_request_bounds(a.qsl, a.batch, cid, U, s0, s1);
   }
   if (r >= a.batch || s0 < 0) return;
-  const int j = (UPDATE || a.qsl == nullptr) ? cid - r * ((a.q + a.chunk - 1) / a.chunk)
-                                             : cid - (s0 / a.chunk + r);
+  const int j = (UPDATE || a.qsl == nullptr) ? cid - r * ((a.q + U - 1) / U) : cid - (s0 / U + r);
   int L = s1 - s0;
   if (j < 0 || L <= 0 || s0 >= a.num_tokens) return;
   if ((int64_t)s0 + L > a.num_tokens) L = (int)(a.num_tokens - s0);
-  const int t0 = j * a.chunk;
+  const int t0 = j * U;
   if (t0 >= L || !lane_ok) return;
-  const int t1 = min(L, t0 + a.chunk);
+  const int t1 = min(L, t0 + U);
 
   const int64_t xrs = a.x_rs, ors = a.out_rs;
   const S* xb = (const S*)a.x + (int64_t)s0 * xrs + c0;
