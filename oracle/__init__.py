@@ -36,6 +36,10 @@ def lib():
         L.oracle_conv_spec.argtypes = [I32, I32, I32, I32, I32, I32, I32, I32, P, I64, P, I64,
                                        P, P, P, P, I32, I32, I32, P, I64, P, P, P, P, I64,
                                        P, I64, I32]
+        L.oracle_conv_spec_varlen.restype = I32
+        L.oracle_conv_spec_varlen.argtypes = [I32, I32, I32, I32, I32, I32, I32, I32, P, I64,
+                                              P, I64, P, P, P, P, I32, I32, P, P, I64, P, P,
+                                              P, P, I64, P, I64, I32]
         L.oracle_cca.restype = I32
         L.oracle_cca.argtypes = [I32, I32, I32, I32, I32, I32, I32, I32,
                                  P, I64, P, I64, P, I64, P, I64, P, I64, P,
@@ -158,6 +162,38 @@ def conv_spec(case, num_accepted, *, out_dtype: Optional[str] = None, absum: boo
         *_fuse_args(x, token_indices, resid, outer), nthreads or default_threads())
     if rc != 0:
         raise RuntimeError(f"oracle_conv_spec failed: {rc}")
+    return out, pool, ab
+
+
+def conv_spec_varlen(case, num_accepted, qsl, *, out_dtype: Optional[str] = None,
+                     absum: bool = False, row_mask: Optional[np.ndarray] = None,
+                     nthreads: Optional[int] = None, pool: Optional[np.ndarray] = None,
+                     x: Optional[np.ndarray] = None, token_indices: Optional[np.ndarray] = None,
+                     resid: Optional[np.ndarray] = None, outer: Optional[np.ndarray] = None):
+    """Speculative update with a draft count per request: request r owns rows
+    [qsl[r], qsl[r+1]) of x; its slot is case.decode_slots[r] (batch =
+    case.num_decodes). Rows of skipped requests (0 or more than S drafts) keep
+    the zeros `out` starts with. Returns (out, pool_after, absum_or_None)."""
+    odt = out_dtype or case.dtype
+    qsl = _c(qsl, np.int32)
+    B = case.num_decodes
+    T = int(qsl[B])
+    C = case.C
+    x = _c(case.x[:T] if x is None else x)
+    out = np.zeros((x.shape[0], C), _NP[odt])
+    ab = np.zeros((T, C), np.float64) if absum else None
+    pool = np.array(case.pool, copy=True) if pool is None else pool
+    S = _state_len(case, pool)
+    dsl = _c(case.decode_slots, np.int32)
+    acc = _c(num_accepted, np.int32)
+    rm = _c(row_mask, np.uint8)
+    rc = lib().oracle_conv_spec_varlen(
+        C, case.K, case.d, S, _layout(case), 1 if case.act == "silu" else 0, _DT[case.dtype],
+        _DT[odt], _p(x), C, _p(out), C, _p(ab), _p(_c(case.w)), _p(_c(case.bias)), _p(pool),
+        pool.shape[0], B, _p(qsl), _p(dsl), 1, _p(acc), _p(rm),
+        *_fuse_args(x, token_indices, resid, outer), nthreads or default_threads())
+    if rc != 0:
+        raise RuntimeError(f"oracle_conv_spec_varlen failed: {rc}")
     return out, pool, ab
 
 

@@ -33,8 +33,11 @@
 // library depthwise+grouped convolutions and its special cases). The
 // speculative update is pinned by the library convolution of each request's
 // accepted token sequence across chains of steps, by its reduction to the
-// one-token decode, and by its padding and clamping rules; the wide-buffer
-// non-speculative steps by their reduction to the narrow buffer.
+// one-token decode, and by its padding and clamping rules; the per-request
+// draft counts by the same accepted-sequence chains with requests that skip
+// steps, by the page's slices per request in mixed batches, and by reduction
+// to the uniform call; the wide-buffer non-speculative steps by their
+// reduction to the narrow buffer.
 #include <cmath>
 #include <cstdint>
 #include <algorithm>
@@ -258,6 +261,60 @@ void conv_channels(const ConvArgs& a, const std::vector<Req>& reqs, int c0, int 
   }
 }
 
+// Shared by the uniform and the per-request-length calls: request r owns rows
+// [start(r), start(r) + len(r)). A request with len 0 is skipped (the GDN
+// page's loop: `if q_i == 0: continue`); one with len > S cannot be rolled
+// (the kept range S - len would be negative) and is skipped as well.
+template <class Start, class Len>
+void spec_requests(int32_t C, int32_t K, int32_t d, int32_t S, int32_t state_layout, int32_t act,
+                   int32_t io_dtype, int32_t out_dtype, const void* x, int64_t x_rs, void* out,
+                   int64_t out_rs, double* absum, const void* w, const void* bias, void* pool,
+                   int32_t num_slots, int32_t B, Start start_of, Len len_of, const int32_t* slots,
+                   int64_t slot_stride, const int32_t* num_accepted, const uint8_t* row_mask,
+                   const Fuse& fz, int32_t nthreads) {
+  const int H = (K - 1) * d;
+  auto body = [&](int c0, int c1) {
+    std::vector<double> ext, buf((size_t)S);
+    for (int r = 0; r < B; ++r) {
+      const int q = len_of(r);
+      if (q <= 0 || q > S) continue;
+      ext.assign((size_t)(H + q), 0.0);
+      const int32_t slot = slots[r * slot_stride];
+      const bool valid = slot >= 0 && slot < num_slots;
+      const int a = std::min(std::max(num_accepted[r], 1), std::min(q, S - H + 1));
+      const int64_t start = start_of(r);
+      for (int c = c0; c < c1; ++c) {
+        for (int j = 0; j < S; ++j)
+          buf[j] = valid ? ld(pool, io_dtype, sidx(state_layout, slot, C, S, c, j)) : 0.0;
+        for (int u = 0; u < H; ++u) ext[u] = buf[a - 1 + u];
+        for (int t = 0; t < q; ++t) ext[H + t] = ld(x, io_dtype, fz.row(start + t) * x_rs + c);
+        const double b = bias ? ld(bias, io_dtype, c) : 0.0;
+        for (int t = 0; t < q; ++t) {
+          const int64_t row = start + t;
+          if (row_mask && !row_mask[row]) continue;
+          double z = b, A = std::fabs(b);
+          for (int k = 0; k < K; ++k) {
+            double term = ld(w, io_dtype, (int64_t)c * K + k) * ext[H + t - (int64_t)(K - 1 - k) * d];
+            z += term;
+            A += std::fabs(term);
+          }
+          const int64_t prow = fz.row(row);
+          const double y = fuse_value(fz, io_dtype, prow, c, act ? z / (1.0 + std::exp(-z)) : z, &A);
+          st(out, out_dtype, prow * out_rs + c, y);
+          if (absum) absum[row * C + c] = A;
+        }
+        if (valid) {
+          for (int j = 0; j < S - q; ++j)
+            st(pool, io_dtype, sidx(state_layout, slot, C, S, c, j), buf[a + j]);
+          for (int t = 0; t < q; ++t)
+            st(pool, io_dtype, sidx(state_layout, slot, C, S, c, (S - q) + t), ext[H + t]);
+        }
+      }
+    }
+  };
+  parallel_for(C, nthreads, body);
+}
+
 }  // namespace
 
 extern "C" {
@@ -319,6 +376,18 @@ int oracle_conv(int32_t C, int32_t K, int32_t d, int32_t act, int32_t io_dtype,
 //   outputs  = the depthwise definition over ext
 //   pool[s]  = [pool[s][c][a : a+S-q], x_r]      (length S; q <= S required)
 // A slot outside the pool is a padding row: zero window, no write.
+
+// Speculative multi-token update with a rolling state buffer (GDN page,
+// _spec_forward: "roll the buffer: drop the accepted history from the front,
+// append the new draft tokens, keep total length == state_len").
+// pool is (num_slots, C, S), S >= H = (K-1)*d. Request r owns rows
+// [r*q, (r+1)*q) and has `a = num_accepted[r]` accepted tokens from the
+// previous step, clamped to [1, min(q, S-H+1)] (the range in which the
+// page's slices are well formed). Then
+//   ext      = [pool[s][c][a-1 : a-1+H], x_r]     (the window ending at the last accepted input)
+//   outputs  = the depthwise definition over ext
+//   pool[s]  = [pool[s][c][a : a+S-q], x_r]      (length S; q <= S required)
+// A slot outside the pool is a padding row: zero window, no write.
 int oracle_conv_spec(int32_t C, int32_t K, int32_t d, int32_t S, int32_t state_layout, int32_t act,
                      int32_t io_dtype, int32_t out_dtype, const void* x, int64_t x_rs,
                      void* out, int64_t out_rs, double* absum, const void* w,
@@ -327,48 +396,39 @@ int oracle_conv_spec(int32_t C, int32_t K, int32_t d, int32_t S, int32_t state_l
                      const int32_t* num_accepted, const uint8_t* row_mask,
                      const int32_t* token_indices, const void* resid, int64_t resid_rs,
                      const void* outer, int64_t outer_rs, int32_t nthreads) {
-  const Fuse fz{token_indices, resid, resid_rs, outer, outer_rs};
   const int H = (K - 1) * d;
   if (C <= 0 || K <= 0 || d <= 0 || B < 0 || q < 1 || S < H || q > S) return -2;
   if (!dtype_ok(io_dtype) || !dtype_ok(out_dtype)) return -3;
-  const int amax = std::min(q, S - H + 1);
-  auto body = [&](int c0, int c1) {
-    std::vector<double> ext((size_t)(H + q)), buf((size_t)S);
-    for (int r = 0; r < B; ++r) {
-      const int32_t slot = slots[r * slot_stride];
-      const bool valid = slot >= 0 && slot < num_slots;
-      const int a = std::min(std::max(num_accepted[r], 1), amax);
-      const int64_t start = (int64_t)r * q;
-      for (int c = c0; c < c1; ++c) {
-        for (int j = 0; j < S; ++j)
-          buf[j] = valid ? ld(pool, io_dtype, sidx(state_layout, slot, C, S, c, j)) : 0.0;
-        for (int u = 0; u < H; ++u) ext[u] = buf[a - 1 + u];
-        for (int t = 0; t < q; ++t) ext[H + t] = ld(x, io_dtype, fz.row(start + t) * x_rs + c);
-        const double b = bias ? ld(bias, io_dtype, c) : 0.0;
-        for (int t = 0; t < q; ++t) {
-          const int64_t row = start + t;
-          if (row_mask && !row_mask[row]) continue;
-          double z = b, A = std::fabs(b);
-          for (int k = 0; k < K; ++k) {
-            double term = ld(w, io_dtype, (int64_t)c * K + k) * ext[H + t - (int64_t)(K - 1 - k) * d];
-            z += term;
-            A += std::fabs(term);
-          }
-          const int64_t prow = fz.row(row);
-          const double y = fuse_value(fz, io_dtype, prow, c, act ? z / (1.0 + std::exp(-z)) : z, &A);
-          st(out, out_dtype, prow * out_rs + c, y);
-          if (absum) absum[row * C + c] = A;
-        }
-        if (valid) {
-          for (int j = 0; j < S - q; ++j)
-            st(pool, io_dtype, sidx(state_layout, slot, C, S, c, j), buf[a + j]);
-          for (int t = 0; t < q; ++t)
-            st(pool, io_dtype, sidx(state_layout, slot, C, S, c, (S - q) + t), ext[H + t]);
-        }
-      }
-    }
-  };
-  parallel_for(C, nthreads, body);
+  spec_requests(C, K, d, S, state_layout, act, io_dtype, out_dtype, x, x_rs, out, out_rs, absum,
+                w, bias, pool, num_slots, B, [&](int r) { return (int64_t)r * q; },
+                [&](int) { return q; }, slots, slot_stride, num_accepted, row_mask,
+                Fuse{token_indices, resid, resid_rs, outer, outer_rs}, nthreads);
+  return 0;
+}
+
+// The same update with a draft count per request (GDN page, _spec_forward's
+// per-sequence loop over spec_query_start_loc): request r owns rows
+// [qsl[r], qsl[r+1]) and q_r = qsl[r+1] - qsl[r]; the rule above applies with
+// q = q_r. q_r = 0: the request is skipped (nothing read or written);
+// q_r > S: skipped too (its buffer cannot take the drafts).
+int oracle_conv_spec_varlen(int32_t C, int32_t K, int32_t d, int32_t S, int32_t state_layout,
+                            int32_t act, int32_t io_dtype, int32_t out_dtype, const void* x,
+                            int64_t x_rs, void* out, int64_t out_rs, double* absum,
+                            const void* w, const void* bias, void* pool, int32_t num_slots,
+                            int32_t B, const int32_t* qsl, const int32_t* slots,
+                            int64_t slot_stride, const int32_t* num_accepted,
+                            const uint8_t* row_mask, const int32_t* token_indices,
+                            const void* resid, int64_t resid_rs, const void* outer,
+                            int64_t outer_rs, int32_t nthreads) {
+  const int H = (K - 1) * d;
+  if (C <= 0 || K <= 0 || d <= 0 || B < 0 || S < H || !qsl) return -2;
+  if (!dtype_ok(io_dtype) || !dtype_ok(out_dtype)) return -3;
+  for (int r = 0; r < B; ++r)
+    if (qsl[r + 1] < qsl[r] || qsl[r] < 0) return -2;
+  spec_requests(C, K, d, S, state_layout, act, io_dtype, out_dtype, x, x_rs, out, out_rs, absum,
+                w, bias, pool, num_slots, B, [&](int r) { return (int64_t)qsl[r]; },
+                [&](int r) { return qsl[r + 1] - qsl[r]; }, slots, slot_stride, num_accepted,
+                row_mask, Fuse{token_indices, resid, resid_rs, outer, outer_rs}, nthreads);
   return 0;
 }
 

@@ -228,6 +228,43 @@ def config3b_spec(seed: int = SEED_BASE + 0x35, *, C: int = 8192, B: int = 128,
                      num_decodes=B, q=num_spec + 1, num_spec=num_spec)
 
 
+def spec_varlen_case(name: str, seed: int, *, C: int, K: int, d: int, dtype: str, act: str,
+                     w_std: float, bias_std: Optional[float], num_slots: int, B: int,
+                     num_spec: int, q_lens=None, q_max: Optional[int] = None):
+    """Speculative requests with a draft count each (rolling buffer of
+    S = H + num_spec entries). Draft counts are `q_lens`, else uniform in
+    {0 .. q_max} (default num_spec + 1). Returns (case, qsl): request r owns
+    rows [qsl[r], qsl[r+1]) of case.x and slot case.decode_slots[r]
+    (case.num_decodes = B; case.q is not used)."""
+    rng = np.random.default_rng(seed ^ 0x5EC)
+    if q_lens is None:
+        hi = num_spec + 1 if q_max is None else q_max
+        q_lens = rng.integers(0, hi + 1, size=B)
+    q_lens = np.asarray(q_lens, np.int64)
+    assert q_lens.shape[0] == B
+    qsl = np.zeros(B + 1, np.int32)
+    qsl[1:] = np.cumsum(q_lens)
+    T = int(qsl[-1])
+    # T rows as "prefill" lengths give x its shape; the requests are then
+    # re-labelled as speculative ones (all continuing their buffer)
+    base = conv_case(name, seed, C=C, K=K, d=d, dtype=dtype, act=act, w_std=w_std,
+                     bias_std=bias_std, num_slots=num_slots, num_decodes=B, q=1,
+                     num_spec=num_spec)
+    x = _normal(rng, (T, C), 1.0, dtype)
+    from dataclasses import replace
+    return replace(base, x=x), qsl
+
+
+def config3b_spec_varlen(seed: int = SEED_BASE + 0x37, *, C: int = 8192, B: int = 128,
+                         num_spec: int = 3, num_slots: int = 1024):
+    """Speculative update with per-request draft counts uniform in
+    {0 .. num_spec + 1} (the GDN page's per-sequence loop), otherwise as
+    config3b_spec. Returns (case, qsl)."""
+    return spec_varlen_case("cfg3b_spec_varlen", seed, C=C, K=4, d=1, dtype="bf16", act="silu",
+                            w_std=0.25, bias_std=0.1, num_slots=num_slots, B=B,
+                            num_spec=num_spec)
+
+
 def config4(seed: int = SEED_BASE + 4, *, C: int = 8192, num_decodes: int = 256,
             Bp: int = 16, min_len: int = 128, max_len: int = 4096,
             grid: int = 512, num_slots: int = 1024) -> ConvCase:
