@@ -283,6 +283,132 @@ def traffic_for(kernel_key, files=DW_SOURCES):
     return e.get("bytes_per_launch")
 
 
+def time_launches(fn_steps, steps):
+    """Average GPU time per launch (ms) of `steps` back-to-back launches made by
+    fn_steps(), measured two ways with HIP events on the launch stream: eager
+    launches, and one replay of the launches captured in a HIP graph (no host
+    launch cost). Graph replay adds a few us between nodes on large kernels.
+    Either way the average includes the gaps between back-to-back launches (an
+    event pair around each launch would add the events' own cost, which is
+    larger). Returns (eager_ms, graph_ms)."""
+    import torch
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    # a GPU spin ahead of the region lets the host queue all launches before
+    # the first runs, so small kernels are not timed at the host's launch rate
+    torch.cuda._sleep(5_000_000)
+    s.record()
+    fn_steps()
+    e.record()
+    torch.cuda.synchronize()
+    eager = s.elapsed_time(e) / steps
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn_steps()
+    g.replay()                        # untimed first replay
+    torch.cuda.synchronize()
+    s.record()
+    g.replay()
+    e.record()
+    torch.cuda.synchronize()
+    graph = s.elapsed_time(e) / steps
+    return eager, graph
+
+
+def spec_varlen_alg_bytes(case, qsl):
+    """Speculative update with a draft count per request: x read + out written
+    for every draft row; each request with drafts reads and writes its whole
+    state row (S entries: the roll moves all of them); weights, bias, accepted
+    counts and offsets read once."""
+    es, C = case.elsize, case.C
+    qs = [int(qsl[r + 1] - qsl[r]) for r in range(case.num_decodes)]
+    b = int(qsl[-1]) * C * es * 2
+    b += sum(2 * C * case.S * es for r, q in enumerate(qs)
+             if q > 0 and 0 <= case.decode_slots[r] < case.num_slots)
+    b += C * case.K * es + (C * es if case.bias is not None else 0)
+    b += 4 * case.num_decodes + 4 * (case.num_decodes + 1)
+    return b
+
+
+def spec_varlen_bench(args):
+    """Speculative update with per-request draft counts (128 requests, counts
+    uniform in {0..4}, 8192 channels, width 4, rolling buffer of 6 entries,
+    bf16, bias + SiLU). One step = one sc_conv_update_spec_varlen call."""
+    import numpy as np
+    import torch
+    import synthetic
+    import stateful_causal_short_amd as scs
+    from tests._gpu import dev
+    case, qsl = synthetic.config3b_spec_varlen()
+    if args.state_layout == "sd":
+        case = synthetic.as_sd(case)
+    B, T = case.num_decodes, int(qsl[-1])
+    acc = np.minimum(synthetic.num_accepted(synthetic.SEED_BASE + 0x38, B, 4),
+                     np.maximum(np.diff(qsl), 1)).astype(np.int32)
+    alg = spec_varlen_alg_bytes(case, qsl)
+    max_q = int(np.diff(qsl).max())
+    set_bytes = T * case.C * case.elsize * 2 + case.pool.nbytes
+    nsets = int(min(8, max(2, -(-ROTATE_BYTES // set_bytes))))
+    log(f"spec varlen B={B} T={T} C={case.C} S={case.S} layout={case.layout}; "
+        f"alg bytes/step={alg}; {nsets} rotating buffer sets")
+    w = dev(case.w)
+    b = dev(case.bias)
+    slots = dev(np.asarray(case.decode_slots, np.int32))
+    accd = dev(acc)
+    qd = dev(qsl)
+    x0, p0 = dev(case.x), dev(case.pool)
+    sets = [(x0 if i == 0 else x0.clone(), torch.empty_like(x0), p0 if i == 0 else p0.clone())
+            for i in range(nsets)]
+
+    def step(i):
+        x, out, pool = sets[i % nsets]
+        scs.sc_conv_update_spec_varlen(x, out, w, b, pool, slots, accd, qd, max_query_len=max_q,
+                                       dilation=case.d, activation=case.act,
+                                       state_layout=case.layout)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    eager, graph = time_launches(lambda: [step(args.warmup + i) for i in range(args.steps)],
+                                 args.steps)
+    ms = min(eager, graph)
+    gbps = alg / (ms * 1e-3) / 1e9
+    result = {
+        "metric": "tokens/s and achieved HBM GB/s (% of peak), speculative conv update",
+        "value": T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": case.dtype, "data": "synthetic",
+        "config": {"workload": case.name, "requests": B, "tokens": T, "max_query_len": max_q,
+                   "channels": case.C, "width": case.K, "dilation": case.d,
+                   "activation": case.act, "state_slots": case.num_slots, "state_len": case.S,
+                   "state_layout": case.layout},
+        "hbm_gbps": gbps, "pct_peak": 100.0 * gbps / PEAK_GBPS,
+        "kernel_us": {"spec_update": ms * 1e3},
+        "timing": {"step": {"eager_us": eager * 1e3, "graph_us": graph * 1e3}},
+        "roofline": {"kernel": "spec_update", "bound": "hbm", "achieved": gbps,
+                     "peak": PEAK_GBPS, "unit": "GB/s", "frac": gbps / PEAK_GBPS,
+                     "traffic": None, "alg_bytes_per_launch": alg},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        import oracle
+        threads = min(16, oracle.default_threads())
+        runs, t0 = 0, time.perf_counter()
+        while True:
+            oracle.conv_spec_varlen(case, acc, qsl, nthreads=threads)
+            runs += 1
+            el = time.perf_counter() - t0
+            if el >= 10.0 or runs >= 1000:
+                break
+        result["cpu_baseline"] = {
+            "value": T * runs / el, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"the full batch ({T} tokens) run {runs}x through the fp64 oracle, "
+                      f"{el:.1f} s wall on {threads} threads", "cpu_model": cpu_model()}
+    print(json.dumps(result), flush=True)
+
+
 def cca_bench(args):
     """CCA q/k conv on the 32k-token mixed batch (512 decodes + 64 prefills,
     16 q heads, 4 kv heads, head_dim 128, kernels 2 and 2). One step = one
@@ -468,7 +594,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="varlen_prefill",
                     choices=["varlen_prefill", "single", "decode", "update_q4", "spec",
-                             "ple_mixed", "ple_fused", "cca", "copy"])
+                             "spec_varlen", "ple_mixed", "ple_fused", "cca", "copy"])
     ap.add_argument("--state-layout", default="ds", choices=["ds", "sd"],
                     help="state pool layout: (slots, C, S) or (slots, S, C)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -494,6 +620,8 @@ def main():
         return cca_bench(args)
     if args.workload == "copy":
         return copy_calibration(args)
+    if args.workload == "spec_varlen":
+        return spec_varlen_bench(args)
 
     case = conv_workload(args.workload)
     if args.state_layout == "sd":
@@ -527,34 +655,7 @@ def main():
     timing = {}
 
     def timed(name, fn_steps):
-        """Average GPU time per launch of K back-to-back launches, measured two
-        ways with HIP events on the launch stream: eager launches, and one
-        replay of the K launches captured in a HIP graph (no host launch cost).
-        Graph replay adds a few us between nodes on large kernels. The faster
-        is reported and both are kept. Either way the average includes the
-        gaps between back-to-back launches (an event pair around each launch
-        would add the events' own cost, which is larger)."""
-        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        # a GPU spin ahead of the region lets the host queue all K launches
-        # before the first runs, so small kernels are not timed at the host's
-        # launch rate
-        torch.cuda._sleep(5_000_000)
-        s.record()
-        fn_steps()
-        e.record()
-        torch.cuda.synchronize()
-        eager = s.elapsed_time(e) / args.steps
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            fn_steps()
-        g.replay()                        # untimed first replay
-        torch.cuda.synchronize()
-        s.record()
-        g.replay()
-        e.record()
-        torch.cuda.synchronize()
-        graph = s.elapsed_time(e) / args.steps
+        eager, graph = time_launches(fn_steps, args.steps)
         timing[name] = {"eager_us": eager * 1e3, "graph_us": graph * 1e3}
         return min(eager, graph)
 

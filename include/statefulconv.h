@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define SC_ABI_VERSION 2
+#define SC_ABI_VERSION 3
 
 typedef enum {
   SC_OK = 0,
@@ -191,6 +191,32 @@ sc_status sc_conv_update_spec(const sc_conv_desc* desc, const void* x, void* out
                               int32_t num_slots, const int32_t* state_indices,
                               const int32_t* num_accepted_tokens, int32_t batch,
                               int32_t q, const sc_conv_fuse* fuse, void* stream);
+
+/* Speculative update with a draft count per request (GDN page
+ * "vllm.model_executor.layers.mamba.ops.cpu.gdn_attention", _spec_forward,
+ * the per-sequence loop over spec_query_start_loc that serves batches whose
+ * requests draft different numbers of tokens). Request r owns rows
+ * [query_start_loc[r], query_start_loc[r+1]) of x and out; with
+ * q_r = query_start_loc[r+1] - query_start_loc[r], the rule of
+ * sc_conv_update_spec applies to it with q = q_r (a clamped to
+ * [1, min(q_r, S-H+1)]). A request with q_r = 0 is skipped (the page's loop
+ * continues past it): nothing is read or written for it.
+ *   query_start_loc (device) int32 (batch+1), non-decreasing,
+ *                   query_start_loc[0] >= 0, query_start_loc[batch] <= num_tokens.
+ *   max_query_len   (host) a bound on every q_r; must be <= S
+ *                   (SC_ERR_INVALID_ARG otherwise). A request that breaks
+ *                   the bound, or whose rows leave [0, num_tokens), is
+ *                   skipped whole (its rows and slot are left as they were).
+ *   num_tokens      (host) rows of x and out.
+ * Other arguments as for sc_conv_update_spec. batch = 0, num_tokens = 0 or
+ * max_query_len = 0: no-op. */
+sc_status sc_conv_update_spec_varlen(const sc_conv_desc* desc, const void* x, void* out,
+                                     const void* weight, const void* bias, void* state_pool,
+                                     int32_t num_slots, const int32_t* state_indices,
+                                     const int32_t* num_accepted_tokens,
+                                     const int32_t* query_start_loc, int32_t batch,
+                                     int64_t num_tokens, int32_t max_query_len,
+                                     const sc_conv_fuse* fuse, void* stream);
 
 /* Row copies between a slot pool and a dense buffer; each row is row_bytes.
  * gather: dense[i] = pool[idx[i*idx_stride]], or zeros when that index is

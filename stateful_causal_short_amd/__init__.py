@@ -17,7 +17,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libstatefulconv.so")
 
 SC_OK = 0
-SC_ABI_VERSION = 2   # the struct layouts and signatures below
+SC_ABI_VERSION = 3   # the struct layouts and signatures below
 STATUS = {0: "SC_OK", -1: "SC_ERR_NULL_ARG", -2: "SC_ERR_INVALID_ARG",
           -3: "SC_ERR_DTYPE", -4: "SC_ERR_STATE_CAPACITY",
           -5: "SC_ERR_UNSUPPORTED", -6: "SC_ERR_HIP"}
@@ -25,7 +25,8 @@ SC_DTYPE_F32, SC_DTYPE_BF16 = 0, 1
 SC_ACT_NONE, SC_ACT_SILU = 0, 1
 SC_STATE_DS, SC_STATE_SD = 0, 1
 
-EXPORTS = ("sc_conv_prefill_varlen", "sc_conv_update", "sc_conv_update_spec", "sc_state_gather",
+EXPORTS = ("sc_conv_prefill_varlen", "sc_conv_update", "sc_conv_update_spec",
+           "sc_conv_update_spec_varlen", "sc_state_gather",
            "sc_state_scatter", "sc_cca_qk_conv", "sc_status_string",
            "sc_abi_version")
 
@@ -89,6 +90,9 @@ def lib():
         L.sc_conv_update.argtypes = [D, P, P, P, P, P, I32, P, P, I32, I32, F, P]
         L.sc_conv_update_spec.restype = I32
         L.sc_conv_update_spec.argtypes = [D, P, P, P, P, P, I32, P, P, I32, I32, F, P]
+        L.sc_conv_update_spec_varlen.restype = I32
+        L.sc_conv_update_spec_varlen.argtypes = [D, P, P, P, P, P, I32, P, P, P, I32, I64, I32,
+                                                 F, P]
         L.sc_state_gather.restype = I32
         L.sc_state_gather.argtypes = [P, I32, I64, P, I64, I32, P, P]
         L.sc_state_scatter.restype = I32
@@ -293,6 +297,33 @@ def sc_conv_update_spec(x, out, weight, bias, state_pool, state_indices, num_acc
         _ptr(num_accepted_tokens), rows // q, q,
         _fuse(x, out, token_indices, accumulate, outer_residual), _stream(stream, x))
     _check("sc_conv_update_spec", st)
+
+
+def sc_conv_update_spec_varlen(x, out, weight, bias, state_pool, state_indices,
+                               num_accepted_tokens, query_start_loc, *, max_query_len: int,
+                               dilation: int = 1, activation: Optional[str] = "silu",
+                               token_indices=None, accumulate: bool = False,
+                               outer_residual=None, state_layout: str = "ds", stream=None):
+    """Speculative update with a draft count per request: request r owns rows
+    [query_start_loc[r], query_start_loc[r+1]) of x (int32, batch+1 entries);
+    max_query_len bounds every count (<= S). Updates ``state_pool`` in place."""
+    torch = _torch()
+    for name, t in (("num_accepted_tokens", num_accepted_tokens),
+                    ("query_start_loc", query_start_loc)):
+        if t.dtype != torch.int32 or not t.is_contiguous():
+            raise ValueError(f"{name}: expected a contiguous int32 tensor")
+    batch = query_start_loc.shape[0] - 1
+    if batch < 0:
+        raise ValueError("query_start_loc: expected batch + 1 entries")
+    rows = x.shape[0] if token_indices is None else token_indices.shape[0]
+    desc = _conv_desc(x, out, weight, state_pool, dilation, activation, state_indices,
+                      state_layout)
+    st = lib().sc_conv_update_spec_varlen(
+        ctypes.byref(desc), _ptr(x), _ptr(out), _ptr(weight), _ptr(bias),
+        _ptr(state_pool), state_pool.shape[0], _index(state_indices, "state_indices")[0],
+        _ptr(num_accepted_tokens), _ptr(query_start_loc), batch, rows, max_query_len,
+        _fuse(x, out, token_indices, accumulate, outer_residual), _stream(stream, x))
+    _check("sc_conv_update_spec_varlen", st)
 
 
 def sc_state_gather(state_pool, idx, dense, *, stream=None):

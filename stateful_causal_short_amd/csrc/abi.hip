@@ -236,6 +236,57 @@ sc_status sc_conv_update_spec(const sc_conv_desc* desc, const void* x, void* out
                                        (hipStream_t)stream));
 }
 
+sc_status sc_conv_update_spec_varlen(const sc_conv_desc* desc, const void* x, void* out,
+                                     const void* weight, const void* bias, void* state_pool,
+                                     int32_t num_slots, const int32_t* state_indices,
+                                     const int32_t* num_accepted_tokens,
+                                     const int32_t* query_start_loc, int32_t batch,
+                                     int64_t num_tokens, int32_t max_query_len,
+                                     const sc_conv_fuse* fuse, void* stream) {
+  if (!desc) return SC_ERR_NULL_ARG;
+  int H = 0;
+  sc_status st = check_conv_desc(desc, &H);
+  if (st != SC_OK) return st;
+  if ((st = check_fuse(fuse, desc)) != SC_OK) return st;
+  if (batch < 0 || num_tokens < 0 || max_query_len < 0 || num_slots < 0)
+    return SC_ERR_INVALID_ARG;
+  // the rolled buffer keeps S - q old entries: every request's drafts must fit
+  if (max_query_len > desc->state_len) return SC_ERR_INVALID_ARG;
+  if (batch == 0 || num_tokens == 0 || max_query_len == 0) return SC_OK;
+  if (!x || !out || !weight || !state_indices || !num_accepted_tokens || !query_start_loc)
+    return SC_ERR_NULL_ARG;
+  if (!state_pool && num_slots > 0) return SC_ERR_NULL_ARG;
+  if (x == out) return SC_ERR_INVALID_ARG;
+  if (num_tokens > 0x7FFFFFFFLL) return SC_ERR_UNSUPPORTED;
+  sc::ConvArgs a{};
+  a.x = x;
+  a.out = out;
+  a.w = weight;
+  a.bias = bias;
+  a.pool = state_pool;
+  a.qsl = query_start_loc;
+  a.slots = state_indices;
+  a.has_init = nullptr;
+  a.num_acc = num_accepted_tokens;
+  a.x_rs = desc->x_row_stride;
+  a.out_rs = desc->out_row_stride;
+  a.slot_stride = desc->state_indices_stride;
+  a.num_tokens = num_tokens;
+  a.C = desc->channels;
+  a.num_slots = num_slots;
+  a.batch = batch;
+  a.q = max_query_len;
+  a.ckpt_grid = 0;
+  a.S = desc->state_len;
+  a.sd = desc->state_layout == SC_STATE_SD ? 1 : 0;
+  if ((st = apply_fuse(fuse, out, a)) != SC_OK) return st;
+  const bool aligned = conv_aligned(desc, x, out, weight, bias, state_pool) &&
+                       (!a.outer || al16(a.outer));
+  return from_hip(sc::launch_conv_spec(a, desc->dtype, desc->width, desc->dilation,
+                                       desc->activation == SC_ACT_SILU, aligned,
+                                       (hipStream_t)stream));
+}
+
 sc_status sc_state_gather(const void* pool, int32_t num_slots, int64_t row_bytes,
                           const int32_t* idx, int64_t idx_stride, int32_t n, void* dense,
                           void* stream) {

@@ -9,8 +9,10 @@
 // page's slices are well formed) reads the H entries starting at a-1 as its
 // history, produces out[t] = act(b + sum_k w[k] * ext[H + t - (K-1-k)*d]) over
 // ext = [history, x], and leaves its buffer as the entries from a on, cut to
-// S - q, followed by the q new tokens. A plain (non-speculative) update on such
-// a buffer uses the first H entries as the window and leaves the rest as they
+// S - q, followed by the q new tokens. With a draft count per request (the GDN
+// page's loop over spec_query_start_loc) request r owns rows [qsl[r], qsl[r+1])
+// and one with no drafts, or more than S, is skipped whole. A plain
+// (non-speculative) update on such a buffer uses the first H entries as the window and leaves the rest as they
 // were ("only the first width-1 columns hold the real conv state", GDN page,
 // _spec_aware_nonspec).
 //
@@ -56,7 +58,14 @@ __global__ __launch_bounds__(kBlock) void conv_rollbuf(ConvArgs a) {
   const int cbase = cb * kBlock * VEC;
   const int c0 = cbase + tid * VEC;
   const bool lane_ok = c0 < a.C;
-  const int Sl = a.S, q = a.q;
+  const int Sl = a.S;
+  int q = a.q;
+  int64_t start = (int64_t)r * q;
+  if (a.qsl) {   // a draft count per request; a.q bounds them all
+    start = a.qsl[r];
+    q = a.qsl[r + 1] - a.qsl[r];
+    if (q <= 0 || q > a.q || q > Sl || start < 0 || start + q > a.num_tokens) return;
+  }
   const int nvec = (min(a.C - cbase, kBlock * VEC) / VEC) * Sl;
   const int lw = ds_lane_words(Sl, kBlock);  // DS: words per lane in LDS
   uint32_t* rw = (uint32_t*)region;
@@ -85,8 +94,8 @@ __global__ __launch_bounds__(kBlock) void conv_rollbuf(ConvArgs a) {
 
   // physical row of the request's token u (through the row map when fused)
   auto prow = [&](int u) -> int64_t {
-    if constexpr (FUSE) return phys_row(a, (int64_t)r * q + u);
-    else return (int64_t)r * q + u;
+    if constexpr (FUSE) return phys_row(a, start + u);
+    else return start + u;
   };
   // token rows (and fused residuals), then the slot, then the state region
   u32x4 xr[QM], rres[FUSE ? QM : 1], rout[FUSE ? QM : 1];
@@ -296,7 +305,14 @@ __global__ __launch_bounds__(kBlock) void conv_spec_generic(ConvArgs a, int K, i
   if (r >= a.batch) return;
   const int c = cb * kBlock + (int)threadIdx.x;
   if (c >= a.C) return;
-  const int H = (K - 1) * D, Sl = a.S, q = a.q;
+  const int H = (K - 1) * D, Sl = a.S;
+  int q = a.q;
+  int64_t start = (int64_t)r * q;
+  if (a.qsl) {   // a draft count per request; a.q bounds them all
+    start = a.qsl[r];
+    q = a.qsl[r + 1] - a.qsl[r];
+    if (q <= 0 || q > a.q || q > Sl || start < 0 || start + q > a.num_tokens) return;
+  }
   float wt[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k)
@@ -312,7 +328,7 @@ __global__ __launch_bounds__(kBlock) void conv_spec_generic(ConvArgs a, int K, i
     return a.sd ? pool[((int64_t)vs * Sl + u) * a.C + c] : pool[((int64_t)vs * a.C + c) * Sl + u];
   };
   // the request's token u in x / out (through the row map when one is given)
-  auto pr = [&](int u) -> int64_t { return phys_row(a, (int64_t)r * q + u); };
+  auto pr = [&](int u) -> int64_t { return phys_row(a, start + u); };
   for (int t = 0; t < q; ++t) {
     float accf = b;
     for (int k = 0; k < K; ++k) {

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_function():
     assert set(names) == set(scs.EXPORTS)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.sc_abi_version() == 2
+    assert lib.sc_abi_version() == 3
     for s in (0, -1, -2, -3, -4, -5, -6):
         assert lib.sc_status_string(s)
 
@@ -107,6 +107,34 @@ def test_spec_rules():
     assert spec(d, batch=-1) == INVALID
     assert spec(d, x=None, out=None, w=None, slots=None, acc=None, pool=None, batch=0) == OK
     assert spec(d, q=0) == OK
+
+
+def spec_varlen(d, *, x=P, out=P2, w=P, pool=P, num_slots=4, slots=P, acc=P, qsl=P, batch=2,
+                T=6, maxq=3, fuse=None):
+    return scs.lib().sc_conv_update_spec_varlen(
+        None if d is None else ctypes.byref(d), x, out, w, None, pool, num_slots, slots, acc,
+        qsl, batch, T, maxq, None if fuse is None else ctypes.byref(fuse), None)
+
+
+def test_spec_varlen_rules():
+    d = desc(state_len=6)
+    assert spec_varlen(None) == NULL
+    assert spec_varlen(d, qsl=None) == NULL
+    assert spec_varlen(d, acc=None) == NULL
+    assert spec_varlen(d, slots=None) == NULL
+    assert spec_varlen(d, pool=None) == NULL
+    assert spec_varlen(d, out=P) == INVALID            # out aliases x
+    assert spec_varlen(d, maxq=7) == INVALID           # 7 drafts do not fit 6 entries
+    assert spec_varlen(d, maxq=7, batch=0) == INVALID  # checked before the zero-work exit
+    assert spec_varlen(d, maxq=-1) == INVALID
+    assert spec_varlen(d, batch=-1) == INVALID
+    assert spec_varlen(d, T=-1) == INVALID
+    assert spec_varlen(d, T=1 << 31) == UNSUPPORTED
+    assert spec_varlen(desc(state_len=2)) == CAPACITY
+    none = dict(x=None, out=None, w=None, slots=None, acc=None, qsl=None, pool=None)
+    assert spec_varlen(d, batch=0, **none) == OK
+    assert spec_varlen(d, T=0, **none) == OK
+    assert spec_varlen(d, maxq=0, **none) == OK
 
 
 def test_null_arguments():
