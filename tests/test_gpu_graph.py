@@ -51,3 +51,48 @@ def test_graph_replays_match_eager():
         torch.cuda.synchronize()
         np.testing.assert_array_equal(host(out), eager_out, err_msg=f"replay {rep} out")
         np.testing.assert_array_equal(host(pool), eager_pool, err_msg=f"replay {rep} pool")
+
+
+def test_graph_replays_match_eager_speculative():
+    """The speculative calls (uniform draft count, then a draft count per
+    request) under capture, replayed several times against the eager result."""
+    import torch
+    import stateful_causal_short_amd as scs
+    case, qsl = synthetic.spec_varlen_case("graph_spec", 6101, C=2048, K=4, d=1, dtype="bf16",
+                                           act="silu", w_std=0.4, bias_std=0.2, num_slots=96,
+                                           B=40, num_spec=3)
+    print(f"[gpu] graph replay speculative B={case.num_decodes} T={int(qsl[-1])}", flush=True)
+    B = case.num_decodes
+    x = dev(case.x)
+    out = torch.zeros_like(x)
+    xu = dev(synthetic._normal(np.random.default_rng(6102), (B * 4, case.C), 1.0, "bf16"))
+    outu = torch.zeros_like(xu)
+    pool0 = dev(case.pool)
+    pool = pool0.clone()
+    w, b = dev(case.w), dev(case.bias)
+    slots = dev(np.asarray(case.decode_slots, np.int32))
+    acc = dev(synthetic.num_accepted(6103, B, 4, lo=0, hi=5))
+    q = dev(qsl)
+
+    def step():
+        scs.sc_conv_update_spec(xu, outu, w, b, pool, slots, acc, q=4)
+        scs.sc_conv_update_spec_varlen(x, out, w, b, pool, slots, acc, q, max_query_len=4)
+
+    step()
+    torch.cuda.synchronize()
+    eager = (host(outu), host(out), host(pool))
+    g = torch.cuda.CUDAGraph()
+    pool.copy_(pool0)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(3):
+        pool.copy_(pool0)
+        out.zero_()
+        outu.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for got, want, what in zip((host(outu), host(out), host(pool)), eager,
+                                   ("uniform out", "varlen out", "pool")):
+            np.testing.assert_array_equal(got, want, err_msg=f"replay {rep} {what}")
