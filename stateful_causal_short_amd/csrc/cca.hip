@@ -325,6 +325,7 @@ __global__ __launch_bounds__(kBlock) void cca_state_update_vec(CcaArgs a) {
 // ---------------------------------------------------------------------------
 constexpr int kCcaThreads = 512;   // 8 waves: 16 output channels each
 constexpr int kCcaMT = 32;         // token rows per tile
+constexpr int kCcaRowTiles = kCcaThreads / kCcaMT;   // tiles whose row info is resolved at once
 
 template <int T0>
 struct CcaSmem {
@@ -338,8 +339,8 @@ struct CcaSmem {
   uint16_t w1[HD * T0];                 // depthwise weights: (cca_hslot(c), c % 4, tap)
   uint16_t bb[2 * HD];                  // (cca_hslot(c)): depthwise biases of 4 channels, then grouped
   int32_t qsl_s[kQslCache];
-  int row_p[2][MT];                     // position in the request (-1: no row), by tile parity
-  int row_src[2][MT];                   // prefill request index, or -2 - t for decode row t
+  int row_p[kCcaRowTiles][MT];          // position in the request (-1: no row), per tile of a batch
+  int row_src[kCcaRowTiles][MT];        // prefill request index, or -2 - t for decode row t
 };
 
 // Phase A gives a lane 8 channels v*8 .. v*8+7 of a row and computes them as
@@ -356,16 +357,15 @@ __host__ __device__ constexpr int cca_waves_per_simd(int t0, int gmax) {
   return (t0 <= 2 && gmax <= 4) ? SC_CCA_MIN_WAVES : 2;
 }
 
-// Row info of the tile starting at token ta (threads 0 .. 31, one row each).
-// `cur` is the thread's prefill request index from its previous (earlier)
-// tile: the search gallops forward from it, then bisects.
+// Row info of token row t: position in its request (-1: no row) and source
+// (prefill request index, or -2 - t for decode row t). `cur` is the thread's
+// prefill request index from its previous (earlier) row: the search gallops
+// forward from it, then bisects.
 template <typename QP>
-__device__ __forceinline__ void cca_tile_rows(const CcaArgs& a, int64_t ta, QP qsl,
-                                              int* rp, int* rs, int& cur) {
-  const int i = (int)threadIdx.x;
-  if (i >= kCcaMT) return;
-  const int64_t t = ta + i;
-  int p = -1, src = -1;
+__device__ __forceinline__ void cca_row(const CcaArgs& a, int64_t t, QP qsl, int& cur, int& p,
+                                        int& src) {
+  p = -1;
+  src = -1;
   if (t < a.num_tokens) {
     if (t < a.num_decodes) {
       p = 0;
@@ -392,8 +392,6 @@ __device__ __forceinline__ void cca_tile_rows(const CcaArgs& a, int64_t ta, QP q
       }
     }
   }
-  rp[i] = p;
-  rs[i] = src;
 }
 
 // Slot and has-state flag of a row's request (global reads: request starts only).
@@ -529,15 +527,29 @@ __device__ __forceinline__ void cca_persist_body(const CcaArgs& a, CcaSmem<T0>& 
 
   int rcur = 0;
   const gptr<int32_t> qsl_g = (gptr<int32_t>)a.prefill_qsl;
-  auto rows = [&](int64_t ta, int* rp, int* rs) {
-    if (use_lds_qsl) cca_tile_rows(a, ta, sm.qsl_s, rp, rs, rcur);
-    else cca_tile_rows(a, ta, qsl_g, rp, rs, rcur);
+  // row info of tiles u0 .. u0 + kCcaRowTiles - 1: one row per thread, so the
+  // searches of a whole batch run side by side once per kCcaRowTiles tiles
+  auto rows_batch = [&](int u0) {
+    const int j = tid / MT, ii = tid - j * MT;
+    int p = -1, src = -1;
+    if (u0 + j < my_tiles) {
+      const int64_t t = (int64_t)tile_ta(u0 + j) + ii;
+      if (use_lds_qsl) cca_row(a, t, sm.qsl_s, rcur, p, src);
+      else cca_row(a, t, qsl_g, rcur, p, src);
+    }
+    sm.row_p[j][ii] = p;
+    sm.row_src[j][ii] = src;
   };
   auto tile = [&](int u, Pref& f) {
-    const int cur = u & 1;
     const uint32_t ta = tile_ta(u);
-    const int* rp = sm.row_p[cur];
-    const int* rsrc_ = sm.row_src[cur];
+    // (every read of the previous batch's row info precedes the previous
+    // tile's second barrier)
+    if (u % kCcaRowTiles == 0) {
+      rows_batch(u);
+      __syncthreads();
+    }
+    const int* rp = sm.row_p[u % kCcaRowTiles];
+    const int* rsrc_ = sm.row_src[u % kCcaRowTiles];
     // ---- (A) depthwise rows, the request-start and tile-start side rows, residual ----
     // The lane's 8 channels are done in two halves of 4, one after the other,
     // which halves the fp32 working set of this phase.
@@ -642,7 +654,6 @@ __device__ __forceinline__ void cca_persist_body(const CcaArgs& a, CcaSmem<T0>& 
     u32x4 val = f.val;
     const int vp = vitem ? rp[vr] : -1;
     const int vsrc = vitem ? rsrc_[vr] : -1;
-    if (u + 1 < my_tiles) rows(tile_ta(u + 1), sm.row_p[cur ^ 1], sm.row_src[cur ^ 1]);
     if (u + AHEAD < my_tiles) issue(u + AHEAD, f);
     // store offsets of this tile (row info is rewritten by the next tile)
     const uint32_t ooff = rp[i] >= 0 ? o_lane + ta * ors32 : kOff;
@@ -712,16 +723,12 @@ __device__ __forceinline__ void cca_persist_body(const CcaArgs& a, CcaSmem<T0>& 
     Pref fa;
     issue(0, fa);
     __syncthreads();   // qsl and parameters visible
-    rows(tile_ta(0), sm.row_p[0], sm.row_src[0]);
-    __syncthreads();
     for (int u = 0; u < my_tiles; ++u) tile(u, fa);
   } else {
     Pref fa, fb;
     issue(0, fa);
     if (my_tiles > 1) issue(1, fb);
     __syncthreads();   // qsl and parameters visible
-    rows(tile_ta(0), sm.row_p[0], sm.row_src[0]);
-    __syncthreads();
     for (int u = 0; u < my_tiles; u += 2) {
       tile(u, fa);
       if (u + 1 < my_tiles) tile(u + 1, fb);
