@@ -650,12 +650,12 @@ __device__ __forceinline__ void cca_persist_body(const CcaArgs& a, CcaSmem<T0>& 
       }
       *(u32x4*)(sm.act + (i + 1) * AROW + v * 8) = u32x4{dwh[0].x, dwh[0].y, dwh[1].x, dwh[1].y};
     }
-    // value item of this tile, then the next tiles' rows and loads
+    // value item of this tile, then the next tile's loads
     u32x4 val = f.val;
     const int vp = vitem ? rp[vr] : -1;
     const int vsrc = vitem ? rsrc_[vr] : -1;
     if (u + AHEAD < my_tiles) issue(u + AHEAD, f);
-    // store offsets of this tile (row info is rewritten by the next tile)
+    // store offsets of this tile (its row info is rewritten by a later batch)
     const uint32_t ooff = rp[i] >= 0 ? o_lane + ta * ors32 : kOff;
     const uint32_t voff = vp >= 0 ? ov_lane + ta * ors32 : kOff;
     __syncthreads();
