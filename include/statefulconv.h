@@ -271,6 +271,21 @@ sc_status sc_cca_qk_conv(const sc_cca_desc* desc, const void* q, const void* k,
                          const uint8_t* prefill_has_initial_state,
                          int64_t num_tokens, void* stream);
 
+/* Checks the device-side preconditions the calls above document but cannot
+ * check without a host sync (a debugging and test aid, not for the hot path):
+ * waits for `stream`, copies the metadata to the host and returns
+ * SC_ERR_INVALID_ARG if
+ *   query_start_loc (device, batch+1, or NULL to skip) is not non-decreasing
+ *                   from query_start_loc[0] = 0 to query_start_loc[batch] = num_tokens;
+ *   state_indices   (device, batch rows of idx_stride, or NULL to skip) has an
+ *                   entry >= num_slots, or two equal non-negative entries
+ *                   (negative entries are padding rows);
+ * else SC_OK. It allocates no device memory and launches nothing. batch = 0:
+ * SC_OK without touching the pointers; a HIP error while copying: SC_ERR_HIP. */
+sc_status sc_validate_metadata(const int32_t* query_start_loc, const int32_t* state_indices,
+                               int64_t idx_stride, int32_t batch, int64_t num_tokens,
+                               int32_t num_slots, void* stream);
+
 /* Static string for a status code. */
 const char* sc_status_string(sc_status status);
 

@@ -26,7 +26,7 @@ SC_ACT_NONE, SC_ACT_SILU = 0, 1
 SC_STATE_DS, SC_STATE_SD = 0, 1
 
 EXPORTS = ("sc_conv_prefill_varlen", "sc_conv_update", "sc_conv_update_spec",
-           "sc_conv_update_spec_varlen", "sc_state_gather",
+           "sc_conv_update_spec_varlen", "sc_validate_metadata", "sc_state_gather",
            "sc_state_scatter", "sc_cca_qk_conv", "sc_status_string",
            "sc_abi_version")
 
@@ -93,6 +93,8 @@ def lib():
         L.sc_conv_update_spec_varlen.restype = I32
         L.sc_conv_update_spec_varlen.argtypes = [D, P, P, P, P, P, I32, P, P, P, I32, I64, I32,
                                                  F, P]
+        L.sc_validate_metadata.restype = I32
+        L.sc_validate_metadata.argtypes = [P, P, I64, I32, I64, I32, P]
         L.sc_state_gather.restype = I32
         L.sc_state_gather.argtypes = [P, I32, I64, P, I64, I32, P, P]
         L.sc_state_scatter.restype = I32
@@ -324,6 +326,28 @@ def sc_conv_update_spec_varlen(x, out, weight, bias, state_pool, state_indices,
         _ptr(num_accepted_tokens), _ptr(query_start_loc), batch, rows, max_query_len,
         _fuse(x, out, token_indices, accumulate, outer_residual), _stream(stream, x))
     _check("sc_conv_update_spec_varlen", st)
+
+
+def sc_validate_metadata(query_start_loc=None, state_indices=None, *, num_tokens: int = 0,
+                         num_slots: int = 0, batch: Optional[int] = None, stream=None) -> bool:
+    """Host check of the device-side preconditions (syncs the stream): True if
+    query_start_loc runs non-decreasing from 0 to num_tokens and the
+    non-negative state indices are distinct and below num_slots."""
+    torch = _torch()
+    if batch is None:
+        batch = (query_start_loc.shape[0] - 1) if query_start_loc is not None else \
+            (state_indices.shape[0] if state_indices is not None else 0)
+    if query_start_loc is not None and (query_start_loc.dtype != torch.int32 or
+                                        not query_start_loc.is_contiguous()):
+        raise ValueError("query_start_loc: expected a contiguous int32 tensor")
+    p, s = _index(state_indices, "state_indices") if state_indices is not None else (None, 1)
+    like = query_start_loc if query_start_loc is not None else state_indices
+    st = lib().sc_validate_metadata(_ptr(query_start_loc), p, s, batch, num_tokens, num_slots,
+                                    None if like is None else _stream(stream, like))
+    if st == -2:
+        return False
+    _check("sc_validate_metadata", st)
+    return True
 
 
 def sc_state_gather(state_pool, idx, dense, *, stream=None):

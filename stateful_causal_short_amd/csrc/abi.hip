@@ -3,6 +3,9 @@
 // in include/statefulconv.h.
 #include <stdint.h>
 
+#include <unordered_set>
+#include <vector>
+
 #include "statefulconv.h"
 #include "kernels.hpp"
 #include "cca.hpp"
@@ -71,6 +74,39 @@ sc_status from_hip(hipError_t e) {
 extern "C" {
 
 int32_t sc_abi_version(void) { return SC_ABI_VERSION; }
+
+sc_status sc_validate_metadata(const int32_t* query_start_loc, const int32_t* state_indices,
+                               int64_t idx_stride, int32_t batch, int64_t num_tokens,
+                               int32_t num_slots, void* stream) {
+  if (batch < 0 || num_tokens < 0 || num_slots < 0 || idx_stride < 1) return SC_ERR_INVALID_ARG;
+  if (batch == 0) return SC_OK;
+  hipStream_t st = (hipStream_t)stream;
+  if (query_start_loc) {
+    std::vector<int32_t> q((size_t)batch + 1);
+    if (hipMemcpyAsync(q.data(), query_start_loc, q.size() * sizeof(int32_t),
+                       hipMemcpyDeviceToHost, st) != hipSuccess ||
+        hipStreamSynchronize(st) != hipSuccess)
+      return SC_ERR_HIP;
+    if (q[0] != 0 || (int64_t)q[(size_t)batch] != num_tokens) return SC_ERR_INVALID_ARG;
+    for (int32_t r = 0; r < batch; ++r)
+      if (q[(size_t)r + 1] < q[(size_t)r]) return SC_ERR_INVALID_ARG;
+  }
+  if (state_indices) {
+    const size_t n = (size_t)(batch - 1) * (size_t)idx_stride + 1;
+    std::vector<int32_t> s(n);
+    if (hipMemcpyAsync(s.data(), state_indices, n * sizeof(int32_t), hipMemcpyDeviceToHost,
+                       st) != hipSuccess ||
+        hipStreamSynchronize(st) != hipSuccess)
+      return SC_ERR_HIP;
+    std::unordered_set<int32_t> seen;
+    for (int32_t r = 0; r < batch; ++r) {
+      const int32_t v = s[(size_t)r * (size_t)idx_stride];
+      if (v < 0) continue;
+      if (v >= num_slots || !seen.insert(v).second) return SC_ERR_INVALID_ARG;
+    }
+  }
+  return SC_OK;
+}
 
 const char* sc_status_string(sc_status s) {
   switch (s) {

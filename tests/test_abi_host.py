@@ -242,3 +242,12 @@ def test_fuse_descriptor_rules():
                     batch=0) == OK
         # the outer residual must not be the output
         assert call(dd, fuse=sc_conv_fuse(outer_residual=P2, outer_row_stride=64)) == INVALID
+
+
+def test_validate_metadata_host_rules():
+    lib = scs.lib()
+    assert lib.sc_validate_metadata(None, None, 1, 0, 0, 0, None) == OK     # nothing to check
+    assert lib.sc_validate_metadata(None, None, 1, 3, 10, 4, None) == OK    # both skipped
+    assert lib.sc_validate_metadata(None, None, 1, -1, 0, 0, None) == INVALID
+    assert lib.sc_validate_metadata(None, None, 0, 1, 0, 0, None) == INVALID
+    assert lib.sc_validate_metadata(None, None, 1, 1, -5, 0, None) == INVALID

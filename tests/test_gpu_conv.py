@@ -264,3 +264,30 @@ def test_state_gather_scatter(row_bytes, dtype):
     scs.sc_state_scatter(dev(newd), dev(idx), pd)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(host(pd), exp_pool)
+
+
+def test_validate_metadata():
+    import torch
+    import stateful_causal_short_amd as scs
+    case = synthetic.config2()
+    qsl = dev(case.qsl_p)
+    slots = dev(np.asarray(case.prefill_slots, np.int32))
+    T, S = int(case.qsl_p[-1]), case.num_slots
+    print(f"[gpu] validate metadata B={case.num_prefills} T={T}", flush=True)
+    assert scs.sc_validate_metadata(qsl, slots, num_tokens=T, num_slots=S)
+    assert not scs.sc_validate_metadata(qsl, slots, num_tokens=T + 1, num_slots=S)
+    bad = case.qsl_p.copy()
+    bad[4] = bad[3] - 1                        # goes backwards
+    assert not scs.sc_validate_metadata(dev(bad), None, num_tokens=T, num_slots=S)
+    dup = np.asarray(case.prefill_slots, np.int32).copy()
+    dup[5] = dup[1]
+    assert not scs.sc_validate_metadata(None, dev(dup), num_tokens=T, num_slots=S)
+    pad = np.asarray(case.prefill_slots, np.int32).copy()
+    pad[2] = pad[6] = -1                       # repeated padding rows are fine
+    assert scs.sc_validate_metadata(None, dev(pad), num_tokens=T, num_slots=S)
+    big = np.asarray(case.prefill_slots, np.int32).copy()
+    big[0] = S
+    assert not scs.sc_validate_metadata(None, dev(big), num_tokens=T, num_slots=S)
+    two_d = dev(np.stack([np.asarray(case.prefill_slots, np.int32), np.arange(8, dtype=np.int32)], 1))
+    assert scs.sc_validate_metadata(None, two_d, num_tokens=T, num_slots=S)
+    torch.cuda.synchronize()
