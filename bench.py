@@ -6,7 +6,9 @@
 One step = one pass of the hot path over one batch already resident in HBM.
 The default workload is the varlen prefill batch (8 sequences, lengths
 U{1..2048}, 8192 channels, width 4, bf16, bias + SiLU, 64-slot state pool):
-state gather, conv, bias, SiLU and state write-back in one kernel. Other
+state gather, conv, bias, SiLU and state write-back in one kernel. Its JSON
+line also carries a secondary "decode" object: the 512-request one-token
+decode batch timed the same way (the metric names the decode conv too). Other
 workloads (decode, multi-token update, dilated mixed batch with checkpoints,
 CCA) are selectable for measurement tables.
 
@@ -598,6 +600,8 @@ def main():
     ap.add_argument("--state-layout", default="ds", choices=["ds", "sd"],
                     help="state pool layout: (slots, C, S) or (slots, S, C)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="varlen_prefill: skip the secondary decode measurement")
     ap.add_argument("--traffic-from", metavar="DIR",
                     help="rewrite profiles/traffic.json from rocprofv3 --pmc runs under DIR "
                          "and exit (CPU only)")
@@ -707,10 +711,45 @@ def main():
         },
         "cpu_baseline": None,
     }
+    if args.workload == "varlen_prefill" and not args.no_decode:
+        # the metric names the decode conv too: the 512-request decode batch,
+        # timed the same way, in the same process (a secondary figure; `value`
+        # stays the varlen prefill's)
+        result["decode"] = decode_secondary(args)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         result["cpu_baseline"] = cpu_baseline_conv(case, num_accepted=acc, fused=fused)
     print(json.dumps(result), flush=True)
+
+
+def decode_secondary(args):
+    """Decode (512 requests x 1 token, 8192 channels, width 4, bf16, bias + SiLU,
+    1024-slot pool): K back-to-back launches after W warmup, timed as the main
+    workload is; per-launch time, tokens/s and the kernel's roofline fraction."""
+    import torch
+    case = conv_workload("decode")
+    if args.state_layout == "sd":
+        import synthetic
+        case = synthetic.as_sd(case)
+    dec_b, _ = conv_kernel_bytes(case)
+    set_bytes = case.T * case.C * case.elsize * 2 + case.pool.nbytes
+    nsets = int(min(8, max(2, -(-ROTATE_BYTES // set_bytes))))
+    run = ConvRunner(case, nsets)
+    for i in range(args.warmup):
+        run.step(i)
+    torch.cuda.synchronize()
+    eager, graph = time_launches(lambda: [run.step(args.warmup + i) for i in range(args.steps)],
+                                 args.steps)
+    ms = min(eager, graph)
+    gbps = dec_b / (ms * 1e-3) / 1e9
+    log(f"decode: {ms * 1e3:.2f} us/launch ({gbps:.0f} GB/s)")
+    return {"workload": case.name, "requests": case.num_decodes, "tokens": case.T,
+            "state_layout": case.layout, "kernel_us": ms * 1e3,
+            "timing": {"eager_us": eager * 1e3, "graph_us": graph * 1e3},
+            "tokens_per_s": case.T / (ms * 1e-3),
+            "roofline": {"kernel": "decode_update", "bound": "hbm", "achieved": gbps,
+                         "peak": PEAK_GBPS, "unit": "GB/s", "frac": gbps / PEAK_GBPS,
+                         "traffic": None, "alg_bytes_per_launch": dec_b}}
 
 
 if __name__ == "__main__":
