@@ -291,3 +291,61 @@ def test_validate_metadata():
     two_d = dev(np.stack([np.asarray(case.prefill_slots, np.int32), np.arange(8, dtype=np.int32)], 1))
     assert scs.sc_validate_metadata(None, two_d, num_tokens=T, num_slots=S)
     torch.cuda.synchronize()
+
+
+def test_offsets_beyond_2gib_match_small_offsets():
+    """Token rows and state slots more than 2 GiB into their tensors: a 320k-token
+    varlen batch (x is 2.6 GB) gives bit for bit the outputs and states of each
+    request run alone from row 0, and a decode on a 2.5 GB pool matches the same
+    slots copied into a small pool (the small cases are pinned to the oracle
+    elsewhere; this checks the 64-bit addressing)."""
+    import torch
+    import stateful_causal_short_amd as scs
+    C, K = 4096, 4
+    rng = np.random.default_rng(0xB16)
+    block = dev(synthetic._normal(rng, (4096, C), 1.0, "bf16"))
+    w = dev(synthetic._normal(rng, (C, K), 0.25, "bf16"))
+    b = dev(synthetic._normal(rng, (C,), 0.1, "bf16"))
+    lens = [150_001, 119_997, 50_011]
+    T = sum(lens)
+    print(f"[gpu] large offsets: prefill T={T} C={C} ({T * C * 2 / 2**30:.2f} GiB of x)", flush=True)
+    x = block.repeat((T + 4095) // 4096, 1)[:T].contiguous()
+    x[::7777] *= -0.5                                  # break the period a little
+    qsl = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    slots = np.array([5, 0, 3], np.int32)
+    h = np.array([1, 0, 1], np.uint8)
+    pool0 = dev(synthetic._normal(rng, (8, C, 3), 1.0, "bf16"))
+    out = torch.empty_like(x)
+    pool = pool0.clone()
+    scs.sc_conv_prefill_varlen(x, out, w, b, pool, dev(qsl), dev(slots), dev(h), activation="silu")
+    torch.cuda.synchronize()
+    for r in range(3):
+        xr = x[int(qsl[r]):int(qsl[r + 1])].contiguous()
+        o1 = torch.empty_like(xr)
+        p1 = pool0.clone()
+        scs.sc_conv_prefill_varlen(xr, o1, w, b, p1, dev(np.array([0, lens[r]], np.int32)),
+                                   dev(slots[r:r + 1]), dev(h[r:r + 1]), activation="silu")
+        torch.cuda.synchronize()
+        assert torch.equal(o1, out[int(qsl[r]):int(qsl[r + 1])]), f"request {r} outputs"
+        assert torch.equal(p1[int(slots[r])], pool[int(slots[r])]), f"request {r} state"
+        del xr, o1, p1
+    del x, out
+    torch.cuda.empty_cache()
+
+    n_slots, B = 100_000, 64
+    print(f"[gpu] large offsets: decode B={B} on {n_slots} slots "
+          f"({n_slots * C * 3 * 2 / 2**30:.2f} GiB pool)", flush=True)
+    big = torch.empty((n_slots, C, 3), dtype=torch.bfloat16, device="cuda")
+    big.copy_(block[:3].t().reshape(1, C, 3).expand(n_slots, C, 3))
+    sl = np.sort(rng.choice(np.arange(n_slots - 5000, n_slots), B, replace=False)).astype(np.int32)
+    assert int(sl[0]) * C * 3 * 2 > 2**31
+    big[torch.from_numpy(sl).long().cuda()] = dev(synthetic._normal(rng, (B, C, 3), 1.0, "bf16"))
+    xd = dev(synthetic._normal(rng, (B, C), 1.0, "bf16"))
+    small = big[torch.from_numpy(sl).long().cuda()].clone()
+    od1, od2 = torch.empty_like(xd), torch.empty_like(xd)
+    scs.sc_conv_update(xd, od1, w, b, big, dev(sl), None, q=1, activation="silu")
+    scs.sc_conv_update(xd, od2, w, b, small, dev(np.arange(B, dtype=np.int32)), None, q=1,
+                       activation="silu")
+    torch.cuda.synchronize()
+    assert torch.equal(od1, od2)
+    assert torch.equal(big[torch.from_numpy(sl).long().cuda()], small)
