@@ -349,3 +349,16 @@ def test_offsets_beyond_2gib_match_small_offsets():
     torch.cuda.synchronize()
     assert torch.equal(od1, od2)
     assert torch.equal(big[torch.from_numpy(sl).long().cuda()], small)
+
+
+@pytest.mark.parametrize("C,lens,dtype", [
+    (32768, [5, 70, 130, 1], "bf16"),     # 16 channel blocks per chunk
+    (64, [100_000, 3], "bf16"),           # one long request, 8 live lanes per workgroup
+    (24_576, [40, 12, 13, 300], "f32"),   # wide rows in fp32
+])
+def test_wide_rows_and_long_requests(C, lens, dtype):
+    case = conv_case("wide_long", 1100 + C % 997 + len(lens), C=C, K=4, d=1, dtype=dtype,
+                     act="silu", w_std=0.25, bias_std=0.1,
+                     num_slots=8 + len(lens) + sum(n // 64 for n in lens), num_decodes=4, q=1,
+                     prefill_lens=lens, prefill_h_p=0.5, ckpt_grid=64)
+    parity(case)
