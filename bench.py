@@ -49,13 +49,13 @@ def log(msg):
 def conv_workload(name):
     import synthetic
     return {
-        "varlen_prefill": synthetic.config2,
-        "single": synthetic.config1,
-        "decode": synthetic.config3a,
-        "update_q4": synthetic.config3b,
-        "spec": synthetic.config3b_spec,
-        "ple_mixed": synthetic.config4,
-        "ple_fused": synthetic.config4,
+        "varlen_prefill": synthetic.varlen_prefill_8seq,
+        "single": synthetic.single_seq_64ch,
+        "decode": synthetic.decode_512req,
+        "update_q4": synthetic.update_128req_q4,
+        "spec": synthetic.spec_128req_q4,
+        "ple_mixed": synthetic.ple_mixed_batch,
+        "ple_fused": synthetic.ple_mixed_batch,
     }[name]()
 
 
@@ -341,7 +341,7 @@ def spec_varlen_bench(args):
     import synthetic
     import stateful_causal_short_amd as scs
     from tests._gpu import dev
-    case, qsl = synthetic.config3b_spec_varlen()
+    case, qsl = synthetic.spec_varlen_128req()
     if args.state_layout == "sd":
         case = synthetic.as_sd(case)
     B, T = case.num_decodes, int(qsl[-1])
@@ -418,7 +418,7 @@ def cca_bench(args):
     import numpy as np
     import torch
     import synthetic
-    case = synthetic.config5()
+    case = synthetic.cca_mixed_32k()
     main_b, upd_b = cca_alg_bytes(case)
     set_bytes = main_b
     nsets = int(min(6, max(2, -(-ROTATE_BYTES // set_bytes))))
@@ -567,7 +567,7 @@ def traffic_from(d):
             ks = sorted(k for k in pv if "cca_" in k)
             kern = ks
             kib[counter] = sum(statistics.median(pv[k]) for k in ks)
-        main_b, upd_b = cca_alg_bytes(synthetic.config5())
+        main_b, upd_b = cca_alg_bytes(synthetic.cca_mixed_32k())
         entries["cca:cca_main+state"] = (kib, " + ".join(kern), main_b + upd_b,
                                          source_sha(CCA_SOURCES))
     path = os.path.join(ROOT, "profiles", "traffic.json")

@@ -115,7 +115,7 @@ const char* sc_status_string(sc_status s) {
     case SC_ERR_INVALID_ARG: return "invalid size, stride, enum or grid";
     case SC_ERR_DTYPE: return "unsupported dtype";
     case SC_ERR_STATE_CAPACITY: return "state_len smaller than (width-1)*dilation";
-    case SC_ERR_UNSUPPORTED: return "configuration not supported by this build";
+    case SC_ERR_UNSUPPORTED: return "configuration not supported by this library";
     case SC_ERR_HIP: return "HIP launch error";
   }
   return "unknown status";

@@ -32,8 +32,8 @@ SEED_BASE = 0x5C0DE000
 
 __all__ = [
     "SEED_BASE", "ConvCase", "CcaCase", "bf16_bits", "bf16_to_f32",
-    "conv_case", "cca_case", "config1", "config2", "config3a", "config3b",
-    "config4", "config5", "storage_dtype",
+    "conv_case", "cca_case", "single_seq_64ch", "varlen_prefill_8seq", "decode_512req", "update_128req_q4",
+    "ple_mixed_batch", "cca_mixed_32k", "storage_dtype",
 ]
 
 
@@ -186,44 +186,44 @@ def conv_case(name: str, seed: int, *, C: int, K: int, d: int, dtype: str,
                     ckpt_grid=ckpt_grid, cu_ckpt=cu_ckpt, ckpt_slots=ckpt_slots)
 
 
-def config1(seed: int = SEED_BASE + 1) -> ConvCase:
+def single_seq_64ch(seed: int = SEED_BASE + 1) -> ConvCase:
     """Single sequence, 64 channels, width 4, fp32, no activation, zero state."""
-    return conv_case("cfg1_single_f32", seed, C=64, K=4, d=1, dtype="f32",
+    return conv_case("single_seq_64ch_f32", seed, C=64, K=4, d=1, dtype="f32",
                      act="none", w_std=0.25, bias_std=0.1, num_slots=1,
                      prefill_lens=[256], prefill_h_all=0)
 
 
-def config2(seed: int = SEED_BASE + 2, *, C: int = 8192, B: int = 8,
+def varlen_prefill_8seq(seed: int = SEED_BASE + 2, *, C: int = 8192, B: int = 8,
             max_len: int = 2048, num_slots: int = 64) -> ConvCase:
     """Varlen prefill: B sequences, lengths U{1..max_len}, bf16, bias, SiLU."""
     rng = np.random.default_rng(seed ^ 0xA5A5)
     lens = rng.integers(1, max_len + 1, size=B)
-    return conv_case("cfg2_varlen_prefill", seed, C=C, K=4, d=1, dtype="bf16",
+    return conv_case("varlen_prefill_8seq_8192ch", seed, C=C, K=4, d=1, dtype="bf16",
                      act="silu", w_std=0.25, bias_std=0.1, num_slots=num_slots,
                      prefill_lens=lens, prefill_h_p=0.5)
 
 
-def config3a(seed: int = SEED_BASE + 3, *, C: int = 8192, B: int = 512,
+def decode_512req(seed: int = SEED_BASE + 3, *, C: int = 8192, B: int = 512,
              num_slots: int = 1024) -> ConvCase:
     """Decode: B requests x 1 token, state continued, bf16, bias, SiLU."""
-    return conv_case("cfg3a_decode_q1", seed, C=C, K=4, d=1, dtype="bf16",
+    return conv_case("decode_512req_8192ch", seed, C=C, K=4, d=1, dtype="bf16",
                      act="silu", w_std=0.25, bias_std=0.1, num_slots=num_slots,
                      num_decodes=B, q=1)
 
 
-def config3b(seed: int = SEED_BASE + 0x33, *, C: int = 8192, B: int = 128,
+def update_128req_q4(seed: int = SEED_BASE + 0x33, *, C: int = 8192, B: int = 128,
              q: int = 4, num_slots: int = 1024) -> ConvCase:
     """Multi-token update: B requests x q tokens, all consumed."""
-    return conv_case("cfg3b_update_q4", seed, C=C, K=4, d=1, dtype="bf16",
+    return conv_case("update_128req_q4_8192ch", seed, C=C, K=4, d=1, dtype="bf16",
                      act="silu", w_std=0.25, bias_std=0.1, num_slots=num_slots,
                      num_decodes=B, q=q)
 
 
-def config3b_spec(seed: int = SEED_BASE + 0x35, *, C: int = 8192, B: int = 128,
+def spec_128req_q4(seed: int = SEED_BASE + 0x35, *, C: int = 8192, B: int = 128,
                   num_spec: int = 3, num_slots: int = 1024) -> ConvCase:
     """Speculative update: B requests x (num_spec + 1) tokens on a rolling
     buffer of (K-1) + num_spec entries (accepted counts from num_accepted)."""
-    return conv_case("cfg3b_spec_rollback", seed, C=C, K=4, d=1, dtype="bf16",
+    return conv_case("spec_128req_q4_8192ch", seed, C=C, K=4, d=1, dtype="bf16",
                      act="silu", w_std=0.25, bias_std=0.1, num_slots=num_slots,
                      num_decodes=B, q=num_spec + 1, num_spec=num_spec)
 
@@ -255,24 +255,24 @@ def spec_varlen_case(name: str, seed: int, *, C: int, K: int, d: int, dtype: str
     return replace(base, x=x), qsl
 
 
-def config3b_spec_varlen(seed: int = SEED_BASE + 0x37, *, C: int = 8192, B: int = 128,
+def spec_varlen_128req(seed: int = SEED_BASE + 0x37, *, C: int = 8192, B: int = 128,
                          num_spec: int = 3, num_slots: int = 1024):
     """Speculative update with per-request draft counts uniform in
     {0 .. num_spec + 1} (the GDN page's per-sequence loop), otherwise as
-    config3b_spec. Returns (case, qsl)."""
-    return spec_varlen_case("cfg3b_spec_varlen", seed, C=C, K=4, d=1, dtype="bf16", act="silu",
+    spec_128req_q4. Returns (case, qsl)."""
+    return spec_varlen_case("spec_varlen_128req_8192ch", seed, C=C, K=4, d=1, dtype="bf16", act="silu",
                             w_std=0.25, bias_std=0.1, num_slots=num_slots, B=B,
                             num_spec=num_spec)
 
 
-def config4(seed: int = SEED_BASE + 4, *, C: int = 8192, num_decodes: int = 256,
+def ple_mixed_batch(seed: int = SEED_BASE + 4, *, C: int = 8192, num_decodes: int = 256,
             Bp: int = 16, min_len: int = 128, max_len: int = 4096,
             grid: int = 512, num_slots: int = 1024) -> ConvCase:
     """Dilated PLE-style mixed batch: decodes then varlen prefills with
     checkpoints every ``grid`` tokens; width 4, dilation 3, no bias/act."""
     rng = np.random.default_rng(seed ^ 0xA5A5)
     lens = rng.integers(min_len, max_len + 1, size=Bp)
-    return conv_case("cfg4_ple_dilated_mixed", seed, C=C, K=4, d=3,
+    return conv_case("ple_mixed_8192ch_d3", seed, C=C, K=4, d=3,
                      dtype="bf16", act="none", w_std=0.05, bias_std=None,
                      num_slots=num_slots, num_decodes=num_decodes, q=1,
                      prefill_lens=lens, prefill_h_p=0.5, ckpt_grid=grid)
@@ -382,10 +382,10 @@ def cca_case(name: str, seed: int, *, nq: int = 16, nkv: int = 4, hd: int = 128,
     return case
 
 
-def config5(seed: int = SEED_BASE + 5, **kw) -> CcaCase:
+def cca_mixed_32k(seed: int = SEED_BASE + 5, **kw) -> CcaCase:
     """CCA q/k conv: 16 q heads, 4 kv heads, head_dim 128, kernels 2 and 2,
     512 decodes + 64 prefills, 32768 tokens in all."""
-    return cca_case("cfg5_cca_mixed", seed, **kw)
+    return cca_case("cca_mixed_32k_tokens", seed, **kw)
 
 
 def num_accepted(seed: int, batch: int, q: int, lo: int = 1, hi: Optional[int] = None) -> np.ndarray:

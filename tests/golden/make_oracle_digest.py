@@ -18,10 +18,10 @@ import synthetic  # noqa: E402
 
 
 def cases():
-    yield "cfg1_single_f32", synthetic.config1()
-    yield "cfg4_small", synthetic.config4(C=64, num_decodes=8, Bp=3, min_len=5,
+    yield "single_seq_64ch_f32", synthetic.single_seq_64ch()
+    yield "ple_mixed_small", synthetic.ple_mixed_batch(C=64, num_decodes=8, Bp=3, min_len=5,
                                           max_len=70, grid=16, num_slots=64)
-    yield "cfg5_small", synthetic.cca_case("cfg5_small", synthetic.SEED_BASE + 55,
+    yield "cca_mixed_small", synthetic.cca_case("cca_mixed_small", synthetic.SEED_BASE + 55,
                                            nq=4, nkv=2, hd=16, num_decodes=4,
                                            num_prefills=3, num_prefill_tokens=20,
                                            num_slots=16)

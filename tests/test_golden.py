@@ -38,7 +38,7 @@ def test_depthwise_state_len_follows_page_formulas():
                                    num_slots=2, prefill_lens=[3])
         assert case.H == c["state_len"] and case.pool.shape[2] == c["state_len"]
     for c in g["gdn_state_len"]["cases"]:
-        assert synthetic.config2(C=8, B=1, max_len=4).pool.shape[2] == c["state_len"]
+        assert synthetic.varlen_prefill_8seq(C=8, B=1, max_len=4).pool.shape[2] == c["state_len"]
 
 
 def test_oracle_regression_digest():

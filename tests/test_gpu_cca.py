@@ -56,12 +56,12 @@ def sample_rows(case, n_random=384, seed=1):
     return m
 
 
-def test_config5_full():
-    case = synthetic.config5()
+def test_cca_mixed_32k_full():
+    case = synthetic.cca_mixed_32k()
     parity(case, row_mask=sample_rows(case))
 
 
-def test_config5_small_tile_edges():
+def test_cca_small_tile_edges():
     case = synthetic.cca_case("cca_edges", 501, num_decodes=70,
                               prefill_lens=[1, 2, 3, 62, 63, 64, 65, 130, 7], num_slots=128)
     case.prefill_h[:] = [0, 1, 1, 0, 1, 0, 1, 1, 0]

@@ -55,33 +55,33 @@ def parity(case, *, full_rows=True, **kw):
 # ----------------------------------------------------------------------------
 # the five workload shapes (CCA is in test_gpu_cca.py)
 # ----------------------------------------------------------------------------
-def test_config1_single_sequence_f32():
-    parity(synthetic.config1())
+def test_single_sequence_64ch_f32():
+    parity(synthetic.single_seq_64ch())
 
 
-def test_config2_small_ragged():
-    parity(synthetic.config2(C=512, B=8, max_len=300))
+def test_varlen_prefill_small_ragged():
+    parity(synthetic.varlen_prefill_8seq(C=512, B=8, max_len=300))
 
 
-def test_config2_full():
-    parity(synthetic.config2(), full_rows=False)
+def test_varlen_prefill_8seq_full():
+    parity(synthetic.varlen_prefill_8seq(), full_rows=False)
 
 
-def test_config3a_decode_full():
-    parity(synthetic.config3a())
+def test_decode_512req_full():
+    parity(synthetic.decode_512req())
 
 
-def test_config3b_multi_token_full():
-    parity(synthetic.config3b())
+def test_update_128req_q4_full():
+    parity(synthetic.update_128req_q4())
 
 
-def test_config4_small_dilated_mixed_with_checkpoints():
-    parity(synthetic.config4(C=512, num_decodes=16, Bp=6, min_len=5, max_len=700,
+def test_ple_mixed_small_with_checkpoints():
+    parity(synthetic.ple_mixed_batch(C=512, num_decodes=16, Bp=6, min_len=5, max_len=700,
                              grid=64, num_slots=128))
 
 
-def test_config4_full():
-    parity(synthetic.config4(), full_rows=False)
+def test_ple_mixed_full():
+    parity(synthetic.ple_mixed_batch(), full_rows=False)
 
 
 # ----------------------------------------------------------------------------
@@ -269,7 +269,7 @@ def test_state_gather_scatter(row_bytes, dtype):
 def test_validate_metadata():
     import torch
     import stateful_causal_short_amd as scs
-    case = synthetic.config2()
+    case = synthetic.varlen_prefill_8seq()
     qsl = dev(case.qsl_p)
     slots = dev(np.asarray(case.prefill_slots, np.int32))
     T, S = int(case.qsl_p[-1]), case.num_slots

@@ -58,7 +58,7 @@ def fused_parity(case, xp, perm, R, O, *, accumulate=True, outer=True, num_accep
 def test_ple_mixed_batch_fused():
     # the PLE shape: width 4, dilation 3, no bias or activation, decodes then
     # varlen prefills with checkpoints, gated output += conv + hidden states
-    case = synthetic.config4(C=2048, num_decodes=40, Bp=6, min_len=20, max_len=700,
+    case = synthetic.ple_mixed_batch(C=2048, num_decodes=40, Bp=6, min_len=20, max_len=700,
                              grid=64, num_slots=256)
     xp, perm, R, O = scatter(case, 37, 4001)
     fused_parity(case, xp, perm, R, O)

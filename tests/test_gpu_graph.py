@@ -14,7 +14,7 @@ pytestmark = pytest.mark.gpu
 def test_graph_replays_match_eager():
     import torch
     import stateful_causal_short_amd as scs
-    case = synthetic.config4(C=2048, num_decodes=32, Bp=5, min_len=20, max_len=900,
+    case = synthetic.ple_mixed_batch(C=2048, num_decodes=32, Bp=5, min_len=20, max_len=900,
                              grid=128, num_slots=256)
     print(f"[gpu] graph replay T={case.T} C={case.C}", flush=True)
     nd = case.num_decode_tokens

@@ -79,7 +79,7 @@ def test_sd_speculative(K, d, n, dtype):
 
 
 def test_sd_fused_ple_batch():
-    case = as_sd(synthetic.config4(C=2048, num_decodes=40, Bp=6, min_len=20, max_len=500,
+    case = as_sd(synthetic.ple_mixed_batch(C=2048, num_decodes=40, Bp=6, min_len=20, max_len=500,
                                    grid=64, num_slots=256))
     rng = np.random.default_rng(6401)
     n = case.T + 19

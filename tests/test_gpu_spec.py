@@ -32,8 +32,8 @@ def spec_parity(case, acc, **kw):
     return out, pool
 
 
-def test_spec_config3b_shape():
-    case = synthetic.config3b_spec()
+def test_spec_128req_q4_shape():
+    case = synthetic.spec_128req_q4()
     spec_parity(case, synthetic.num_accepted(77, case.num_decodes, case.q))
 
 

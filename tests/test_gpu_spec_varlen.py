@@ -68,7 +68,7 @@ def varlen_parity(case, acc, qsl, max_q=None, **kw):
 
 @pytest.mark.parametrize("layout", ["ds", "sd"])
 def test_spec_varlen_128_requests_8192_channels(layout):
-    case, qsl = synthetic.config3b_spec_varlen()
+    case, qsl = synthetic.spec_varlen_128req()
     if layout == "sd":
         case = synthetic.as_sd(case)
     acc = np.minimum(synthetic.num_accepted(91, case.num_decodes, 4), np.maximum(np.diff(qsl), 1))
