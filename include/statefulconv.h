@@ -104,7 +104,9 @@ typedef struct {
 typedef struct {
   int32_t grid;              /* g; 0 = no export; else g >= H required */
   const int32_t* cu_ckpt;    /* (device) B+1 exclusive prefix of checkpoint counts */
-  const int32_t* ckpt_slots; /* (device) destination slots, flat */
+  const int32_t* ckpt_slots; /* (device) destination slots, flat; NULL (an empty
+                                array: no request reaches a checkpoint) exports
+                                nothing */
 } sc_ckpt_desc;
 
 /* Residual fusion and row mapping, optional on every depthwise call (PLE page

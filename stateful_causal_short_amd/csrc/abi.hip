@@ -146,7 +146,10 @@ sc_status sc_conv_prefill_varlen(const sc_conv_desc* desc, const void* x, void* 
   if (!x || !out || !weight || !query_start_loc || !state_indices || !has_initial_state)
     return SC_ERR_NULL_ARG;
   if (!state_pool && num_slots > 0 && H > 0) return SC_ERR_NULL_ARG;
-  if (grid && (!ckpt->cu_ckpt || !ckpt->ckpt_slots)) return SC_ERR_NULL_ARG;
+  if (grid && !ckpt->cu_ckpt) return SC_ERR_NULL_ARG;
+  // no destination slots (an empty array: no request is long enough to reach a
+  // checkpoint) means nothing to export
+  if (grid && !ckpt->ckpt_slots) grid = 0;
   if (x == out) return SC_ERR_INVALID_ARG;
   if (num_tokens > 0x7FFFFFFFLL) return SC_ERR_UNSUPPORTED;
   sc::ConvArgs a{};

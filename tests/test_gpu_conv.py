@@ -362,3 +362,13 @@ def test_wide_rows_and_long_requests(C, lens, dtype):
                      num_slots=8 + len(lens) + sum(n // 64 for n in lens), num_decodes=4, q=1,
                      prefill_lens=lens, prefill_h_p=0.5, ckpt_grid=64)
     parity(case)
+
+
+def test_checkpoint_grid_with_no_checkpoint_reached():
+    # every request is shorter than the grid: the destination array is empty
+    # (a NULL data pointer), which exports nothing
+    case = conv_case("ckpt_none", 1201, C=512, K=4, d=3, dtype="bf16", act="none",
+                     w_std=0.1, bias_std=None, num_slots=16, num_decodes=2, q=1,
+                     prefill_lens=[5, 30, 17], prefill_h_p=0.5, ckpt_grid=64)
+    assert int(case.cu_ckpt[-1]) == 0 and case.ckpt_slots.size == 0
+    parity(case)

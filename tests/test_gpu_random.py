@@ -1,0 +1,78 @@
+"""Seeded random parity sweep of the depthwise calls against the CPU oracle:
+mixed decode + varlen prefill batches (lengths including 0), random width,
+dilation, channel count (aligned or not), dtype, activation and bias, both state
+layouts, buffers widened for speculative rollback, padding slots, checkpoints,
+strided rows, and fused residuals with a row map. Every case stays inside the
+calls' documented preconditions.
+
+Bar: state bit-exact; outputs within 2 bf16 ulp (bf16) or 1e-5 relative (fp32)
+of the oracle's float64 value, or within 2^-20 of the sum of |terms|."""
+import numpy as np
+import pytest
+
+import oracle
+import synthetic
+from synthetic import conv_case
+from tests._gpu import check_close, run_conv_case, run_fused_case
+
+pytestmark = pytest.mark.gpu
+
+FLOOR = 2.0 ** -20
+
+
+def random_case(seed):
+    rng = np.random.default_rng(seed)
+    K = int(rng.choice([1, 2, 3, 4, 4, 4, 5]))
+    d = int(rng.choice([1, 1, 2, 3]))
+    H = (K - 1) * d
+    C = int(rng.choice([8, 24, 256, 1000, 2056, 4096]))
+    dtype = str(rng.choice(["bf16", "f32"]))
+    act = str(rng.choice(["silu", "none"]))
+    bias = None if rng.random() < 0.3 else 0.2
+    nd = int(rng.choice([0, 1, 7]))
+    q = int(rng.choice([1, 1, 2, 3, 4]))
+    lens = [int(v) for v in rng.integers(0, 71, size=int(rng.choice([0, 1, 5])))]
+    if nd == 0 and not lens:
+        lens = [int(rng.integers(1, 40))]
+    grid = 0 if (H == 0 or rng.random() < 0.5) else int(H * rng.choice([1, 2, 3]))
+    num_spec = int(rng.choice([0, 0, 2]))
+    need = nd + len(lens) + (sum(n // grid for n in lens) if grid else 0)
+    case = conv_case("random", seed, C=C, K=K, d=d, dtype=dtype, act=act, w_std=0.4,
+                     bias_std=bias, num_slots=need + 6, num_decodes=nd, q=q, prefill_lens=lens,
+                     prefill_h_p=0.5, ckpt_grid=grid, num_spec=num_spec)
+    if nd and rng.random() < 0.5:
+        case.decode_h = (rng.random(nd) < 0.7).astype(np.uint8)
+    if len(lens) > 1 and rng.random() < 0.4:
+        case.prefill_slots[int(rng.integers(0, len(lens)))] = -1      # a padding row
+    if rng.random() < 0.4:
+        case = synthetic.as_sd(case)
+    return case, rng
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_random_depthwise_batches(seed):
+    case, rng = random_case(0x7A0000 + seed)
+    mode = str(rng.choice(["plain", "plain", "strided", "fused"]))
+    print(f"[gpu] random seed={seed} mode={mode} T={case.T} C={case.C} K={case.K} d={case.d} "
+          f"S={case.S} {case.dtype} act={case.act} bias={case.bias is not None} "
+          f"decodes={case.num_decodes}x{case.q} lens={list(np.diff(case.qsl_p))} "
+          f"grid={case.ckpt_grid} layout={case.layout}", flush=True)
+    if mode == "fused":
+        n = case.T + 5
+        perm = rng.permutation(n)[:case.T].astype(np.int32)
+        xp = synthetic._normal(rng, (n, case.C), 1.0, case.dtype)
+        xp[perm] = case.x
+        R = synthetic._normal(rng, (n, case.C), 1.0, case.dtype)
+        O = synthetic._normal(rng, (n, case.C), 1.0, case.dtype) if rng.random() < 0.5 else None
+        out, pool = run_fused_case(case, xp, perm, resid=R, outer=O)
+        ref, rpool, ab = oracle.conv(case, out_dtype="f64", absum=True, x=xp,
+                                     token_indices=perm, resid=R, outer=O)
+        np.testing.assert_array_equal(pool, rpool, err_msg="state pool not bit-exact")
+        check_close(out[perm], ref[perm], ab, case.dtype, FLOOR, what="fused out")
+        unused = np.setdiff1d(np.arange(n), perm)
+        np.testing.assert_array_equal(out[unused], R[unused])
+        return
+    out, pool = run_conv_case(case, x_pad=16 if mode == "strided" else 0)
+    ref, rpool, ab = oracle.conv(case, out_dtype="f64", absum=True)
+    np.testing.assert_array_equal(pool, rpool, err_msg="state pool not bit-exact")
+    check_close(out, ref, ab, case.dtype, FLOOR)
