@@ -259,7 +259,8 @@ typedef struct {
  *   conv_state[s] = last n raw inputs; delayed_state[s] = last v_del row.
  *   q (T, nq*hd), k (T, nkv*hd), v_cur, v_del (T, nkv*hd/2), out
  *   (T, (nq+2*nkv)*hd); w_dw (C, t0), b_dw (C), w_gr (C, hd, t1), b_gr (C),
- *   delayed_init (nkv*hd/2) or NULL; conv_state (num_slots, C, n),
+ *   delayed_init (nkv*hd/2) or NULL; conv_state (num_slots, C, n; may be NULL
+ *   when n = 0),
  *   delayed_state (num_slots, nkv*hd/2); slot arrays int32, has-state uint8.
  *   All (device). num_tokens must equal num_decodes + prefill_qsl[last]. */
 sc_status sc_cca_qk_conv(const sc_cca_desc* desc, const void* q, const void* k,

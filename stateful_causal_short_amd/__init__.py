@@ -151,7 +151,11 @@ def _dtype_code(t) -> int:
 
 
 def _rows(t, name):
-    if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
+    if t.dim() != 2:
+        raise ValueError(f"{name}: expected a 2-D tensor")
+    if t.numel() == 0:
+        return t.shape[1]        # no rows to address (zero-work calls are no-ops)
+    if t.shape[1] > 1 and t.stride(1) != 1:
         raise ValueError(f"{name}: expected a 2-D tensor with unit channel stride")
     # with at most one row the row stride is never used
     return t.stride(0) if t.shape[0] > 1 else t.shape[1]

@@ -376,7 +376,9 @@ sc_status sc_cca_qk_conv(const sc_cca_desc* desc, const void* q, const void* k,
   if (num_decodes > 0 && !decode_slots) return SC_ERR_NULL_ARG;
   if (num_prefills > 0 && (!prefill_qsl || !prefill_slots || !prefill_has_initial_state))
     return SC_ERR_NULL_ARG;
-  if (num_slots > 0 && (!conv_state || !delayed_state)) return SC_ERR_NULL_ARG;
+  // with t0 = t1 = 1 there is no conv history (an empty, possibly NULL, pool)
+  const bool has_history = desc->t0 + desc->t1 - 2 > 0;
+  if (num_slots > 0 && ((has_history && !conv_state) || !delayed_state)) return SC_ERR_NULL_ARG;
   if (num_tokens > 0x7FFFFFFFLL || C > 0x7FFFFFFFLL) return SC_ERR_UNSUPPORTED;
   sc::CcaArgs a{};
   a.q = q;

@@ -252,3 +252,13 @@ def test_validate_metadata_host_rules():
     assert lib.sc_validate_metadata(None, None, 1, -1, 0, 0, None) == INVALID
     assert lib.sc_validate_metadata(None, None, 0, 1, 0, 0, None) == INVALID
     assert lib.sc_validate_metadata(None, None, 1, 1, -5, 0, None) == INVALID
+
+
+def test_binding_accepts_empty_row_tensors():
+    import numpy as np
+    import torch
+    for shape in ((0, 8), (0, 1), (0, 4096)):
+        t = torch.from_numpy(np.zeros(shape, np.float32))
+        assert scs._rows(t, "x") == shape[1]
+    with pytest.raises(ValueError):
+        scs._rows(torch.zeros(3, 4).t(), "x")       # channel stride 3

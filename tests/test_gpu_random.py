@@ -76,3 +76,83 @@ def test_random_depthwise_batches(seed):
     ref, rpool, ab = oracle.conv(case, out_dtype="f64", absum=True)
     np.testing.assert_array_equal(pool, rpool, err_msg="state pool not bit-exact")
     check_close(out, ref, ab, case.dtype, FLOOR)
+
+
+# ---------------------------------------------------------------------------
+# speculative update: uniform draft count and one count per request
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("seed", range(24))
+def test_random_speculative_batches(seed):
+    from tests._gpu import run_spec_case
+    from tests.test_gpu_spec_varlen import run_varlen
+    rng = np.random.default_rng(0x7B0000 + seed)
+    K = int(rng.choice([2, 3, 4, 4, 5]))
+    d = int(rng.choice([1, 1, 2, 3]))
+    n = int(rng.integers(1, 6))
+    S = (K - 1) * d + n
+    C = int(rng.choice([8, 24, 256, 1000, 2056]))
+    dtype = str(rng.choice(["bf16", "f32"]))
+    act = str(rng.choice(["silu", "none"]))
+    B = int(rng.integers(1, 20))
+    varlen = bool(rng.random() < 0.5)
+    sd = bool(rng.random() < 0.4)
+    print(f"[gpu] random spec seed={seed} K={K} d={d} S={S} C={C} {dtype} act={act} B={B} "
+          f"varlen={varlen} sd={sd}", flush=True)
+    if varlen:
+        max_q = int(rng.integers(1, S + 1))
+        case, qsl = synthetic.spec_varlen_case("rspec", 0x7B0000 + seed, C=C, K=K, d=d,
+                                               dtype=dtype, act=act, w_std=0.4, bias_std=0.2,
+                                               num_slots=B + 5, B=B, num_spec=n, q_max=max_q)
+    else:
+        q = int(rng.integers(1, S + 1))
+        case = conv_case("rspec", 0x7B0000 + seed, C=C, K=K, d=d, dtype=dtype, act=act,
+                         w_std=0.4, bias_std=0.2, num_slots=B + 5, num_decodes=B, q=q,
+                         num_spec=n)
+    if B > 2 and rng.random() < 0.5:
+        case.decode_slots[int(rng.integers(0, B))] = -1
+    if sd:
+        case = synthetic.as_sd(case)
+    acc = rng.integers(-1, S + 3, size=B).astype(np.int32)   # includes out-of-range counts
+    if varlen:
+        max_q = max(int(np.diff(qsl).max()), 1)
+        out, pool = run_varlen(case, acc, qsl, max_q)
+        ref, rpool, ab = oracle.conv_spec_varlen(case, acc, qsl, out_dtype="f64", absum=True)
+    else:
+        out, pool = run_spec_case(case, acc)
+        ref, rpool, ab = oracle.conv_spec(case, acc, out_dtype="f64", absum=True)
+    np.testing.assert_array_equal(pool, rpool, err_msg="state pool not bit-exact")
+    check_close(out, ref, ab, case.dtype, FLOOR)
+
+
+# ---------------------------------------------------------------------------
+# CCA: head counts, head size and both kernel widths (MFMA and one-thread paths)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("seed", range(16))
+def test_random_cca_batches(seed):
+    from tests._gpu import cca_floor_rel, run_cca_case
+    rng = np.random.default_rng(0x7C0000 + seed)
+    nq, nkv = [(4, 2), (2, 2), (8, 2), (16, 4), (4, 1)][int(rng.integers(0, 5))]
+    hd = int(rng.choice([16, 32, 128, 128]))
+    t0 = int(rng.choice([1, 2, 2, 3]))
+    t1 = int(rng.choice([1, 2, 2, 3]))
+    nd = int(rng.choice([0, 3, 40]))
+    lens = [int(v) for v in rng.integers(0, 90, size=int(rng.choice([0, 2, 6])))]
+    if nd == 0 and sum(lens) == 0:
+        lens = [int(rng.integers(1, 60))]
+    case = synthetic.cca_case("rcca", 0x7C0000 + seed, nq=nq, nkv=nkv, hd=hd, t0=t0, t1=t1,
+                              num_decodes=nd, prefill_lens=lens,
+                              num_slots=nd + len(lens) + 4)
+    no_init = bool(rng.random() < 0.3)
+    print(f"[gpu] random cca seed={seed} nq={nq} nkv={nkv} hd={hd} t0={t0} t1={t1} "
+          f"decodes={nd} lens={lens} no_delayed_init={no_init}", flush=True)
+    out, cs, ds = run_cca_case(case, no_delayed_init=no_init)
+    from dataclasses import replace
+    ocase = replace(case, delayed_init=np.zeros_like(case.delayed_init)) if no_init else case
+    ref, _, _, ab = oracle.cca(ocase, out_dtype="f64", dw_mode=1, absum=True)
+    _, rcs, rds, _ = oracle.cca(ocase, dw_mode=1)
+    np.testing.assert_array_equal(cs, rcs, err_msg="conv state not bit-exact")
+    np.testing.assert_array_equal(ds, rds, err_msg="delayed state not bit-exact")
+    C = case.C
+    np.testing.assert_array_equal(synthetic.bf16_to_f32(out[:, C:]).astype(np.float64),
+                                  ref[:, C:], err_msg="value half not bit-exact")
+    check_close(out[:, :C], ref[:, :C], ab[:, :C], "bf16", cca_floor_rel(case), what="q/k")
