@@ -49,7 +49,7 @@ def random_case(seed):
     return case, rng
 
 
-@pytest.mark.parametrize("seed", range(40))
+@pytest.mark.parametrize("seed", range(120))
 def test_random_depthwise_batches(seed):
     case, rng = random_case(0x7A0000 + seed)
     mode = str(rng.choice(["plain", "plain", "strided", "fused"]))
@@ -81,7 +81,7 @@ def test_random_depthwise_batches(seed):
 # ---------------------------------------------------------------------------
 # speculative update: uniform draft count and one count per request
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("seed", range(24))
+@pytest.mark.parametrize("seed", range(64))
 def test_random_speculative_batches(seed):
     from tests._gpu import run_spec_case
     from tests.test_gpu_spec_varlen import run_varlen
@@ -127,7 +127,7 @@ def test_random_speculative_batches(seed):
 # ---------------------------------------------------------------------------
 # CCA: head counts, head size and both kernel widths (MFMA and one-thread paths)
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("seed", range(16))
+@pytest.mark.parametrize("seed", range(40))
 def test_random_cca_batches(seed):
     from tests._gpu import cca_floor_rel, run_cca_case
     rng = np.random.default_rng(0x7C0000 + seed)
@@ -156,3 +156,29 @@ def test_random_cca_batches(seed):
     np.testing.assert_array_equal(synthetic.bf16_to_f32(out[:, C:]).astype(np.float64),
                                   ref[:, C:], err_msg="value half not bit-exact")
     check_close(out[:, :C], ref[:, :C], ab[:, :C], "bf16", cca_floor_rel(case), what="q/k")
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_random_large_depthwise_batches(seed):
+    """Wide rows and long requests: 8192 channels, up to 3000 tokens a request,
+    the vector kernels' shapes (width 4 or 2, dilation 1-3), either layout."""
+    rng = np.random.default_rng(0x7D0000 + seed)
+    K, d = [(4, 1), (4, 2), (4, 3), (2, 1)][int(rng.integers(0, 4))]
+    H = (K - 1) * d
+    lens = [int(v) for v in rng.integers(0, 3001, size=int(rng.integers(1, 7)))]
+    nd = int(rng.choice([0, 64]))
+    q = int(rng.choice([1, 2, 4]))
+    grid = 0 if rng.random() < 0.5 else int(max(H, 1) * rng.choice([64, 128]))
+    need = nd + len(lens) + (sum(n // grid for n in lens) if grid else 0)
+    case = conv_case("rlarge", 0x7D0000 + seed, C=8192, K=K, d=d, dtype="bf16",
+                     act=str(rng.choice(["silu", "none"])), w_std=0.25, bias_std=0.1,
+                     num_slots=need + 4, num_decodes=nd, q=q, prefill_lens=lens,
+                     prefill_h_p=0.5, ckpt_grid=grid)
+    if rng.random() < 0.5:
+        case = synthetic.as_sd(case)
+    print(f"[gpu] random large seed={seed} T={case.T} K={K} d={d} decodes={nd}x{q} "
+          f"lens={lens} grid={grid} layout={case.layout}", flush=True)
+    out, pool = run_conv_case(case)
+    ref, rpool, ab = oracle.conv(case, out_dtype="f64", absum=True)
+    np.testing.assert_array_equal(pool, rpool, err_msg="state pool not bit-exact")
+    check_close(out, ref, ab, case.dtype, FLOOR)
