@@ -723,8 +723,16 @@ hipError_t launch_kd(const ConvArgs& a, int qc, dim3 grid, hipStream_t s) {
               : launch_kd_l<E, K, D, SILU, false>(a, qc, grid, s);
 }
 
-// tokens per one-pass prefill chunk for history length H (must be >= H)
-constexpr int pairs_chunk(int H) { return H <= 4 ? SC_PAIRS_CHUNK_SMALL : (H <= 8 ? 8 : 16); }
+// tokens per one-pass prefill chunk for history length H (must be >= H).
+// `small` launches (tokens x channels <= kSmallLaunch) are bound by their ramp
+// and drain, where shorter chunks finish sooner; larger ones by bandwidth,
+// where longer chunks re-read fewer halo rows. Measured at 8192 channels: 8
+// tokens won by 7.8 / 2.5 / 1.1% at 2.6k / 5.3k / 7.4k tokens, 12 by 1.8 /
+// 3.6 / 6.8% at 9.1k / 11.8k / 15.3k tokens.
+constexpr int64_t kSmallLaunch = int64_t(1) << 26;
+constexpr int pairs_chunk(int H, bool small) {
+  return H <= 4 ? (small ? 8 : SC_PAIRS_CHUNK_SMALL) : (H <= 8 ? 8 : 16);
+}
 // requests per update workgroup
 constexpr int update_reqs(int H, int Q, bool sd) {
   if (H <= 4) return Q == 1 ? (sd ? SC_UPDATE_REQS_SD : SC_UPDATE_REQS) : SC_UPDATE_REQS_MULTI;
@@ -734,11 +742,15 @@ constexpr int update_reqs(int H, int Q, bool sd) {
 template <int K, int D, bool SILU, bool FUSE, bool SD>
 hipError_t launch_pairs_l(const ConvArgs& a, int qc, dim3 grid, hipStream_t s) {
   constexpr int H = (K - 1) * D;
+  if (qc == 0 && a.chunk == pairs_chunk(H, true) && pairs_chunk(H, true) != pairs_chunk(H, false)) {
+    hipLaunchKernelGGL((conv_pairs<K, D, pairs_chunk(H, true), SILU, false, FUSE, SD>), grid, dim3(kBlock), 0, s, a);
+    return hipGetLastError();
+  }
   switch (qc) {
     case 1: hipLaunchKernelGGL((conv_update_pairs<K, D, 1, update_reqs(H, 1, SD), SILU, FUSE, SD>), grid, dim3(kBlock), 0, s, a); break;
     case 2: hipLaunchKernelGGL((conv_update_pairs<K, D, 2, update_reqs(H, 2, SD), SILU, FUSE, SD>), grid, dim3(kBlock), 0, s, a); break;
     case 4: hipLaunchKernelGGL((conv_update_pairs<K, D, 4, update_reqs(H, 4, SD), SILU, FUSE, SD>), grid, dim3(kBlock), 0, s, a); break;
-    default: hipLaunchKernelGGL((conv_pairs<K, D, pairs_chunk(H), SILU, false, FUSE, SD>), grid, dim3(kBlock), 0, s, a); break;
+    default: hipLaunchKernelGGL((conv_pairs<K, D, pairs_chunk(H, false), SILU, false, FUSE, SD>), grid, dim3(kBlock), 0, s, a); break;
   }
   return hipGetLastError();
 }
@@ -760,7 +772,8 @@ hipError_t launch_pairs(const ConvArgs& a, int K, int D, int qc, dim3 grid, hipS
 template <class E, bool SILU>
 hipError_t launch_typed(const ConvArgs& a, int K, int D, bool fast, int qc, dim3 grid,
                         hipStream_t s, bool fuse) {
-  if (a.chunk == pairs_chunk((K - 1) * D) && fast && E::VEC == 8 && pairs_shape(K, D) &&
+  if ((a.chunk == pairs_chunk((K - 1) * D, true) || a.chunk == pairs_chunk((K - 1) * D, false)) &&
+      fast && E::VEC == 8 && pairs_shape(K, D) &&
       !SC_NO_PAIRS)
     return fuse ? launch_pairs<SILU, true>(a, K, D, qc, grid, s)
                 : launch_pairs<SILU, false>(a, K, D, qc, grid, s);
@@ -804,7 +817,8 @@ hipError_t launch_conv(ConvArgs a, int dtype, int K, int D, bool silu_act, bool 
                     (!fuse || pairs_ok);
   // the one-pass kernel takes its halo from x: its chunk covers H by construction
   const bool pairs = fast && pairs_ok;
-  a.chunk = pairs ? pairs_chunk(H) : fast ? kChunk : (H > kChunk ? H : kChunk);
+  const bool small = (int64_t)a.num_tokens * a.C <= kSmallLaunch;
+  a.chunk = pairs ? pairs_chunk(H, small) : fast ? kChunk : (H > kChunk ? H : kChunk);
   int qc = 0;
   if (fast && uniform && (a.q == 1 || a.q == 2 || a.q == 4) && a.q <= a.chunk) qc = a.q;
   const int64_t per_block_ch = (int64_t)kBlock * (fast ? vec : 1);
