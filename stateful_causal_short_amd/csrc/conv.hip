@@ -739,6 +739,55 @@ constexpr int update_reqs(int H, int Q, bool sd) {
   return Q == 1 ? 2 : 1;
 }
 
+// Compute units of the current device (cached per device; 256 if unknown).
+int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+      n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
+// Requests per one-token update workgroup (H <= 4) by batch size: each
+// workgroup is a single round of loads, so the launch should fill the device
+// once without splitting it thinner than that. A DS pool (state transposed
+// through LDS) is fastest at two workgroups per CU, an SD pool at one; so take
+// the largest R in {1, 2, 4, 8} whose workgroup count still reaches that
+// target. On a DS pool, when even R = 8 needs more than one round, 4 (two
+// LDS batches fewer) measured faster. Measured optimum at 8192 channels on
+// 256 CUs: DS R = 1, 1, 2, 4, 8, 4 and SD R = 1, 2, 4, 8, 8, 8 for 64, 128,
+// 256, 512, 1024, 2048 requests.
+int update_reqs_rt(int H, bool sd, int64_t batch, int n_cblk) {
+  if (H > 4) return update_reqs(H, 1, sd);
+  const int64_t target = (int64_t)device_cus() * (sd ? 1 : 2);
+  auto wgs = [&](int R) { return (batch + R - 1) / R * n_cblk; };
+  if (!sd && wgs(8) > target) return 4;
+  int R = 8;
+  while (R > 1 && wgs(R) < target) R >>= 1;
+  return R;
+}
+
+template <int K, int D, bool SILU, bool FUSE, bool SD>
+hipError_t launch_update1(const ConvArgs& a, dim3 grid, hipStream_t s) {
+  constexpr int H = (K - 1) * D;
+  if constexpr (H > 4) {
+    hipLaunchKernelGGL((conv_update_pairs<K, D, 1, update_reqs(H, 1, SD), SILU, FUSE, SD>), grid, dim3(kBlock), 0, s, a);
+  } else {
+    switch (a.ureqs) {
+      case 1: hipLaunchKernelGGL((conv_update_pairs<K, D, 1, 1, SILU, FUSE, SD>), grid, dim3(kBlock), 0, s, a); break;
+      case 2: hipLaunchKernelGGL((conv_update_pairs<K, D, 1, 2, SILU, FUSE, SD>), grid, dim3(kBlock), 0, s, a); break;
+      case 4: hipLaunchKernelGGL((conv_update_pairs<K, D, 1, 4, SILU, FUSE, SD>), grid, dim3(kBlock), 0, s, a); break;
+      default: hipLaunchKernelGGL((conv_update_pairs<K, D, 1, 8, SILU, FUSE, SD>), grid, dim3(kBlock), 0, s, a); break;
+    }
+  }
+  return hipGetLastError();
+}
+
 template <int K, int D, bool SILU, bool FUSE, bool SD>
 hipError_t launch_pairs_l(const ConvArgs& a, int qc, dim3 grid, hipStream_t s) {
   constexpr int H = (K - 1) * D;
@@ -747,7 +796,7 @@ hipError_t launch_pairs_l(const ConvArgs& a, int qc, dim3 grid, hipStream_t s) {
     return hipGetLastError();
   }
   switch (qc) {
-    case 1: hipLaunchKernelGGL((conv_update_pairs<K, D, 1, update_reqs(H, 1, SD), SILU, FUSE, SD>), grid, dim3(kBlock), 0, s, a); break;
+    case 1: return launch_update1<K, D, SILU, FUSE, SD>(a, grid, s);
     case 2: hipLaunchKernelGGL((conv_update_pairs<K, D, 2, update_reqs(H, 2, SD), SILU, FUSE, SD>), grid, dim3(kBlock), 0, s, a); break;
     case 4: hipLaunchKernelGGL((conv_update_pairs<K, D, 4, update_reqs(H, 4, SD), SILU, FUSE, SD>), grid, dim3(kBlock), 0, s, a); break;
     default: hipLaunchKernelGGL((conv_pairs<K, D, pairs_chunk(H, false), SILU, false, FUSE, SD>), grid, dim3(kBlock), 0, s, a); break;
@@ -825,7 +874,9 @@ hipError_t launch_conv(ConvArgs a, int dtype, int K, int D, bool silu_act, bool 
   a.n_cblk = (int)((a.C + per_block_ch - 1) / per_block_ch);
   int64_t n_chunks;
   if (pairs && qc) {
-    const int R = update_reqs(H, qc, a.sd != 0);
+    const int R = qc == 1 ? update_reqs_rt(H, a.sd != 0, a.batch, a.n_cblk)
+                          : update_reqs(H, qc, a.sd != 0);
+    a.ureqs = R;
     n_chunks = (a.batch + R - 1) / R;     // workgroup groups of R requests
   } else if (uniform) {
     n_chunks = (int64_t)a.batch * ((a.q + a.chunk - 1) / a.chunk);

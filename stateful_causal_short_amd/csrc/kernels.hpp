@@ -74,6 +74,7 @@ struct ConvArgs {
   int32_t sd;                // 1: pool is (num_slots, S, C) ("SD"), else (num_slots, C, S)
   // filled by launch_conv
   int32_t chunk, n_cblk, n_logical, per_xcd;
+  int32_t ureqs;             // requests per one-token update workgroup (host side)
 };
 
 struct ConvLaunchInfo {
