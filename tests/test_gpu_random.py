@@ -113,15 +113,47 @@ def test_random_speculative_batches(seed):
     if sd:
         case = synthetic.as_sd(case)
     acc = rng.integers(-1, S + 3, size=B).astype(np.int32)   # includes out-of-range counts
+    fused = bool(rng.random() < 0.35)
+    T = int(qsl[-1]) if varlen else B * case.q
+    fz, perm = {}, None
+    if fused:
+        n_phys = T + 3
+        perm = rng.permutation(n_phys)[:T].astype(np.int32)
+        xp = synthetic._normal(rng, (n_phys, C), 1.0, dtype)
+        xp[perm] = case.x[:T]
+        R = synthetic._normal(rng, (n_phys, C), 1.0, dtype)
+        O = synthetic._normal(rng, (n_phys, C), 1.0, dtype) if rng.random() < 0.5 else None
+        fz = dict(x=xp, token_indices=perm, resid=R, outer=O)
+    print(f"[gpu]   fused={fused}", flush=True)
     if varlen:
         max_q = max(int(np.diff(qsl).max()), 1)
-        out, pool = run_varlen(case, acc, qsl, max_q)
-        ref, rpool, ab = oracle.conv_spec_varlen(case, acc, qsl, out_dtype="f64", absum=True)
+        out, pool = run_varlen(case, acc, qsl, max_q, **fz)
+        ref, rpool, ab = oracle.conv_spec_varlen(case, acc, qsl, out_dtype="f64", absum=True,
+                                                 **fz)
+    elif fused:
+        out, pool = run_fused_case(case, fz["x"], perm, resid=fz["resid"], outer=fz["outer"],
+                                   num_accepted=acc)
+        ref, rpool, ab = oracle.conv_spec(case, acc, out_dtype="f64", absum=True, **fz)
     else:
         out, pool = run_spec_case(case, acc)
         ref, rpool, ab = oracle.conv_spec(case, acc, out_dtype="f64", absum=True)
     np.testing.assert_array_equal(pool, rpool, err_msg="state pool not bit-exact")
-    check_close(out, ref, ab, case.dtype, FLOOR)
+    if fused:
+        # rows of skipped requests keep their residual in both (the oracle starts its
+        # output from zeros and adds the residual only where it computes)
+        live = np.zeros(T, bool)
+        if varlen:
+            for r in range(B):
+                q_r = int(qsl[r + 1] - qsl[r])
+                if 0 < q_r <= S:
+                    live[int(qsl[r]):int(qsl[r + 1])] = True
+        else:
+            live[:] = True
+        check_close(out[perm[live]], ref[perm[live]], ab[live], case.dtype, FLOOR, what="fused out")
+        untouched = np.setdiff1d(np.arange(out.shape[0]), perm[live])
+        np.testing.assert_array_equal(out[untouched], fz["resid"][untouched])
+    else:
+        check_close(out, ref, ab, case.dtype, FLOOR)
 
 
 # ---------------------------------------------------------------------------
