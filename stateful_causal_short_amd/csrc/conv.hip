@@ -765,10 +765,13 @@ int device_cus() {
 // LDS batches fewer) measured faster. Measured optimum at 8192 channels on
 // 256 CUs: DS R = 1, 1, 2, 4, 8, 4 and SD R = 1, 2, 4, 8, 8, 8 for 64, 128,
 // 256, 512, 1024, 2048 requests.
+// Longer histories (H > 4) take at most 2 requests per workgroup: for the
+// 9-entry PLE history on a DS pool, R = 1, 2, 2~1 were fastest at 64, 256,
+// 1024 requests, and R = 4 never was.
 int update_reqs_rt(int H, bool sd, int64_t batch, int n_cblk) {
-  if (H > 4) return update_reqs(H, 1, sd);
   const int64_t target = (int64_t)device_cus() * (sd ? 1 : 2);
   auto wgs = [&](int R) { return (batch + R - 1) / R * n_cblk; };
+  if (H > 4) return wgs(2) >= target ? 2 : 1;
   if (!sd && wgs(8) > target) return 4;
   int R = 8;
   while (R > 1 && wgs(R) < target) R >>= 1;
@@ -779,7 +782,10 @@ template <int K, int D, bool SILU, bool FUSE, bool SD>
 hipError_t launch_update1(const ConvArgs& a, dim3 grid, hipStream_t s) {
   constexpr int H = (K - 1) * D;
   if constexpr (H > 4) {
-    hipLaunchKernelGGL((conv_update_pairs<K, D, 1, update_reqs(H, 1, SD), SILU, FUSE, SD>), grid, dim3(kBlock), 0, s, a);
+    if (a.ureqs == 1)
+      hipLaunchKernelGGL((conv_update_pairs<K, D, 1, 1, SILU, FUSE, SD>), grid, dim3(kBlock), 0, s, a);
+    else
+      hipLaunchKernelGGL((conv_update_pairs<K, D, 1, 2, SILU, FUSE, SD>), grid, dim3(kBlock), 0, s, a);
   } else {
     switch (a.ureqs) {
       case 1: hipLaunchKernelGGL((conv_update_pairs<K, D, 1, 1, SILU, FUSE, SD>), grid, dim3(kBlock), 0, s, a); break;
