@@ -372,3 +372,40 @@ def test_checkpoint_grid_with_no_checkpoint_reached():
                      prefill_lens=[5, 30, 17], prefill_h_p=0.5, ckpt_grid=64)
     assert int(case.cu_ckpt[-1]) == 0 and case.ckpt_slots.size == 0
     parity(case)
+
+
+@pytest.mark.parametrize("layout", ["ds", "sd"])
+def test_launch_size_rules_do_not_change_results(layout):
+    """The launcher picks the prefill chunk length and the decode requests per
+    workgroup from the launch size. One large call (12-token chunks; 4 or 8
+    requests per workgroup) and the same requests split into small calls
+    (8-token chunks; 1 request per workgroup) must agree bit for bit."""
+    import torch
+    import stateful_causal_short_amd as scs
+    C = 8192
+    lens = [1900, 2100, 1700, 2300, 1500, 2000]                 # 11,500 tokens: above 2^26
+    case = conv_case("rules", 1301, C=C, K=4, d=1, dtype="bf16", act="silu", w_std=0.25,
+                     bias_std=0.1, num_slots=1200, num_decodes=1024, q=1, prefill_lens=lens,
+                     prefill_h_p=0.5)
+    if layout == "sd":
+        case = synthetic.as_sd(case)
+    print(f"[gpu] launch-size rules {layout}: T={case.T}", flush=True)
+    big_out, big_pool = run_conv_case(case)
+    nd = case.num_decodes
+    x, w, b = dev(case.x), dev(case.w), dev(case.bias)
+    out = torch.zeros_like(x)
+    pool = dev(case.pool)
+    kw = dict(dilation=1, activation="silu", state_layout=layout)
+    for i in range(0, nd, 64):                                  # 64-request decode calls
+        scs.sc_conv_update(x[i:i + 64], out[i:i + 64], w, b, pool,
+                           dev(case.decode_slots[i:i + 64]), None, q=1, **kw)
+    starts = nd + case.qsl_p[:-1]
+    for r, L in enumerate(lens):                                # one prefill call per request
+        s0 = int(starts[r])
+        scs.sc_conv_prefill_varlen(x[s0:s0 + L], out[s0:s0 + L], w, b, pool,
+                                   dev(np.array([0, L], np.int32)),
+                                   dev(case.prefill_slots[r:r + 1]),
+                                   dev(np.asarray(case.prefill_h[r:r + 1], np.uint8)), **kw)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(out), big_out)
+    np.testing.assert_array_equal(host(pool), big_pool)
