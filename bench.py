@@ -548,17 +548,21 @@ def traffic_from(d):
                    for c in ("FETCH_SIZE", "WRITE_SIZE"))
 
     entries = {}
-    if have("varlen_prefill"):
+    # depthwise workloads: the one library kernel of the run (largest counters)
+    for workload, kern in (("varlen_prefill", "prefill"), ("decode", "decode_update")):
+        if not have(workload):
+            continue
         kib, names = {}, {}
         for counter in ("FETCH_SIZE", "WRITE_SIZE"):
-            pv = per_kernel("varlen_prefill", counter)
-            cand = {k: statistics.median(v) for k, v in pv.items() if not k.startswith("__amd")}
+            pv = per_kernel(workload, counter)
+            cand = {k: statistics.median(v) for k, v in pv.items() if k.startswith("void sc::")}
             names[counter] = max(cand, key=cand.get)
             kib[counter] = cand[names[counter]]
         if names["FETCH_SIZE"] != names["WRITE_SIZE"]:
             raise SystemExit(f"different dominant kernels: {names}")
-        _, alg = conv_kernel_bytes(conv_workload("varlen_prefill"))
-        entries["varlen_prefill:prefill"] = (kib, names["FETCH_SIZE"], alg, source_sha())
+        dec_b, pre_b = conv_kernel_bytes(conv_workload(workload))
+        alg = pre_b if kern == "prefill" else dec_b
+        entries[f"{workload}:{kern}"] = (kib, names["FETCH_SIZE"], alg, source_sha())
     if have("cca"):
         import synthetic
         kib, kern = {}, []
@@ -749,7 +753,9 @@ def decode_secondary(args):
             "tokens_per_s": case.T / (ms * 1e-3),
             "roofline": {"kernel": "decode_update", "bound": "hbm", "achieved": gbps,
                          "peak": PEAK_GBPS, "unit": "GB/s", "frac": gbps / PEAK_GBPS,
-                         "traffic": None, "alg_bytes_per_launch": dec_b}}
+                         "traffic": traffic_for("decode:decode_update")
+                         if args.state_layout == "ds" else None,
+                         "alg_bytes_per_launch": dec_b}}
 
 
 if __name__ == "__main__":
