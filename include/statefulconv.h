@@ -284,7 +284,9 @@ sc_status sc_cca_qk_conv(const sc_cca_desc* desc, const void* q, const void* k,
  *                   entry >= num_slots, or two equal non-negative entries
  *                   (negative entries are padding rows);
  * else SC_OK. It allocates no device memory and launches nothing. batch = 0:
- * SC_OK without touching the pointers; a HIP error while copying: SC_ERR_HIP. */
+ * SC_OK without touching the pointers; a HIP error while copying: SC_ERR_HIP;
+ * negative sizes, idx_stride < 1, or arrays too large to copy to the host:
+ * SC_ERR_INVALID_ARG. */
 sc_status sc_validate_metadata(const int32_t* query_start_loc, const int32_t* state_indices,
                                int64_t idx_stride, int32_t batch, int64_t num_tokens,
                                int32_t num_slots, void* stream);

@@ -3,6 +3,7 @@
 // in include/statefulconv.h.
 #include <stdint.h>
 
+#include <new>
 #include <unordered_set>
 #include <vector>
 
@@ -69,18 +70,11 @@ sc_status from_hip(hipError_t e) {
   return SC_ERR_HIP;
 }
 
-}  // namespace
-
-extern "C" {
-
-int32_t sc_abi_version(void) { return SC_ABI_VERSION; }
-
-sc_status sc_validate_metadata(const int32_t* query_start_loc, const int32_t* state_indices,
-                               int64_t idx_stride, int32_t batch, int64_t num_tokens,
-                               int32_t num_slots, void* stream) {
-  if (batch < 0 || num_tokens < 0 || num_slots < 0 || idx_stride < 1) return SC_ERR_INVALID_ARG;
-  if (batch == 0) return SC_OK;
-  hipStream_t st = (hipStream_t)stream;
+// host side of sc_validate_metadata: copies the arrays and checks them
+sc_status validate_metadata_host(const int32_t* query_start_loc,
+                                 const int32_t* state_indices, int64_t idx_stride,
+                                 int32_t batch, int64_t num_tokens, int32_t num_slots,
+                                 hipStream_t st) {
   if (query_start_loc) {
     std::vector<int32_t> q((size_t)batch + 1);
     if (hipMemcpyAsync(q.data(), query_start_loc, q.size() * sizeof(int32_t),
@@ -92,6 +86,7 @@ sc_status sc_validate_metadata(const int32_t* query_start_loc, const int32_t* st
       if (q[(size_t)r + 1] < q[(size_t)r]) return SC_ERR_INVALID_ARG;
   }
   if (state_indices) {
+    if (idx_stride > (INT64_MAX / 4 - 1) / batch) return SC_ERR_INVALID_ARG;
     const size_t n = (size_t)(batch - 1) * (size_t)idx_stride + 1;
     std::vector<int32_t> s(n);
     if (hipMemcpyAsync(s.data(), state_indices, n * sizeof(int32_t), hipMemcpyDeviceToHost,
@@ -108,6 +103,27 @@ sc_status sc_validate_metadata(const int32_t* query_start_loc, const int32_t* st
   return SC_OK;
 }
 
+}  // namespace
+
+extern "C" {
+
+int32_t sc_abi_version(void) { return SC_ABI_VERSION; }
+
+sc_status sc_validate_metadata(const int32_t* query_start_loc, const int32_t* state_indices,
+                               int64_t idx_stride, int32_t batch, int64_t num_tokens,
+                               int32_t num_slots, void* stream) {
+  if (batch < 0 || num_tokens < 0 || num_slots < 0 || idx_stride < 1) return SC_ERR_INVALID_ARG;
+  if (batch == 0) return SC_OK;
+  // the host copies below must not let an allocation failure leave the C ABI
+  try {
+    return validate_metadata_host(query_start_loc, state_indices, idx_stride, batch,
+                                  num_tokens, num_slots, (hipStream_t)stream);
+  } catch (const std::bad_alloc&) {
+    return SC_ERR_INVALID_ARG;
+  }
+}
+
+
 const char* sc_status_string(sc_status s) {
   switch (s) {
     case SC_OK: return "ok";
@@ -116,7 +132,7 @@ const char* sc_status_string(sc_status s) {
     case SC_ERR_DTYPE: return "unsupported dtype";
     case SC_ERR_STATE_CAPACITY: return "state_len smaller than (width-1)*dilation";
     case SC_ERR_UNSUPPORTED: return "configuration not supported by this library";
-    case SC_ERR_HIP: return "HIP launch error";
+    case SC_ERR_HIP: return "HIP runtime error (launch or copy)";
   }
   return "unknown status";
 }

@@ -252,6 +252,10 @@ def test_validate_metadata_host_rules():
     assert lib.sc_validate_metadata(None, None, 1, -1, 0, 0, None) == INVALID
     assert lib.sc_validate_metadata(None, None, 0, 1, 0, 0, None) == INVALID
     assert lib.sc_validate_metadata(None, None, 1, 1, -5, 0, None) == INVALID
+    # a stride whose index span overflows is rejected before any copy (the
+    # pointer is never dereferenced)
+    assert lib.sc_validate_metadata(None, ctypes.c_void_p(256), 1 << 62, 3, 0, 4, None) == INVALID
+    assert scs.lib().sc_status_string(-6) == b"HIP runtime error (launch or copy)"
 
 
 def test_binding_accepts_empty_row_tensors():
