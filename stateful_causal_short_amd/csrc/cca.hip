@@ -769,20 +769,11 @@ hipError_t launch_cca(const CcaArgs& a, hipStream_t stream) {
   if (mfma) {
     // persistent grid: a multiple of the head-group count, as many workgroups
     // as fit on the device at once, never more than there are tiles to share
-    static int cu_count[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-    if (cu_count[dev] == 0) {
-      int n = 0;
-      if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
-        n = 256;
-      cu_count[dev] = n;
-    }
     const int NG = a.nq + a.nkv;
     const bool g8 = a.nq / a.nkv > 4;
     const int per_cu = cca_waves_per_simd(a.t0, g8 ? 8 : 4) / 2;   // resident 8-wave workgroups per CU
     const int64_t ntiles = (a.num_tokens + kCcaMT - 1) / kCcaMT;
-    int64_t S = (int64_t)cu_count[dev] * per_cu / NG;
+    int64_t S = (int64_t)device_cus() * per_cu / NG;
     if (S < 1) S = 1;
     if (S > ntiles) S = ntiles;
     CcaArgs b = a;

@@ -14,6 +14,10 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 constexpr int kBlock = 256;      // threads per workgroup (4 wave64)
 constexpr int kXcds = 8;         // MI355X: 8 XCDs, workgroups dealt round-robin
 
+// Compute units of the current device (host; cached per device, 256 if the
+// runtime cannot say); safe to call from several host threads.
+int device_cus();
+
 __device__ __forceinline__ u32x4 ld16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }

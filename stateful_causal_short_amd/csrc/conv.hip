@@ -19,6 +19,8 @@
 // State hazard: only the chunk holding a request's first tokens reads the
 // request's slot (chunks are at least H long, so later chunks take their halo
 // from x), and the same lanes write the new state after reading the old one.
+#include <atomic>
+
 #include "conv_device.hpp"
 
 namespace sc {
@@ -696,6 +698,21 @@ __global__ __launch_bounds__(kBlock) void conv_generic(ConvArgs a, int K, int D)
 // ---------------------------------------------------------------------------
 // host-side launch selection
 // ---------------------------------------------------------------------------
+// Each per-device slot is an atomic that every racing writer sets to the same
+// value.
+int device_cus() {
+  static std::atomic<int> cus[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+      n = 256;
+    cus[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 namespace {
 
 bool fast_shape(int K, int D) {
@@ -742,19 +759,6 @@ constexpr int update_reqs(int H, int Q, bool sd) {
   return Q == 1 ? 2 : 1;
 }
 
-// Compute units of the current device (cached per device; 256 if unknown).
-int device_cus() {
-  static int cus[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
-      n = 256;
-    cus[dev] = n;
-  }
-  return cus[dev];
-}
 
 // Requests per one-token update workgroup (H <= 4) by batch size: each
 // workgroup is a single round of loads, so the launch should fill the device
