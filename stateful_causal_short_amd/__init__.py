@@ -129,17 +129,30 @@ def _torch():
 
 
 def _ptr(t) -> Optional[int]:
-    return None if t is None else t.data_ptr()
+    """Device address of a tensor (None passes through). Every tensor argument
+    is read or written by a kernel, so a host tensor is rejected here rather
+    than handed to the GPU as an address."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"expected a tensor on the GPU, got one on {t.device}")
+    return t.data_ptr()
 
 
 def _stream(stream, like=None) -> Optional[int]:
     """Raw HIP stream: the given one, else torch's current stream on the device
     of tensor `like` (or the current device)."""
+    torch = _torch()
+    if like is not None and not like.is_cuda:
+        raise ValueError(f"expected a tensor on the GPU, got one on {like.device}")
+    cur = torch.cuda.current_device()
+    if like is not None and like.get_device() != cur:
+        # the library launches on the current device
+        raise ValueError(f"tensors are on cuda:{like.get_device()} but the current device is "
+                         f"cuda:{cur}; call under torch.cuda.device({like.get_device()})")
     if stream is not None:
         return stream.cuda_stream
-    torch = _torch()
-    dev = like.get_device() if like is not None else torch.cuda.current_device()
-    return torch._C._cuda_getCurrentRawStream(dev)
+    return torch._C._cuda_getCurrentRawStream(cur)
 
 
 def _dtype_code(t) -> int:
@@ -169,7 +182,7 @@ def _index(t, name) -> Tuple[int, int]:
     if t.dim() not in (1, 2):
         raise ValueError(f"{name}: expected a 1-D or 2-D tensor")
     # with at most one row the stride is never used (empty tensors may report 0)
-    return t.data_ptr(), (t.stride(0) if t.shape[0] > 1 else 1)
+    return _ptr(t), (t.stride(0) if t.shape[0] > 1 else 1)
 
 
 def _flags(t, name):
@@ -178,7 +191,7 @@ def _flags(t, name):
         return None
     if t.dtype not in (torch.bool, torch.uint8) or not t.is_contiguous():
         raise ValueError(f"{name}: expected a contiguous bool/uint8 tensor")
-    return t.data_ptr()
+    return _ptr(t)
 
 
 def _check(fn: str, status: int):

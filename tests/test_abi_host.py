@@ -266,3 +266,22 @@ def test_binding_accepts_empty_row_tensors():
         assert scs._rows(t, "x") == shape[1]
     with pytest.raises(ValueError):
         scs._rows(torch.zeros(3, 4).t(), "x")       # channel stride 3
+
+
+def test_binding_rejects_host_tensors():
+    """Every tensor argument is a device address for a kernel: the binding
+    refuses a host tensor before anything reaches the library."""
+    import torch
+    C = 64
+    x = torch.zeros(4, C, dtype=torch.bfloat16)
+    w = torch.zeros(C, 4, dtype=torch.bfloat16)
+    pool = torch.zeros(8, C, 3, dtype=torch.bfloat16)
+    idx = torch.arange(4, dtype=torch.int32)
+    with pytest.raises(ValueError, match="on the GPU"):
+        scs.sc_conv_update(x, torch.zeros_like(x), w, None, pool, idx, q=1)
+    qsl = torch.tensor([0, 4], dtype=torch.int32)
+    h = torch.ones(1, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="on the GPU"):
+        scs.sc_conv_prefill_varlen(x, torch.zeros_like(x), w, None, pool, qsl, idx[:1], h)
+    with pytest.raises(ValueError, match="on the GPU"):
+        scs.sc_state_gather(pool, idx, torch.zeros(4, C, 3, dtype=torch.bfloat16))
