@@ -174,15 +174,19 @@ def _rows(t, name):
     return t.stride(0) if t.shape[0] > 1 else t.shape[1]
 
 
-def _index(t, name) -> Tuple[int, int]:
-    """int32 slot indices: 1-D, or 2-D whose column 0 holds the slot."""
+def _index_stride(t, name) -> int:
+    """Row stride of int32 slot indices: 1-D, or 2-D whose column 0 holds the slot."""
     torch = _torch()
     if t.dtype != torch.int32:
         raise ValueError(f"{name}: expected int32")
     if t.dim() not in (1, 2):
         raise ValueError(f"{name}: expected a 1-D or 2-D tensor")
     # with at most one row the stride is never used (empty tensors may report 0)
-    return _ptr(t), (t.stride(0) if t.shape[0] > 1 else 1)
+    return t.stride(0) if t.shape[0] > 1 else 1
+
+
+def _index(t, name) -> Tuple[int, int]:
+    return _ptr(t), _index_stride(t, name)
 
 
 def _flags(t, name):
@@ -207,8 +211,9 @@ def _fuse(x, out, token_indices, accumulate, outer_residual):
     if token_indices is not None and (token_indices.dtype != torch.int32 or
                                       not token_indices.is_contiguous()):
         raise ValueError("token_indices: expected a contiguous int32 tensor")
-    if outer_residual is not None and outer_residual.shape[0] != out.shape[0]:
-        raise ValueError("outer_residual: expected as many rows as out")
+    if outer_residual is not None and (outer_residual.shape[0] != out.shape[0] or
+                                       outer_residual.dtype != x.dtype):
+        raise ValueError("outer_residual: expected as many rows as out, in x's dtype")
     if token_indices is not None and out.shape[0] != x.shape[0]:
         raise ValueError("with token_indices, x and out are the full batch tensors")
     return ctypes.byref(sc_conv_fuse(
@@ -217,19 +222,36 @@ def _fuse(x, out, token_indices, accumulate, outer_residual):
         outer_row_stride=0 if outer_residual is None else _rows(outer_residual, "outer_residual")))
 
 
+def _covers(batch, **tensors):
+    """Per-request arrays (slots, flags, counts) must hold at least `batch`
+    entries: the kernels read entry r for every request r."""
+    for name, t in tensors.items():
+        if t is not None and t.shape[0] < batch:
+            raise ValueError(f"{name}: {t.shape[0]} entries for {batch} requests")
+
+
 def _conv_desc(x, out, weight, state_pool, dilation, activation, state_indices,
-               state_layout="ds"):
+               state_layout="ds", bias=None):
     C = x.shape[1]
     K = weight.shape[-1]
     act = {"silu": SC_ACT_SILU, "none": SC_ACT_NONE, None: SC_ACT_NONE}[activation]
+    # one dtype for every float tensor: the library reads them all as x's
+    for name, t in (("out", out), ("weight", weight), ("bias", bias),
+                    ("state_pool", state_pool)):
+        if t is not None and t.dtype != x.dtype:
+            raise ValueError(f"{name}: dtype {t.dtype} differs from x's {x.dtype}")
+    if out.dim() != 2 or out.shape[1] != C or out.shape[0] < x.shape[0]:
+        raise ValueError("out: expected at least as many (rows, C) as x")
     if weight.numel() != C * K or not weight.is_contiguous():
         raise ValueError("weight: expected a contiguous (C, K) or (C, 1, K) tensor")
+    if bias is not None and (bias.numel() != C or not bias.is_contiguous()):
+        raise ValueError("bias: expected a contiguous tensor of C entries")
     sd = {"ds": False, "sd": True}[state_layout]
     if not state_pool.is_contiguous() or state_pool.dim() != 3 or \
             state_pool.shape[2 if sd else 1] != C:
         raise ValueError("state_pool: expected a contiguous (num_slots, C, S) tensor, or "
                          "(num_slots, S, C) with state_layout='sd'")
-    _, sst = _index(state_indices, "state_indices")
+    sst = _index_stride(state_indices, "state_indices")
     return sc_conv_desc(channels=C, width=K, dilation=dilation,
                         state_len=state_pool.shape[1 if sd else 2], dtype=_dtype_code(x),
                         activation=act, x_row_stride=_rows(x, "x"),
@@ -257,10 +279,14 @@ def sc_conv_prefill_varlen(x, out, weight, bias, state_pool, query_start_loc,
     outer_residual is added too.
     """
     desc = _conv_desc(x, out, weight, state_pool, dilation, activation, state_indices,
-                      state_layout)
+                      state_layout, bias)
+    _covers(query_start_loc.shape[0] - 1, state_indices=state_indices,
+            has_initial_state=has_initial_state)
     cd = None
     if ckpt is not None:
         grid, cu, slots = ckpt
+        if grid:
+            _covers(query_start_loc.shape[0], cu_ckpt=cu)
         cd = ctypes.byref(sc_ckpt_desc(grid=grid, cu_ckpt=_ptr(cu), ckpt_slots=_ptr(slots)))
     st = lib().sc_conv_prefill_varlen(
         ctypes.byref(desc), _ptr(x), _ptr(out), _ptr(weight), _ptr(bias),
@@ -285,8 +311,9 @@ def sc_conv_update(x, out, weight, bias, state_pool, state_indices,
     if rows % max(q, 1):
         raise ValueError("rows must be a multiple of q")
     desc = _conv_desc(x, out, weight, state_pool, dilation, activation, state_indices,
-                      state_layout)
+                      state_layout, bias)
     B = rows // q if q else 0
+    _covers(B, state_indices=state_indices, has_initial_state=has_initial_state)
     st = lib().sc_conv_update(
         ctypes.byref(desc), _ptr(x), _ptr(out), _ptr(weight), _ptr(bias),
         _ptr(state_pool), state_pool.shape[0], _index(state_indices, "state_indices")[0],
@@ -309,7 +336,8 @@ def sc_conv_update_spec(x, out, weight, bias, state_pool, state_indices, num_acc
     if num_accepted_tokens.dtype != torch.int32 or not num_accepted_tokens.is_contiguous():
         raise ValueError("num_accepted_tokens: expected a contiguous int32 tensor")
     desc = _conv_desc(x, out, weight, state_pool, dilation, activation, state_indices,
-                      state_layout)
+                      state_layout, bias)
+    _covers(rows // q, state_indices=state_indices, num_accepted_tokens=num_accepted_tokens)
     st = lib().sc_conv_update_spec(
         ctypes.byref(desc), _ptr(x), _ptr(out), _ptr(weight), _ptr(bias),
         _ptr(state_pool), state_pool.shape[0], _index(state_indices, "state_indices")[0],
@@ -336,7 +364,8 @@ def sc_conv_update_spec_varlen(x, out, weight, bias, state_pool, state_indices,
         raise ValueError("query_start_loc: expected batch + 1 entries")
     rows = x.shape[0] if token_indices is None else token_indices.shape[0]
     desc = _conv_desc(x, out, weight, state_pool, dilation, activation, state_indices,
-                      state_layout)
+                      state_layout, bias)
+    _covers(batch, state_indices=state_indices, num_accepted_tokens=num_accepted_tokens)
     st = lib().sc_conv_update_spec_varlen(
         ctypes.byref(desc), _ptr(x), _ptr(out), _ptr(weight), _ptr(bias),
         _ptr(state_pool), state_pool.shape[0], _index(state_indices, "state_indices")[0],
@@ -409,6 +438,16 @@ def sc_cca_qk_conv(q, k, v_cur, v_del, out, w_dw, b_dw, w_gr, b_gr, delayed_init
                     ("conv_state", conv_state), ("delayed_state", delayed_state)):
         if not t.is_contiguous():
             raise ValueError(f"{name}: expected a contiguous tensor")
+    # one dtype for every float tensor: the library reads them all as q's
+    for name, t in (("k", k), ("v_cur", v_cur), ("v_del", v_del), ("out", out),
+                    ("w_dw", w_dw), ("b_dw", b_dw), ("w_gr", w_gr), ("b_gr", b_gr),
+                    ("delayed_init", delayed_init), ("conv_state", conv_state),
+                    ("delayed_state", delayed_state)):
+        if t is not None and t.dtype != q.dtype:
+            raise ValueError(f"{name}: dtype {t.dtype} differs from q's {q.dtype}")
+    if npf:
+        _covers(npf, prefill_slots=prefill_slots,
+                prefill_has_initial_state=prefill_has_initial_state)
     st = lib().sc_cca_qk_conv(
         ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v_cur), _ptr(v_del), _ptr(out),
         _ptr(w_dw), _ptr(b_dw), _ptr(w_gr), _ptr(b_gr), _ptr(delayed_init),
@@ -419,6 +458,6 @@ def sc_cca_qk_conv(q, k, v_cur, v_del, out, w_dw, b_dw, w_gr, b_gr, delayed_init
 
 
 __all__ = ["lib", "ScError", "LIB_PATH", "EXPORTS", "sc_conv_desc", "sc_ckpt_desc",
-           "sc_cca_desc", "sc_conv_fuse", "sc_conv_prefill_varlen", "sc_conv_update", "sc_conv_update_spec",
-           "sc_state_gather",
-           "sc_state_scatter", "sc_cca_qk_conv"]
+           "sc_cca_desc", "sc_conv_fuse", "sc_conv_prefill_varlen", "sc_conv_update",
+           "sc_conv_update_spec", "sc_conv_update_spec_varlen", "sc_validate_metadata",
+           "sc_state_gather", "sc_state_scatter", "sc_cca_qk_conv"]

@@ -285,3 +285,36 @@ def test_binding_rejects_host_tensors():
         scs.sc_conv_prefill_varlen(x, torch.zeros_like(x), w, None, pool, qsl, idx[:1], h)
     with pytest.raises(ValueError, match="on the GPU"):
         scs.sc_state_gather(pool, idx, torch.zeros(4, C, 3, dtype=torch.bfloat16))
+
+
+def test_binding_checks_dtypes_and_batch_coverage():
+    """Float tensors share x's dtype (a bf16 pool read as fp32 would run past
+    its end) and per-request arrays cover the batch; both are refused before
+    any device address is taken, so meta tensors (no storage) suffice."""
+    import torch
+    C = 64
+    m = dict(device="meta")
+    x = torch.empty(8, C, dtype=torch.bfloat16, **m)
+    w = torch.empty(C, 4, dtype=torch.bfloat16, **m)
+    pool = torch.empty(16, C, 3, dtype=torch.bfloat16, **m)
+    idx = torch.empty(8, dtype=torch.int32, **m)
+    for kw, what in ((dict(out=torch.empty(8, C, dtype=torch.float32, **m)), "out"),
+                     (dict(weight=w.float()), "weight"),
+                     (dict(state_pool=pool.float()), "state_pool"),
+                     (dict(bias=torch.empty(C, dtype=torch.float32, **m)), "bias"),
+                     (dict(bias=torch.empty(C - 1, dtype=torch.bfloat16, **m)), "bias"),
+                     (dict(out=torch.empty(7, C, dtype=torch.bfloat16, **m)), "out"),
+                     (dict(state_indices=idx[:7]), "state_indices")):
+        a = dict(x=x, out=torch.empty_like(x), weight=w, bias=None, state_pool=pool,
+                 state_indices=idx)
+        a.update(kw)
+        with pytest.raises(ValueError, match=what):
+            scs.sc_conv_update(a["x"], a["out"], a["weight"], a["bias"], a["state_pool"],
+                               a["state_indices"], q=1)
+    with pytest.raises(ValueError, match="num_accepted_tokens"):
+        scs.sc_conv_update_spec(x, torch.empty_like(x), w, None, pool, idx[:2],
+                                torch.empty(1, dtype=torch.int32, **m), q=4)
+    qsl = torch.empty(4, dtype=torch.int32, **m)
+    with pytest.raises(ValueError, match="has_initial_state"):
+        scs.sc_conv_prefill_varlen(x, torch.empty_like(x), w, None, pool, qsl, idx,
+                                   torch.empty(2, dtype=torch.uint8, **m))
