@@ -10,6 +10,7 @@ library is missing, import-time loading fails loudly.
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 from typing import Optional, Tuple
 
@@ -396,10 +397,24 @@ def sc_validate_metadata(query_start_loc=None, state_indices=None, *, num_tokens
     return True
 
 
+def _copy_rows(state_pool, idx, dense) -> int:
+    """Bytes per slot row; the pool and the dense buffer must agree on it, be
+    contiguous, and the dense buffer must hold a row per index."""
+    for name, t in (("state_pool", state_pool), ("dense", dense)):
+        if not t.is_contiguous() or t.dim() < 1:
+            raise ValueError(f"{name}: expected a contiguous tensor of rows")
+    row_of = lambda t: (t.numel() // t.shape[0] if t.shape[0] else
+                        math.prod(t.shape[1:])) * t.element_size()
+    if row_of(state_pool) != row_of(dense):
+        raise ValueError(f"state_pool rows hold {row_of(state_pool)} bytes, dense rows "
+                         f"{row_of(dense)}")
+    _covers(idx.shape[0], dense=dense)
+    return max(row_of(dense), 1)
+
+
 def sc_state_gather(state_pool, idx, dense, *, stream=None):
     """dense[i] = state_pool[idx[i]] (zeros for an index outside the pool)."""
-    row = state_pool[0].numel() * state_pool.element_size() if state_pool.shape[0] else \
-        dense[0].numel() * dense.element_size()
+    row = _copy_rows(state_pool, idx, dense)
     p, s = _index(idx, "idx")
     st = lib().sc_state_gather(_ptr(state_pool), state_pool.shape[0], row, p, s,
                                idx.shape[0], _ptr(dense), _stream(stream, dense))
@@ -408,7 +423,7 @@ def sc_state_gather(state_pool, idx, dense, *, stream=None):
 
 def sc_state_scatter(dense, idx, state_pool, *, stream=None):
     """state_pool[idx[i]] = dense[i] (indices outside the pool skipped)."""
-    row = dense[0].numel() * dense.element_size() if dense.shape[0] else 1
+    row = _copy_rows(state_pool, idx, dense)
     p, s = _index(idx, "idx")
     st = lib().sc_state_scatter(_ptr(dense), row, p, s, idx.shape[0], _ptr(state_pool),
                                 state_pool.shape[0], _stream(stream, dense))

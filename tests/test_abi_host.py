@@ -318,3 +318,18 @@ def test_binding_checks_dtypes_and_batch_coverage():
     with pytest.raises(ValueError, match="has_initial_state"):
         scs.sc_conv_prefill_varlen(x, torch.empty_like(x), w, None, pool, qsl, idx,
                                    torch.empty(2, dtype=torch.uint8, **m))
+
+
+def test_binding_checks_state_copy_rows():
+    """Gather and scatter copy whole slot rows: the pool and the dense buffer
+    must agree on the row size and the dense buffer must hold a row per index."""
+    import torch
+    m = dict(device="meta", dtype=torch.bfloat16)
+    pool = torch.empty(16, 64, 3, **m)
+    idx = torch.empty(4, dtype=torch.int32, device="meta")
+    with pytest.raises(ValueError, match="bytes"):
+        scs.sc_state_gather(pool, idx, torch.empty(4, 64, 2, **m))
+    with pytest.raises(ValueError, match="bytes"):
+        scs.sc_state_scatter(torch.empty(4, 64, 3, dtype=torch.float32, device="meta"), idx, pool)
+    with pytest.raises(ValueError, match="dense"):
+        scs.sc_state_gather(pool, idx, torch.empty(3, 64, 3, **m))
