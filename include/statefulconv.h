@@ -221,10 +221,22 @@ sc_status sc_conv_update_spec_varlen(const sc_conv_desc* desc, const void* x, vo
                                      const sc_conv_fuse* fuse, void* stream);
 
 /* Row copies between a slot pool and a dense buffer; each row is row_bytes.
+ * They are the state gather and write-back of "vllm.model_executor.models.zaya",
+ * ZayaCCA._mix_with_state, on their own: that method reads each request's
+ * history as the pool row its slot index names, masked to zeros when the
+ * request has no initial state, and afterwards writes the new history back to
+ * the same row; the GDN page ("vllm.model_executor.layers.mamba.ops.cpu.
+ * gdn_attention", _spec_forward) indexes its conv-state cache by slot in the
+ * same way. Byte copies, so bit-exact for any dtype and either layout.
  * gather: dense[i] = pool[idx[i*idx_stride]], or zeros when that index is
  *         outside [0, num_slots) (a padding row has no history).
- * scatter: pool[idx[i*idx_stride]] = dense[i]; out-of-range indices skipped.
- *   pool, dense, idx (device); n rows; row_bytes >= 1. */
+ * scatter: pool[idx[i*idx_stride]] = dense[i]; out-of-range indices skipped;
+ *          two equal in-range indices race (a documented precondition:
+ *          distinct indices, as sc_validate_metadata checks).
+ *   pool, dense, idx (device, caller-owned); n rows; row_bytes >= 1.
+ * Errors: NULL pointer with n > 0 -> SC_ERR_NULL_ARG; negative n or
+ * num_slots, row_bytes < 1 or idx_stride < 1 -> SC_ERR_INVALID_ARG;
+ * launch failure -> SC_ERR_HIP. n = 0: no-op. Asynchronous on `stream`. */
 sc_status sc_state_gather(const void* pool, int32_t num_slots, int64_t row_bytes,
                           const int32_t* idx, int64_t idx_stride, int32_t n,
                           void* dense, void* stream);
@@ -250,7 +262,10 @@ typedef struct {
  * state), then prefill rows with offsets prefill_qsl (rebased to 0).
  * With C = (nq+nkv)*hd raw channels [q | k] and n = t0+t1-2:
  *   dw   = depthwise conv (t0 taps, bias) of [history, raw], materialised in
- *          bf16 (fp32 fused multiply-add chain, bias first, taps in order)
+ *          bf16: an fp32 fused multiply-add chain (bias first, taps in order)
+ *          rounded to bf16, which is the exact value rounded once except
+ *          where the chain's own rounding moves it across a bf16 midpoint
+ *          (a few values in 10^7 on normally distributed data)
  *   yg   = grouped conv (nq+nkv groups of hd, t1 taps, bias) of dw, fp32 acc.
  *   out row = [yg_q + 0.5(q + k of the head's kv group) |
  *              yg_k + mean over the group's q heads of that residual |

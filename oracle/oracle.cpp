@@ -17,15 +17,18 @@
 //    per-sequence conv over [prior, x] in `_spec_forward`.
 //  * "vllm.models.qwen4_exp.nvidia.ple_layer", Qwen4ExpPLELayer: dilated
 //    conv (state length (kernel-1)*dilation, Conv1d with padding and
-//    dilation), prefill checkpoints ("the conv window ending at a checkpoint
-//    is a copy of its last inputs"; offsets are multiples of the grid).
+//    dilation), prefill checkpoints (the comment in the layer's constructor:
+//    the window that ends at a checkpoint holds the raw inputs just before it;
+//    offsets are multiples of the grid, `get_kv_cache_spec`).
 //
 // Arithmetic: every convolution output is accumulated in double, bias first,
 // then taps in order, and rounded once to the output type (round to nearest,
-// ties to even). The one exception is the CCA depthwise intermediate, which the
-// pages materialise in the model dtype before the grouped conv; its pre-rounding
-// value is taken in fp32 (fmaf chain, bias first, taps in order), the kernel's
-// precision, so that both sides round the same number.
+// ties to even). The CCA depthwise intermediate, which the layer's first
+// Conv1d materialises in the model dtype before the grouped conv, is the exact
+// value of bias + taps rounded once to that dtype (dw_mode 2, the default of
+// the Python front); dw_mode 1 (an fp32 fused multiply-add chain, rounded
+// afterwards) is kept as a diagnostic only, to count where such a chain would
+// round differently.
 //
 // Parity pins: every function here is pinned by the CPU tests (zero-state vs.
 // a library convolution, a dense Toeplitz formulation, chunked == one-shot
@@ -41,6 +44,7 @@
 #include <cmath>
 #include <cstdint>
 #include <algorithm>
+#include <atomic>
 #include <cstring>
 #include <thread>
 #include <vector>
@@ -77,6 +81,78 @@ uint16_t double_to_bf16(double v) {
   uint32_t u;
   std::memcpy(&u, &f, 4);
   return sign | (uint16_t)(u >> 16);
+}
+
+// Error-free sum of two doubles (Knuth's TwoSum, round to nearest): s + e
+// equals a + b exactly. Needs strict IEEE evaluation (no contraction).
+template <class T>
+T two_sum(T a, T b, T* e) {
+  const T s = a + b;
+  const T bb = s - a;
+  *e = (a - (s - bb)) + (b - bb);
+  return s;
+}
+
+// Round a binary128 value once to bfloat16 (nearest, ties to even). hi is the
+// nearest double and lo the (sign-exact) remainder; the nearest bf16 of v is
+// that of hi unless hi sits exactly on a bf16 midpoint, where lo decides.
+uint16_t quad_to_bf16(__float128 v) {
+  const double hi = (double)v;
+  const double lo = (double)(v - (__float128)hi);
+  const uint16_t r = double_to_bf16(hi);
+  if (lo == 0.0 || std::isinf(hi) || hi == 0.0) return r;
+  int e;
+  std::frexp(std::fabs(hi), &e);
+  const double half = std::ldexp(1.0, e - 9);          // half a bf16 spacing at hi
+  const double m = std::fabs(hi) / half;
+  if (m != std::floor(m) || std::fmod(m, 2.0) == 0.0) return r;   // not a midpoint
+  // midpoint: round away from hi in the direction of lo
+  const double below = (std::floor(m) - 1.0) * half, above = (std::floor(m) + 1.0) * half;
+  const double mag = ((lo > 0.0) == (hi > 0.0)) ? above : below;
+  return double_to_bf16(hi > 0.0 ? mag : -mag);
+}
+
+float quad_to_f32(__float128 v) {
+  const double hi = (double)v;
+  const double lo = (double)(v - (__float128)hi);
+  const float r = (float)hi;
+  if (lo == 0.0 || (double)r == hi) return r;      // no rounding decided by lo
+  // hi is a float midpoint only if it has exactly 25 significant bits
+  const double other = (double)std::nextafter(r, (hi > (double)r) ? INFINITY : -INFINITY);
+  if (hi - (double)r != other - hi) return r;         // not a midpoint
+  return ((lo > 0.0) == (other > (double)r)) ? (float)other : r;
+}
+
+// Exact value of bias + sum_a w[a] * x[a] (n <= 8 taps, products of io values),
+// rounded once to io dtype `dt` (for F64 the double sum itself). Each product
+// of two bf16 or fp32 values is exact in double; the running sum is certified
+// exact with TwoSum, and when a step loses bits the whole sum is redone in
+// binary128 with the same certificate. Returns false if even that is inexact
+// (terms spanning more than ~90 binades), which no pinned or random input does.
+bool exact_dw(int dt, double bias, const double* w, const double* x, int n, double* out) {
+  if (dt == F64) {
+    double s = bias;
+    for (int a = 0; a < n; ++a) s += w[a] * x[a];
+    *out = s;
+    return true;
+  }
+  bool exact = true;
+  double s = bias, e;
+  for (int a = 0; a < n && exact; ++a) {
+    s = two_sum(s, w[a] * x[a], &e);
+    exact = e == 0.0;
+  }
+  if (exact) {
+    *out = dt == BF16 ? bf16_to_double(double_to_bf16(s)) : (double)(float)s;
+    return true;
+  }
+  __float128 q = bias, qe;
+  for (int a = 0; a < n; ++a) {
+    q = two_sum(q, (__float128)w[a] * (__float128)x[a], &qe);
+    if (qe != 0) return false;
+  }
+  *out = dt == BF16 ? bf16_to_double(quad_to_bf16(q)) : (double)quad_to_f32(q);
+  return true;
 }
 
 double ld(const void* p, int dt, int64_t i) {
@@ -331,7 +407,8 @@ uint16_t oracle_double_to_bf16(double v) { return double_to_bf16(v); }
 // S = state_len >= H = (K-1)*d (0 means H). When S > H (a buffer sized for
 // speculative rollback) the non-speculative steps keep their window in the
 // first H columns and leave the rest alone, as the GDN page's wide-buffer path
-// does ("only the first width-1 columns hold the real conv state").
+// does (`_spec_aware_nonspec`: the live window is the leading width-1 entries
+// of each row).
 // absum (nullable, (T, C) doubles, by logical row) receives |b| + sum_k |w*x|
 // (+ |resid| + |outer|) per output.
 // row_mask (nullable, T bytes, by logical row): rows with mask 0 are not written.
@@ -366,20 +443,8 @@ int oracle_conv(int32_t C, int32_t K, int32_t d, int32_t act, int32_t io_dtype,
 }
 
 // Speculative multi-token update with a rolling state buffer (GDN page,
-// _spec_forward: "roll the buffer: drop the accepted history from the front,
-// append the new draft tokens, keep total length == state_len").
-// pool is (num_slots, C, S), S >= H = (K-1)*d. Request r owns rows
-// [r*q, (r+1)*q) and has `a = num_accepted[r]` accepted tokens from the
-// previous step, clamped to [1, min(q, S-H+1)] (the range in which the
-// page's slices are well formed). Then
-//   ext      = [pool[s][c][a-1 : a-1+H], x_r]     (the window ending at the last accepted input)
-//   outputs  = the depthwise definition over ext
-//   pool[s]  = [pool[s][c][a : a+S-q], x_r]      (length S; q <= S required)
-// A slot outside the pool is a padding row: zero window, no write.
-
-// Speculative multi-token update with a rolling state buffer (GDN page,
-// _spec_forward: "roll the buffer: drop the accepted history from the front,
-// append the new draft tokens, keep total length == state_len").
+// _spec_forward: after the step the row loses its accepted prefix at the front
+// and gains the new drafts at the back, so its length stays state_len).
 // pool is (num_slots, C, S), S >= H = (K-1)*d. Request r owns rows
 // [r*q, (r+1)*q) and has `a = num_accepted[r]` accepted tokens from the
 // previous step, clamped to [1, min(q, S-H+1)] (the range in which the
@@ -438,8 +503,9 @@ int oracle_conv_spec_varlen(int32_t C, int32_t K, int32_t d, int32_t S, int32_t 
 // n = t0 + t1 - 2 raw inputs per channel. Per request and channel, ext is the
 // raw input extended by the history (zeros without initial state).
 //   dw(c,u)  = b1_c + sum_{a<t0} w1[c,a] * ext[c][u-(t0-1)+a]
-//              (dw_mode 1: fp32 fmaf chain then rounded to io dtype;
-//               dw_mode 0: exact double, not rounded)
+//              (dw_mode 2: the exact value rounded once to the io dtype;
+//               dw_mode 1, diagnostic: an fp32 fmaf chain, bias first, then
+//               rounded to the io dtype; dw_mode 0: the double sum, not rounded)
 //   yg(o,t)  = b2_o + sum_{j<hd} sum_{b<t1} W2[o,j,b] * dw(g*hd+j, n+t-(t1-1)+b),
 //              g = o / hd  (grouped conv weight (C, hd, t1))
 //   qres[h]  = 0.5 * (q[h] + k[h / G]),  G = nq / nkv      (per head, per dim)
@@ -449,6 +515,10 @@ int oracle_conv_spec_varlen(int32_t C, int32_t K, int32_t d, int32_t S, int32_t 
 //              value (has state) or delayed_init (NULL = zeros).
 // State: conv_state[slot][c][j] = ext[c][len + j] (j < n);
 //        delayed_state[slot] = v_del[last row of the request].
+// dw_chain_diff (nullable; dw_mode 2, bf16): receives the number of depthwise
+// values that an fp32 fmaf chain (bias first, taps in order) would round to a
+// different bf16 value than the exact one (a diagnostic, not a result).
+// Returns -4 if a depthwise sum is not exact even in binary128.
 int oracle_cca(int32_t nq, int32_t nkv, int32_t hd, int32_t t0, int32_t t1,
                int32_t io_dtype, int32_t out_dtype, int32_t dw_mode,
                const void* qp, int64_t q_rs, const void* kp, int64_t k_rs,
@@ -460,9 +530,12 @@ int oracle_cca(int32_t nq, int32_t nkv, int32_t hd, int32_t t0, int32_t t1,
                int64_t dstride, int32_t num_prefills, const int32_t* qsl_p,
                const int32_t* prefill_slots, int64_t pstride,
                const uint8_t* prefill_h, const uint8_t* row_mask,
-               int32_t nthreads) {
+               int64_t* dw_chain_diff, int32_t nthreads) {
   if (nq <= 0 || nkv <= 0 || hd <= 0 || t0 <= 0 || t1 <= 0 || nq % nkv) return -2;
+  if (dw_mode < 0 || dw_mode > 2 || (dw_mode == 2 && t0 > 8)) return -2;
   if (!dtype_ok(io_dtype) || !dtype_ok(out_dtype)) return -3;
+  std::atomic<bool> inexact_any{false};
+  std::atomic<int64_t> chain_diff{0};
   const int C = (nq + nkv) * hd, n = t0 + t1 - 2, G = nq / nkv;
   const int qdim = nq * hd, vd = nkv * hd / 2, W = (nq + 2 * nkv) * hd;
   const int ngroups = nq + nkv;
@@ -478,6 +551,8 @@ int oracle_cca(int32_t nq, int32_t nkv, int32_t hd, int32_t t0, int32_t t1,
   // Conv part, one group (hd dw channels in, hd conv channels out) at a time.
   auto groups = [&](int g0, int g1) {
     std::vector<double> ext, dw;
+    bool inexact = false;
+    int64_t ndiff = 0;
     for (const Req& r : reqs) {
       if (r.len <= 0) continue;
       const bool valid = r.slot >= 0 && r.slot < num_slots;
@@ -496,7 +571,22 @@ int oracle_cca(int32_t nq, int32_t nkv, int32_t hd, int32_t t0, int32_t t1,
           for (int64_t t = 0; t < r.len; ++t) e[n + t] = raw(r.start + t, c);
           for (int64_t u = t0 - 1; u < E; ++u) {
             double v;
-            if (dw_mode == 1) {
+            if (dw_mode == 2) {
+              // the Conv1d output materialised in the io dtype: exact value,
+              // one rounding
+              double wa[8], xa[8];
+              for (int a = 0; a < t0; ++a) {
+                wa[a] = ld(w_dw, io_dtype, (int64_t)c * t0 + a);
+                xa[a] = e[u - (t0 - 1) + a];
+              }
+              if (!exact_dw(io_dtype, ld(b_dw, io_dtype, c), wa, xa, t0, &v)) inexact = true;
+              if (dw_chain_diff && io_dtype == BF16) {
+                // diagnostic: would an fp32 fmaf chain (bias first) round elsewhere?
+                float acc = (float)ld(b_dw, io_dtype, c);
+                for (int a = 0; a < t0; ++a) acc = std::fmaf((float)wa[a], (float)xa[a], acc);
+                if (bf16_to_double(double_to_bf16(acc)) != v) ++ndiff;
+              }
+            } else if (dw_mode == 1) {
               float acc = (float)ld(b_dw, io_dtype, c);
               for (int a = 0; a < t0; ++a)
                 acc = std::fmaf((float)ld(w_dw, io_dtype, (int64_t)c * t0 + a),
@@ -553,8 +643,12 @@ int oracle_cca(int32_t nq, int32_t nkv, int32_t hd, int32_t t0, int32_t t1,
                  ext[(size_t)j * E + r.len + jj]);
       }
     }
+    if (inexact) inexact_any = true;
+    if (dw_chain_diff && ndiff) chain_diff += ndiff;
   };
   parallel_for(ngroups, nthreads, groups);
+  if (inexact_any) return -4;   // a depthwise sum that binary128 cannot hold exactly
+  if (dw_chain_diff) *dw_chain_diff = chain_diff;
 
   // Value part: current value copied, delayed value shifted by one token.
   for (const Req& r : reqs) {

@@ -430,6 +430,33 @@ def sc_state_scatter(dense, idx, state_pool, *, stream=None):
     _check("sc_state_scatter", st)
 
 
+def _cca_shapes(q, k, v_cur, v_del, out, w_dw, b_dw, w_gr, b_gr, delayed_init, conv_state,
+                delayed_state, nq, nkv, hd, t0, t1):
+    """The CCA kernels address every tensor from the head counts and the token
+    count (q's rows): each tensor must hold what they reach."""
+    if nq < 1 or nkv < 1 or hd < 2 or nq % nkv or hd % 2 or t0 < 1 or t1 < 1:
+        raise ValueError("expected num_q_heads a multiple of num_kv_heads, an even "
+                         "head_dim and kernel widths >= 1")
+    C, vd, W, n = (nq + nkv) * hd, nkv * hd // 2, (nq + 2 * nkv) * hd, t0 + t1 - 2
+    T = q.shape[0] if q.dim() == 2 else -1
+    for name, t, cols in (("q", q, nq * hd), ("k", k, nkv * hd), ("v_cur", v_cur, vd),
+                          ("v_del", v_del, vd), ("out", out, W)):
+        if t.dim() != 2 or t.shape[1] != cols or t.shape[0] != T:
+            raise ValueError(f"{name}: expected ({T}, {cols}), got {tuple(t.shape)}")
+    for name, t, numel in (("w_dw", w_dw, C * t0), ("b_dw", b_dw, C),
+                           ("w_gr", w_gr, C * hd * t1), ("b_gr", b_gr, C),
+                           ("delayed_init", delayed_init, vd)):
+        if t is not None and t.numel() != numel:
+            raise ValueError(f"{name}: expected {numel} elements, got {t.numel()}")
+    slots = conv_state.shape[0] if conv_state.dim() else 0
+    if conv_state.dim() != 3 or tuple(conv_state.shape[1:]) != (C, n):
+        raise ValueError(f"conv_state: expected (num_slots, {C}, {n}), got "
+                         f"{tuple(conv_state.shape)}")
+    if delayed_state.dim() != 2 or tuple(delayed_state.shape) != (slots, vd):
+        raise ValueError(f"delayed_state: expected ({slots}, {vd}), got "
+                         f"{tuple(delayed_state.shape)}")
+
+
 def sc_cca_qk_conv(q, k, v_cur, v_del, out, w_dw, b_dw, w_gr, b_gr, delayed_init,
                    conv_state, delayed_state, decode_slots, prefill_qsl, prefill_slots,
                    prefill_has_initial_state, *, num_q_heads: int, num_kv_heads: int,
@@ -438,6 +465,8 @@ def sc_cca_qk_conv(q, k, v_cur, v_del, out, w_dw, b_dw, w_gr, b_gr, delayed_init
 
     Rows: len(decode_slots) one-token decodes, then prefills (prefill_qsl
     rebased to 0). Pass decode_slots / prefill tensors as None when absent."""
+    _cca_shapes(q, k, v_cur, v_del, out, w_dw, b_dw, w_gr, b_gr, delayed_init, conv_state,
+                delayed_state, num_q_heads, num_kv_heads, head_dim, t0, t1)
     nd = 0 if decode_slots is None else decode_slots.shape[0]
     npf = 0 if prefill_qsl is None else prefill_qsl.shape[0] - 1
     dp, ds = _index(decode_slots, "decode_slots") if nd else (None, 1)

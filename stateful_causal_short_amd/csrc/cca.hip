@@ -354,7 +354,7 @@ __device__ __forceinline__ constexpr int cca_hslot(int c) { return ((c >> 2) & 1
 // windows and larger groups need more than 128 registers and run one
 // workgroup per CU.
 __host__ __device__ constexpr int cca_waves_per_simd(int t0, int gmax) {
-  return (t0 <= 2 && gmax <= 4) ? SC_CCA_MIN_WAVES : 2;
+  return (t0 <= 2 && gmax <= 4) ? 4 : 2;
 }
 
 // Row info of token row t: position in its request (-1: no row) and source
@@ -420,7 +420,7 @@ __device__ __forceinline__ void cca_persist_body(const CcaArgs& a, CcaSmem<T0>& 
   constexpr bool isk = ISK;
   // tiles of loads in flight ahead of the one computed: the k head also
   // holds the bundle's q rows per tile, so it keeps one tile in flight
-  constexpr int AHEAD = ISK ? 1 : SC_CCA_AHEAD;
+  constexpr int AHEAD = 1;
 
   const int NG = a.nq + a.nkv, G = a.nq / a.nkv;
   const float inv_g = 1.0f / (float)G;           // exact when G is a power of two
@@ -765,7 +765,7 @@ hipError_t launch_cca(const CcaArgs& a, hipStream_t stream) {
   const int64_t max_rs = std::max(std::max(a.q_rs, a.k_rs), std::max(std::max(a.vc_rs, a.vd_rs), a.out_rs));
   const bool fits32 = a.num_tokens * max_rs * 2 <= 0x7FFFFFFFLL;
   const bool mfma = a.hd == 128 && a.t1 == 2 && a.t0 >= 1 && a.t0 <= 4 && (al & 15) == 0 &&
-                    strides16 && vd % 8 == 0 && a.nq / a.nkv <= 8 && fits32 && !SC_CCA_GENERIC;
+                    strides16 && vd % 8 == 0 && a.nq / a.nkv <= 8 && fits32;
   if (mfma) {
     // persistent grid: a multiple of the head-group count, as many workgroups
     // as fit on the device at once, never more than there are tiles to share

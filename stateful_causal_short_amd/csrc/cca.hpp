@@ -6,16 +6,6 @@
 
 namespace sc {
 
-#ifndef SC_CCA_AHEAD
-#define SC_CCA_AHEAD 1       // tiles of raw rows in flight ahead of the one being computed (1 or 2)
-#endif
-#ifndef SC_CCA_MIN_WAVES
-#define SC_CCA_MIN_WAVES 4   // waves per SIMD of the main kernel for depthwise width <= 2 (2 or 4)
-#endif
-#ifndef SC_CCA_GENERIC
-#define SC_CCA_GENERIC 0     // 1 = always use the scalar CCA kernel
-#endif
-
 // CCA launch arguments.
 struct CcaArgs {
   const void* q;

@@ -30,11 +30,7 @@ __device__ __forceinline__ u32x4 ld16_stream(const void* p) {
 }
 // Streaming store: the output is not re-read by this kernel.
 __device__ __forceinline__ void st16_stream(void* p, u32x4 v) {
-#if defined(SC_PLAIN_STORES) && SC_PLAIN_STORES
-  *reinterpret_cast<u32x4*>(p) = v;
-#else
   __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
-#endif
 }
 
 // bf16 storage: 8 channels per 16-byte vector; element 2i is the low half of

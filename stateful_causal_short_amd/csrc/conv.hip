@@ -112,10 +112,6 @@ __device__ __forceinline__ void write_state_rows(const ConvArgs& a, int32_t slot
 // ---------------------------------------------------------------------------
 template <class E, int K, int D, int U, bool SILU, int QC, bool SD>
 __global__ __launch_bounds__(kBlock) void conv_fast(ConvArgs a) {
-#if SC_LDS_PAD > 0
-  __shared__ uint8_t occupancy_pad[SC_LDS_PAD];
-  if (a.C < 0) occupancy_pad[threadIdx.x] = 0;
-#endif
   constexpr int H = (K - 1) * D;
   constexpr int VEC = E::VEC;
   using S = typename E::S;
@@ -185,7 +181,7 @@ __global__ __launch_bounds__(kBlock) void conv_fast(ConvArgs a) {
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int t = min(tb + u, w.t1 - 1);
-        xr[u] = SC_NT_LOADS ? ld16_stream(xb + (int64_t)t * xrs) : ld16(xb + (int64_t)t * xrs);
+        xr[u] = ld16_stream(xb + (int64_t)t * xrs);
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) E::unpack(xr[u], win[H + u]);
@@ -227,10 +223,6 @@ __global__ __launch_bounds__(kBlock) void conv_fast(ConvArgs a) {
 
 template <int K, int D, int U, bool SILU, bool UPDATE, bool FUSE, bool SD>
 __global__ __launch_bounds__(kBlock) void conv_pairs(ConvArgs a) {
-#if SC_PAIRS_LDS_RESERVE > 0
-  __shared__ uint8_t residency_cap[SC_PAIRS_LDS_RESERVE];
-  if (a.C < 0) residency_cap[threadIdx.x] = 0;   // never taken: keeps the reservation
-#endif
   using E = BF16;
   using S = E::S;
   constexpr int H = (K - 1) * D;
@@ -302,7 +294,7 @@ __global__ __launch_bounds__(kBlock) void conv_pairs(ConvArgs a) {
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     const int t = UPDATE ? u : min(t0 + u, t1 - 1);
-    raw[H + u] = SC_NT_LOADS ? ld16_stream(xrow(t)) : ld16(xrow(t));
+    raw[H + u] = ld16_stream(xrow(t));
   }
   // the slot is needed by the request's first chunk only (history and write-back)
   int32_t slot = -1;
@@ -474,8 +466,7 @@ __global__ __launch_bounds__(kBlock) void conv_update_pairs(ConvArgs a) {
 #pragma unroll
     for (int u = 0; u < Q; ++u)
       xr[rr][u] = (r < a.batch && lane_ok)
-                      ? (SC_NT_LOADS ? ld16_stream((const S*)a.x + prow(r, u) * a.x_rs + c0)
-                                     : ld16((const S*)a.x + prow(r, u) * a.x_rs + c0))
+                      ? ld16_stream((const S*)a.x + prow(r, u) * a.x_rs + c0)
                       : u32x4{0, 0, 0, 0};
   }
   // fused residuals, issued with the token rows
@@ -518,7 +509,7 @@ __global__ __launch_bounds__(kBlock) void conv_update_pairs(ConvArgs a) {
       for (int k = 0; k < H; ++k) {
         const int vi = tid + k * kBlock;
         st[rr][k] = (hflag[rr] && vi < nvec)
-                        ? (SC_NT_LOADS ? ld16_stream(sp + vi * VEC) : ld16(sp + vi * VEC))
+                        ? ld16_stream(sp + vi * VEC)
                         : u32x4{0, 0, 0, 0};
       }
     }
@@ -724,7 +715,7 @@ bool pairs_shape(int K, int D) {
 
 template <class E, int K, int D, bool SILU, bool SD>
 hipError_t launch_kd_l(const ConvArgs& a, int qc, dim3 grid, hipStream_t s) {
-  constexpr int U = ((K - 1) * D <= 4) ? SC_UNROLL_SMALL_H : SC_UNROLL_LARGE_H;
+  constexpr int U = kUnroll;
   switch (qc) {
     case 1: hipLaunchKernelGGL((conv_fast<E, K, D, U, SILU, 1, SD>), grid, dim3(kBlock), 0, s, a); break;
     case 2: hipLaunchKernelGGL((conv_fast<E, K, D, U, SILU, 2, SD>), grid, dim3(kBlock), 0, s, a); break;
@@ -751,11 +742,11 @@ hipError_t launch_kd(const ConvArgs& a, int qc, dim3 grid, hipStream_t s) {
 constexpr int64_t kSmallLaunch = int64_t(1) << 26;
 constexpr int64_t kSmallLaunchSD = int64_t(1) << 25;
 constexpr int pairs_chunk(int H, bool small) {
-  return H <= 4 ? (small ? 8 : SC_PAIRS_CHUNK_SMALL) : (H <= 8 ? 8 : 16);
+  return H <= 4 ? (small ? 8 : kPairsChunkLarge) : (H <= 8 ? 8 : 16);
 }
 // requests per update workgroup
 constexpr int update_reqs(int H, int Q, bool sd) {
-  if (H <= 4) return Q == 1 ? (sd ? SC_UPDATE_REQS_SD : SC_UPDATE_REQS) : SC_UPDATE_REQS_MULTI;
+  if (H <= 4) return Q == 1 ? (sd ? kUpdateReqsSD : kUpdateReqsDS) : kUpdateReqsMulti;
   return Q == 1 ? 2 : 1;
 }
 
@@ -805,14 +796,18 @@ template <int K, int D, bool SILU, bool FUSE, bool SD>
 hipError_t launch_pairs_l(const ConvArgs& a, int qc, dim3 grid, hipStream_t s) {
   constexpr int H = (K - 1) * D;
   if (qc == 0 && a.chunk == pairs_chunk(H, true) && pairs_chunk(H, true) != pairs_chunk(H, false)) {
-    hipLaunchKernelGGL((conv_pairs<K, D, pairs_chunk(H, true), SILU, false, FUSE, SD>), grid, dim3(kBlock), 0, s, a);
+    hipLaunchKernelGGL((conv_pairs<K, D, pairs_chunk(H, true), SILU, false, FUSE, SD>), grid, dim3(kBlock),
+                       kPairsResidencyLds, s, a);
     return hipGetLastError();
   }
   switch (qc) {
     case 1: return launch_update1<K, D, SILU, FUSE, SD>(a, grid, s);
     case 2: hipLaunchKernelGGL((conv_update_pairs<K, D, 2, update_reqs(H, 2, SD), SILU, FUSE, SD>), grid, dim3(kBlock), 0, s, a); break;
     case 4: hipLaunchKernelGGL((conv_update_pairs<K, D, 4, update_reqs(H, 4, SD), SILU, FUSE, SD>), grid, dim3(kBlock), 0, s, a); break;
-    default: hipLaunchKernelGGL((conv_pairs<K, D, pairs_chunk(H, false), SILU, false, FUSE, SD>), grid, dim3(kBlock), 0, s, a); break;
+    default:
+      hipLaunchKernelGGL((conv_pairs<K, D, pairs_chunk(H, false), SILU, false, FUSE, SD>), grid,
+                         dim3(kBlock), kPairsResidencyLds, s, a);
+      break;
   }
   return hipGetLastError();
 }
@@ -835,8 +830,7 @@ template <class E, bool SILU>
 hipError_t launch_typed(const ConvArgs& a, int K, int D, bool fast, int qc, dim3 grid,
                         hipStream_t s, bool fuse) {
   if ((a.chunk == pairs_chunk((K - 1) * D, true) || a.chunk == pairs_chunk((K - 1) * D, false)) &&
-      fast && E::VEC == 8 && pairs_shape(K, D) &&
-      !SC_NO_PAIRS)
+      fast && E::VEC == 8 && pairs_shape(K, D))
     return fuse ? launch_pairs<SILU, true>(a, K, D, qc, grid, s)
                 : launch_pairs<SILU, false>(a, K, D, qc, grid, s);
   if (fast && !fuse) {
@@ -873,7 +867,7 @@ hipError_t launch_conv(ConvArgs a, int dtype, int K, int D, bool silu_act, bool 
   // (an SD pool keeps a lane's entries as vectors at any S; a DS one only at S == H)
   const bool rows_ok = a.S == H || a.sd;
   const bool pairs_ok = rows_ok && aligned16 && (a.C % vec == 0) && dtype == 1 &&
-                        pairs_shape(K, D) && !SC_NO_PAIRS &&
+                        pairs_shape(K, D) &&
                         (!a.outer || (a.outer_rs * 2) % 16 == 0);
   const bool fast = rows_ok && aligned16 && (a.C % vec == 0) && fast_shape(K, D) &&
                     (!fuse || pairs_ok);

@@ -17,11 +17,7 @@ namespace sc {
 // so consecutive chunks of the same channels (whose halos overlap) share an L2.
 __device__ __forceinline__ int logical_block(int n_logical, int per_xcd) {
   const int b = (int)blockIdx.x;
-#if SC_NO_XCD_REMAP
-  const int lb = b;
-#else
   const int lb = (b % kXcds) * per_xcd + b / kXcds;
-#endif
   return lb < n_logical ? lb : -1;
 }
 

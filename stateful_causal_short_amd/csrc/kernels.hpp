@@ -7,47 +7,21 @@
 
 namespace sc {
 
-#ifndef SC_PREFILL_CHUNK
-#define SC_PREFILL_CHUNK 16
-#endif
-#ifndef SC_UNROLL_SMALL_H
-#define SC_UNROLL_SMALL_H 16
-#endif
-#ifndef SC_UNROLL_LARGE_H
-#define SC_UNROLL_LARGE_H 16
-#endif
-#ifndef SC_NO_XCD_REMAP
-#define SC_NO_XCD_REMAP 0
-#endif
-#ifndef SC_NT_LOADS
-#define SC_NT_LOADS 1   // streaming (non-temporal) loads of token rows read once
-#endif
-#ifndef SC_LDS_PAD
-#define SC_LDS_PAD 0
-#endif
-#ifndef SC_PAIRS_LDS_RESERVE
-// LDS each one-pass prefill workgroup reserves only to cap residency (the
-// kernel itself uses none): a gfx950 CU has 160 KiB, so 48 KiB admits three
-// 4-wave workgroups per CU. Three measured faster than the five the register
-// count allows (and than two or four): fewer streams contend for HBM.
-#define SC_PAIRS_LDS_RESERVE 49152
-#endif
-#ifndef SC_NO_PAIRS
-#define SC_NO_PAIRS 0
-#endif
-#ifndef SC_PAIRS_CHUNK_SMALL
-#define SC_PAIRS_CHUNK_SMALL 12
-#endif
-#ifndef SC_UPDATE_REQS
-#define SC_UPDATE_REQS 4
-#endif
-#ifndef SC_UPDATE_REQS_SD
-#define SC_UPDATE_REQS_SD 8   // requests per q = 1 update workgroup on an SD pool (H <= 4)
-#endif
-#ifndef SC_UPDATE_REQS_MULTI
-#define SC_UPDATE_REQS_MULTI 1   // requests per update workgroup for q = 2, 4 (H <= 4)
-#endif
-constexpr int kChunk = SC_PREFILL_CHUNK;   // tokens per prefill chunk (>= H for the fast kernels)
+// Launch constants of the depthwise kernels (measured choices, see the
+// launchers in conv.hip):
+constexpr int kChunk = 16;              // tokens per chunk of the fp32 / generic prefill
+constexpr int kUnroll = 16;             // tokens per register-window step of conv_fast
+constexpr int kPairsChunkLarge = 12;    // bf16 one-pass prefill chunk on large launches (H <= 4)
+constexpr int kUpdateReqsDS = 4;        // requests per one-token update workgroup, DS pool
+constexpr int kUpdateReqsSD = 8;        // the same on an SD pool
+constexpr int kUpdateReqsMulti = 1;     // requests per workgroup for q = 2, 4 (H <= 4)
+// LDS each bf16 one-pass prefill workgroup reserves at launch (dynamic
+// shared memory the kernel never touches): a gfx950 CU has 160 KiB, so
+// 48 KiB admits three 4-wave workgroups per CU, where the 91 registers alone
+// would admit five. LDS and registers are the only per-launch residency
+// controls the hardware has; three measured faster than two, four or five
+// (fewer row streams contend less for HBM).
+constexpr unsigned kPairsResidencyLds = 49152;
 
 // Depthwise conv launch arguments (by value into the kernel).
 struct ConvArgs {

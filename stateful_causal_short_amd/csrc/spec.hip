@@ -12,9 +12,9 @@
 // S - q, followed by the q new tokens. With a draft count per request (the GDN
 // page's loop over spec_query_start_loc) request r owns rows [qsl[r], qsl[r+1])
 // and one with no drafts, or more than S, is skipped whole. A plain
-// (non-speculative) update on such a buffer uses the first H entries as the window and leaves the rest as they
-// were ("only the first width-1 columns hold the real conv state", GDN page,
-// _spec_aware_nonspec).
+// (non-speculative) update on such a buffer uses the first H entries as the
+// window and leaves the rest as they were (GDN page, _spec_aware_nonspec: the
+// live window is the leading width-1 entries of each row).
 //
 // Layout: pool (num_slots, C, S). A workgroup takes one request and 256
 // vectors of channels; their state rows form one contiguous region of 256 * S

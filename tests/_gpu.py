@@ -113,25 +113,37 @@ def ulp_bf16(ref: np.ndarray) -> np.ndarray:
 
 
 def check_close(gpu: np.ndarray, ref64: np.ndarray, absum: np.ndarray, dtype: str,
-                floor_rel: float, *, what: str = "out", mask=None):
+                floor_rel: float, *, what: str = "out", mask=None, slab_rows: int = 2048):
     """Output tolerance: |gpu - ref| <= 2 bf16 ulp(ref) (bf16) or 1e-5 |ref|
     (fp32), or <= floor_rel * (sum of |terms|) — the fp32 accumulation bound,
-    which only matters where the sum cancels. Returns the share of elements
-    that passed through the floor alone."""
+    which only matters where the sum cancels. Every element is checked, in
+    slabs of rows so that the temporaries stay small at full size. Returns the
+    share of elements that passed through the floor alone."""
     if mask is not None:
         gpu, ref64, absum = gpu[mask], ref64[mask], absum[mask]
-    g = as_f64(gpu, dtype)
-    diff = np.abs(g - ref64)
-    tol = 2.0 * ulp_bf16(ref64) if dtype == "bf16" else 1e-5 * np.abs(ref64)
-    floor = floor_rel * absum
-    ok = (diff <= tol) | (diff <= floor)
-    if not ok.all():
-        bad = np.argwhere(~ok)
-        i = tuple(bad[0])
+    n_bad, first, n_floor = 0, None, 0
+    rows = gpu.shape[0] if gpu.ndim else 1
+    for r0 in range(0, max(rows, 1), slab_rows):
+        sl = slice(r0, r0 + slab_rows)
+        g = as_f64(gpu[sl], dtype)
+        ref = ref64[sl]
+        diff = np.abs(g - ref)
+        tol = 2.0 * ulp_bf16(ref) if dtype == "bf16" else 1e-5 * np.abs(ref)
+        floor = floor_rel * absum[sl]
+        ok = (diff <= tol) | (diff <= floor)
+        if not ok.all():
+            bad = np.argwhere(~ok)
+            n_bad += len(bad)
+            if first is None:
+                i = tuple(bad[0])
+                first = (tuple([i[0] + r0, *i[1:]]), g[i], ref[i], tol[i], floor[i])
+        n_floor += int(((diff > tol) & (diff <= floor)).sum())
+    if n_bad:
+        i, gv, rv, tv, fv = first
         raise AssertionError(
-            f"{what}: {len(bad)} of {ok.size} outside tolerance; first at {i}: "
-            f"gpu={g[i]!r} ref={ref64[i]!r} tol={tol[i]!r} floor={floor[i]!r}")
-    return float(((diff > tol) & (diff <= floor)).sum()) / max(1, ok.size)
+            f"{what}: {n_bad} of {gpu.size} outside tolerance; first at {i}: "
+            f"gpu={gv!r} ref={rv!r} tol={tv!r} floor={fv!r}")
+    return float(n_floor) / max(1, gpu.size)
 
 
 def run_cca_case(case, *, conv_state=None, delayed_state=None, fused=False,

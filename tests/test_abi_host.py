@@ -333,3 +333,45 @@ def test_binding_checks_state_copy_rows():
         scs.sc_state_scatter(torch.empty(4, 64, 3, dtype=torch.float32, device="meta"), idx, pool)
     with pytest.raises(ValueError, match="dense"):
         scs.sc_state_gather(pool, idx, torch.empty(3, 64, 3, **m))
+
+
+def test_binding_checks_cca_shapes():
+    """The CCA kernels address every tensor from the head counts and q's row
+    count: a tensor of the wrong shape is refused before any device address is
+    taken (meta tensors, no storage)."""
+    import torch
+    nq, nkv, hd, t0, t1, T, S = 4, 2, 16, 2, 2, 10, 6
+    C, vd, W, n = (nq + nkv) * hd, nkv * hd // 2, (nq + 2 * nkv) * hd, t0 + t1 - 2
+    m = dict(device="meta", dtype=torch.bfloat16)
+    good = dict(q=torch.empty(T, nq * hd, **m), k=torch.empty(T, nkv * hd, **m),
+                v_cur=torch.empty(T, vd, **m), v_del=torch.empty(T, vd, **m),
+                out=torch.empty(T, W, **m), w_dw=torch.empty(C, t0, **m),
+                b_dw=torch.empty(C, **m), w_gr=torch.empty(C, hd, t1, **m),
+                b_gr=torch.empty(C, **m), delayed_init=torch.empty(vd, **m),
+                conv_state=torch.empty(S, C, n, **m), delayed_state=torch.empty(S, vd, **m))
+    bad = [("q", torch.empty(T, nq * hd + 8, **m)), ("k", torch.empty(T - 1, nkv * hd, **m)),
+           ("v_cur", torch.empty(T, vd - 8, **m)), ("v_del", torch.empty(T + 1, vd, **m)),
+           ("out", torch.empty(T, W - 8, **m)), ("out", torch.empty(T - 1, W, **m)),
+           ("w_dw", torch.empty(C, t0 + 1, **m)), ("b_dw", torch.empty(C - 1, **m)),
+           ("w_gr", torch.empty(C, hd, t1 + 1, **m)), ("b_gr", torch.empty(C + 8, **m)),
+           ("delayed_init", torch.empty(vd + 1, **m)),
+           ("conv_state", torch.empty(S, C, n + 1, **m)),
+           ("conv_state", torch.empty(S, C - 16, n, **m)),
+           ("delayed_state", torch.empty(S - 1, vd, **m)),
+           ("delayed_state", torch.empty(S, vd * 2, **m))]
+    idx = torch.empty(2, dtype=torch.int32, device="meta")
+    for name, t in bad:
+        a = dict(good)
+        a[name] = t
+        with pytest.raises(ValueError, match=name):
+            scs.sc_cca_qk_conv(a["q"], a["k"], a["v_cur"], a["v_del"], a["out"], a["w_dw"],
+                               a["b_dw"], a["w_gr"], a["b_gr"], a["delayed_init"],
+                               a["conv_state"], a["delayed_state"], idx, None, None, None,
+                               num_q_heads=nq, num_kv_heads=nkv, head_dim=hd, t0=t0, t1=t1)
+    with pytest.raises(ValueError, match="head"):
+        scs.sc_cca_qk_conv(*good.values(), idx, None, None, None, num_q_heads=3,
+                           num_kv_heads=2, head_dim=hd, t0=t0, t1=t1)
+    # the good shapes pass the shape check and stop at the first device address
+    with pytest.raises(ValueError, match="on the GPU"):
+        scs.sc_cca_qk_conv(*good.values(), idx, None, None, None, num_q_heads=nq,
+                           num_kv_heads=nkv, head_dim=hd, t0=t0, t1=t1)

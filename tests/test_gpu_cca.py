@@ -3,9 +3,14 @@
 Bar: conv and delayed states bit-exact; value half of the output (v_cur copy
 and delayed shift) bit-exact; q/k outputs within 2 bf16 ulp of the oracle's
 float64 result, or within the fp32 accumulation bound n * 2^-24 of the sum of
-|terms| (n = bias + hd*t1 products + residual terms). Both sides take the
-depthwise intermediate's bf16 rounding from the same fp32 fused multiply-add
-chain (bias first, taps in order), so that decision is identical."""
+|terms| (n = bias + hd*t1 products + residual terms). Every output row is
+checked. The oracle takes the depthwise intermediate as the layer's first
+Conv1d materialises it: the exact value rounded once to bf16. The kernel
+rounds an fp32 fused multiply-add chain (bias first, taps in order); the
+oracle counts, as a diagnostic, the depthwise values where such a chain rounds
+to a different bf16 value, and each test prints that count. Where it does, the
+grouped stage moves the output by at most |W2| times one bf16 spacing of the
+depthwise value, inside the output tolerance."""
 from dataclasses import replace
 
 import numpy as np
@@ -18,47 +23,29 @@ from tests._gpu import cca_floor_rel, check_close, run_cca_case
 pytestmark = pytest.mark.gpu
 
 
-def parity(case, *, row_mask=None, **kw):
+def parity(case, **kw):
     print(f"[gpu] cca {case.name} T={case.T} nq={case.nq} nkv={case.nkv} hd={case.hd} "
           f"t0={case.t0} t1={case.t1} kw={kw}", flush=True)
     out, cs, ds = run_cca_case(case, **kw)
     ocase = case
     if kw.get("no_delayed_init"):
         ocase = replace(case, delayed_init=np.zeros_like(case.delayed_init))
-    ref, _, _, absum = oracle.cca(ocase, out_dtype="f64", dw_mode=1, absum=True,
-                                  row_mask=row_mask)
-    _, rcs, rds, _ = oracle.cca(ocase, dw_mode=1, row_mask=np.zeros(case.T, np.uint8))
+    nd = []
+    ref, rcs, rds, absum = oracle.cca(ocase, out_dtype="f64", absum=True, chain_diff=nd)
     np.testing.assert_array_equal(cs, rcs, err_msg="conv state not bit-exact")
     np.testing.assert_array_equal(ds, rds, err_msg="delayed state not bit-exact")
     C = case.C
-    m = None if row_mask is None else row_mask.astype(bool)
     # value half: exact copies
-    ref_v = ref[:, C:] if m is None else ref[m][:, C:]
-    got_v = out[:, C:] if m is None else out[m][:, C:]
-    np.testing.assert_array_equal(synthetic.bf16_to_f32(got_v).astype(np.float64), ref_v,
-                                  err_msg="value half not bit-exact")
+    np.testing.assert_array_equal(synthetic.bf16_to_f32(out[:, C:]).astype(np.float64),
+                                  ref[:, C:], err_msg="value half not bit-exact")
     frac = check_close(out[:, :C], ref[:, :C], absum[:, :C], "bf16", cca_floor_rel(case),
-                       what="q/k", mask=m)
-    print(f"[gpu] cca {case.name}: ok (floor-only share {frac:.2e})", flush=True)
-
-
-def sample_rows(case, n_random=384, seed=1):
-    m = np.zeros(case.T, np.uint8)
-    m[:min(case.T, 80)] = 1                              # decodes and first tile
-    starts = case.num_decodes + case.qsl_p[:-1]
-    for s, L in zip(starts, np.diff(case.qsl_p)):
-        m[s:s + min(int(L), 3)] = 1                      # history rows
-        m[max(s, s + L - 2):s + L] = 1
-    for e in range(64, case.T, 64):
-        m[e - 1:e + 1] = 1                               # tile edges
-    rng = np.random.default_rng(seed)
-    m[rng.integers(0, case.T, n_random)] = 1
-    return m
+                       what="q/k")
+    print(f"[gpu] cca {case.name}: ok (floor-only share {frac:.2e}; depthwise values an "
+          f"fp32 chain rounds elsewhere: {nd[0]} of {case.T * case.C})", flush=True)
 
 
 def test_cca_mixed_32k_full():
-    case = synthetic.cca_mixed_32k()
-    parity(case, row_mask=sample_rows(case))
+    parity(synthetic.cca_mixed_32k())
 
 
 def test_cca_small_tile_edges():
