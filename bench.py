@@ -6,21 +6,26 @@
 One step = one pass of the hot path over one batch already resident in HBM.
 The default workload is the varlen prefill batch (8 sequences, lengths
 U{1..2048}, 8192 channels, width 4, bf16, bias + SiLU, 64-slot state pool):
-state gather, conv, bias, SiLU and state write-back in one kernel. Its JSON
-line also carries a secondary "decode" object: the 512-request one-token
-decode batch timed the same way (the metric names the decode conv too). Other
-workloads (decode, multi-token update, dilated mixed batch with checkpoints,
-CCA) are selectable for measurement tables.
+state gather, conv, bias, SiLU and state write-back in one kernel; `value` is
+its tokens/s. The same JSON line carries secondary objects for the method's
+other workloads, each timed the same way in the same process: "decode" (512
+requests x 1 token), "update_q4" (128 requests x 4 tokens), "ple_mixed"
+(dilated PLE batch: 256 decodes + 16 prefills with checkpoints; each kernel
+and their sum) and "cca" (the 32k-token CCA q/k conv, main kernel + state
+update), plus "copy_ceiling" (the practical HBM ceiling of a plain copy) and,
+for every timed batch, "parity": one step on pristine inputs checked against
+the oracle outside the timed region (state bit-exact, every output within
+tolerance, and how many passed only through the accumulation floor).
 
 Timing: W untimed eager steps, then K steps timed twice, bracketed by device
 synchronisation and HIP events on the launch stream: as eager back-to-back
 launches and as one replay of the K steps captured in a HIP graph (no host
 launch cost inside the timed region); the faster is reported, both are kept.
 For a batch with two kernels, each kernel's average comes from K launches of
-that kernel alone, timed the same way. Several
-identical buffer sets (x, out, state pool) are rotated so that each step's
-inputs were last touched >= 1 GiB of traffic earlier and come from HBM, not the
-256 MB Infinity Cache. Prints one JSON line on stdout; progress on stderr.
+that kernel alone, timed the same way. Identical buffer sets (x, out, state
+pool) are rotated so that each step's inputs were last touched >= 1 GiB of
+traffic earlier and come from HBM, not the 256 MB Infinity Cache. Prints one
+JSON line on stdout; progress on stderr.
 """
 from __future__ import annotations
 
@@ -41,6 +46,31 @@ ROTATE_BYTES = 1 << 30      # rotate buffer sets until >= 1 GiB is cycled
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def rotation_sets(touched_bytes, alloc_bytes, cap_bytes=24 << 30):
+    """Buffer sets to rotate so that a step's data was last touched >= 1 GiB
+    of traffic earlier (L2 and the 256 MB Infinity Cache hold none of it):
+    ceil(1 GiB / bytes one step touches), at least 2, within a memory cap."""
+    n = max(2, -(-ROTATE_BYTES // max(1, touched_bytes)))
+    return int(max(2, min(n, cap_bytes // max(1, alloc_bytes))))
+
+
+def cpu_threads():
+    """(threads, affinity_cores, cgroup_quota): the CPU baseline runs on every
+    core in the affinity mask, unless a cgroup CPU quota grants fewer cores'
+    worth of time (then on that many)."""
+    import math
+    n = len(os.sched_getaffinity(0))
+    quota = None
+    try:
+        with open("/sys/fs/cgroup/cpu.max") as f:
+            q, per = f.read().split()[:2]
+        if q != "max":
+            quota = max(1, math.ceil(int(q) / int(per)))
+    except (OSError, ValueError):
+        pass
+    return (min(n, quota) if quota else n), n, quota
 
 
 # ---------------------------------------------------------------------------
@@ -214,9 +244,8 @@ class CcaRunner:
 
 def cpu_baseline_conv(case, budget_s=10.0, num_accepted=None, fused=False):
     """The oracle, as it stands, on the same batch; repeated until ~budget_s."""
-    import numpy as np
     import oracle
-    threads = min(16, oracle.default_threads())
+    threads, aff, quota = cpu_threads()
     fz = dict(resid=case.x, outer=case.x) if fused else {}
     runs, t0 = 0, time.perf_counter()
     while True:
@@ -231,9 +260,10 @@ def cpu_baseline_conv(case, budget_s=10.0, num_accepted=None, fused=False):
     res = {"value": case.T * runs / el, "unit": "tokens/s", "cores": threads,
            "kind": "oracle",
            "sample": f"the full batch ({case.T} tokens) run {runs}x through the fp64 "
-                     f"oracle, {el:.1f} s wall on {threads} threads"}
-    # one thread, one run of the batch, when that stays within the budget
-    if threads > 1 and el / runs * threads <= budget_s:
+                     f"oracle, {el:.1f} s wall on {threads} threads",
+           "affinity_cores": aff, "cgroup_cpu_quota": quota}
+    # one thread, one run of the batch (bounded: at most ~2x the budget)
+    if threads > 1 and el / runs * threads <= 2 * budget_s:
         t1 = time.perf_counter()
         if num_accepted is None:
             oracle.conv(case, nthreads=1, **fz)
@@ -349,8 +379,7 @@ def spec_varlen_bench(args):
                      np.maximum(np.diff(qsl), 1)).astype(np.int32)
     alg = spec_varlen_alg_bytes(case, qsl)
     max_q = int(np.diff(qsl).max())
-    set_bytes = T * case.C * case.elsize * 2 + case.pool.nbytes
-    nsets = int(min(8, max(2, -(-ROTATE_BYTES // set_bytes))))
+    nsets = rotation_sets(alg, T * case.C * case.elsize * 2 + case.pool.nbytes)
     log(f"spec varlen B={B} T={T} C={case.C} S={case.S} layout={case.layout}; "
         f"alg bytes/step={alg}; {nsets} rotating buffer sets")
     w = dev(case.w)
@@ -396,7 +425,7 @@ def spec_varlen_bench(args):
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         import oracle
-        threads = min(16, oracle.default_threads())
+        threads, _, _ = cpu_threads()
         runs, t0 = 0, time.perf_counter()
         while True:
             oracle.conv_spec_varlen(case, acc, qsl, nthreads=threads)
@@ -420,8 +449,7 @@ def cca_bench(args):
     import synthetic
     case = synthetic.cca_mixed_32k()
     main_b, upd_b = cca_alg_bytes(case)
-    set_bytes = main_b
-    nsets = int(min(6, max(2, -(-ROTATE_BYTES // set_bytes))))
+    nsets = rotation_sets(main_b + upd_b, main_b + upd_b)
     log(f"CCA T={case.T} C={case.C}; alg bytes/step main={main_b} state={upd_b}; "
         f"{nsets} rotating buffer sets")
     run = CcaRunner(case, nsets)
@@ -464,7 +492,7 @@ def cca_bench(args):
 def cpu_baseline_cca(case, budget_s=10.0):
     """The CCA oracle, as it stands, on the same batch; repeated until ~budget_s."""
     import oracle
-    threads = min(16, oracle.default_threads())
+    threads, _, _ = cpu_threads()
     runs, t0 = 0, time.perf_counter()
     while True:
         oracle.cca(case, nthreads=threads)
@@ -593,6 +621,215 @@ def traffic_from(d):
 
 
 # ---------------------------------------------------------------------------
+# parity of a timed batch (outside the timed region)
+# ---------------------------------------------------------------------------
+def conv_parity(case, run):
+    """Restores buffer set 0 to the batch's pristine state, runs one step and
+    checks it against the oracle on the same inputs: state pool bit-exact, every
+    output element within the tolerance (2 bf16 ulp or 1e-5 relative, or the fp32
+    accumulation floor 2^-20 of the sum of |terms|). floor_passes counts the
+    elements that passed through the floor alone."""
+    import numpy as np
+    import torch
+    import oracle
+    from tests._gpu import check_close, dev, host
+    x, out, pool, _ = run.sets[0]
+    pool.copy_(dev(case.pool))
+    out.zero_()
+    run.step(0)
+    torch.cuda.synchronize()
+    got, gpool = host(out), host(pool)
+    ref, rpool, ab = oracle.conv(case, out_dtype="f64", absum=True)
+    res = {"reference": "oracle", "rows_checked": int(case.T), "elements": int(ref.size),
+           "state_bit_exact": bool(np.array_equal(gpool, rpool))}
+    try:
+        share = check_close(got, ref, ab, case.dtype, 2.0 ** -20)
+        res["outputs_within_tolerance"] = True
+        res["floor_passes"] = int(round(share * ref.size))
+    except AssertionError as e:
+        res["outputs_within_tolerance"] = False
+        res["floor_passes"] = None
+        res["error"] = str(e)[:300]
+    res["pass"] = res["state_bit_exact"] and res["outputs_within_tolerance"]
+    return res
+
+
+def cca_parity(case, run):
+    """As conv_parity for the CCA call: both state pools and the value half
+    bit-exact, the q/k half within 2 bf16 ulp or the fp32 accumulation floor."""
+    import numpy as np
+    import torch
+    import oracle
+    import synthetic
+    from tests._gpu import cca_floor_rel, check_close, dev, host
+    q, k, vc, vdl, out, cs, ds = run.sets[0]
+    cs.copy_(dev(case.conv_state))
+    ds.copy_(dev(case.delayed_state))
+    out.zero_()
+    run.step(0)
+    torch.cuda.synchronize()
+    got, gcs, gds = host(out), host(cs), host(ds)
+    nd = []
+    ref, rcs, rds, ab = oracle.cca(case, out_dtype="f64", absum=True, chain_diff=nd)
+    C = case.C
+    res = {"reference": "oracle", "rows_checked": int(case.T), "elements": int(ref.size),
+           "state_bit_exact": bool(np.array_equal(gcs, rcs) and np.array_equal(gds, rds)),
+           "value_half_bit_exact": bool(np.array_equal(
+               synthetic.bf16_to_f32(got[:, C:]).astype(np.float64), ref[:, C:])),
+           "depthwise_values_an_fp32_chain_rounds_elsewhere": nd[0]}
+    try:
+        share = check_close(got[:, :C], ref[:, :C], ab[:, :C], "bf16", cca_floor_rel(case))
+        res["outputs_within_tolerance"] = True
+        res["floor_passes"] = int(round(share * ref[:, :C].size))
+    except AssertionError as e:
+        res["outputs_within_tolerance"] = False
+        res["floor_passes"] = None
+        res["error"] = str(e)[:300]
+    res["pass"] = (res["state_bit_exact"] and res["value_half_bit_exact"]
+                   and res["outputs_within_tolerance"])
+    return res
+
+
+def roofline(kernel, alg_bytes, us, traffic=None):
+    gbps = alg_bytes / (us * 1e-6) / 1e9
+    return {"kernel": kernel, "bound": "hbm", "achieved": gbps, "peak": PEAK_GBPS,
+            "unit": "GB/s", "frac": gbps / PEAK_GBPS, "traffic": traffic,
+            "alg_bytes_per_launch": alg_bytes}
+
+
+# ---------------------------------------------------------------------------
+# one depthwise workload: step time, per-kernel times, rooflines, parity
+# ---------------------------------------------------------------------------
+def measure_conv(args, workload, *, parity=True, quiet=False):
+    import torch
+    import synthetic
+    case = conv_workload(workload)
+    if args.state_layout == "sd":
+        case = synthetic.as_sd(case)
+    acc = None
+    if workload == "spec":
+        acc = synthetic.num_accepted(synthetic.SEED_BASE + 0x36, case.num_decodes, case.q)
+        alg = dec_b = spec_alg_bytes(case)
+        pre_b = 0
+    else:
+        alg = conv_alg_bytes(case)
+        dec_b, pre_b = conv_kernel_bytes(case)
+    fused = workload == "ple_fused"
+    if fused:
+        # every output element also reads its residual and outer residual
+        alg += fused_extra_bytes(case)
+        dec_b += 2 * case.num_decode_tokens * case.C * case.elsize
+        pre_b += 2 * (case.T - case.num_decode_tokens) * case.C * case.elsize
+    alloc = case.T * case.C * case.elsize * (4 if fused else 2) + case.pool.nbytes
+    nsets = rotation_sets(alg, alloc)
+    log(f"{case.name}: T={case.T} C={case.C} K={case.K} d={case.d} {case.dtype} "
+        f"act={case.act}; alg bytes/step={alg}; {nsets} rotating buffer sets")
+    run = ConvRunner(case, nsets, acc, fused=fused)
+    for i in range(args.warmup):
+        run.step(i)
+    torch.cuda.synchronize()
+    timing = {}
+
+    def timed(name, fn_steps):
+        eager, graph = time_launches(fn_steps, args.steps)
+        timing[name] = {"eager_us": eager * 1e3, "graph_us": graph * 1e3}
+        return min(eager, graph)
+
+    ms_step = timed("step", lambda: [run.step(args.warmup + i) for i in range(args.steps)])
+    # per-kernel averages: with one kernel per step, the timed region itself;
+    # otherwise K launches of each kernel alone, timed the same way
+    if len(run.kernels) == 1:
+        kms = {run.kernels[0]: ms_step}
+    else:
+        kms = {k: timed(k, lambda k=k: [run.step(i, only=k) for i in range(args.steps)])
+               for k in run.kernels}
+    log(f"{case.name}: {ms_step * 1e3:.2f} us/step; per kernel "
+        + ", ".join(f"{k}={v * 1e3:.2f} us" for k, v in kms.items()))
+    kb = {"prefill": pre_b, "decode_update": dec_b, "spec_update": dec_b}
+    key = {"varlen_prefill": "varlen_prefill", "decode": "decode"}.get(workload)
+    roofs = {k: roofline(k, kb[k], v * 1e3,
+                         traffic_for(f"{key}:{k}") if key and args.state_layout == "ds" else None)
+             for k, v in kms.items()}
+    res = {"workload": case.name, "tokens": case.T, "decodes": case.num_decodes,
+           "decode_q": case.q, "prefills": case.num_prefills, "channels": case.C,
+           "width": case.K, "dilation": case.d, "activation": case.act,
+           "state_slots": case.num_slots, "state_len": case.S, "state_layout": case.layout,
+           "checkpoint_grid": case.ckpt_grid, "fused_residuals": fused,
+           "rotating_sets": nsets, "step_us": ms_step * 1e3,
+           "kernel_us": {k: v * 1e3 for k, v in kms.items()}, "timing": timing,
+           "tokens_per_s": case.T / (ms_step * 1e-3),
+           "alg_bytes_per_step": alg, "hbm_gbps": alg / (ms_step * 1e-3) / 1e9,
+           "roofline": roofs}
+    if len(kms) > 1:
+        tot = sum(kms.values())
+        res["kernels_sum_us"] = tot * 1e3
+        res["roofline_sum"] = roofline("+".join(kms), sum(kb[k] for k in kms), tot * 1e3)
+    if parity and acc is None and not fused:
+        log(f"{case.name}: parity against the oracle ...")
+        res["parity"] = conv_parity(case, run)
+        log(f"{case.name}: parity {'pass' if res['parity']['pass'] else 'FAIL'}")
+    return case, run, res, acc, fused
+
+
+def measure_cca(args, *, parity=True):
+    import torch
+    import synthetic
+    case = synthetic.cca_mixed_32k()
+    main_b, upd_b = cca_alg_bytes(case)
+    nsets = rotation_sets(main_b + upd_b, main_b + upd_b)
+    log(f"CCA T={case.T} C={case.C}; alg bytes/step main={main_b} state={upd_b}; "
+        f"{nsets} rotating buffer sets")
+    run = CcaRunner(case, nsets)
+    for i in range(args.warmup):
+        run.step(i)
+    torch.cuda.synchronize()
+    eager, graph = time_launches(lambda: [run.step(args.warmup + i) for i in range(args.steps)],
+                                 args.steps)
+    ms = min(eager, graph)
+    flops = 2.0 * case.T * case.C * case.hd * case.t1
+    log(f"CCA: {ms * 1e3:.2f} us/step ({(main_b + upd_b) / (ms * 1e-3) / 1e9:.0f} GB/s)")
+    res = {"workload": case.name, "tokens": case.T, "decodes": case.num_decodes,
+           "prefills": case.num_prefills, "q_heads": case.nq, "kv_heads": case.nkv,
+           "head_dim": case.hd, "t0": case.t0, "t1": case.t1, "rotating_sets": nsets,
+           "step_us": ms * 1e3, "timing": {"eager_us": eager * 1e3, "graph_us": graph * 1e3},
+           "tokens_per_s": case.T / (ms * 1e-3),
+           "grouped_conv_tflops": flops / (ms * 1e-3) / 1e12,
+           "roofline": roofline("cca_main+state_update", main_b + upd_b, ms * 1e3,
+                                traffic_for("cca:cca_main+state", CCA_SOURCES))}
+    if parity:
+        log("CCA: parity against the oracle ...")
+        res["parity"] = cca_parity(case, run)
+        log(f"CCA: parity {'pass' if res['parity']['pass'] else 'FAIL'}")
+    return case, run, res
+
+
+def copy_ceiling(args):
+    """The practical HBM ceiling: the library's row copy (sc_state_gather with
+    identity indices) moving 1 GiB in and 1 GiB out per launch, two buffer
+    sets alternated, 10 launches after 2 warmup launches."""
+    import torch
+    import stateful_causal_short_amd as scs
+    row = 48 * 1024
+    rows = (1 << 30) // row
+    src = [torch.ones(rows, row, dtype=torch.uint8, device="cuda") for _ in range(2)]
+    dst = [torch.empty_like(src[0]) for _ in range(2)]
+    idx = torch.arange(rows, dtype=torch.int32, device="cuda")
+    for i in range(2):
+        scs.sc_state_gather(src[i % 2], idx, dst[i % 2])
+    torch.cuda.synchronize()
+    steps = 10
+    eager, _ = time_launches(
+        lambda: [scs.sc_state_gather(src[i % 2], idx, dst[i % 2]) for i in range(steps)], steps)
+    nbytes = 2 * rows * row
+    gbps = nbytes / (eager * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    log(f"copy ceiling: {gbps:.0f} GB/s")
+    return {"kernel": "row_copy", "bytes_per_launch": nbytes, "us_per_launch": eager * 1e3,
+            "achieved": gbps, "unit": "GB/s", "frac_of_peak": gbps / PEAK_GBPS}
+
+
+# ---------------------------------------------------------------------------
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -604,8 +841,11 @@ def main():
     ap.add_argument("--state-layout", default="ds", choices=["ds", "sd"],
                     help="state pool layout: (slots, C, S) or (slots, S, C)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-decode", action="store_true",
-                    help="varlen_prefill: skip the secondary decode measurement")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="varlen_prefill: only the headline workload (no decode, update, "
+                         "PLE, CCA or copy-ceiling objects)")
+    ap.add_argument("--no-parity", action="store_true",
+                    help="skip the oracle check of the timed batches")
     ap.add_argument("--traffic-from", metavar="DIR",
                     help="rewrite profiles/traffic.json from rocprofv3 --pmc runs under DIR "
                          "and exit (CPU only)")
@@ -617,7 +857,6 @@ def main():
               f"--gpus {args.gpus} is not supported", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
     import stateful_causal_short_amd as scs
     scs.lib()
@@ -631,59 +870,10 @@ def main():
     if args.workload == "spec_varlen":
         return spec_varlen_bench(args)
 
-    case = conv_workload(args.workload)
-    if args.state_layout == "sd":
-        import synthetic
-        case = synthetic.as_sd(case)
-    acc = None
-    if args.workload == "spec":
-        import synthetic
-        acc = synthetic.num_accepted(synthetic.SEED_BASE + 0x36, case.num_decodes, case.q)
-        alg = dec_b = spec_alg_bytes(case)
-        pre_b = 0
-    else:
-        alg = conv_alg_bytes(case)
-        dec_b, pre_b = conv_kernel_bytes(case)
-    fused = args.workload == "ple_fused"
-    if fused:
-        # every output element also reads its residual and outer residual
-        alg += fused_extra_bytes(case)
-        dec_b += 2 * case.num_decode_tokens * case.C * case.elsize
-        pre_b += 2 * (case.T - case.num_decode_tokens) * case.C * case.elsize
-    set_bytes = case.T * case.C * case.elsize * 2 + case.pool.nbytes
-    nsets = int(min(8, max(2, -(-ROTATE_BYTES // set_bytes))))
-    log(f"T={case.T} C={case.C} K={case.K} d={case.d} {case.dtype} act={case.act}; "
-        f"alg bytes/step={alg}; {nsets} rotating buffer sets")
-    run = ConvRunner(case, nsets, acc, fused=fused)
-    for i in range(args.warmup):
-        run.step(i)
-    torch.cuda.synchronize()
-    log(f"warmup {args.warmup} done")
-
-    timing = {}
-
-    def timed(name, fn_steps):
-        eager, graph = time_launches(fn_steps, args.steps)
-        timing[name] = {"eager_us": eager * 1e3, "graph_us": graph * 1e3}
-        return min(eager, graph)
-
-    # timed region: K back-to-back steps
-    ms_step = timed("step", lambda: [run.step(args.warmup + i) for i in range(args.steps)])
-    # per-kernel averages: with one kernel per step, the timed region itself;
-    # otherwise K launches of each kernel alone, timed the same way
-    if len(run.kernels) == 1:
-        kms = {run.kernels[0]: ms_step}
-    else:
-        kms = {k: timed(k, lambda k=k: [run.step(i, only=k) for i in range(args.steps)])
-               for k in run.kernels}
-    log(f"timed {args.steps} steps: {ms_step * 1e3:.2f} us/step; per-kernel us: "
-        + ", ".join(f"{k}={v * 1e3:.2f}" for k, v in kms.items()))
-
+    case, run, m, acc, fused = measure_conv(args, args.workload, parity=not args.no_parity)
+    ms_step = m["step_us"] * 1e-3
     # dominant kernel: the prefill kernel when present
-    dom = "prefill" if "prefill" in kms else run.kernels[0]
-    dom_bytes = pre_b if dom == "prefill" else dec_b
-    achieved = dom_bytes / (kms[dom] * 1e-3) / 1e9
-    key = f"{args.workload}:{dom}"
+    dom = "prefill" if "prefill" in m["roofline"] else run.kernels[0]
     result = {
         "metric": METRIC,
         "value": case.T / (ms_step * 1e-3),
@@ -704,58 +894,35 @@ def main():
             "state_slots": case.num_slots, "checkpoint_grid": case.ckpt_grid,
             "state_len": case.S, "state_layout": case.layout, "fused_residuals": fused,
         },
-        "hbm_gbps": alg / (ms_step * 1e-3) / 1e9,
-        "pct_peak": 100.0 * alg / (ms_step * 1e-3) / 1e9 / PEAK_GBPS,
-        "kernel_us": {k: v * 1e3 for k, v in kms.items()},
-        "timing": timing,
-        "roofline": {
-            "kernel": dom, "bound": "hbm", "achieved": achieved, "peak": PEAK_GBPS,
-            "unit": "GB/s", "frac": achieved / PEAK_GBPS,
-            "traffic": traffic_for(key), "alg_bytes_per_launch": dom_bytes,
-        },
+        "hbm_gbps": m["hbm_gbps"],
+        "pct_peak": 100.0 * m["hbm_gbps"] / PEAK_GBPS,
+        "kernel_us": m["kernel_us"],
+        "timing": m["timing"],
+        "rotating_sets": m["rotating_sets"],
+        "roofline": m["roofline"][dom],
+        "parity": m.get("parity"),
         "cpu_baseline": None,
     }
-    if args.workload == "varlen_prefill" and not args.no_decode:
-        # the metric names the decode conv too: the 512-request decode batch,
-        # timed the same way, in the same process (a secondary figure; `value`
-        # stays the varlen prefill's)
-        result["decode"] = decode_secondary(args)
+    if "roofline_sum" in m:
+        result["roofline_sum"] = m["roofline_sum"]
+    if args.workload == "varlen_prefill" and not args.no_secondary:
+        # The metric names the decode conv too, and the other workloads of the
+        # method ride along as secondary objects (each timed the same way, in
+        # the same process; `value` stays the varlen prefill's).
+        for name, wl in (("decode", "decode"), ("update_q4", "update_q4"),
+                         ("ple_mixed", "ple_mixed")):
+            _, r2, res2, _, _ = measure_conv(args, wl, parity=not args.no_parity)
+            result[name] = res2
+            del r2
+            torch.cuda.empty_cache()
+        _, r3, result["cca"] = measure_cca(args, parity=not args.no_parity)
+        del r3
+        torch.cuda.empty_cache()
+        result["copy_ceiling"] = copy_ceiling(args)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
         result["cpu_baseline"] = cpu_baseline_conv(case, num_accepted=acc, fused=fused)
     print(json.dumps(result), flush=True)
-
-
-def decode_secondary(args):
-    """Decode (512 requests x 1 token, 8192 channels, width 4, bf16, bias + SiLU,
-    1024-slot pool): K back-to-back launches after W warmup, timed as the main
-    workload is; per-launch time, tokens/s and the kernel's roofline fraction."""
-    import torch
-    case = conv_workload("decode")
-    if args.state_layout == "sd":
-        import synthetic
-        case = synthetic.as_sd(case)
-    dec_b, _ = conv_kernel_bytes(case)
-    set_bytes = case.T * case.C * case.elsize * 2 + case.pool.nbytes
-    nsets = int(min(8, max(2, -(-ROTATE_BYTES // set_bytes))))
-    run = ConvRunner(case, nsets)
-    for i in range(args.warmup):
-        run.step(i)
-    torch.cuda.synchronize()
-    eager, graph = time_launches(lambda: [run.step(args.warmup + i) for i in range(args.steps)],
-                                 args.steps)
-    ms = min(eager, graph)
-    gbps = dec_b / (ms * 1e-3) / 1e9
-    log(f"decode: {ms * 1e3:.2f} us/launch ({gbps:.0f} GB/s)")
-    return {"workload": case.name, "requests": case.num_decodes, "tokens": case.T,
-            "state_layout": case.layout, "kernel_us": ms * 1e3,
-            "timing": {"eager_us": eager * 1e3, "graph_us": graph * 1e3},
-            "tokens_per_s": case.T / (ms * 1e-3),
-            "roofline": {"kernel": "decode_update", "bound": "hbm", "achieved": gbps,
-                         "peak": PEAK_GBPS, "unit": "GB/s", "frac": gbps / PEAK_GBPS,
-                         "traffic": traffic_for("decode:decode_update")
-                         if args.state_layout == "ds" else None,
-                         "alg_bytes_per_launch": dec_b}}
 
 
 if __name__ == "__main__":

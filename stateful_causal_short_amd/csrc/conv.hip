@@ -286,6 +286,16 @@ __global__ __launch_bounds__(kBlock) void conv_pairs(ConvArgs a) {
     else return xb + (int64_t)t * xrs;
   };
 
+  // the slot is needed by the request's first chunk only (history and
+  // write-back); its scalar load goes out before the rows so that the state
+  // loads, which wait on it, start while the rows are in flight; the
+  // has-state flag is read after them and applied to the loaded history
+  int32_t slot = -1;
+  bool valid = false, hflag = false;
+  if (j == 0) {
+    slot = a.slots[(int64_t)r * a.slot_stride];
+    valid = slot >= 0 && slot < a.num_slots;
+  }
   u32x4 raw[H + U];
   if (j > 0) {
 #pragma unroll
@@ -296,18 +306,17 @@ __global__ __launch_bounds__(kBlock) void conv_pairs(ConvArgs a) {
     const int t = UPDATE ? u : min(t0 + u, t1 - 1);
     raw[H + u] = ld16_stream(xrow(t));
   }
-  // the slot is needed by the request's first chunk only (history and write-back)
-  int32_t slot = -1;
-  bool valid = false, hflag = false;
   u32x4 old[H];
 #pragma unroll
   for (int v = 0; v < H; ++v) old[v] = u32x4{0, 0, 0, 0};
-  if (j == 0) {
-    slot = a.slots[(int64_t)r * a.slot_stride];
-    valid = slot >= 0 && slot < a.num_slots;
-    hflag = valid && (a.has_init ? a.has_init[r] != 0 : true);
+  if (valid) load_state_rows<E, H, SD>(a, slot, c0, old);   // history rows
+  if (valid) {
+    hflag = a.has_init ? uniform_flag(a.has_init, r) : true;
+    if (!hflag) {
+#pragma unroll
+      for (int v = 0; v < H; ++v) old[v] = u32x4{0, 0, 0, 0};
+    }
   }
-  if (hflag) load_state_rows<E, H, SD>(a, slot, c0, old);   // history rows
   Work w;
   w.r = r;
   w.j = j;
@@ -450,10 +459,24 @@ __global__ __launch_bounds__(kBlock) void conv_update_pairs(ConvArgs a) {
     if (a.bias) bsv = ld16((const S*)a.bias + c0);
   }
 
-  // issue every request's loads: the token rows first (independent of the
-  // slot), then the slot indices, then the state (unit stride over the region)
+  // issue every request's loads: the slot indices first (workgroup-uniform
+  // scalar loads; requests past the batch read the last request's entry and
+  // are masked), then the token rows (independent of the slot), then the
+  // state of every valid slot, which waits on the slots only. The has-state
+  // flags are read last and applied to the loaded history (a request without
+  // state reads its slot needlessly but never waits on its flag).
   int32_t slot[R];
   bool valid[R], hflag[R];
+#pragma unroll
+  for (int rr = 0; rr < R; ++rr) {
+    const int rc = min(grp * R + rr, a.batch - 1);
+    slot[rr] = a.slots[(int64_t)rc * a.slot_stride];
+  }
+#pragma unroll
+  for (int rr = 0; rr < R; ++rr) {
+    if (grp * R + rr >= a.batch) slot[rr] = -1;
+    valid[rr] = slot[rr] >= 0 && slot[rr] < a.num_slots;
+  }
   u32x4 st[R][H], xr[R][Q];
   // physical row of request r's token u (through the row map when fused)
   auto prow = [&](int r, int u) -> int64_t {
@@ -485,13 +508,6 @@ __global__ __launch_bounds__(kBlock) void conv_update_pairs(ConvArgs a) {
       }
     }
   }
-#pragma unroll
-  for (int rr = 0; rr < R; ++rr) {
-    const int r = grp * R + rr;
-    slot[rr] = r < a.batch ? a.slots[(int64_t)r * a.slot_stride] : -1;
-    valid[rr] = slot[rr] >= 0 && slot[rr] < a.num_slots;
-    hflag[rr] = valid[rr] && (a.has_init ? a.has_init[r] != 0 : true);
-  }
   if constexpr (SD) {
     // SD pool: entry k of the lane's channels is one vector, unit stride across lanes
 #pragma unroll
@@ -499,7 +515,7 @@ __global__ __launch_bounds__(kBlock) void conv_update_pairs(ConvArgs a) {
       const S* sp = (const S*)a.pool + (int64_t)(valid[rr] ? slot[rr] : 0) * a.S * a.C + c0;
 #pragma unroll
       for (int k = 0; k < H; ++k)
-        st[rr][k] = (hflag[rr] && lane_ok) ? ld16_stream(sp + (int64_t)k * a.C) : u32x4{0, 0, 0, 0};
+        st[rr][k] = (valid[rr] && lane_ok) ? ld16_stream(sp + (int64_t)k * a.C) : u32x4{0, 0, 0, 0};
     }
   } else {
 #pragma unroll
@@ -508,10 +524,19 @@ __global__ __launch_bounds__(kBlock) void conv_update_pairs(ConvArgs a) {
 #pragma unroll
       for (int k = 0; k < H; ++k) {
         const int vi = tid + k * kBlock;
-        st[rr][k] = (hflag[rr] && vi < nvec)
+        st[rr][k] = (valid[rr] && vi < nvec)
                         ? ld16_stream(sp + vi * VEC)
                         : u32x4{0, 0, 0, 0};
       }
+    }
+  }
+#pragma unroll
+  for (int rr = 0; rr < R; ++rr) {
+    const bool h = a.has_init ? uniform_flag(a.has_init, min(grp * R + rr, a.batch - 1)) : true;
+    hflag[rr] = valid[rr] && h;
+    if (!hflag[rr]) {
+#pragma unroll
+      for (int k = 0; k < H; ++k) st[rr][k] = u32x4{0, 0, 0, 0};
     }
   }
   float bs[VEC];

@@ -61,6 +61,18 @@ __device__ __forceinline__ int find_request_bounds(const int32_t* qsl, int B, in
   return r;
 }
 
+// Has-state flag of request r when r is the same for the whole workgroup:
+// the aligned 32-bit word holding the flag byte is read with a scalar load
+// (gfx9 has no scalar byte load; a vector byte load would make the next
+// vmcnt wait cover every row load issued before it). The word never leaves
+// the 4-byte-aligned block of the flag, so it stays inside the flag's page.
+__device__ __forceinline__ bool uniform_flag(const uint8_t* flags, int64_t r) {
+  typedef const __attribute__((address_space(1))) uint32_t* gword;
+  const uintptr_t p = (uintptr_t)(flags + r);
+  const uint32_t word = *(gword)(p & ~(uintptr_t)3);
+  return ((word >> (8 * (p & 3))) & 0xFFu) != 0;
+}
+
 struct Work {
   int r, j, L, t0, t1;
   int64_t start;

@@ -120,7 +120,7 @@ __global__ __launch_bounds__(kBlock) void conv_rollbuf(ConvArgs a) {
   if constexpr (SPEC) {
     acc = min(max(a.num_acc[r], 1), min(q, Sl - H + 1));
   } else {
-    hist = valid && (a.has_init ? a.has_init[r] != 0 : true);
+    hist = valid && (a.has_init ? uniform_flag(a.has_init, r) : true);
   }
   // SD pool (num_slots, S, C): entry k of the lane's channels is one vector;
   // the lane keeps its own column region[k * kBlock + tid] (no other lane
