@@ -75,6 +75,11 @@ def lib():
     """Load libstatefulconv.so (raises if it has not been built)."""
     global _lib
     if _lib is None:
+        # torch first: it carries its own HIP runtime, and the library must
+        # bind to that one (loaded first, the library would pull in the
+        # system runtime and the process would hold two, whose device
+        # pointers and streams the other does not know)
+        _torch()
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(
                 f"{LIB_PATH} is missing: build it with "

@@ -375,3 +375,18 @@ def test_binding_checks_cca_shapes():
     with pytest.raises(ValueError, match="on the GPU"):
         scs.sc_cca_qk_conv(*good.values(), idx, None, None, None, num_q_heads=nq,
                            num_kv_heads=nkv, head_dim=hd, t0=t0, t1=t1)
+
+
+def test_library_shares_torchs_hip_runtime():
+    """Loading the library before torch must not put a second HIP runtime in
+    the process: the binding imports torch first, so the library binds to
+    torch's runtime and device pointers and streams mean the same to both."""
+    import subprocess
+    import sys
+    code = ("import stateful_causal_short_amd as scs; scs.lib(); import torch; "
+            "maps = open('/proc/self/maps').read(); "
+            "print(len({l.split()[-1] for l in maps.splitlines() if 'libamdhip64' in l}))")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
+                       cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.strip() == "1"
