@@ -459,25 +459,26 @@ __global__ __launch_bounds__(kBlock) void conv_update_pairs(ConvArgs a) {
     if (a.bias) bsv = ld16((const S*)a.bias + c0);
   }
 
-  // issue every request's loads: the slot indices first (workgroup-uniform
-  // scalar loads; requests past the batch read the last request's entry and
-  // are masked), then the token rows (independent of the slot), then the
-  // state of every valid slot, which waits on the slots only. The has-state
-  // flags are read last and applied to the loaded history (a request without
-  // state reads its slot needlessly but never waits on its flag).
+  // issue every request's loads: the token rows (independent of the slot),
+  // the slot indices and has-state flags (workgroup-uniform scalar loads),
+  // then the state (unit stride over the region), which waits on the slots
+  // only. With one request per workgroup the slot load goes out before the
+  // token rows (6.78 vs 6.90 us on the 128 x 4 update); with several, after
+  // them (12.53 vs 12.82 us on the 512-request decode, the state loads then
+  // start a few scalar round trips after the rows).
   int32_t slot[R];
   bool valid[R], hflag[R];
-#pragma unroll
-  for (int rr = 0; rr < R; ++rr) {
-    const int rc = min(grp * R + rr, a.batch - 1);
-    slot[rr] = a.slots[(int64_t)rc * a.slot_stride];
-  }
-#pragma unroll
-  for (int rr = 0; rr < R; ++rr) {
-    if (grp * R + rr >= a.batch) slot[rr] = -1;
-    valid[rr] = slot[rr] >= 0 && slot[rr] < a.num_slots;
-  }
   u32x4 st[R][H], xr[R][Q];
+  auto load_slots = [&]() {
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr) {
+      const int r = grp * R + rr;
+      slot[rr] = r < a.batch ? a.slots[(int64_t)r * a.slot_stride] : -1;
+      valid[rr] = slot[rr] >= 0 && slot[rr] < a.num_slots;
+      hflag[rr] = valid[rr] && (a.has_init ? uniform_flag(a.has_init, r) : true);
+    }
+  };
+  if constexpr (R == 1) load_slots();
   // physical row of request r's token u (through the row map when fused)
   auto prow = [&](int r, int u) -> int64_t {
     if constexpr (FUSE) return phys_row(a, (int64_t)r * Q + u);
@@ -508,6 +509,7 @@ __global__ __launch_bounds__(kBlock) void conv_update_pairs(ConvArgs a) {
       }
     }
   }
+  if constexpr (R > 1) load_slots();
   if constexpr (SD) {
     // SD pool: entry k of the lane's channels is one vector, unit stride across lanes
 #pragma unroll
@@ -515,7 +517,7 @@ __global__ __launch_bounds__(kBlock) void conv_update_pairs(ConvArgs a) {
       const S* sp = (const S*)a.pool + (int64_t)(valid[rr] ? slot[rr] : 0) * a.S * a.C + c0;
 #pragma unroll
       for (int k = 0; k < H; ++k)
-        st[rr][k] = (valid[rr] && lane_ok) ? ld16_stream(sp + (int64_t)k * a.C) : u32x4{0, 0, 0, 0};
+        st[rr][k] = (hflag[rr] && lane_ok) ? ld16_stream(sp + (int64_t)k * a.C) : u32x4{0, 0, 0, 0};
     }
   } else {
 #pragma unroll
@@ -524,19 +526,8 @@ __global__ __launch_bounds__(kBlock) void conv_update_pairs(ConvArgs a) {
 #pragma unroll
       for (int k = 0; k < H; ++k) {
         const int vi = tid + k * kBlock;
-        st[rr][k] = (valid[rr] && vi < nvec)
-                        ? ld16_stream(sp + vi * VEC)
-                        : u32x4{0, 0, 0, 0};
+        st[rr][k] = (hflag[rr] && vi < nvec) ? ld16_stream(sp + vi * VEC) : u32x4{0, 0, 0, 0};
       }
-    }
-  }
-#pragma unroll
-  for (int rr = 0; rr < R; ++rr) {
-    const bool h = a.has_init ? uniform_flag(a.has_init, min(grp * R + rr, a.batch - 1)) : true;
-    hflag[rr] = valid[rr] && h;
-    if (!hflag[rr]) {
-#pragma unroll
-      for (int k = 0; k < H; ++k) st[rr][k] = u32x4{0, 0, 0, 0};
     }
   }
   float bs[VEC];
