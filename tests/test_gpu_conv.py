@@ -389,3 +389,36 @@ def test_launch_size_rules_do_not_change_results(layout):
     torch.cuda.synchronize()
     np.testing.assert_array_equal(host(out), big_out)
     np.testing.assert_array_equal(host(pool), big_pool)
+
+
+@pytest.mark.parametrize("batch", [256, 512, 1024])
+@pytest.mark.parametrize("off", [1, 2, 3])
+def test_has_state_flags_at_every_byte_offset(batch, off):
+    """The update and prefill kernels read a request's has-state flag as the
+    aligned 32-bit word that holds it: flags passed as a view that starts 1-3
+    bytes into its buffer, at batch sizes that put 2, 4 and 8 requests in a
+    decode workgroup, pick out the right byte."""
+    import torch
+    import stateful_causal_short_amd as scs
+    case = conv_case("flags", 1300 + batch + off, C=8192, K=4, d=1, dtype="bf16", act="silu",
+                     w_std=0.25, bias_std=0.1, num_slots=batch + 16, num_decodes=batch, q=1,
+                     prefill_lens=[5, 40, 3, 17, 64], prefill_h_p=0.5)
+    rng = np.random.default_rng(off)
+    case.decode_h = (rng.random(batch) < 0.6).astype(np.uint8)
+    print(f"[gpu] flags batch={batch} off={off}", flush=True)
+    dbuf = np.full(batch + 8, 0xAB, np.uint8)
+    dbuf[off:off + batch] = case.decode_h
+    pbuf = np.full(case.num_prefills + 8, 0xCD, np.uint8)
+    pbuf[off:off + case.num_prefills] = case.prefill_h
+    xd, od = dev(case.x), torch.zeros(case.T, case.C, dtype=torch.bfloat16, device="cuda")
+    pd, wd, bd = dev(case.pool), dev(case.w), dev(case.bias)
+    nd = case.num_decode_tokens
+    scs.sc_conv_update(xd[:nd], od[:nd], wd, bd, pd, dev(np.asarray(case.decode_slots, np.int32)),
+                       dev(dbuf)[off:off + batch], q=1, activation="silu")
+    scs.sc_conv_prefill_varlen(xd[nd:], od[nd:], wd, bd, pd, dev(case.qsl_p),
+                               dev(np.asarray(case.prefill_slots, np.int32)),
+                               dev(pbuf)[off:off + case.num_prefills], activation="silu")
+    torch.cuda.synchronize()
+    ref, ref_pool, absum = oracle.conv(case, out_dtype="f64", absum=True)
+    np.testing.assert_array_equal(host(pd), ref_pool, err_msg="state pool not bit-exact")
+    check_close(host(od), ref, absum, "bf16", FLOOR)
