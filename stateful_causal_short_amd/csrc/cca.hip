@@ -14,7 +14,9 @@
 // Two launches: the main kernel only reads the state pools; cca_state_update
 // (ordered after it on the stream) writes them, so no workgroup can overwrite a
 // history another workgroup still has to read, and main-kernel tiles may mix
-// decode and prefill rows freely.
+// decode and prefill rows freely. On the MFMA path the state update also writes
+// the delayed-value columns of each request's first row (from the saved value
+// it then replaces), which keeps that rare case out of the main kernel's loop.
 //
 // The main kernel for hd = 128, t1 = 2 (the ZAYA shape) is cca_persist_main
 // below (persistent, weight-stationary, grouped conv on MFMA); other shapes
@@ -44,6 +46,15 @@ __device__ __forceinline__ uint32_t pk_bf16(float lo, float hi) {
 }
 __device__ __forceinline__ uint32_t f2bf(float v) {
   return __builtin_bit_cast(uint16_t, (__bf16)v);
+}
+// acc + w.lo * x.lo + w.hi * x.hi on bf16 pairs (v_dot2c_f32_bf16)
+__device__ __forceinline__ float dot2_pair(uint32_t w, uint32_t x, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), __builtin_bit_cast(bf16x2, x),
+                                         acc, false);
+}
+// element e (0..7) of vectors a (low half) and b (high half) as one bf16 pair
+__device__ __forceinline__ uint32_t cca_pair(const u32x4& a, const u32x4& b, int e) {
+  return __builtin_amdgcn_perm(b[e >> 1], a[e >> 1], (e & 1) ? 0x07060302u : 0x05040100u);
 }
 
 // Row -> (request position, slot, has-state). Decodes first (one row each,
@@ -238,7 +249,12 @@ __global__ __launch_bounds__(kBlock) void cca_state_update(CcaArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// vectorised state update: 8 channels (16 bytes) per lane, history length N
+// vectorised state update (after cca_persist_main): 8 channels (16 bytes) per
+// lane, history length N. It first writes the delayed-value columns of each
+// request's first output row, which take the saved delayed value (continuing
+// request with a valid slot), else delayed_init, else zeros: the main kernel
+// writes the shifted v_del row there for every row and leaves this case here,
+// where the old delayed value is read before it is replaced.
 // ---------------------------------------------------------------------------
 template <int N>
 __global__ __launch_bounds__(kBlock) void cca_state_update_vec(CcaArgs a) {
@@ -261,8 +277,17 @@ __global__ __launch_bounds__(kBlock) void cca_state_update_vec(CcaArgs a) {
     slot = a.prefill_slots[(int64_t)r * a.pslot_stride];
     h = a.prefill_h[r] != 0;
   }
-  if (slot < 0 || slot >= a.num_slots || L <= 0 || start + L > a.num_tokens) return;
+  if (L <= 0 || start + L > a.num_tokens) return;
+  const bool valid = slot >= 0 && slot < a.num_slots;
   const int ncv = C / 8, nvv = vd / 8;
+  for (int e8 = threadIdx.x * 8; e8 < vd; e8 += kBlock * 8) {
+    u32x4 old = {0, 0, 0, 0};
+    if (valid && h) old = ld16((const uint16_t*)a.delayed_state + (int64_t)slot * vd + e8);
+    else if (a.delayed_init) old = ld16((const uint16_t*)a.delayed_init + e8);
+    st16((uint16_t*)a.out + start * a.out_rs + C + vd + e8, old);
+  }
+  __syncthreads();   // every old delayed value read before any is replaced
+  if (!valid) return;
   for (int v = threadIdx.x; v < ncv + nvv; v += kBlock) {
     if (v >= ncv) {
       const int e8 = (v - ncv) * 8;
@@ -332,12 +357,14 @@ struct CcaSmem {
   static constexpr int HD = 128, MT = kCcaMT;
   static constexpr int AROW = HD + 8;   // bf16 LDS rows (padded)
   static constexpr int RROW = HD + 4;   // fp32 residual rows (padded)
+  static constexpr int T0P = (T0 + 1) & ~1;   // taps per channel in LDS: whole pairs
   uint16_t act[(MT + 1) * AROW];        // depthwise rows: row i+1 = token i, row 0 = token -1
   uint16_t prv[MT * AROW];              // depthwise one position back, for request starts
   uint16_t ost[MT * AROW];              // staged bf16 output rows
   float res[MT * RROW];                 // residual + grouped bias, fp32, half-major (cca_hslot)
-  uint16_t w1[HD * T0];                 // depthwise weights: (cca_hslot(c), c % 4, tap)
-  uint16_t bb[2 * HD];                  // (cca_hslot(c)): depthwise biases of 4 channels, then grouped
+  uint16_t w1[HD * T0P];                // depthwise weights: (cca_hslot(c), c % 4, tap), taps padded to even
+  float b1[HD];                         // depthwise biases, fp32, (cca_hslot(c), c % 4)
+  float b2[HD];                         // grouped biases, fp32, same order
   int32_t qsl_s[kQslCache];
   int row_p[kCcaRowTiles][MT];          // position in the request (-1: no row), per tile of a batch
   int row_src[kCcaRowTiles][MT];        // prefill request index, or -2 - t for decode row t
@@ -432,15 +459,21 @@ __device__ __forceinline__ void cca_persist_body(const CcaArgs& a, CcaSmem<T0>& 
   const bool use_lds_qsl = a.num_prefills > 0 && a.num_prefills + 1 <= kQslCache;
   // Value columns (v_cur copied, v_del shifted one token) are dealt over the
   // nq q-head groups only (the k head's workgroups carry the bundle's q rows
-  // instead); item tid = (row vr, vector vk). A row's value columns are 2*nvv/8 lines of 128 bytes (8 vectors); line l
-  // goes to q group l % nq, so each line is read and written whole by 8
-  // consecutive lanes of one workgroup (16-byte pieces from different
-  // workgroups would each cost a partial-line transfer).
+  // instead). A row's value columns are 2*nvv/8 lines of 128 bytes (8
+  // vectors; nvv = 8 nkv, so the first nkv lines are v_cur's, the rest
+  // v_del's); line l goes to q group l % nq, so each line is read and written
+  // whole by 8 consecutive lanes of one workgroup (16-byte pieces from
+  // different workgroups would each cost a partial-line transfer). A group
+  // holds at most two lines; line j of the group is item (row vr, vector vk)
+  // of the 256 threads 256 j .. 256 j + 255, so each wave copies one kind of
+  // line or none (vkind: 0 none, 1 v_cur, 2 v_del, uniform per wave) and
+  // issues only the instructions it needs.
   const int vlines = 2 * nvv / 8;
-  const int mine = (isk || grp >= vlines) ? 0 : 8 * ((vlines - grp + a.nq - 1) / a.nq);
-  const int vr = tid / max(mine, 1), vk = tid - vr * max(mine, 1);
-  const bool vitem = tid < MT * mine;
-  const int vvv = (grp + (vk >> 3) * a.nq) * 8 + (vk & 7);   // this thread's value vector
+  const int nl = (isk || grp >= vlines) ? 0 : (vlines - grp + a.nq - 1) / a.nq;
+  const int vj = tid / (MT * 8), vr = (tid / 8) % MT, vk = tid & 7;
+  const bool vitem = vj < nl;
+  const int vvv = (grp + vj * a.nq) * 8 + vk;   // this thread's value vector
+  const int vkind = __builtin_amdgcn_readfirstlane(vitem ? (vvv < nvv ? 1 : 2) : 0);
   const int64_t qrs = a.q_rs * 2, krs = a.k_rs * 2, ors = a.out_rs * 2;   // bytes
   const int64_t vcb = a.vc_rs * 2, vdb = a.vd_rs * 2;
   const int64_t srs = isk ? krs : qrs;
@@ -449,13 +482,14 @@ __device__ __forceinline__ void cca_persist_body(const CcaArgs& a, CcaSmem<T0>& 
   // ---- setup: parameters and prefill boundaries to LDS, weights to registers ----
   if (use_lds_qsl)
     for (int k = tid; k <= a.num_prefills; k += kCcaThreads) sm.qsl_s[k] = a.prefill_qsl[k];
-  for (int k = tid; k < HD * T0; k += kCcaThreads) {
-    const int cc = k / T0, tap = k - cc * T0;
-    sm.w1[(cca_hslot(cc) * 4 + (cc & 3)) * T0 + tap] = ((const uint16_t*)a.w_dw)[(int64_t)cbase * T0 + k];
+  for (int k = tid; k < HD * SM::T0P; k += kCcaThreads) {
+    const int cc = k / SM::T0P, tap = k - cc * SM::T0P;
+    sm.w1[(cca_hslot(cc) * 4 + (cc & 3)) * SM::T0P + tap] =
+        tap < T0 ? ((const uint16_t*)a.w_dw)[(int64_t)(cbase + cc) * T0 + tap] : (uint16_t)0;
   }
   if (tid < HD) {
-    sm.bb[cca_hslot(tid) * 8 + (tid & 3)] = ((const uint16_t*)a.b_dw)[cbase + tid];
-    sm.bb[cca_hslot(tid) * 8 + 4 + (tid & 3)] = ((const uint16_t*)a.b_gr)[cbase + tid];
+    sm.b1[cca_hslot(tid) * 4 + (tid & 3)] = bf2f(((const uint16_t*)a.b_dw)[cbase + tid]);
+    sm.b2[cca_hslot(tid) * 4 + (tid & 3)] = bf2f(((const uint16_t*)a.b_gr)[cbase + tid]);
   }
   // grouped weights of this wave's 16 output channels, K ordered b*128 + j:
   // one 32-byte run of a (C, hd, t1) row holds taps 0 and 1 of 8 channels
@@ -489,14 +523,18 @@ __device__ __forceinline__ void cca_persist_body(const CcaArgs& a, CcaSmem<T0>& 
   const rsrc_t vcbuf = make_rsrc(a.v_cur, (int64_t)T * vcb);
   const rsrc_t vdbuf = make_rsrc(a.v_del, (int64_t)T * vdb);
   const rsrc_t sbuf = isk ? kbuf : qbuf;
+  const rsrc_t vbuf = vkind == 1 ? vcbuf : vdbuf;                 // this wave's value tensor
+  const uint32_t vrs32 = (uint32_t)(vkind == 1 ? vcb : vdb);
   const uint32_t srs32 = (uint32_t)srs, krs32 = (uint32_t)krs, qrs32 = (uint32_t)qrs;
   const uint32_t ors32 = (uint32_t)ors;
   // per-lane parts of the offsets (row i of the tile; raw slot s is row i-T0+s)
   const uint32_t x_lane = (uint32_t)(i - T0) * srs32 + (uint32_t)scol;
   const uint32_t k_lane = (uint32_t)i * krs32 + (uint32_t)((g * HD + v * 8) * 2);
   const uint32_t q_lane = (uint32_t)i * qrs32 + (uint32_t)((g * G * HD + v * 8) * 2);
-  const uint32_t v_lane = vvv < nvv ? (uint32_t)vr * (uint32_t)vcb + (uint32_t)(vvv * 16)
-                                    : (uint32_t)(vr - 1) * (uint32_t)vdb + (uint32_t)((vvv - nvv) * 16);
+  // value item offset: v_cur row t, or v_del row t-1 (row -1 wraps out of
+  // the resource and reads zeros)
+  const uint32_t v_lane = vkind == 1 ? (uint32_t)vr * (uint32_t)vcb + (uint32_t)(vvv * 16)
+                                     : (uint32_t)(vr - 1) * (uint32_t)vdb + (uint32_t)((vvv - nvv) * 16);
   const uint32_t o_lane = (uint32_t)i * ors32 + (uint32_t)((cbase + v * 8) * 2);
   const uint32_t ov_lane = (uint32_t)vr * ors32 + (uint32_t)((C + vvv * 8) * 2);
 
@@ -504,12 +542,20 @@ __device__ __forceinline__ void cca_persist_body(const CcaArgs& a, CcaSmem<T0>& 
 
   // one tile's loads: raw rows i-T0 .. i of this lane's channel vector (rows
   // of another request are loaded too and never used), the residual rows, and
-  // this thread's value item (v_cur row t, or v_del row t-1 for the shift)
+  // this thread's value item (v_cur row t, or v_del row t-1 for the shift;
+  // one load instruction from the wave's value tensor, skipped by waves
+  // without items: loads into one register from two instructions would make
+  // the compiler wait for every load in flight)
   struct Pref {
     u32x4 x[NR], r[isk ? GMAX : 1], val;
   };
+  // (value loads first: the value store at the next tile's start then waits
+  // for them alone, not for the rows behind them)
   auto issue = [&](int u, Pref& f) {
     const uint32_t ta = tile_ta(u);
+    if constexpr (!isk) {
+      if (vkind != 0) f.val = bld16_stream(vbuf, v_lane + ta * vrs32);
+    }
 #pragma unroll
     for (int s = 0; s < NR; ++s) f.x[s] = bld16(sbuf, x_lane + (ta + s) * srs32);
     if constexpr (!isk) {
@@ -518,10 +564,6 @@ __device__ __forceinline__ void cca_persist_body(const CcaArgs& a, CcaSmem<T0>& 
 #pragma unroll
       for (int qi = 0; qi < GMAX; ++qi)
         f.r[qi] = bld16(qbuf, qi < G ? q_lane + ta * qrs32 + (uint32_t)(qi * HD * 2) : kOff);
-    }
-    if constexpr (!isk) {
-      if (vvv < nvv) f.val = bld16_stream(vcbuf, vitem ? v_lane + ta * (uint32_t)vcb : kOff);
-      else f.val = bld16(vdbuf, vitem ? v_lane + ta * (uint32_t)vdb : kOff);
     }
   };
 
@@ -550,6 +592,13 @@ __device__ __forceinline__ void cca_persist_body(const CcaArgs& a, CcaSmem<T0>& 
     }
     const int* rp = sm.row_p[u % kCcaRowTiles];
     const int* rsrc_ = sm.row_src[u % kCcaRowTiles];
+    // value item of this tile, stored first (only the tile's own loads and the
+    // previous tile's stores are in flight here, so its wait is short); at a
+    // request's first token the state update kernel rewrites it with the saved
+    // delayed value
+    if constexpr (!isk) {
+      if (vkind != 0) bst16_stream(obuf, rp[vr] >= 0 ? ov_lane + ta * ors32 : kOff, f.val);
+    }
     // ---- (A) depthwise rows, the request-start and tile-start side rows, residual ----
     // The lane's 8 channels are done in two halves of 4, one after the other,
     // which halves the fp32 working set of this phase.
@@ -560,36 +609,41 @@ __device__ __forceinline__ void cca_persist_body(const CcaArgs& a, CcaSmem<T0>& 
       for (int hf = 0; hf < 2; ++hf) {
         const int c4 = 4 * hf;                        // first channel of the half
         const int hs = hf * 16 + v;                   // the half's parameter / residual block
-        // depthwise weights (ch * T0 + tap), biases of the half
-        uint16_t wl[4 * T0];
+        // depthwise weights of the half as words of two taps (word ch * T0P / 2
+        // + tap / 2), biases in fp32
+        constexpr int WPC = SM::T0P / 2;              // weight words per channel
+        uint32_t wd[4 * WPC];
 #pragma unroll
-        for (int k = 0; k < 4 * T0; k += 4) {
-          const uint2 w4 = *(const uint2*)(sm.w1 + hs * 4 * T0 + k);
-          wl[k] = (uint16_t)(w4.x & 0xFFFFu);
-          wl[k + 1] = (uint16_t)(w4.x >> 16);
-          wl[k + 2] = (uint16_t)(w4.y & 0xFFFFu);
-          wl[k + 3] = (uint16_t)(w4.y >> 16);
+        for (int k = 0; k < 4 * WPC; k += 2) {
+          const uint2 w2 = *(const uint2*)(sm.w1 + hs * 4 * SM::T0P + 2 * k);
+          wd[k] = w2.x;
+          wd[k + 1] = w2.y;
         }
-        const u32x4 bbv = *(const u32x4*)(sm.bb + hs * 8);
-        const uint2 b1h = {bbv[0], bbv[1]}, b2h = {bbv[2], bbv[3]};
-        auto half_el = [&](uint2 w, int ch) -> float {
-          const uint32_t word = ch < 2 ? w.x : w.y;
-          return bf2f((ch & 1) ? (word >> 16) : (word & 0xFFFFu));
-        };
-        auto w1 = [&](int tap, int ch) -> float { return bf2f(wl[ch * T0 + tap]); };
+        const f32x4 b1v = *(const f32x4*)(sm.b1 + hs * 4);
+        const f32x4 b2v = *(const f32x4*)(sm.b2 + hs * 4);
         auto xe = [&](int s, int ch) -> float { return bf2f(BF16::get(f.x[s], c4 + ch)); };
+        // Taps are taken in pairs on v_dot2c_f32_bf16 (products summed in fp32,
+        // then added to the running sum, which starts at the bias), an odd last
+        // tap by fma. xw(t) is the bf16 pair (tap t, tap t + 1) of one channel,
+        // xl() the last tap's input.
+        auto taps = [&](int ch, float acc, auto xw, auto xl) -> float {
+#pragma unroll
+          for (int t = 0; t + 1 < T0; t += 2) acc = dot2_pair(wd[ch * WPC + t / 2], xw(t), acc);
+          if constexpr ((T0 & 1) != 0)
+            acc = __builtin_fmaf(bf2f(wd[ch * WPC + T0 / 2] & 0xFFFFu), xl(), acc);
+          return acc;
+        };
         // depthwise of this row's request at position pos for the half; tap
         // `tap` reads raw slot base + tap when its ext position is >= 0, else
         // the request's history (zeros without state)
         auto dw = [&](int pos, int base) -> uint2 {
           float d[4];
-#pragma unroll
-          for (int ch = 0; ch < 4; ++ch) d[ch] = half_el(b1h, ch);
           if (pos >= T0 - 1) {
 #pragma unroll
-            for (int tap = 0; tap < T0; ++tap)
-#pragma unroll
-              for (int ch = 0; ch < 4; ++ch) d[ch] = __builtin_fmaf(w1(tap, ch), xe(base + tap, ch), d[ch]);
+            for (int ch = 0; ch < 4; ++ch)
+              d[ch] = taps(ch, b1v[ch],
+                           [&](int t) { return cca_pair(f.x[base + t], f.x[base + t + 1], c4 + ch); },
+                           [&]() { return xe(base + T0 - 1, ch); });
           } else {
             // near a request's start: the saved history (global reads, rare)
             int32_t hslot;
@@ -601,21 +655,26 @@ __device__ __forceinline__ void cca_persist_body(const CcaArgs& a, CcaSmem<T0>& 
 #pragma unroll
             for (int q = 0; q < N; ++q) hist[q] = hn ? ld16(hp + q * 8) : u32x4{0, 0, 0, 0};
 #pragma unroll
-            for (int tap = 0; tap < T0; ++tap) {
-              const int ep = pos - (T0 - 1) + tap;   // ext position of the tap
+            for (int ch = 0; ch < 4; ++ch) {
+              // bf16 bits of each tap's input: the raw row, or history entry
+              // N - q for ext position -q (zeros without state)
+              uint32_t xv[T0];
 #pragma unroll
-              for (int ch = 0; ch < 4; ++ch) {
-                float x = xe(base + tap, ch);
+              for (int tap = 0; tap < T0; ++tap) {
+                const int ep = pos - (T0 - 1) + tap;
+                uint32_t x = BF16::get(f.x[base + tap], c4 + ch);
                 if (ep < 0) {
-                  x = 0.f;
+                  x = 0u;
 #pragma unroll
-                  for (int q = 1; q <= N; ++q) {     // position -q = entry N - q
+                  for (int q = 1; q <= N; ++q) {
                     const int el = (c4 + ch) * N + N - q;
-                    if (ep == -q) x = bf2f(BF16::get(hist[el / 8], el % 8));
+                    if (ep == -q) x = BF16::get(hist[el / 8], el % 8);
                   }
                 }
-                d[ch] = __builtin_fmaf(w1(tap, ch), x, d[ch]);
+                xv[tap] = x;
               }
+              d[ch] = taps(ch, b1v[ch], [&](int t) { return xv[t] | (xv[t + 1] << 16); },
+                           [&]() { return bf2f(xv[T0 - 1]); });
             }
           }
           return uint2{pk_bf16(d[0], d[1]), pk_bf16(d[2], d[3])};
@@ -623,9 +682,10 @@ __device__ __forceinline__ void cca_persist_body(const CcaArgs& a, CcaSmem<T0>& 
         // residual + grouped bias, fp32
         float y[4];
         if constexpr (!isk) {
+          // b2 + 0.5 x + 0.5 k: both halves on one v_dot2c (exact products)
 #pragma unroll
           for (int ch = 0; ch < 4; ++ch)
-            y[ch] = half_el(b2h, ch) + 0.5f * (xe(T0, ch) + bf2f(BF16::get(f.r[0], c4 + ch)));
+            y[ch] = dot2_pair(0x3F003F00u, cca_pair(f.x[T0], f.r[0], c4 + ch), b2v[ch]);
         } else {
           // the mean over the bundle's q heads, summed in head order (the
           // rows of heads G .. GMAX-1 were read as zeros)
@@ -634,7 +694,7 @@ __device__ __forceinline__ void cca_persist_body(const CcaArgs& a, CcaSmem<T0>& 
             float s = 0.f;
 #pragma unroll
             for (int qi = 0; qi < GMAX; ++qi) s += bf2f(BF16::get(f.r[qi], c4 + ch));
-            y[ch] = half_el(b2h, ch) + 0.5f * __builtin_fmaf(s, inv_g, xe(T0, ch));
+            y[ch] = b2v[ch] + 0.5f * __builtin_fmaf(s, inv_g, xe(T0, ch));
           }
         }
         uint2 cur_dw = {0u, 0u};
@@ -650,14 +710,10 @@ __device__ __forceinline__ void cca_persist_body(const CcaArgs& a, CcaSmem<T0>& 
       }
       *(u32x4*)(sm.act + (i + 1) * AROW + v * 8) = u32x4{dwh[0].x, dwh[0].y, dwh[1].x, dwh[1].y};
     }
-    // value item of this tile, then the next tile's loads
-    u32x4 val = f.val;
-    const int vp = vitem ? rp[vr] : -1;
-    const int vsrc = vitem ? rsrc_[vr] : -1;
+    // the next tile's loads
     if (u + AHEAD < my_tiles) issue(u + AHEAD, f);
-    // store offsets of this tile (its row info is rewritten by a later batch)
+    // store offset of this tile (its row info is rewritten by a later batch)
     const uint32_t ooff = rp[i] >= 0 ? o_lane + ta * ors32 : kOff;
-    const uint32_t voff = vp >= 0 ? ov_lane + ta * ors32 : kOff;
     __syncthreads();
 
     // ---- (B) grouped conv on MFMA: this wave's 16 channels x 32 tokens ----
@@ -702,21 +758,9 @@ __device__ __forceinline__ void cca_persist_body(const CcaArgs& a, CcaSmem<T0>& 
       o.y = pk_bf16(acc[th][2] + rr.z, acc[th][3] + rr.w);
       *(uint2*)(sm.ost + n * AROW + cl) = o;
     }
-    // value item: a request's first token takes the saved delayed value (or
-    // delayed_init, or zeros) instead of the previous row
-    if (vitem && vvv >= nvv && vp == 0) {
-      int32_t slot;
-      bool hs;
-      cca_row_state(a, vsrc, slot, hs);
-      const int e8 = (vvv - nvv) * 8;
-      if (hs) val = ld16((const uint16_t*)a.delayed_state + (int64_t)slot * vd + e8);
-      else if (a.delayed_init) val = ld16((const uint16_t*)a.delayed_init + e8);
-      else val = u32x4{0, 0, 0, 0};
-    }
     __syncthreads();
-    // full 256-byte row segments of the group's output columns, and the value item
+    // full 256-byte row segments of the group's output columns
     bst16_stream(obuf, ooff, *(const u32x4*)(sm.ost + i * AROW + v * 8));
-    if constexpr (!isk) bst16_stream(obuf, voff, val);
   };
 
   if constexpr (AHEAD == 1) {
@@ -801,7 +845,9 @@ hipError_t launch_cca(const CcaArgs& a, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int reqs = a.num_decodes + a.num_prefills;
-  if (reqs > 0 && a.num_slots > 0) {
+  // (the MFMA path's state update also completes the request-start value
+  // columns, so it runs even without a pool)
+  if (reqs > 0 && (a.num_slots > 0 || mfma)) {
     const int n = a.t0 + a.t1 - 2;
     if (mfma && n >= 1 && n <= 4) {
       switch (n) {
