@@ -710,11 +710,14 @@ __device__ __forceinline__ void cca_persist_body(const CcaArgs& a, CcaSmem<T0>& 
       }
       *(u32x4*)(sm.act + (i + 1) * AROW + v * 8) = u32x4{dwh[0].x, dwh[0].y, dwh[1].x, dwh[1].y};
     }
-    // the next tile's loads
-    if (u + AHEAD < my_tiles) issue(u + AHEAD, f);
     // store offset of this tile (its row info is rewritten by a later batch)
     const uint32_t ooff = rp[i] >= 0 ? o_lane + ta * ors32 : kOff;
     __syncthreads();
+    // the next tile's loads, issued after the barrier: the eight waves'
+    // load instructions queue for the CU's vector memory unit one behind
+    // another, and each wave then goes on to its MFMAs instead of waiting at
+    // the barrier for the last wave's loads to be accepted
+    if (u + AHEAD < my_tiles) issue(u + AHEAD, f);
 
     // ---- (B) grouped conv on MFMA: this wave's 16 channels x 32 tokens ----
     f32x4 acc[2];
