@@ -24,23 +24,39 @@ __device__ __forceinline__ int logical_block(int n_logical, int per_xcd) {
 // Chunk ids of request r are [base(r), base(r+1)) with
 // base(r) = floor(qsl[r] / chunk) + r, an upper bound on the chunks the request
 // needs that is monotone in r and computable per request. So the request owning
-// chunk id `id` is #{i in [1, B] : base(i) <= id}, counted wave-parallel.
+// chunk id `id` is #{i in [1, B] : base(i) <= id}, counted wave-parallel. The
+// predicate base(i) <= id holds for i up to the answer and fails after it, so
+// up to B = 4096 two rounds of loads find it: 64 evenly spaced samples (every
+// step-th index, step = ceil(B / 64)) locate the segment between two samples
+// that holds the boundary, then the step - 1 indices inside it are counted.
+// Larger batches count every index in rounds of 64.
 // Must be called by full waves (uses ballot).
 __device__ __forceinline__ int find_request(const int32_t* qsl, int B, int id, int chunk) {
   const int lane = (int)(threadIdx.x & 63);
-  int cnt = 0;
-  for (int i0 = 1; i0 <= B; i0 += 64) {
-    const int i = i0 + lane;
-    bool p = false;
-    if (i <= B) p = (qsl[i] / chunk + i) <= id;
-    cnt += __popcll(__ballot(p));
+  if (B > 4096) {
+    int cnt = 0;
+    for (int i0 = 1; i0 <= B; i0 += 64) {
+      const int i = i0 + lane;
+      bool p = false;
+      if (i <= B) p = (qsl[i] / chunk + i) <= id;
+      cnt += __popcll(__ballot(p));
+    }
+    return cnt;
   }
-  return cnt;
+  const int step = (B + 63) >> 6;                  // 1 .. 64
+  const int i1 = (lane + 1) * step;                // samples step, 2 step, ... (those <= B)
+  bool p1 = false;
+  if (i1 <= B) p1 = (qsl[i1] / chunk + i1) <= id;
+  const int c1 = __popcll(__ballot(p1));           // the answer is in [c1 step, (c1 + 1) step)
+  const int i2 = c1 * step + 1 + lane;
+  bool p2 = false;
+  if (lane < step - 1 && i2 <= B) p2 = (qsl[i2] / chunk + i2) <= id;
+  return c1 * step + __popcll(__ballot(p2));
 }
 
 // Request lookup that also returns qsl[r] and qsl[r+1]. With B < 64 every
 // needed entry is loaded once by one lane (lane l holds qsl[l]) and read back
-// with readlane; larger batches fall back to find_request plus two loads.
+// with readlane; larger batches use find_request plus two loads.
 // Must be called by full waves.
 __device__ __forceinline__ int find_request_bounds(const int32_t* qsl, int B, int id, int chunk,
                                                    int& s0, int& s1) {
