@@ -262,10 +262,12 @@ typedef struct {
  * state), then prefill rows with offsets prefill_qsl (rebased to 0).
  * With C = (nq+nkv)*hd raw channels [q | k] and n = t0+t1-2:
  *   dw   = depthwise conv (t0 taps, bias) of [history, raw], materialised in
- *          bf16: an fp32 fused multiply-add chain (bias first, taps in order)
- *          rounded to bf16, which is the exact value rounded once except
- *          where the chain's own rounding moves it across a bf16 midpoint
- *          (a few values in 10^7 on normally distributed data)
+ *          bf16: summed in fp32 from the bias (hd = 128, t1 = 2: taps in
+ *          pairs on the two-term bf16 dot product; other shapes: a fused
+ *          multiply-add chain in tap order) and rounded to bf16, which is the
+ *          exact value rounded once except where the fp32 sum's own rounding
+ *          moves it across a bf16 midpoint (a few values in 10^7 on normally
+ *          distributed data)
  *   yg   = grouped conv (nq+nkv groups of hd, t1 taps, bias) of dw, fp32 acc.
  *   out row = [yg_q + 0.5(q + k of the head's kv group) |
  *              yg_k + mean over the group's q heads of that residual |
