@@ -294,6 +294,188 @@ __global__ __launch_bounds__(kBlock) void conv_rollbuf(ConvArgs a) {
   }
 }
 
+// DS pool, K = 4, d = 1 (H = 3), bf16, S entries known at compile time. The
+// workgroup's state region is staged through LDS with unit-stride lanes as in
+// conv_rollbuf, but each lane then reads its own S vectors whole and turns
+// them in registers from channel-major (element ch * S + e) into S entry
+// vectors (element ch of entry e, the SD order), so the window read at the
+// acceptance offset, the roll and the new tokens are whole 16-byte vectors
+// picked by workgroup-uniform selects instead of 16-bit LDS accesses.
+// Same arithmetic as conv_rollbuf (tap pairs on v_dot2c).
+template <int S, bool SILU, bool SPEC>
+__global__ __launch_bounds__(kBlock) void conv_rollbuf_ds(ConvArgs a) {
+  using E = BF16;
+  using St = E::S;
+  constexpr int K = 4, D = 1, H = 3, NP = 2, VEC = 8, QM = kSpecQMax;
+  static_assert(S >= H && S <= kSpecSMax, "state length");
+  __shared__ u32x4 region[kBlock * S];
+
+  const int lb = logical_block(a.n_logical, a.per_xcd);
+  if (lb < 0) return;                       // uniform over the workgroup
+  const int r = lb / a.n_cblk, cb = lb - r * a.n_cblk;
+  if (r >= a.batch) return;
+  const int tid = (int)threadIdx.x;
+  const int cbase = cb * kBlock * VEC;
+  const int c0 = cbase + tid * VEC;
+  const bool lane_ok = c0 < a.C;
+  int q = a.q;
+  int64_t start = (int64_t)r * q;
+  if (a.qsl) {   // a draft count per request; a.q bounds them all
+    start = a.qsl[r];
+    q = a.qsl[r + 1] - a.qsl[r];
+    if (q <= 0 || q > a.q || q > S || start < 0 || start + q > a.num_tokens) return;
+  }
+  const int nvec = (min(a.C - cbase, kBlock * VEC) / VEC) * S;
+
+  uint32_t wp[NP][VEC];
+  u32x4 bsv = u32x4{0, 0, 0, 0};
+  if (lane_ok) {
+    u32x4 wv[NP * 2];
+#pragma unroll
+    for (int v = 0; v < NP * 2; ++v) wv[v] = ld16((const St*)a.w + (int64_t)c0 * K + v * VEC);
+#pragma unroll
+    for (int ch = 0; ch < VEC; ++ch)
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        const int word = ch * NP + p;
+        wp[p][ch] = wv[word >> 2][word & 3];
+      }
+    if (a.bias) bsv = ld16((const St*)a.bias + c0);
+  }
+  u32x4 xr[QM];
+#pragma unroll
+  for (int u = 0; u < QM; ++u)
+    xr[u] = (u < q && lane_ok) ? ld16_stream((const St*)a.x + (start + u) * a.x_rs + c0)
+                               : u32x4{0, 0, 0, 0};
+  const int32_t slot = a.slots[(int64_t)r * a.slot_stride];
+  const bool valid = slot >= 0 && slot < a.num_slots;
+  bool hist = valid;
+  int acc = 1;
+  if constexpr (SPEC) {
+    acc = min(max(a.num_acc[r], 1), min(q, S - H + 1));
+  } else {
+    hist = valid && (a.has_init ? uniform_flag(a.has_init, r) : true);
+  }
+  St* const sp = (St*)a.pool + ((int64_t)(valid ? slot : 0) * a.C + cbase) * S;
+  if (valid) {
+    u32x4 sv[S];
+#pragma unroll
+    for (int k = 0; k < S; ++k) {
+      const int vi = tid + k * kBlock;
+      sv[k] = vi < nvec ? ld16_stream(sp + vi * VEC) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int k = 0; k < S; ++k) {
+      const int vi = tid + k * kBlock;
+      if (vi < nvec) region[vi] = sv[k];
+    }
+  }
+  __syncthreads();
+
+  // the lane's channel-major vectors, then its entry vectors
+  u32x4 ent[S];
+  {
+    u32x4 cm[S];
+#pragma unroll
+    for (int k = 0; k < S; ++k)
+      cm[k] = (valid && lane_ok) ? region[tid * S + k] : u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int e = 0; e < S; ++e)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const int m0 = (2 * w) * S + e, m1 = (2 * w + 1) * S + e;   // channels 2w, 2w+1
+        const uint32_t b0 = 2u * (uint32_t)(m0 & 1), b1 = 4u + 2u * (uint32_t)(m1 & 1);
+        ent[e][w] = __builtin_amdgcn_perm(cm[m1 >> 3][(m1 & 7) >> 1], cm[m0 >> 3][(m0 & 7) >> 1],
+                                          b0 | ((b0 + 1) << 8) | (b1 << 16) | ((b1 + 1) << 24));
+      }
+  }
+
+  // window: entries acc-1 .. acc+H-2 (speculative) or 0 .. H-1; zeros without history
+  u32x4 raw[H + QM];
+#pragma unroll
+  for (int u = 0; u < H; ++u) {
+    u32x4 wv = ent[u];
+    if constexpr (SPEC) {
+#pragma unroll
+      for (int av = 2; av <= S - H + 1; ++av)
+        if (acc == av) wv = ent[av - 1 + u];
+    }
+    raw[u] = hist ? wv : u32x4{0, 0, 0, 0};
+  }
+#pragma unroll
+  for (int u = 0; u < QM; ++u) raw[H + u] = xr[u];
+
+  if (lane_ok) {
+    float bs[VEC];
+    E::unpack(bsv, bs);
+#pragma unroll
+    for (int u = 0; u < QM; ++u) {
+      if (u < q) {
+        float z[VEC];
+#pragma unroll
+        for (int ch = 0; ch < VEC; ++ch) {
+          float accf = bs[ch];
+#pragma unroll
+          for (int p = 0; p < NP; ++p) {
+            const int r0 = H + u - (K - 1 - 2 * p) * D;
+            accf = dot2_bf16(wp[p][ch], row_pair(raw[r0], raw[r0 + D], ch), accf);
+          }
+          z[ch] = SILU ? silu(accf) : accf;
+        }
+        st16_stream((St*)a.out + (start + u) * a.out_rs + c0, E::pack(z));
+      }
+    }
+  }
+  if (!valid) return;                       // uniform over the workgroup
+
+  // new entries: speculative, entry j = old entry acc + j for j < S - q, then
+  // the q tokens; plain, entries j < H = ext[q + j] (ext = window, tokens)
+  u32x4 nent[S];
+#pragma unroll
+  for (int j = 0; j < S; ++j) {
+    if constexpr (SPEC) {
+      u32x4 roll = u32x4{0, 0, 0, 0}, tok = u32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int av = 1; av + j < S; ++av)
+        if (acc == av) roll = ent[av + j];
+#pragma unroll
+      for (int u = 0; u < QM; ++u)
+        if (u == j - (S - q)) tok = xr[u];
+      nent[j] = j < S - q ? roll : tok;
+    } else {
+      u32x4 v = ent[j];
+      if (j < H) {
+#pragma unroll
+        for (int e = 0; e < H + QM; ++e)
+          if (e == q + j) v = raw[e];
+      }
+      nent[j] = v;
+    }
+  }
+  // back to channel-major, into the lane's own region slots
+  if (lane_ok) {
+#pragma unroll
+    for (int k = 0; k < S; ++k) {
+      u32x4 cm;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const int m0 = 8 * k + 2 * w, m1 = m0 + 1;     // elements (channel, entry) = divmod(m, S)
+        const int ch0 = m0 / S, e0 = m0 % S, ch1 = m1 / S, e1 = m1 % S;
+        const uint32_t b0 = 2u * (uint32_t)(ch0 & 1), b1 = 4u + 2u * (uint32_t)(ch1 & 1);
+        cm[w] = __builtin_amdgcn_perm(nent[e1][ch1 >> 1], nent[e0][ch0 >> 1],
+                                      b0 | ((b0 + 1) << 8) | (b1 << 16) | ((b1 + 1) << 24));
+      }
+      region[tid * S + k] = cm;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < S; ++k) {
+    const int vi = tid + k * kBlock;
+    if (vi < nvec) st16_stream(sp + vi * VEC, region[vi]);
+  }
+}
+
 // Any K <= 8, dilation, S, q and alignment: one channel a lane, entries read
 // and rolled in place in global memory.
 template <class E, bool SILU>
@@ -361,6 +543,22 @@ hipError_t launch_rollbuf(const ConvArgs& a, int K, int D, dim3 grid, hipStream_
   const size_t lds = a.sd ? (size_t)kBlock * a.S * sizeof(u32x4)
                           : (size_t)kBlock * ds_lane_words(a.S, kBlock) * 4;
   const dim3 blk(kBlock);
+  if constexpr (E::VEC == 8 && !FUSE) {
+    // DS pool, width 4, no dilation: entries transposed in registers
+    if (!a.sd && K == 4 && D == 1 && a.S >= 3 && a.S <= 10) {
+      switch (a.S) {
+        case 3: hipLaunchKernelGGL((conv_rollbuf_ds<3, SILU, SPEC>), grid, blk, 0, s, a); break;
+        case 4: hipLaunchKernelGGL((conv_rollbuf_ds<4, SILU, SPEC>), grid, blk, 0, s, a); break;
+        case 5: hipLaunchKernelGGL((conv_rollbuf_ds<5, SILU, SPEC>), grid, blk, 0, s, a); break;
+        case 6: hipLaunchKernelGGL((conv_rollbuf_ds<6, SILU, SPEC>), grid, blk, 0, s, a); break;
+        case 7: hipLaunchKernelGGL((conv_rollbuf_ds<7, SILU, SPEC>), grid, blk, 0, s, a); break;
+        case 8: hipLaunchKernelGGL((conv_rollbuf_ds<8, SILU, SPEC>), grid, blk, 0, s, a); break;
+        case 9: hipLaunchKernelGGL((conv_rollbuf_ds<9, SILU, SPEC>), grid, blk, 0, s, a); break;
+        default: hipLaunchKernelGGL((conv_rollbuf_ds<10, SILU, SPEC>), grid, blk, 0, s, a); break;
+      }
+      return hipGetLastError();
+    }
+  }
   if (K == 4 && D == 1) hipLaunchKernelGGL((conv_rollbuf<E, 4, 1, SILU, SPEC, FUSE>), grid, blk, lds, s, a);
   else if (K == 4 && D == 2) hipLaunchKernelGGL((conv_rollbuf<E, 4, 2, SILU, SPEC, FUSE>), grid, blk, lds, s, a);
   else if (K == 4 && D == 3) hipLaunchKernelGGL((conv_rollbuf<E, 4, 3, SILU, SPEC, FUSE>), grid, blk, lds, s, a);

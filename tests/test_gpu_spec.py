@@ -163,6 +163,34 @@ def test_wide_buffer_nonspec_calls(q, d, dtype):
     check_close(out, ref, absum, dtype, FLOOR)
 
 
+@pytest.mark.parametrize("n", [0, 1, 2, 3, 4, 5, 6, 7])
+@pytest.mark.parametrize("C", [1000, 2056])
+def test_ds_register_path_every_buffer_length(n, C):
+    """Width 4, no dilation, bf16, DS pool, S = 3 + n: the entries are
+    transposed in registers. Speculative calls (counts out of range included,
+    a padding slot) and plain calls on the same widened buffer, with channel
+    counts that leave a workgroup's last lanes empty."""
+    S = 3 + n
+    rng = np.random.default_rng(3800 + 17 * n + C)
+    for q in sorted({1, min(n + 1, S), S}):
+        act = "silu" if (q + n) % 2 else "none"
+        case = conv_case("spec_ds", 3800 + 31 * n + q + C, C=C, K=4, d=1, dtype="bf16",
+                         act=act, w_std=0.4, bias_std=0.2, num_slots=64, num_decodes=29,
+                         q=q, num_spec=n)
+        case.decode_slots[5] = -1
+        acc = rng.integers(-1, S + 3, size=29).astype(np.int32)
+        spec_parity(case, acc)
+        wide = conv_case("wide_ds", 3900 + 31 * n + q + C, C=C, K=4, d=1, dtype="bf16",
+                         act=act, w_std=0.4, bias_std=0.2, num_slots=64, num_decodes=29,
+                         q=q, num_spec=n)
+        wide.decode_h = (np.arange(29) % 3 != 1).astype(np.uint8)
+        wide.decode_slots[7] = -1
+        out, pool = run_conv_case(wide)
+        ref, ref_pool, absum = oracle.conv(wide, out_dtype="f64", absum=True)
+        np.testing.assert_array_equal(pool, ref_pool, err_msg=f"wide q={q}: pool not bit-exact")
+        check_close(out, ref, absum, "bf16", FLOOR)
+
+
 def test_spec_zero_work_and_errors():
     import torch
     import stateful_causal_short_amd as scs
