@@ -9,7 +9,8 @@ U{1..2048}, 8192 channels, width 4, bf16, bias + SiLU, 64-slot state pool):
 state gather, conv, bias, SiLU and state write-back in one kernel; `value` is
 its tokens/s. The same JSON line carries secondary objects for the method's
 other workloads, each timed the same way in the same process: "decode" (512
-requests x 1 token), "update_q4" (128 requests x 4 tokens), "ple_mixed"
+requests x 1 token), "update_q4" (128 requests x 4 tokens), "spec" (128
+requests x 4 speculative tokens on a 6-entry rolling buffer), "ple_mixed"
 (dilated PLE batch: 256 decodes + 16 prefills with checkpoints; each kernel
 and their sum) and "cca" (the 32k-token CCA q/k conv, main kernel + state
 update), plus "copy_ceiling" (the practical HBM ceiling of a plain copy) and,
@@ -623,6 +624,34 @@ def traffic_from(d):
 # ---------------------------------------------------------------------------
 # parity of a timed batch (outside the timed region)
 # ---------------------------------------------------------------------------
+def spec_parity(case, run, acc):
+    """conv_parity for the speculative update: the oracle's rolling buffer
+    with the same accepted counts."""
+    import numpy as np
+    import torch
+    import oracle
+    from tests._gpu import check_close, dev, host
+    x, out, pool, _ = run.sets[0]
+    pool.copy_(dev(case.pool))
+    out.zero_()
+    run.step(0)
+    torch.cuda.synchronize()
+    got, gpool = host(out), host(pool)
+    ref, rpool, ab = oracle.conv_spec(case, acc, out_dtype="f64", absum=True)
+    res = {"reference": "oracle", "rows_checked": int(case.T), "elements": int(ref.size),
+           "state_bit_exact": bool(np.array_equal(gpool, rpool))}
+    try:
+        share = check_close(got, ref, ab, case.dtype, 2.0 ** -20)
+        res["outputs_within_tolerance"] = True
+        res["floor_passes"] = int(round(share * ref.size))
+    except AssertionError as e:
+        res["outputs_within_tolerance"] = False
+        res["floor_passes"] = None
+        res["error"] = str(e)[:300]
+    res["pass"] = res["state_bit_exact"] and res["outputs_within_tolerance"]
+    return res
+
+
 def conv_parity(case, run):
     """Restores buffer set 0 to the batch's pristine state, runs one step and
     checks it against the oracle on the same inputs: state pool bit-exact, every
@@ -764,9 +793,9 @@ def measure_conv(args, workload, *, parity=True, quiet=False):
         tot = sum(kms.values())
         res["kernels_sum_us"] = tot * 1e3
         res["roofline_sum"] = roofline("+".join(kms), sum(kb[k] for k in kms), tot * 1e3)
-    if parity and acc is None and not fused:
+    if parity and not fused:
         log(f"{case.name}: parity against the oracle ...")
-        res["parity"] = conv_parity(case, run)
+        res["parity"] = conv_parity(case, run) if acc is None else spec_parity(case, run, acc)
         log(f"{case.name}: parity {'pass' if res['parity']['pass'] else 'FAIL'}")
     return case, run, res, acc, fused
 
@@ -910,7 +939,7 @@ def main():
         # method ride along as secondary objects (each timed the same way, in
         # the same process; `value` stays the varlen prefill's).
         for name, wl in (("decode", "decode"), ("update_q4", "update_q4"),
-                         ("ple_mixed", "ple_mixed")):
+                         ("spec", "spec"), ("ple_mixed", "ple_mixed")):
             _, r2, res2, _, _ = measure_conv(args, wl, parity=not args.no_parity)
             result[name] = res2
             del r2
