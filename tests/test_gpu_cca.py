@@ -5,12 +5,14 @@ and delayed shift) bit-exact; q/k outputs within 2 bf16 ulp of the oracle's
 float64 result, or within the fp32 accumulation bound n * 2^-24 of the sum of
 |terms| (n = bias + hd*t1 products + residual terms). Every output row is
 checked. The oracle takes the depthwise intermediate as the layer's first
-Conv1d materialises it: the exact value rounded once to bf16. The kernel
-rounds an fp32 fused multiply-add chain (bias first, taps in order); the
-oracle counts, as a diagnostic, the depthwise values where such a chain rounds
-to a different bf16 value, and each test prints that count. Where it does, the
-grouped stage moves the output by at most |W2| times one bf16 spacing of the
-depthwise value, inside the output tolerance."""
+Conv1d materialises it: the exact value rounded once to bf16. The kernel sums
+it in fp32 from the bias (taps in pairs on the two-term dot product on the
+MFMA path, a fused multiply-add chain in tap order otherwise), which can land
+on the other side of a bf16 midpoint; the oracle counts, as a diagnostic, the
+depthwise values where an fp32 fused multiply-add chain rounds to a different
+bf16 value, and each test prints that count. Where the kernel's value differs,
+the grouped stage moves the output by at most |W2| times one bf16 spacing of
+the depthwise value, inside the output tolerance."""
 from dataclasses import replace
 
 import numpy as np
@@ -94,6 +96,20 @@ def test_padding_slots_fused_rows_and_no_delayed_init():
     case.prefill_slots[1] = -5
     case.prefill_h[:] = 1
     parity(case, fused=True, no_delayed_init=True)
+
+
+@pytest.mark.parametrize("no_init", [False, True])
+def test_empty_state_pool(no_init):
+    # zero slots: every request is a padding row, so histories are zeros and the
+    # first token of each request takes delayed_init (or zeros) as its delayed
+    # value; nothing is written to the (empty) pools
+    case = synthetic.cca_case("cca_nopool", 803 + int(no_init), num_decodes=5,
+                              prefill_lens=[3, 40, 1, 70], num_slots=16)
+    n = case.t0 + case.t1 - 2
+    vd = case.nkv * case.hd // 2
+    case = replace(case, conv_state=np.zeros((0, case.C, n), case.conv_state.dtype),
+                   delayed_state=np.zeros((0, vd), case.delayed_state.dtype))
+    parity(case, no_delayed_init=no_init)
 
 
 def test_gpu_cca_chunked_equals_one_shot():
