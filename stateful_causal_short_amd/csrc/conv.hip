@@ -256,7 +256,8 @@ __global__ __launch_bounds__(kBlock) void conv_pairs(ConvArgs a) {
     if (a.bias && lane_ok) bsv = ld16((const S*)a.bias + c0);
   }
 
-  // chunk -> request (one round of loads), bounds and chunk range
+  // chunk -> request (one round of loads below 64 requests, three from 64 on:
+  // two for the request, one for its bounds), bounds and chunk range
   // (the launcher sets a.chunk = U for this kernel; U as a constant turns the
   // divisions below into multiplies)
   int r, s0 = 0, s1 = 0;
