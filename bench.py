@@ -444,27 +444,10 @@ def spec_varlen_bench(args):
 def cca_bench(args):
     """CCA q/k conv on the 32k-token mixed batch (512 decodes + 64 prefills,
     16 q heads, 4 kv heads, head_dim 128, kernels 2 and 2). One step = one
-    sc_cca_qk_conv call: the fused main kernel, then the state update."""
-    import numpy as np
-    import torch
-    import synthetic
-    case = synthetic.cca_mixed_32k()
-    main_b, upd_b = cca_alg_bytes(case)
-    nsets = rotation_sets(main_b + upd_b, main_b + upd_b)
-    log(f"CCA T={case.T} C={case.C}; alg bytes/step main={main_b} state={upd_b}; "
-        f"{nsets} rotating buffer sets")
-    run = CcaRunner(case, nsets)
-    for i in range(args.warmup):
-        run.step(i)
-    torch.cuda.synchronize()
-    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    s.record()
-    for i in range(args.steps):
-        run.step(args.warmup + i)
-    e.record()
-    torch.cuda.synchronize()
-    ms = s.elapsed_time(e) / args.steps
-    flops = 2.0 * case.T * case.C * case.hd * case.t1
+    sc_cca_qk_conv call: the fused main kernel, then the state update, timed
+    as the default line's CCA object is (measure_cca)."""
+    case, run, m = measure_cca(args, parity=not args.no_parity)
+    ms = m["step_us"] * 1e-3
     result = {
         "metric": "tokens/s and achieved HBM GB/s (% of peak), CCA q/k conv",
         "value": case.T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,
@@ -474,14 +457,13 @@ def cca_bench(args):
         "config": {"workload": case.name, "decodes": case.num_decodes,
                    "prefills": case.num_prefills, "tokens": case.T, "q_heads": case.nq,
                    "kv_heads": case.nkv, "head_dim": case.hd, "t0": case.t0, "t1": case.t1},
-        "hbm_gbps": (main_b + upd_b) / (ms * 1e-3) / 1e9,
-        "pct_peak": 100.0 * (main_b + upd_b) / (ms * 1e-3) / 1e9 / PEAK_GBPS,
-        "grouped_conv_tflops": flops / (ms * 1e-3) / 1e12,
-        "roofline": {"kernel": "cca_main+state", "bound": "hbm",
-                     "achieved": (main_b + upd_b) / (ms * 1e-3) / 1e9, "peak": PEAK_GBPS,
-                     "unit": "GB/s", "frac": (main_b + upd_b) / (ms * 1e-3) / 1e9 / PEAK_GBPS,
-                     "traffic": traffic_for("cca:cca_main+state", CCA_SOURCES),
-                     "alg_bytes_per_launch": main_b + upd_b},
+        "hbm_gbps": m["roofline"]["achieved"],
+        "pct_peak": 100.0 * m["roofline"]["frac"],
+        "grouped_conv_tflops": m["grouped_conv_tflops"],
+        "timing": m["timing"],
+        "rotating_sets": m["rotating_sets"],
+        "roofline": m["roofline"],
+        "parity": m.get("parity"),
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
@@ -698,8 +680,8 @@ def cca_parity(case, run):
     run.step(0)
     torch.cuda.synchronize()
     got, gcs, gds = host(out), host(cs), host(ds)
-    nd = []
-    ref, rcs, rds, ab = oracle.cca(case, out_dtype="f64", absum=True, chain_diff=nd)
+    nd, al = [], []
+    ref, rcs, rds, ab = oracle.cca(case, out_dtype="f64", absum=True, chain_diff=nd, allow=al)
     C = case.C
     res = {"reference": "oracle", "rows_checked": int(case.T), "elements": int(ref.size),
            "state_bit_exact": bool(np.array_equal(gcs, rcs) and np.array_equal(gds, rds)),
@@ -707,7 +689,8 @@ def cca_parity(case, run):
                synthetic.bf16_to_f32(got[:, C:]).astype(np.float64), ref[:, C:])),
            "depthwise_values_an_fp32_chain_rounds_elsewhere": nd[0]}
     try:
-        share = check_close(got[:, :C], ref[:, :C], ab[:, :C], "bf16", cca_floor_rel(case))
+        share = check_close(got[:, :C], ref[:, :C], ab[:, :C], "bf16", cca_floor_rel(case),
+                            allow=al[0][:, :C])
         res["outputs_within_tolerance"] = True
         res["floor_passes"] = int(round(share * ref[:, :C].size))
     except AssertionError as e:

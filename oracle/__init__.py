@@ -44,7 +44,7 @@ def lib():
         L.oracle_cca.argtypes = [I32, I32, I32, I32, I32, I32, I32, I32,
                                  P, I64, P, I64, P, I64, P, I64, P, I64, P,
                                  P, P, P, P, P, P, P, I32, I32, P, I64, I32, P, P,
-                                 I64, P, P, P, I32]
+                                 I64, P, P, P, P, I32]
         L.oracle_state_gather.restype = I32
         L.oracle_state_gather.argtypes = [I32, I64, P, I32, P, I64, I32, P]
         L.oracle_state_scatter.restype = I32
@@ -199,7 +199,8 @@ def conv_spec_varlen(case, num_accepted, qsl, *, out_dtype: Optional[str] = None
 
 def cca(case, *, out_dtype: Optional[str] = None, dw_mode: int = 2,
         absum: bool = False, row_mask: Optional[np.ndarray] = None,
-        nthreads: Optional[int] = None, io_override=None, chain_diff: Optional[list] = None):
+        nthreads: Optional[int] = None, io_override=None, chain_diff: Optional[list] = None,
+        allow: Optional[list] = None):
     """Run the CCA oracle on a :class:`synthetic.CcaCase`.
 
     Returns ``(out, conv_state_after, delayed_state_after, absum_or_None)``.
@@ -209,6 +210,10 @@ def cca(case, *, out_dtype: Optional[str] = None, dw_mode: int = 2,
     ``io_override`` = (dtype_name, dict of arrays) lets pins feed float64 copies.
     ``chain_diff``: a list that receives the number of depthwise values an fp32
     fma chain would round differently from the exact value (dw_mode 2, bf16).
+    ``allow``: a list that receives a (T, W) float64 array (dw_mode 2): for each
+    conv output, the most it moves when its depthwise inputs are summed in fp32
+    in any order before their rounding (zero where no input lies within the
+    fp32 summation bound of a rounding boundary; zero for value columns).
     """
     io = case.dtype
     arrs = dict(q=case.q, k=case.k, v_cur=case.v_cur, v_del=case.v_del,
@@ -230,6 +235,7 @@ def cca(case, *, out_dtype: Optional[str] = None, dw_mode: int = 2,
     ph = _c(case.prefill_h, np.uint8)
     rm = _c(row_mask, np.uint8)
     nd = np.zeros(1, np.int64) if chain_diff is not None else None
+    al = np.zeros((T, Wd), np.float64) if allow is not None else None
     rc = lib().oracle_cca(
         case.nq, case.nkv, case.hd, case.t0, case.t1, _DT[io], _DT[odt], dw_mode,
         _p(a["q"]), a["q"].shape[1], _p(a["k"]), a["k"].shape[1],
@@ -237,12 +243,14 @@ def cca(case, *, out_dtype: Optional[str] = None, dw_mode: int = 2,
         _p(out), Wd, _p(ab), _p(a["w_dw"]), _p(a["b_dw"]), _p(a["w_gr"]),
         _p(a["b_gr"]), _p(a["delayed_init"]), _p(a["conv_state"]),
         _p(a["delayed_state"]), case.num_slots, case.num_decodes, _p(dsl), 1,
-        case.num_prefills, _p(qsl), _p(psl), 1, _p(ph), _p(rm), _p(nd),
+        case.num_prefills, _p(qsl), _p(psl), 1, _p(ph), _p(rm), _p(nd), _p(al),
         nthreads or default_threads())
     if rc != 0:
         raise RuntimeError(f"oracle_cca failed: {rc}")
     if chain_diff is not None:
         chain_diff.append(int(nd[0]))
+    if allow is not None:
+        allow.append(al)
     return out, a["conv_state"], a["delayed_state"], ab
 
 

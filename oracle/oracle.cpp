@@ -155,6 +155,19 @@ bool exact_dw(int dt, double bias, const double* w, const double* x, int n, doub
   return true;
 }
 
+// Spread of the roundings to io dtype `dt` of the values within e of s: the
+// largest distance from r (the rounding of the exact value) to the rounding of
+// any value in [s - e, s + e]. Rounding to nearest is monotone, so those
+// roundings lie between the roundings of s - e and s + e. Zero unless a
+// rounding boundary lies within e of s.
+double round_spread(int dt, double s, double e, double r) {
+  if (dt == F64) return 0.0;
+  auto rnd = [&](double v) {
+    return dt == BF16 ? bf16_to_double(double_to_bf16(v)) : (double)(float)v;
+  };
+  return std::fmax(rnd(s + e) - r, r - rnd(s - e));
+}
+
 double ld(const void* p, int dt, int64_t i) {
   switch (dt) {
     case F32: return (double)((const float*)p)[i];
@@ -518,6 +531,12 @@ int oracle_conv_spec_varlen(int32_t C, int32_t K, int32_t d, int32_t S, int32_t 
 // dw_chain_diff (nullable; dw_mode 2, bf16): receives the number of depthwise
 // values that an fp32 fmaf chain (bias first, taps in order) would round to a
 // different bf16 value than the exact one (a diagnostic, not a result).
+// dw_allow (nullable, (T, W) doubles, dw_mode 2): for each conv output, the
+// most it can move when its depthwise inputs are summed in fp32 in any order
+// before the rounding to the io dtype: sum over its inputs of |W2| times the
+// rounding spread of that input, where the spread is taken over the values
+// within the fp32 summation bound gamma_{t0+1} (|b1| + sum |w1 x|) of the exact
+// sum (a tolerance term for the checker, not a result; zero for value columns).
 // Returns -4 if a depthwise sum is not exact even in binary128.
 int oracle_cca(int32_t nq, int32_t nkv, int32_t hd, int32_t t0, int32_t t1,
                int32_t io_dtype, int32_t out_dtype, int32_t dw_mode,
@@ -530,7 +549,7 @@ int oracle_cca(int32_t nq, int32_t nkv, int32_t hd, int32_t t0, int32_t t1,
                int64_t dstride, int32_t num_prefills, const int32_t* qsl_p,
                const int32_t* prefill_slots, int64_t pstride,
                const uint8_t* prefill_h, const uint8_t* row_mask,
-               int64_t* dw_chain_diff, int32_t nthreads) {
+               int64_t* dw_chain_diff, double* dw_allow, int32_t nthreads) {
   if (nq <= 0 || nkv <= 0 || hd <= 0 || t0 <= 0 || t1 <= 0 || nq % nkv) return -2;
   if (dw_mode < 0 || dw_mode > 2 || (dw_mode == 2 && t0 > 8)) return -2;
   if (!dtype_ok(io_dtype) || !dtype_ok(out_dtype)) return -3;
@@ -549,8 +568,14 @@ int oracle_cca(int32_t nq, int32_t nkv, int32_t hd, int32_t t0, int32_t t1,
   };
 
   // Conv part, one group (hd dw channels in, hd conv channels out) at a time.
+  // fp32 summation bound of bias + t0 products, any order (each product and
+  // each of the t0 additions rounded at most once), plus the double sum's own
+  // rounding
+  const double u32 = std::ldexp(1.0, -24);
+  const double gam = (t0 + 1) * u32 / (1.0 - (t0 + 1) * u32) + (t0 + 1) * std::ldexp(1.0, -52);
+  const bool want_allow = dw_allow && dw_mode == 2;
   auto groups = [&](int g0, int g1) {
-    std::vector<double> ext, dw;
+    std::vector<double> ext, dw, spr;
     bool inexact = false;
     int64_t ndiff = 0;
     for (const Req& r : reqs) {
@@ -561,6 +586,7 @@ int oracle_cca(int32_t nq, int32_t nkv, int32_t hd, int32_t t0, int32_t t1,
         // ext and dw for the group's input channels, indexed [j][u]
         ext.assign((size_t)hd * E, 0.0);
         dw.assign((size_t)hd * E, 0.0);
+        if (want_allow) spr.assign((size_t)hd * E, 0.0);
         for (int j = 0; j < hd; ++j) {
           const int c = g * hd + j;
           double* e = &ext[(size_t)j * E];
@@ -580,6 +606,14 @@ int oracle_cca(int32_t nq, int32_t nkv, int32_t hd, int32_t t0, int32_t t1,
                 xa[a] = e[u - (t0 - 1) + a];
               }
               if (!exact_dw(io_dtype, ld(b_dw, io_dtype, c), wa, xa, t0, &v)) inexact = true;
+              if (want_allow) {
+                double sd = ld(b_dw, io_dtype, c), A1 = std::fabs(sd);
+                for (int a = 0; a < t0; ++a) {
+                  sd += wa[a] * xa[a];
+                  A1 += std::fabs(wa[a] * xa[a]);
+                }
+                spr[(size_t)j * E + u] = round_spread(io_dtype, sd, gam * A1, v);
+              }
               if (dw_chain_diff && io_dtype == BF16) {
                 // diagnostic: would an fp32 fmaf chain (bias first) round elsewhere?
                 float acc = (float)ld(b_dw, io_dtype, c);
@@ -607,13 +641,14 @@ int oracle_cca(int32_t nq, int32_t nkv, int32_t hd, int32_t t0, int32_t t1,
           if (row_mask && !row_mask[row]) continue;
           for (int oo = 0; oo < hd; ++oo) {
             const int o = g * hd + oo;
-            double y = ld(b_gr, io_dtype, o), A = std::fabs(y);
+            double y = ld(b_gr, io_dtype, o), A = std::fabs(y), allow = 0.0;
             for (int j = 0; j < hd; ++j)
               for (int b = 0; b < t1; ++b) {
-                double term = ld(w_gr, io_dtype, ((int64_t)o * hd + j) * t1 + b) *
-                              dw[(size_t)j * E + u - (t1 - 1) + b];
+                const double w2 = ld(w_gr, io_dtype, ((int64_t)o * hd + j) * t1 + b);
+                double term = w2 * dw[(size_t)j * E + u - (t1 - 1) + b];
                 y += term;
                 A += std::fabs(term);
+                if (want_allow) allow += std::fabs(w2) * spr[(size_t)j * E + u - (t1 - 1) + b];
               }
             double res;
             if (o < qdim) {   // query head h = g, paired key head h / G
@@ -634,6 +669,7 @@ int oracle_cca(int32_t nq, int32_t nkv, int32_t hd, int32_t t0, int32_t t1,
             }
             st(out, out_dtype, row * out_rs + o, y + res);
             if (absum) absum[row * W + o] = A;
+            if (dw_allow) dw_allow[row * W + o] = allow;
           }
         }
         if (valid)
@@ -667,6 +703,10 @@ int oracle_cca(int32_t nq, int32_t nkv, int32_t hd, int32_t t0, int32_t t1,
         if (absum) {
           absum[row * W + C + e] = 0.0;
           absum[row * W + C + vd + e] = 0.0;
+        }
+        if (dw_allow) {
+          dw_allow[row * W + C + e] = 0.0;
+          dw_allow[row * W + C + vd + e] = 0.0;
         }
       }
     }

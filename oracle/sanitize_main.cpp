@@ -50,7 +50,7 @@ int oracle_cca(int32_t nq, int32_t nkv, int32_t hd, int32_t t0, int32_t t1, int3
                const int32_t* decode_slots, int64_t dstride, int32_t num_prefills,
                const int32_t* qsl_p, const int32_t* prefill_slots, int64_t pstride,
                const uint8_t* prefill_h, const uint8_t* row_mask, int64_t* dw_chain_diff,
-               int32_t nthreads);
+               double* dw_allow, int32_t nthreads);
 int oracle_state_gather(int32_t elsize, int64_t row_elems, const void* pool, int32_t num_slots,
                         const int32_t* idx, int64_t idx_stride, int32_t n, void* dense);
 int oracle_state_scatter(int32_t elsize, int64_t row_elems, const void* dense,
@@ -171,13 +171,13 @@ void cca_batch(int nq, int nkv, int hd, int t0, int t1, int dw_mode, int odt) {
   auto wgr = randbuf(1, (size_t)C * hd * t1), bgr = randbuf(1, C), di = randbuf(1, vd);
   auto cs = randbuf(1, (size_t)slots * C * n), ds = randbuf(1, (size_t)slots * vd);
   auto out = randbuf(odt, (size_t)T * W);
-  std::vector<double> ab((size_t)T * W);
+  std::vector<double> ab((size_t)T * W), allow((size_t)T * W);
   int64_t diff = -1;
   expect(oracle_cca(nq, nkv, hd, t0, t1, 1, odt, dw_mode, qb.data(), nq * hd, kb.data(),
                     nkv * hd, vc.data(), vd, vdl.data(), vd, out.data(), W, ab.data(),
                     wdw.data(), bdw.data(), wgr.data(), bgr.data(), di.data(), cs.data(),
                     ds.data(), slots, nd, dsl.data(), 1, np, qsl.data(), psl.data(), 1,
-                    ph.data(), mask.data(), dw_mode == 2 ? &diff : nullptr, 3),
+                    ph.data(), mask.data(), dw_mode == 2 ? &diff : nullptr, allow.data(), 3),
          "oracle_cca");
 }
 

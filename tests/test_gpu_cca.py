@@ -32,8 +32,9 @@ def parity(case, **kw):
     ocase = case
     if kw.get("no_delayed_init"):
         ocase = replace(case, delayed_init=np.zeros_like(case.delayed_init))
-    nd = []
-    ref, rcs, rds, absum = oracle.cca(ocase, out_dtype="f64", absum=True, chain_diff=nd)
+    nd, al = [], []
+    ref, rcs, rds, absum = oracle.cca(ocase, out_dtype="f64", absum=True, chain_diff=nd,
+                                      allow=al)
     np.testing.assert_array_equal(cs, rcs, err_msg="conv state not bit-exact")
     np.testing.assert_array_equal(ds, rds, err_msg="delayed state not bit-exact")
     C = case.C
@@ -41,7 +42,7 @@ def parity(case, **kw):
     np.testing.assert_array_equal(synthetic.bf16_to_f32(out[:, C:]).astype(np.float64),
                                   ref[:, C:], err_msg="value half not bit-exact")
     frac = check_close(out[:, :C], ref[:, :C], absum[:, :C], "bf16", cca_floor_rel(case),
-                       what="q/k")
+                       what="q/k", allow=al[0][:, :C])
     print(f"[gpu] cca {case.name}: ok (floor-only share {frac:.2e}; depthwise values an "
           f"fp32 chain rounds elsewhere: {nd[0]} of {case.T * case.C})", flush=True)
 
@@ -85,6 +86,41 @@ def test_many_short_and_empty_prefills(nq, nkv):
     case = synthetic.cca_case("cca_many", 951 + nq, nq=nq, nkv=nkv, hd=128, num_decodes=37,
                               prefill_lens=lens, num_slots=1200)
     assert (case.T + 31) // 32 > 2 * 256 // (nq + nkv)
+    parity(case)
+
+
+def kv_helper_split(T, nq, nkv, cus=256):
+    """The launcher's tile split on a device with `cus` compute units: S main
+    workgroups per head group (as many as fit resident), and for each kv-head
+    group `hp` helpers taking its tiles from `jk * S` on (hp = 0: no helpers)."""
+    ntiles = (T + 31) // 32
+    per_cu = 2 if nq // nkv <= 4 else 1           # t0 = 2
+    NG = nq + nkv
+    S = min(max(cus * per_cu // NG, 1), ntiles)
+    hp = (cus * per_cu - S * NG) // nkv
+    if hp > 0 and S >= 8:
+        jk = -(-ntiles // (S + hp))
+        if jk * S < ntiles:
+            return S, hp, jk
+    return S, 0, 0
+
+
+@pytest.mark.parametrize("nq,nkv,decodes,lens", [
+    (16, 4, 100, [1200, 3, 2000, 1697]),          # 157 tiles: helpers take 150-156
+    (4, 2, 40, [2450, 3000]),                     # 172 tiles: one helper takes 170-171
+    (8, 1, 64, [9000, 7, 10929]),                 # 625 tiles: four helpers take 560-624
+])
+def test_kv_head_helpers(nq, nkv, decodes, lens):
+    """Batches whose tile count makes the launcher split the kv-head groups'
+    tiles between their main workgroups and helpers (with a ragged share among
+    the helpers), checked on every row."""
+    T = decodes + sum(lens)
+    S, hp, jk = kv_helper_split(T, nq, nkv)
+    assert hp > 0 and jk * S < (T + 31) // 32
+    case = synthetic.cca_case("cca_kvhelp", 960 + nq, nq=nq, nkv=nkv, hd=128,
+                              num_decodes=decodes, prefill_lens=lens,
+                              num_slots=decodes + len(lens) + 8)
+    case.prefill_h[:] = 1
     parity(case)
 
 
