@@ -327,11 +327,12 @@ __global__ __launch_bounds__(kBlock) void cca_state_update_vec(CcaArgs a) {
 
 // ---------------------------------------------------------------------------
 // MFMA main kernel (hd = 128, t1 = 2, t0 = T0 <= 4): persistent and
-// weight-stationary. The grid holds a multiple of NG = nq + nkv workgroups;
-// workgroup (head group grp, lane k0) walks the 32-row tiles k0, k0 + S,
-// k0 + 2S, ... (S = workgroups per group), so every tile is visited by the NG
-// workgroups of one S-slice at about the same time, and each workgroup loads
-// the 128 x 256 grouped weight of its head group once. Each of the 8 waves
+// weight-stationary. The grid holds S workgroups per head group (NG = nq +
+// nkv groups), plus helpers for the kv-head groups in the slots left over;
+// main workgroup (head group grp, lane k0) walks the 32-row tiles k0, k0 + S,
+// k0 + 2S, ..., so every tile is visited by the NG workgroups of one S-slice
+// at about the same time, and each workgroup loads the 128 x 256 grouped
+// weight of its head group once. Each of the 8 waves
 // keeps the slice of 16 output channels it multiplies in registers.
 //
 // Per tile: (A) the depthwise output of each row at its own position goes to
@@ -455,6 +456,7 @@ __device__ __forceinline__ void cca_persist_body(const CcaArgs& a, CcaSmem<T0>& 
   const int g = isk ? grp - a.nq : grp / G;       // kv head of the bundle
   const int cbase = grp * HD;                      // raw / output channel base
   const int tid = (int)threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const bool wave0 = __builtin_amdgcn_readfirstlane(wv) == 0;
   const int v = tid & 15, i = tid >> 4;            // depthwise: channel vector, tile row
   const bool use_lds_qsl = a.num_prefills > 0 && a.num_prefills + 1 <= kQslCache;
   // Value columns (v_cur copied, v_del shifted one token) are dealt over the
@@ -556,8 +558,12 @@ __device__ __forceinline__ void cca_persist_body(const CcaArgs& a, CcaSmem<T0>& 
     if constexpr (!isk) {
       if (vkind != 0) f.val = bld16_stream(vbuf, v_lane + ta * vrs32);
     }
+    // raw row i - T0 feeds only the side row before the tile's first row, so
+    // only wave 0 (rows 0-3) loads it
+    if (wave0) f.x[0] = bld16(sbuf, x_lane + ta * srs32);
+    else f.x[0] = u32x4{0, 0, 0, 0};
 #pragma unroll
-    for (int s = 0; s < NR; ++s) f.x[s] = bld16(sbuf, x_lane + (ta + s) * srs32);
+    for (int s = 1; s < NR; ++s) f.x[s] = bld16(sbuf, x_lane + (ta + s) * srs32);
     if constexpr (!isk) {
       f.r[0] = bld16(kbuf, k_lane + ta * krs32);
     } else {
@@ -789,10 +795,27 @@ __global__ __launch_bounds__(kCcaThreads, cca_waves_per_simd(T0, GMAX)) void cca
   const int lb = logical_block_cca(a);
   if (lb < 0) return;
   const int NG = a.nq + a.nkv;
-  const int grp = lb % NG, k0 = lb / NG, S = a.n_logical / NG;
   const int64_t ntiles = (a.num_tokens + kCcaMT - 1) / kCcaMT;
-  if (k0 >= ntiles) return;
-  const int my_tiles = (int)((ntiles - 1 - k0) / S + 1);
+  int grp, k0, S, my_tiles;
+  if (lb < a.n_main) {
+    // main workgroup: tiles k0, k0 + S, ... (a kv-head group's stop at
+    // kv_main_tiles when it has helpers)
+    grp = lb % NG;
+    k0 = lb / NG;
+    S = a.n_main / NG;
+    if (k0 >= ntiles) return;
+    my_tiles = (int)((ntiles - 1 - k0) / S + 1);
+    if (grp >= a.nq && a.kv_help > 0) my_tiles = min(my_tiles, a.kv_main_tiles);
+  } else {
+    // helper of a kv-head group: the tiles from kv_main_tiles * S on, dealt
+    // over the group's kv_help helpers
+    const int h = lb - a.n_main;
+    grp = a.nq + h / a.kv_help;
+    k0 = a.kv_main_tiles * (a.n_main / NG) + h % a.kv_help;
+    S = a.kv_help;
+    if (k0 >= ntiles) return;
+    my_tiles = (int)((ntiles - 1 - k0) / S + 1);
+  }
   if (grp >= a.nq) cca_persist_body<T0, GMAX, true>(a, sm, grp, k0, S, my_tiles);
   else cca_persist_body<T0, GMAX, false>(a, sm, grp, k0, S, my_tiles);
 }
@@ -824,7 +847,27 @@ hipError_t launch_cca(const CcaArgs& a, hipStream_t stream) {
     if (S < 1) S = 1;
     if (S > ntiles) S = ntiles;
     CcaArgs b = a;
-    b.n_logical = (int)(S * NG);
+    b.n_main = (int)(S * NG);
+    b.kv_help = 0;
+    b.kv_main_tiles = 0;
+    // The slots left over (resident slots minus S * NG) go to the kv-head
+    // groups, whose tiles cost more (G residual rows per lane): kv_help
+    // helpers per kv group take the tail of its tiles, and the group's main
+    // workgroups stop after kv_main_tiles, the smallest count the helpers
+    // can match. The main walk keeps one stride S for all groups, so the
+    // partners of a tile still read it at about the same time.
+    {
+      const int64_t spare = (int64_t)device_cus() * per_cu - S * NG;
+      const int64_t hp = spare / a.nkv;
+      if (hp > 0 && S >= 8) {
+        const int64_t jk = (ntiles + S + hp - 1) / (S + hp);
+        if (jk * S < ntiles) {
+          b.kv_help = (int)hp;
+          b.kv_main_tiles = (int)jk;
+        }
+      }
+    }
+    b.n_logical = b.n_main + b.kv_help * a.nkv;
     b.per_xcd = (b.n_logical + 7) / 8;
     dim3 grid((unsigned)(b.per_xcd * 8));
     const dim3 block(kCcaThreads);

@@ -27,7 +27,9 @@ struct CcaArgs {
   int64_t q_rs, k_rs, vc_rs, vd_rs, out_rs, dslot_stride, pslot_stride;
   int64_t num_tokens;
   int32_t nq, nkv, hd, t0, t1, num_slots, num_decodes, num_prefills;
-  int32_t n_logical, per_xcd;   // filled by launch_cca
+  // filled by launch_cca: workgroup count and per-XCD share, the main
+  // workgroups (S per head group), and the kv-head groups' tail split
+  int32_t n_logical, per_xcd, n_main, kv_main_tiles, kv_help;
 };
 
 hipError_t launch_cca(const CcaArgs& a, hipStream_t stream);
