@@ -12,7 +12,11 @@ __device__ __forceinline__ T zero_el() {
   else return T(0);
 }
 
-// One or more workgroups per row; `bpr` workgroups share a row.
+// One or more workgroups per row; `bpr` workgroups share a row. Each thread
+// copies up to kCopyUnroll elements per pass, all loads issued before the
+// first store so that many are in flight; the rows are streamed through
+// (nontemporal loads and stores: a row is touched once).
+constexpr int kCopyUnroll = 4;
 template <typename T, bool GATHER>
 __global__ __launch_bounds__(kBlock) void row_copy(const void* src, void* dst,
                                                    int64_t row_elems, int32_t num_slots,
@@ -29,9 +33,20 @@ __global__ __launch_bounds__(kBlock) void row_copy(const void* src, void* dst,
   const int64_t dst_row = GATHER ? row : (int64_t)s;
   const T* sp = (const T*)src + src_row * row_elems;
   T* dp = (T*)dst + dst_row * row_elems;
-  for (int64_t e = (int64_t)part * kBlock + threadIdx.x; e < row_elems;
-       e += (int64_t)bpr * kBlock) {
-    dp[e] = valid ? sp[e] : zero_el<T>();
+  const int64_t stride = (int64_t)bpr * kBlock;
+  for (int64_t e0 = (int64_t)part * kBlock + threadIdx.x; e0 < row_elems;
+       e0 += kCopyUnroll * stride) {
+    T v[kCopyUnroll];
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) {
+      const int64_t e = e0 + u * stride;
+      v[u] = (valid && e < row_elems) ? __builtin_nontemporal_load(sp + e) : zero_el<T>();
+    }
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) {
+      const int64_t e = e0 + u * stride;
+      if (e < row_elems) __builtin_nontemporal_store(v[u], dp + e);
+    }
   }
 }
 
@@ -41,7 +56,7 @@ hipError_t launch_t(bool gather, const void* src, void* dst, int64_t row_bytes,
                     int32_t num_slots, const int32_t* idx, int64_t idx_stride, int32_t n,
                     hipStream_t stream) {
   const int64_t row_elems = row_bytes / (int64_t)sizeof(T);
-  int64_t bpr = (row_elems + 4 * kBlock - 1) / (4 * kBlock);
+  int64_t bpr = (row_elems + kCopyUnroll * kBlock - 1) / (kCopyUnroll * kBlock);
   if (bpr < 1) bpr = 1;
   if (bpr > 64) bpr = 64;
   const int64_t blocks = (int64_t)n * bpr;

@@ -233,7 +233,13 @@ def test_gpu_chunked_equals_gpu_one_shot():
 
 
 @pytest.mark.parametrize("row_bytes,dtype", [(3 * 8192 * 2, np.uint16), (6, np.uint16),
-                                             (12, np.float32)])
+                                             (12, np.float32),
+                                             # 5000 16-byte pieces: 5 workgroups a row,
+                                             # a ragged last pass
+                                             (16 * 5000, np.uint16),
+                                             # 70001 pieces: 64 workgroups a row (the
+                                             # cap), two passes, ragged
+                                             (16 * 70001, np.uint16)])
 def test_state_gather_scatter(row_bytes, dtype):
     import torch
     import stateful_causal_short_amd as scs
