@@ -152,17 +152,20 @@ def check_close(gpu: np.ndarray, ref64: np.ndarray, absum: np.ndarray, dtype: st
 
 
 def run_cca_case(case, *, conv_state=None, delayed_state=None, fused=False,
-                 no_delayed_init=False):
+                 no_delayed_init=False, fused_width=None):
     """Runs a CcaCase through sc_cca_qk_conv. Returns (out, conv_state_after,
     delayed_state_after) as NumPy arrays. fused=True passes q, k, v_cur and
-    v_del as column slices of one (T, X) projection output (strided rows)."""
+    v_del as column slices of one (T, X) projection output (strided rows);
+    X = fused_width when given (else their widths + 8)."""
     import torch
     import stateful_causal_short_amd as scs
     T = case.T
     if fused:
         parts = [case.q, case.k, case.v_cur, case.v_del]
         widths = [p.shape[1] for p in parts]
-        big = np.zeros((T, sum(widths) + 8), np.uint16)
+        X = sum(widths) + 8 if fused_width is None else fused_width
+        assert X >= sum(widths)
+        big = np.zeros((T, X), np.uint16)
         off, views = 0, []
         for p_, wdt in zip(parts, widths):
             big[:, off:off + wdt] = p_

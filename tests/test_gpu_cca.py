@@ -124,6 +124,46 @@ def test_kv_head_helpers(nq, nkv, decodes, lens):
     parity(case)
 
 
+@pytest.mark.parametrize("T,path", [(65_000, "mfma"), (66_000, "one-thread")])
+def test_row_offsets_near_and_past_2gib(T, path):
+    """q, k, v_cur and v_del as column slices of one projection output with
+    32 KiB rows. At 65,000 tokens its last rows lie just under 2 GiB into the
+    buffer, where the MFMA kernel's 32-bit offsets end. At 66,000 they lie
+    past it, and the launcher takes the one-thread kernel (64-bit offsets).
+    Outputs are checked against the oracle on sampled rows (every request's
+    first and last rows, the last 64 rows of the batch, 600 random rows), and
+    the states in full."""
+    X = 16384
+    lens = [30_000, 17, T - 40 - 30_017]
+    case = synthetic.cca_case("cca_2gib", 970 + T % 7, num_decodes=40, prefill_lens=lens,
+                              num_slots=64)
+    case.prefill_h[:] = [1, 0, 1]
+    last_byte = ((T - 1) * X + case.q.shape[1] + case.k.shape[1] + 2 * case.v_cur.shape[1]) * 2
+    assert (last_byte < 2 ** 31) == (path == "mfma")
+    print(f"[gpu] cca offsets: T={T} rows of {X * 2} bytes, last byte {last_byte:,} ({path})",
+          flush=True)
+    rng = np.random.default_rng(T)
+    rows = set(range(T - 64, T)) | set(int(v) for v in rng.integers(0, T, 600))
+    starts = [0] + list(np.cumsum([1] * case.num_decodes + lens))
+    for s0 in starts[:-1]:
+        rows |= {s0, s0 + 1, s0 + 2}
+    for s1 in starts[1:]:
+        rows |= {s1 - 1, s1 - 2}
+    mask = np.zeros(T, bool)
+    mask[[r for r in rows if 0 <= r < T]] = True
+    out, cs, ds = run_cca_case(case, fused=True, fused_width=X)
+    al = []
+    ref, rcs, rds, absum = oracle.cca(case, out_dtype="f64", absum=True, row_mask=mask, allow=al)
+    np.testing.assert_array_equal(cs, rcs, err_msg="conv state not bit-exact")
+    np.testing.assert_array_equal(ds, rds, err_msg="delayed state not bit-exact")
+    C = case.C
+    np.testing.assert_array_equal(synthetic.bf16_to_f32(out[mask, C:]).astype(np.float64),
+                                  ref[mask, C:], err_msg="value half not bit-exact")
+    check_close(out[:, :C], ref[:, :C], absum[:, :C], "bf16", cca_floor_rel(case),
+                what="q/k", mask=mask, allow=al[0][:, :C])
+    print(f"[gpu] cca offsets T={T}: ok on {int(mask.sum())} rows", flush=True)
+
+
 def test_padding_slots_fused_rows_and_no_delayed_init():
     case = synthetic.cca_case("cca_pad", 801, num_decodes=6, prefill_lens=[4, 80, 1],
                               num_slots=16)
