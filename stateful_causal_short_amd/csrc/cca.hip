@@ -356,12 +356,14 @@ constexpr int kCcaRowTiles = kCcaThreads / kCcaMT;   // tiles whose row info is 
 template <int T0>
 struct CcaSmem {
   static constexpr int HD = 128, MT = kCcaMT;
-  static constexpr int AROW = HD + 8;   // bf16 LDS rows (padded)
+  // bf16 rows of the depthwise tiles, padded by 32 bytes: the MFMA B reads
+  // (16 rows x 4 16-byte pieces per instruction) then meet no bank conflict
+  static constexpr int AROW = HD + 16;
   static constexpr int RROW = HD + 4;   // fp32 residual rows (padded)
   static constexpr int T0P = (T0 + 1) & ~1;   // taps per channel in LDS: whole pairs
   uint16_t act[(MT + 1) * AROW];        // depthwise rows: row i+1 = token i, row 0 = token -1
   uint16_t prv[MT * AROW];              // depthwise one position back, for request starts
-  uint16_t ost[MT * AROW];              // staged bf16 output rows
+  uint16_t ost[MT * HD];                // staged bf16 output rows, unpadded, pieces swizzled (cca_ost)
   float res[MT * RROW];                 // residual + grouped bias, fp32, half-major (cca_hslot)
   uint16_t w1[HD * T0P];                // depthwise weights: (cca_hslot(c), c % 4, tap), taps padded to even
   float b1[HD];                         // depthwise biases, fp32, (cca_hslot(c), c % 4)
@@ -375,6 +377,14 @@ struct CcaSmem {
 // two halves of 4. Its LDS parameters and residual rows are stored by block
 // (half, v), so that the 16 lanes of a row touch one contiguous run per half.
 __device__ __forceinline__ constexpr int cca_hslot(int c) { return ((c >> 2) & 1) * 16 + (c >> 3); }
+
+// Element offset of (row r, column e) in the output staging rows: 128-element
+// rows, the 16-byte piece e / 8 stored at piece (e / 8) ^ (r % 16). The
+// epilogue writes 8 bytes per lane down 16 rows and the store reads whole
+// rows; with this swizzle neither meets more than a two-way bank conflict.
+__device__ __forceinline__ int cca_ost(int r, int e) {
+  return r * 128 + ((((e >> 3) ^ r) & 15) << 3) + (e & 7);
+}
 
 // Waves per SIMD the main kernel is compiled for: 4 (two resident 8-wave
 // workgroups per CU, so one's phase A overlaps the other's MFMA and stores)
@@ -765,11 +775,11 @@ __device__ __forceinline__ void cca_persist_body(const CcaArgs& a, CcaSmem<T0>& 
       uint2 o;
       o.x = pk_bf16(acc[th][0] + rr.x, acc[th][1] + rr.y);
       o.y = pk_bf16(acc[th][2] + rr.z, acc[th][3] + rr.w);
-      *(uint2*)(sm.ost + n * AROW + cl) = o;
+      *(uint2*)(sm.ost + cca_ost(n, cl)) = o;
     }
     __syncthreads();
     // full 256-byte row segments of the group's output columns
-    bst16_stream(obuf, ooff, *(const u32x4*)(sm.ost + i * AROW + v * 8));
+    bst16_stream(obuf, ooff, *(const u32x4*)(sm.ost + cca_ost(i, v * 8)));
   };
 
   if constexpr (AHEAD == 1) {
