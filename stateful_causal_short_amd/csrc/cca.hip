@@ -370,7 +370,7 @@ struct CcaSmem {
   float b2[HD];                         // grouped biases, fp32, same order
   int32_t qsl_s[kQslCache];
   int row_p[kCcaRowTiles][MT];          // position in the request (-1: no row), per tile of a batch
-  int row_src[kCcaRowTiles][MT];        // prefill request index, or -2 - t for decode row t
+  int row_hs[kCcaRowTiles][MT];         // saved-history slot of a row at position < T0, else -1
 };
 
 // Phase A gives a lane 8 channels v*8 .. v*8+7 of a row and computes them as
@@ -587,16 +587,25 @@ __device__ __forceinline__ void cca_persist_body(const CcaArgs& a, CcaSmem<T0>& 
   const gptr<int32_t> qsl_g = (gptr<int32_t>)a.prefill_qsl;
   // row info of tiles u0 .. u0 + kCcaRowTiles - 1: one row per thread, so the
   // searches of a whole batch run side by side once per kCcaRowTiles tiles
+  // (with the history slot of rows near a request's start: their depthwise
+  // windows reach into the saved history, and phase A then needs only the
+  // history load itself)
   auto rows_batch = [&](int u0) {
     const int j = tid / MT, ii = tid - j * MT;
-    int p = -1, src = -1;
+    int p = -1, src = -1, hs = -1;
     if (u0 + j < my_tiles) {
       const int64_t t = (int64_t)tile_ta(u0 + j) + ii;
       if (use_lds_qsl) cca_row(a, t, sm.qsl_s, rcur, p, src);
       else cca_row(a, t, qsl_g, rcur, p, src);
+      if (p >= 0 && p < T0) {
+        int32_t slot;
+        bool h;
+        cca_row_state(a, src, slot, h);
+        hs = h ? slot : -1;
+      }
     }
     sm.row_p[j][ii] = p;
-    sm.row_src[j][ii] = src;
+    sm.row_hs[j][ii] = hs;
   };
   auto tile = [&](int u, Pref& f) {
     const uint32_t ta = tile_ta(u);
@@ -607,7 +616,7 @@ __device__ __forceinline__ void cca_persist_body(const CcaArgs& a, CcaSmem<T0>& 
       __syncthreads();
     }
     const int* rp = sm.row_p[u % kCcaRowTiles];
-    const int* rsrc_ = sm.row_src[u % kCcaRowTiles];
+    const int* rhs = sm.row_hs[u % kCcaRowTiles];
     // value item of this tile, stored first (only the tile's own loads and the
     // previous tile's stores are in flight here, so its wait is short); at a
     // request's first token the state update kernel rewrites it with the saved
@@ -662,9 +671,8 @@ __device__ __forceinline__ void cca_persist_body(const CcaArgs& a, CcaSmem<T0>& 
                            [&]() { return xe(base + T0 - 1, ch); });
           } else {
             // near a request's start: the saved history (global reads, rare)
-            int32_t hslot;
-            bool hn;
-            cca_row_state(a, rsrc_[i], hslot, hn);
+            const int32_t hslot = rhs[i];
+            const bool hn = hslot >= 0;
             const uint16_t* hp = (const uint16_t*)a.conv_state +
                                  ((int64_t)(hn ? hslot : 0) * C + cbase + v * 8) * N;
             u32x4 hist[N];
