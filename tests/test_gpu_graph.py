@@ -1,5 +1,6 @@
 """The library's launches under HIP graph capture: every replay of a captured
-decode + prefill (with checkpoints) must equal the eager result bit for bit.
+decode + prefill (with checkpoints), speculative update or CCA call must equal
+the eager result bit for bit.
 Between replays the program does its own eager work (restoring the pool,
 clearing the output) and synchronises."""
 import numpy as np
@@ -95,4 +96,49 @@ def test_graph_replays_match_eager_speculative():
         torch.cuda.synchronize()
         for got, want, what in zip((host(outu), host(out), host(pool)), eager,
                                    ("uniform out", "varlen out", "pool")):
+            np.testing.assert_array_equal(got, want, err_msg=f"replay {rep} {what}")
+
+
+def test_graph_replays_match_eager_cca():
+    """The CCA call (main kernel, then the state update) under capture: a
+    batch of decodes and prefills large enough for the kv-head helpers,
+    replayed several times against the eager result, pools restored and the
+    output cleared by eager work between replays."""
+    import torch
+    import stateful_causal_short_amd as scs
+    case = synthetic.cca_case("graph_cca", 6201, num_decodes=96,
+                              prefill_lens=[2500, 1, 3100, 700, 1800], num_slots=128)
+    print(f"[gpu] graph replay cca T={case.T}", flush=True)
+    q, k, vc, vd = dev(case.q), dev(case.k), dev(case.v_cur), dev(case.v_del)
+    out = torch.zeros((case.T, case.out_width), dtype=torch.bfloat16, device="cuda")
+    cs0, ds0 = dev(case.conv_state), dev(case.delayed_state)
+    cs, ds = cs0.clone(), ds0.clone()
+    params = [dev(case.w_dw), dev(case.b_dw), dev(case.w_gr), dev(case.b_gr), dev(case.delayed_init)]
+    dsl, qsl, psl = dev(case.decode_slots), dev(case.qsl_p), dev(case.prefill_slots)
+    ph = dev(np.asarray(case.prefill_h, np.uint8))
+
+    def step():
+        scs.sc_cca_qk_conv(q, k, vc, vd, out, *params, cs, ds, dsl, qsl, psl, ph,
+                           num_q_heads=case.nq, num_kv_heads=case.nkv, head_dim=case.hd,
+                           t0=case.t0, t1=case.t1)
+
+    step()
+    torch.cuda.synchronize()
+    eager = (host(out), host(cs), host(ds))
+    g = torch.cuda.CUDAGraph()
+    cs.copy_(cs0)
+    ds.copy_(ds0)
+    out.zero_()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(3):
+        cs.copy_(cs0)
+        ds.copy_(ds0)
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for got, want, what in zip((host(out), host(cs), host(ds)), eager,
+                                   ("out", "conv state", "delayed state")):
             np.testing.assert_array_equal(got, want, err_msg=f"replay {rep} {what}")
