@@ -89,12 +89,12 @@ def test_many_short_and_empty_prefills(nq, nkv):
     parity(case)
 
 
-def kv_helper_split(T, nq, nkv, cus=256):
+def kv_helper_split(T, nq, nkv, cus=256, t0=2):
     """The launcher's tile split on a device with `cus` compute units: S main
     workgroups per head group (as many as fit resident), and for each kv-head
     group `hp` helpers taking its tiles from `jk * S` on (hp = 0: no helpers)."""
     ntiles = (T + 31) // 32
-    per_cu = 2 if nq // nkv <= 4 else 1           # t0 = 2
+    per_cu = 2 if (t0 <= 2 and nq // nkv <= 4) else 1
     NG = nq + nkv
     S = min(max(cus * per_cu // NG, 1), ntiles)
     hp = (cus * per_cu - S * NG) // nkv
@@ -105,19 +105,20 @@ def kv_helper_split(T, nq, nkv, cus=256):
     return S, 0, 0
 
 
-@pytest.mark.parametrize("nq,nkv,decodes,lens", [
-    (16, 4, 100, [1200, 3, 2000, 1697]),          # 157 tiles: helpers take 150-156
-    (4, 2, 40, [2450, 3000]),                     # 172 tiles: one helper takes 170-171
-    (8, 1, 64, [9000, 7, 10929]),                 # 625 tiles: four helpers take 560-624
+@pytest.mark.parametrize("nq,nkv,t0,decodes,lens", [
+    (16, 4, 2, 100, [1200, 3, 2000, 1697]),       # 157 tiles: helpers take 150-156
+    (4, 2, 2, 40, [2450, 3000]),                  # 172 tiles: one helper takes 170-171
+    (8, 1, 2, 64, [9000, 7, 10929]),              # 625 tiles: four helpers take 560-624
+    (16, 4, 3, 30, [4000, 1, 5669]),              # one workgroup per CU: S = 12, 4 helpers
 ])
-def test_kv_head_helpers(nq, nkv, decodes, lens):
+def test_kv_head_helpers(nq, nkv, t0, decodes, lens):
     """Batches whose tile count makes the launcher split the kv-head groups'
     tiles between their main workgroups and helpers (with a ragged share among
     the helpers), checked on every row."""
     T = decodes + sum(lens)
-    S, hp, jk = kv_helper_split(T, nq, nkv)
+    S, hp, jk = kv_helper_split(T, nq, nkv, t0=t0)
     assert hp > 0 and jk * S < (T + 31) // 32
-    case = synthetic.cca_case("cca_kvhelp", 960 + nq, nq=nq, nkv=nkv, hd=128,
+    case = synthetic.cca_case("cca_kvhelp", 960 + nq + 7 * (t0 - 2), nq=nq, nkv=nkv, hd=128, t0=t0,
                               num_decodes=decodes, prefill_lens=lens,
                               num_slots=decodes + len(lens) + 8)
     case.prefill_h[:] = 1
