@@ -237,25 +237,6 @@ __global__ __launch_bounds__(kBlock) void conv_pairs(ConvArgs a) {
   const int c0 = (cb * kBlock + (int)threadIdx.x) * VEC;
   const bool lane_ok = c0 < a.C;
 
-  // Loads in the order they are consumed (vmcnt retires in issue order).
-  // The weights do not depend on the request: issue them before the lookup.
-  uint32_t wp[NP][VEC];
-  u32x4 bsv = u32x4{0, 0, 0, 0};
-  {
-    u32x4 wv[NP * 2];
-#pragma unroll
-    for (int v = 0; v < NP * 2; ++v)
-      wv[v] = lane_ok ? ld16((const S*)a.w + (int64_t)c0 * K + v * VEC) : u32x4{0, 0, 0, 0};
-#pragma unroll
-    for (int ch = 0; ch < VEC; ++ch)
-#pragma unroll
-      for (int p = 0; p < NP; ++p) {
-        const int word = ch * NP + p;
-        wp[p][ch] = wv[word >> 2][word & 3];
-      }
-    if (a.bias && lane_ok) bsv = ld16((const S*)a.bias + c0);
-  }
-
   // chunk -> request (one round of loads below 64 requests, three from 64 on:
   // two for the request, one for its bounds), bounds and chunk range
   // (the launcher sets a.chunk = U for this kernel; U as a constant turns the
@@ -277,6 +258,27 @@ __global__ __launch_bounds__(kBlock) void conv_pairs(ConvArgs a) {
   const int t0 = j * U;
   if (t0 >= L || !lane_ok) return;
   const int t1 = min(L, t0 + U);
+
+  // Loads in the order they are consumed (vmcnt retires in issue order).
+  // The weights go out after the request lookup: ahead of it, the wait for
+  // the lookup's own load would cover them too, and a workgroup whose chunk
+  // id holds no rows would load them for nothing.
+  uint32_t wp[NP][VEC];
+  u32x4 bsv = u32x4{0, 0, 0, 0};
+  {
+    u32x4 wv[NP * 2];
+#pragma unroll
+    for (int v = 0; v < NP * 2; ++v)
+      wv[v] = lane_ok ? ld16((const S*)a.w + (int64_t)c0 * K + v * VEC) : u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int ch = 0; ch < VEC; ++ch)
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        const int word = ch * NP + p;
+        wp[p][ch] = wv[word >> 2][word & 3];
+      }
+    if (a.bias && lane_ok) bsv = ld16((const S*)a.bias + c0);
+  }
 
   const int64_t xrs = a.x_rs, ors = a.out_rs;
   const S* xb = (const S*)a.x + (int64_t)s0 * xrs + c0;

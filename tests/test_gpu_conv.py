@@ -78,12 +78,13 @@ def test_chunk_edges_and_short_requests(d):
     parity(case)
 
 
-@pytest.mark.parametrize("B", [64, 65, 129, 1000, 4096, 4097])
+@pytest.mark.parametrize("B", [63, 64, 65, 129, 256, 1000, 4095, 4096, 4097, 16129])
 @pytest.mark.parametrize("dtype,d", [("bf16", 1), ("bf16", 3), ("f32", 1)])
 def test_many_prefills_request_lookup(B, dtype, d):
     # batches of B short prefills (zero-length ones included): the chunk ->
-    # request lookup takes two rounds of loads for 64 <= B <= 4096 and counts
-    # every entry above; the bf16 prefill kernel and the fp32 one resolve it
+    # request lookup takes one round of loads below 64 requests, two for
+    # 64 <= B <= 4096 and counts every entry above; the bf16 prefill kernel
+    # and the fp32 one resolve it
     rng = np.random.default_rng(7000 + B)
     lens = rng.choice([0, 1, 2, 3, 7, 8, 9, 12, 13, 16, 17, 25], size=B)
     case = conv_case(f"many{B}", 7100 + B + d, C=256, K=4, d=d, dtype=dtype, act="silu",
