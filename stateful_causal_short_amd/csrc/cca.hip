@@ -491,18 +491,25 @@ __device__ __forceinline__ void cca_persist_body(const CcaArgs& a, CcaSmem<T0>& 
   const int64_t srs = isk ? krs : qrs;
   const int scol = ((isk ? g : grp) * HD + v * 8) * 2;    // byte column of the raw input
 
-  // ---- setup: parameters and prefill boundaries to LDS, weights to registers ----
-  if (use_lds_qsl)
-    for (int k = tid; k <= a.num_prefills; k += kCcaThreads) sm.qsl_s[k] = a.prefill_qsl[k];
-  for (int k = tid; k < HD * SM::T0P; k += kCcaThreads) {
-    const int cc = k / SM::T0P, tap = k - cc * SM::T0P;
-    sm.w1[(cca_hslot(cc) * 4 + (cc & 3)) * SM::T0P + tap] =
-        tap < T0 ? ((const uint16_t*)a.w_dw)[(int64_t)(cbase + cc) * T0 + tap] : (uint16_t)0;
+  // ---- setup: prefill boundaries and parameters (loaded here, stored to LDS
+  // once the first tile's loads are out: loads retire in issue order, so a
+  // store after each would serialise their round trips), weights to registers ----
+  static_assert(kQslCache % kCcaThreads == 0 && HD * SM::T0P <= kCcaThreads, "setup items");
+  constexpr int QPT = kQslCache / kCcaThreads;   // boundaries per thread
+  int32_t qv[QPT];
+#pragma unroll
+  for (int m = 0; m < QPT; ++m) {
+    const int k = tid + m * kCcaThreads;
+    qv[m] = use_lds_qsl && k <= a.num_prefills ? a.prefill_qsl[k] : 0;
   }
-  if (tid < HD) {
-    sm.b1[cca_hslot(tid) * 4 + (tid & 3)] = bf2f(((const uint16_t*)a.b_dw)[cbase + tid]);
-    sm.b2[cca_hslot(tid) * 4 + (tid & 3)] = bf2f(((const uint16_t*)a.b_gr)[cbase + tid]);
-  }
+  const int w1c = tid / SM::T0P, w1t = tid - w1c * SM::T0P;   // this thread's (channel, tap)
+  const uint16_t w1v = tid < HD * SM::T0P && w1t < T0
+                           ? ((const uint16_t*)a.w_dw)[(int64_t)(cbase + w1c) * T0 + w1t]
+                           : (uint16_t)0;
+  // (every thread loads a bias pair, threads from HD on a duplicate: a load
+  // under a branch would be waited for where the branch ends)
+  const uint16_t b1raw = ((const uint16_t*)a.b_dw)[cbase + (tid & (HD - 1))];
+  const uint16_t b2raw = ((const uint16_t*)a.b_gr)[cbase + (tid & (HD - 1))];
   // grouped weights of this wave's 16 output channels, K ordered b*128 + j:
   // one 32-byte run of a (C, hd, t1) row holds taps 0 and 1 of 8 channels
   bf16x8 wf[8];
@@ -790,15 +797,29 @@ __device__ __forceinline__ void cca_persist_body(const CcaArgs& a, CcaSmem<T0>& 
     bst16_stream(obuf, ooff, *(const u32x4*)(sm.ost + cca_ost(i, v * 8)));
   };
 
+  auto store_params = [&]() {
+#pragma unroll
+    for (int m = 0; m < QPT; ++m) {
+      const int k = tid + m * kCcaThreads;
+      if (use_lds_qsl && k <= a.num_prefills) sm.qsl_s[k] = qv[m];
+    }
+    if (tid < HD * SM::T0P) sm.w1[(cca_hslot(w1c) * 4 + (w1c & 3)) * SM::T0P + w1t] = w1v;
+    if (tid < HD) {
+      sm.b1[cca_hslot(tid) * 4 + (tid & 3)] = bf2f(b1raw);
+      sm.b2[cca_hslot(tid) * 4 + (tid & 3)] = bf2f(b2raw);
+    }
+  };
   if constexpr (AHEAD == 1) {
     Pref fa;
     issue(0, fa);
+    store_params();
     __syncthreads();   // qsl and parameters visible
     for (int u = 0; u < my_tiles; ++u) tile(u, fa);
   } else {
     Pref fa, fb;
     issue(0, fa);
     if (my_tiles > 1) issue(1, fb);
+    store_params();
     __syncthreads();   // qsl and parameters visible
     for (int u = 0; u < my_tiles; u += 2) {
       tile(u, fa);
