@@ -751,15 +751,14 @@ hipError_t launch_kd(const ConvArgs& a, int qc, dim3 grid, hipStream_t s) {
 }
 
 // tokens per one-pass prefill chunk for history length H (must be >= H).
-// `small` launches (tokens x channels at most kSmallLaunch on a DS pool,
-// kSmallLaunchSD on an SD pool) are bound by their ramp and drain, where
-// shorter chunks finish sooner; larger ones by bandwidth, where longer chunks
-// re-read fewer halo rows. Measured at 8192 channels on a DS pool: 8 tokens
-// won by 7.8 / 2.5 / 1.1% at 2.6k / 5.3k / 7.4k tokens, 12 by 1.8 / 3.6 / 6.8%
-// at 9.1k / 11.8k / 15.3k tokens; on an SD pool 8 won by 7.9% at 2.6k tokens
-// and lost by 1% at 7.4k.
+// `small` launches (tokens x channels at most kSmallLaunch) are bound by
+// their ramp and drain, where shorter chunks finish sooner; larger ones by
+// bandwidth, where longer chunks re-read fewer halo rows. Measured at 8192
+// channels: 8 tokens won by 7.8 / 2.5 / 1.1% at 2.6k / 5.3k / 7.4k tokens, 12
+// by 1.8 / 3.6 / 6.8% at 9.1k / 11.8k / 15.3k tokens (DS pool); with the
+// weights loaded after the request lookup, the same rule holds on an SD pool
+// (8 faster by 8% at 2.6k and 3% at 7.4k tokens, 12 by 2–6% at 15k–33k).
 constexpr int64_t kSmallLaunch = int64_t(1) << 26;
-constexpr int64_t kSmallLaunchSD = int64_t(1) << 25;
 constexpr int pairs_chunk(int H, bool small) {
   return H <= 4 ? (small ? 8 : kPairsChunkLarge) : (H <= 8 ? 8 : 16);
 }
@@ -892,7 +891,7 @@ hipError_t launch_conv(ConvArgs a, int dtype, int K, int D, bool silu_act, bool 
                     (!fuse || pairs_ok);
   // the one-pass kernel takes its halo from x: its chunk covers H by construction
   const bool pairs = fast && pairs_ok;
-  const bool small = (int64_t)a.num_tokens * a.C <= (a.sd ? kSmallLaunchSD : kSmallLaunch);
+  const bool small = (int64_t)a.num_tokens * a.C <= kSmallLaunch;
   a.chunk = pairs ? pairs_chunk(H, small) : fast ? kChunk : (H > kChunk ? H : kChunk);
   int qc = 0;
   if (fast && uniform && (a.q == 1 || a.q == 2 || a.q == 4) && a.q <= a.chunk) qc = a.q;
